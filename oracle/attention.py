@@ -1,0 +1,75 @@
+"""Paged decode attention, as its plain definition, in float64.
+
+Paging only changes where the keys and values live: the model still sees each
+sequence as contiguous (chester-dev.com "vLLM transforme la mémoire GPU …",
+section on PagedAttention and the logical/physical split; deeplearn.tn
+"PagedAttention : comment optimiser la mémoire GPU …", block-table section), and
+the kernel gathers the physical blocks through the table (deepsonar
+"PagedAttention de vLLM …", §2.2 and §2.6).  So the oracle reassembles each
+sequence's K and V in logical order and runs textbook softmax attention for its
+one query per head.
+
+Readings: query head h uses KV head h // (Hq / Hkv) (consecutive groups share a
+KV head; §2.1 of the deepsonar page has 64 query heads sharing 8 KV heads);
+scores are scale x (q . k) with no mask beyond the context length.
+"""
+import numpy as np
+
+from .lowp import storage_bits_to_f64
+from .pool import gather_sequence
+
+
+def dense_decode(q, k, v, scale):
+    """One sequence: q[Hq][d], k/v[ctx][Hkv][d] float64 -> out[Hq][d]."""
+    hq, hkv = q.shape[0], k.shape[1]
+    if hq % hkv:
+        raise ValueError("query heads must be a multiple of KV heads")
+    group = hq // hkv
+    out = np.empty_like(q, dtype=np.float64)
+    for h in range(hq):
+        g = h // group
+        z = float(scale) * (k[:, g, :] @ q[h])
+        w = np.exp(z - z.max())
+        out[h] = (w @ v[:, g, :]) / w.sum()
+    return out
+
+
+def paged_decode(q, k_pool, v_pool, tables, context_lens, scale, dtype, block_size, seqs=None):
+    """q: float64 [B][Hq][d] (already the values of the rounded storage type).
+
+    tables[b] lists sequence b's physical blocks in logical order; context_lens[b]
+    is its number of tokens.  Returns float64 [B][Hq][d]; with `seqs` given, only
+    those batch rows are computed (the others are NaN).
+    """
+    q = np.asarray(q, dtype=np.float64)
+    out = np.full(q.shape, np.nan)
+    rows = range(q.shape[0]) if seqs is None else seqs
+    for b in rows:
+        L = int(context_lens[b])
+        if L < 1:
+            raise ValueError("context length must be >= 1")
+        kb, vb = gather_sequence(k_pool, v_pool, tables[b], L, block_size)
+        k = storage_bits_to_f64(kb, dtype)
+        v = storage_bits_to_f64(vb, dtype)
+        out[b] = dense_decode(q[b], k, v, scale)
+    return out
+
+
+def partial_state(z, v):
+    """Softmax state of one slice of tokens: (max score, sum of weights, weighted V)."""
+    m = z.max()
+    w = np.exp(z - m)
+    return m, w.sum(), w @ v
+
+
+def lse_merge(states):
+    """Combine slice states into the softmax-weighted mean over all their tokens.
+
+    Each slice's weights are relative to its own maximum; rescaling every slice to
+    the overall maximum makes them comparable, then the weighted sums add up
+    (the incremental softmax of deeplearn.tn, PagedAttention vs. FlashAttention).
+    """
+    big_m = max(s[0] for s in states)
+    num = sum(np.exp(m - big_m) * acc for m, _, acc in states)
+    den = sum(np.exp(m - big_m) * l for m, l, _ in states)
+    return num / den
