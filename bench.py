@@ -1,0 +1,231 @@
+#!/usr/bin/env python3
+"""Decode-step benchmark of the paged KV cache on one MI355X.
+
+A step is one pass of the decode hot path over one batch already resident in HBM:
+  reshape_and_cache  (write each sequence's new token into its slot)
+  paged attention    (partition kernel over 512-token partitions)
+  partition merge    (log-sum-exp reduce of multi-partition sequences)
+for the GQA workload of 128 sequences, 64 query heads over 8 KV heads, head_dim 128,
+bf16 KV, 16-token blocks scattered through a pool 1.25x the need, context lengths
+lognormal around 2048 (capped at 8192).  The host allocator's work for the step
+(slot reservation) happens before timing; the step re-writes the same slots, so every
+step is the same work.
+
+Prints one JSON line: decode KV GB/s over the whole step (algorithmic bytes / step
+time), seq-tokens/s, the partition kernel against the HBM roofline (HIP events on the
+launch stream), and the CPU oracle timed on the host cores as a baseline.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", type=int, default=3, help="workload 1..5 (default 3: GQA 72B shape)")
+    ap.add_argument("--partition-tokens", type=int, default=512)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="bound on the oracle's timed CPU work")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+def attention_bytes(lens, nblocks, w, out_elem):
+    kv = int(lens.sum()) * 2 * w.num_kv_heads * w.head_dim * w.elem_bytes
+    q = len(lens) * w.num_q_heads * w.head_dim * w.elem_bytes
+    out = len(lens) * w.num_q_heads * w.head_dim * out_elem
+    return kv, kv + q + out + 4 * int(nblocks) + 4 * len(lens)
+
+
+def cpu_baseline(w, seconds):
+    """The oracle's attention on the same workload, timed on the host cores over a
+    bounded prefix of the batch (pool build and input rounding are not timed)."""
+    import numpy as np
+    from oracle import replay as oreplay
+    from oracle.attention import paged_decode
+    from oracle.lowp import to_storage_bits, storage_bits_to_f64
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    except Exception:
+        blas_threads = None
+    log("[bench] cpu baseline: oracle replay (untimed)")
+    r = oreplay.run(w, compute_attention=False)
+    attends = w.attend_ops()
+    qidx = attends[-1][2]
+    tables, lens = r.tables[-1], r.context_lens[-1]
+    q = storage_bits_to_f64(to_storage_bits(w.q[qidx], w.dtype), w.dtype)
+    done, kv_bytes = 0, 0
+    t0 = time.perf_counter()
+    while done < len(lens) and time.perf_counter() - t0 < seconds:
+        paged_decode(q, r.k_pool, r.v_pool, tables, lens, w.scale, w.dtype, w.block_size,
+                     seqs=[done])
+        kv_bytes += int(lens[done]) * 2 * w.num_kv_heads * w.head_dim * w.elem_bytes
+        done += 1
+    dt = time.perf_counter() - t0
+    cores = len(os.sched_getaffinity(0))
+    return {
+        "value": round(kv_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": cores,
+        "blas_threads": blas_threads, "kind": "oracle",
+        "seq_tokens_per_s": round(done / dt, 3),
+        "sample": f"fp64 NumPy oracle attention for the first {done} of {len(lens)} sequences "
+                  f"of the same step ({int(lens[:done].sum())} context tokens), {dt:.1f} s",
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(the path shards by sequence or KV head with no exchange, but this build "
+              "measures a single MI355X)", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+    import workloads as W
+    from paged_kv_cache_15_amd import binding as B
+    from paged_kv_cache_15_amd.cache import PagedKVCache, TORCH_DTYPES
+    from paged_kv_cache_15_amd.replay import to_device
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    log(f"[bench] building workload {args.config}")
+    w = W.make_config(args.config)
+    cache = PagedKVCache(w.num_blocks, w.num_kv_heads, w.head_dim, w.dtype, w.block_size,
+                         w.free_order, device=dev)
+    last_append = last_attend = None
+    t_host = 0.0
+    for op in w.ops:
+        if op[0] == "create":
+            cache.create()
+        elif op[0] == "fork":
+            cache.fork(op[1])
+        elif op[0] == "free":
+            cache.free(op[1])
+        elif op[0] == "append":
+            k, v = w.kv[op[3]]
+            kd, vd = to_device(k, w.dtype, dev), to_device(v, w.dtype, dev)
+            t0 = time.perf_counter()
+            slots, copies = B.paged_kv_append_batch(cache.pool, op[1], op[2])
+            t_host = time.perf_counter() - t0
+            if len(copies):
+                pairs = torch.from_numpy(np.ascontiguousarray(copies)).to(dev)
+                B.paged_kv_copy_blocks(cache.desc, cache.k_pool, cache.v_pool, pairs, len(copies))
+            slot_d = torch.from_numpy(slots).to(dev)
+            B.reshape_and_cache(cache.desc, kd, vd, cache.k_pool, cache.v_pool, slot_d)
+            last_append = (kd, vd, slot_d, len(op[1]))
+        elif op[0] == "attend":
+            last_attend = op
+    torch.cuda.synchronize()
+    new_k, new_v, slot_d, n_app = last_append
+    seqs, qidx = last_attend[1], last_attend[2]
+    tables, lens = cache.block_tables(seqs)
+    nb_total = int((tables >= 0).sum())
+    tables_d = torch.from_numpy(tables).to(dev)
+    lens_d = torch.from_numpy(lens).to(dev)
+    q = to_device(w.q[qidx], w.dtype, dev)
+    out_dtype = w.dtype
+    out = torch.empty((len(seqs), w.num_q_heads, w.head_dim), dtype=TORCH_DTYPES[out_dtype], device=dev)
+    max_ctx = int(lens.max())
+    pt = args.partition_tokens
+    ws_bytes = B.paged_attention_workspace_bytes(len(seqs), w.num_q_heads, w.head_dim, max_ctx, pt)
+    ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step(ev=None):
+        B.reshape_and_cache(cache.desc, new_k, new_v, cache.k_pool, cache.v_pool, slot_d,
+                            stream=stream)
+        if ev is not None:
+            ev[0].record(stream)
+        B.paged_attention_partition(cache.desc, out, out_dtype, q, cache.k_pool, cache.v_pool,
+                                    tables_d, lens_d, w.num_q_heads, max_ctx, float(w.scale), pt,
+                                    ws, stream)
+        if ev is not None:
+            ev[1].record(stream)
+        B.paged_attention_reduce(cache.desc, out, out_dtype, lens_d, w.num_q_heads, max_ctx, pt,
+                                 ws, stream)
+        if ev is not None:
+            ev[2].record(stream)
+
+    log(f"[bench] warmup {args.warmup} steps")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    log(f"[bench] timing {args.steps} steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        starts[i].record(stream)
+        step(evs[i])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    part_ms = sum(evs[i][0].elapsed_time(evs[i][1]) for i in range(args.steps)) / args.steps
+    red_ms = sum(evs[i][1].elapsed_time(evs[i][2]) for i in range(args.steps)) / args.steps
+    rac_ms = sum(starts[i].elapsed_time(evs[i][0]) for i in range(args.steps)) / args.steps
+    ms_per_step = elapsed * 1e3 / args.steps
+
+    kv_bytes, attn_bytes = attention_bytes(lens, nb_total, w, out.element_size())
+    write_bytes = 2 * 2 * n_app * w.num_kv_heads * w.head_dim * w.elem_bytes + 4 * n_app
+    step_bytes = attn_bytes + write_bytes
+    value = step_bytes / (ms_per_step * 1e-3) / 1e9
+    achieved = attn_bytes / (part_ms * 1e-3) / 1e9
+    res = {
+        "metric": "decode KV GB/s (% of HBM peak) + seq-tokens/s, paged attention, 1 MI355X",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded N(0,1) q/k/v, seeded lengths and pool permutation)",
+        "config": {
+            "workload": w.name,
+            "batch": len(seqs), "q_heads": w.num_q_heads, "kv_heads": w.num_kv_heads,
+            "head_dim": w.head_dim, "block_size": w.block_size, "kv_dtype": w.dtype,
+            "context_tokens": int(lens.sum()), "max_context": max_ctx,
+            "partition_tokens": pt, "pool_blocks": w.num_blocks, "parallelism": "single GPU",
+        },
+        "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
+        "seq_tokens_per_s": round(len(seqs) / (ms_per_step * 1e-3), 1),
+        "kv_bytes_per_step": kv_bytes,
+        "step_bytes": step_bytes,
+        "kernel_ms": {"reshape_and_cache": round(rac_ms, 5), "paged_attention_partition": round(part_ms, 5),
+                      "paged_attention_reduce": round(red_ms, 5)},
+        "host_alloc_ms_per_step": round(t_host * 1e3, 4),
+        "roofline": {
+            "kernel": "paged_attention_partition",
+            "bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+            "algorithmic_bytes_per_launch": attn_bytes,
+        },
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        del new_k, new_v
+        res["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

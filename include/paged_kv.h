@@ -1,0 +1,258 @@
+/*
+ * paged_kv.h — C ABI of libpagedkv.so: a paged KV cache and its decode attention
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * Sources of the method (cited by page title and section):
+ *   [DS]  deepsonar.com.cn, "PagedAttention de vLLM : comment la gestion de la VRAM
+ *         soutient l'inférence des grands modèles" (§2.1 KV bytes; §2.2 blocks, block
+ *         table, on-demand allocation; §2.3 reference counts and copy-on-write; §2.4
+ *         free-block queue; §2.6 the block table handed to the attention kernel;
+ *         §VII minimal skeleton).
+ *   [CD]  chester-dev.com, "vLLM transforme la mémoire GPU en système d'exploitation
+ *         pour LLM" (section on PagedAttention turning history into reusable blocks:
+ *         logical order kept, physical placement scattered).
+ *   [DL]  deeplearn.tn, "PagedAttention : comment optimiser la mémoire GPU lors de
+ *         l'inférence des LLM" (worked allocation example with block size 4; the
+ *         block-table section; PagedAttention vs. FlashAttention: tiles in on-chip
+ *         memory with an incremental softmax).
+ *
+ * Conventions for every entry point:
+ *   - Returns a paged_kv_status; never throws, never aborts.  On failure nothing is
+ *     launched and host state is unchanged unless the entry point says otherwise;
+ *     paged_kv_last_error() then describes the failure (thread-local string).
+ *   - "device" pointers are HIP device memory owned by the caller unless stated;
+ *     "host" pointers are ordinary process memory.  The library keeps no pointer
+ *     to caller memory after a call returns, except the pool buffers handed to
+ *     paged_kv_pool_create.
+ *   - Device work is enqueued on `stream` (a hipStream_t passed as void*; NULL is the
+ *     null stream) and is asynchronous: no call on the decode path synchronises the
+ *     device.
+ *   - A pool object is not thread-safe; calls on distinct pools may run concurrently.
+ *
+ * Memory layout of the KV pool (the pages leave it open; this is the library's):
+ *   X = 16 / element bytes (8 for fp16/bf16, 4 for fp32); BS = block size.
+ *   K pool: [num_blocks][num_kv_heads][head_dim / X][BS][X]
+ *   V pool: [num_blocks][num_kv_heads][head_dim][BS]
+ *   Element d of the key (value) of the token in slot `slot` = block * BS + offset,
+ *   KV head h, is K[block][h][d / X][offset][d % X] (V[block][h][d][offset]).
+ *   One (block, KV head) tile of K or of V is BS * head_dim contiguous elements.
+ */
+#ifndef PAGED_KV_H
+#define PAGED_KV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    PAGED_KV_OK = 0,
+    PAGED_KV_ERR_INVALID_ARG = 1,     /* null pointer, bad size, unsupported shape value */
+    PAGED_KV_ERR_OUT_OF_BLOCKS = 2,   /* the free queue cannot supply the blocks needed */
+    PAGED_KV_ERR_UNSUPPORTED = 3,     /* valid request this build has no kernel for */
+    PAGED_KV_ERR_HIP = 4,             /* a HIP runtime call failed */
+    PAGED_KV_ERR_NO_SUCH_SEQ = 5,     /* unknown or released sequence id */
+    PAGED_KV_ERR_BUFFER_TOO_SMALL = 6 /* caller buffer (copies list, workspace) too small */
+} paged_kv_status;
+
+typedef enum { PAGED_KV_F32 = 0, PAGED_KV_F16 = 1, PAGED_KV_BF16 = 2 } paged_kv_dtype;
+
+/* Pool shape.  block_size: tokens per block (any >= 1 for the allocator; 16 for the
+ * device kernels, [DS] §2.2 "often 16 tokens").  dtype: element type of K and V (and
+ * of the queries given to paged_attention_decode). */
+typedef struct {
+    int32_t num_blocks;
+    int32_t block_size;
+    int32_t num_kv_heads;
+    int32_t head_dim;
+    int32_t dtype;      /* paged_kv_dtype */
+    int32_t flags;      /* PAGED_KV_POOL_* bits */
+} paged_kv_pool_desc;
+
+/* Allocator only: no device memory is allocated or referenced by the pool object. */
+#define PAGED_KV_POOL_HOST_ONLY 1
+
+typedef struct paged_kv_pool paged_kv_pool; /* opaque host-side object */
+
+/* ---------------------------------------------------------------- misc ---- */
+
+/* Message for a status code (static string). */
+const char* paged_kv_status_string(paged_kv_status status);
+
+/* Detail of the last failure on the calling thread ("" if none). */
+const char* paged_kv_last_error(void);
+
+/* [DS] §2.1: KV-cache bytes per token = 2 (K and V) x layers x KV heads x head dim x
+ * bytes per element.  Returns 0 if any argument is negative. */
+uint64_t paged_kv_bytes_per_token(int32_t layers, int32_t kv_heads, int32_t head_dim,
+                                  int32_t dtype_bytes);
+
+/* Bytes of one pool (K or V) for `desc`: num_blocks * num_kv_heads * block_size *
+ * head_dim * element bytes.  0 if desc is invalid. */
+size_t paged_kv_pool_bytes(const paged_kv_pool_desc* desc);
+
+/* ------------------------------------------------------- pool + allocator ---- */
+
+/* [DS] §2.2, §VII step 1: carve the KV memory into desc->num_blocks fixed-size blocks.
+ *   free_order  host int32[num_blocks], a permutation of 0..num_blocks-1: the initial
+ *               free-queue order, head first ([DS] §2.4: allocation takes the head).
+ *               NULL = 0, 1, ..., num_blocks-1.
+ *   k_pool, v_pool  device buffers of paged_kv_pool_bytes(desc) bytes each, owned by
+ *               the caller and left untouched; or both NULL: the library allocates
+ *               them (hipMalloc, contents set to all-ones bytes, i.e. NaN) and frees
+ *               them in paged_kv_pool_destroy.  Ignored with PAGED_KV_POOL_HOST_ONLY.
+ *   out         receives the pool object.
+ * Errors: INVALID_ARG (sizes < 1, head_dim not a multiple of X, bad dtype, free_order
+ * not a permutation, exactly one of k_pool/v_pool NULL), HIP (allocation failed). */
+paged_kv_status paged_kv_pool_create(const paged_kv_pool_desc* desc, const int32_t* free_order,
+                                     void* k_pool, void* v_pool, paged_kv_pool** out);
+
+/* Release the pool object (and the buffers it allocated itself).  NULL is a no-op. */
+void paged_kv_pool_destroy(paged_kv_pool* pool);
+
+/* The pool's device buffers (NULL, NULL for a host-only pool) and its descriptor. */
+paged_kv_status paged_kv_pool_buffers(const paged_kv_pool* pool, void** k_pool, void** v_pool);
+paged_kv_status paged_kv_pool_get_desc(const paged_kv_pool* pool, paged_kv_pool_desc* desc);
+
+/* New empty sequence.  Ids are 0, 1, 2, ... in create/fork order, never reused. */
+paged_kv_status paged_kv_seq_create(paged_kv_pool* pool, int32_t* seq_id);
+
+/* [DS] §2.3: new sequence sharing every block of `parent`; each shared block's
+ * reference count goes up by one.  No block is copied here. */
+paged_kv_status paged_kv_seq_fork(paged_kv_pool* pool, int32_t parent, int32_t* child);
+
+/* [DS] §2.2, §2.3, §VII steps 2-3; [DL] worked example.  Reserve slots for n_tokens
+ * new tokens of `seq`, in order.  A block is taken from the head of the free queue
+ * only when the token lands at offset 0 of a new block.  If the sequence's last block
+ * is partly filled and shared (count > 1), it is first copied to a fresh block: the
+ * (source, destination) pair is reported and the sequence's table points at the copy.
+ *   slots_out   host int32[n_tokens]: slot = physical block * block_size + offset.
+ *   copies_out  host int32[2 * max_copies]: (src, dst) pairs, to be applied with
+ *               paged_kv_copy_blocks before the new tokens are written (at most 1).
+ *   n_copies    receives the number of pairs written.
+ * Errors: NO_SUCH_SEQ; INVALID_ARG (n_tokens < 0, null outputs); OUT_OF_BLOCKS and
+ * BUFFER_TOO_SMALL leave the allocator exactly as it was. */
+paged_kv_status paged_kv_seq_append(paged_kv_pool* pool, int32_t seq, int32_t n_tokens,
+                                    int32_t* slots_out, int32_t* copies_out, int32_t max_copies,
+                                    int32_t* n_copies);
+
+/* paged_kv_seq_append over several sequences, in order (one decode step appends one
+ * token to each).  slots_out: host int32[sum(counts)] grouped by sequence in input
+ * order; copies_out: host int32[2 * max_copies].  Stops at the first sequence that
+ * fails: *n_done receives the number of sequences fully appended (their appends
+ * stay); the failing one and those after it are unchanged. */
+paged_kv_status paged_kv_append_batch(paged_kv_pool* pool, const int32_t* seqs,
+                                      const int32_t* counts, int32_t n_seqs, int32_t* slots_out,
+                                      int32_t* copies_out, int32_t max_copies, int32_t* n_copies,
+                                      int32_t* n_done);
+
+/* Release a sequence (finished, cancelled or preempted): its blocks, in logical order,
+ * lose one reference; each block reaching zero goes to the tail of the free queue. */
+paged_kv_status paged_kv_seq_free(paged_kv_pool* pool, int32_t seq);
+
+/* [DS] §2.6: the block table handed to the attention kernel.  Writes host
+ * int32 tables_out[n][max_blocks] (physical ids in logical order, padded with -1)
+ * and host int32 context_lens_out[n] (tokens written).  INVALID_ARG if a table does
+ * not fit max_blocks. */
+paged_kv_status paged_kv_block_tables(const paged_kv_pool* pool, const int32_t* seq_ids,
+                                      int32_t n, int32_t max_blocks, int32_t* tables_out,
+                                      int32_t* context_lens_out);
+
+/* Tokens and blocks of one sequence. */
+paged_kv_status paged_kv_seq_info(const paged_kv_pool* pool, int32_t seq, int32_t* context_len,
+                                  int32_t* num_blocks);
+
+/* Reference count of a physical block (0 = free). */
+paged_kv_status paged_kv_block_refcount(const paged_kv_pool* pool, int32_t block,
+                                        int32_t* refcount);
+
+/* Pool occupancy: free blocks, used blocks, and reserved-but-empty slots summed over
+ * live sequences (block_size * blocks - tokens, < block_size per sequence: [DS] §2.2). */
+paged_kv_status paged_kv_stats(const paged_kv_pool* pool, int64_t* num_free, int64_t* num_used,
+                               int64_t* waste_slots);
+
+/* ------------------------------------------------------------ device ops ---- */
+
+/* [DS] §2.3: copy-on-write copies.  For each of the n pairs (device int32[n][2],
+ * (src, dst)), block dst of both pools becomes a copy of block src (all heads, all
+ * slots).  Pairs with an id outside [0, num_blocks) are skipped.  Destinations must be
+ * distinct and must not be sources in the same call.  n == 0 launches nothing. */
+paged_kv_status paged_kv_copy_blocks(const paged_kv_pool_desc* desc, void* k_pool, void* v_pool,
+                                     const int32_t* pairs, int32_t n, void* stream);
+
+/* Write each new token's key and value into its slot ([DS] §2.2; [DL] worked example).
+ *   key, value   device, element type desc->dtype, [num_tokens][num_kv_heads][head_dim]
+ *                with token stride key_stride / value_stride elements (>= heads*dim;
+ *                heads and dims contiguous).
+ *   slot_mapping device int32[num_tokens]; -1 = padding, not written; slots outside
+ *                [0, num_blocks * block_size) are not written either.
+ * Layout of the destination: see the top of this file.  Requires block_size 16 and
+ * head_dim a multiple of X.  num_tokens == 0 launches nothing.  Two tokens with one
+ * slot in a call: the surviving value is unspecified. */
+paged_kv_status reshape_and_cache(const paged_kv_pool_desc* desc, const void* key,
+                                  const void* value, int64_t key_stride, int64_t value_stride,
+                                  void* k_pool, void* v_pool, const int32_t* slot_mapping,
+                                  int32_t num_tokens, void* stream);
+
+/* Bytes of workspace paged_attention_decode needs (0 when no sequence can span more
+ * than one partition).  partition_tokens 0 = the default (512). */
+size_t paged_attention_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
+                                       int32_t max_context_len, int32_t partition_tokens);
+
+/* Paged decode attention ([DS] §2.2, §2.6; [CD]; [DL] PagedAttention vs.
+ * FlashAttention): for every sequence s and query head h,
+ *   out[s][h] = sum_t softmax_t(scale * q[s][h] . k_t) v_t  over the context_lens[s]
+ * tokens of s, read through its block table; query head h uses KV head
+ * h / (num_q_heads / num_kv_heads).
+ *   out           device [num_seqs][num_q_heads][head_dim], type out_dtype (desc->dtype
+ *                 or PAGED_KV_F32)
+ *   q             device [num_seqs][num_q_heads][head_dim], type desc->dtype
+ *   k_pool/v_pool device pools (layout above)
+ *   block_tables  device int32[num_seqs][max_blocks_per_seq]; entries past a
+ *                 sequence's last block are never read
+ *   context_lens  device int32[num_seqs]
+ *   max_context_len  host bound on every context_lens[s] (sizes the launch)
+ *   partition_tokens tokens per split-K partition (multiple of 16; 0 = 512).  Sequences
+ *                 longer than one partition are reduced by a log-sum-exp merge.
+ *   workspace     device buffer of paged_attention_workspace_bytes(...) bytes
+ *                 (may be NULL when that is 0); contents on entry are ignored.
+ * A sequence whose context_len is outside [1, max_context_len], or whose table holds
+ * an id outside [0, num_blocks) below its length, gets NaN outputs; nothing outside
+ * the buffers is read.  Requires block_size 16, head_dim 64 or 128,
+ * num_q_heads % num_kv_heads == 0 and a group of at most 16 query heads.
+ * Results do not depend on where blocks sit in the pool, nor on whether a block is
+ * shared: the summation order follows logical token positions only. */
+paged_kv_status paged_attention_decode(const paged_kv_pool_desc* desc, void* out, int32_t out_dtype,
+                                       const void* q, const void* k_pool, const void* v_pool,
+                                       const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                       const int32_t* context_lens, int32_t num_seqs,
+                                       int32_t num_q_heads, int32_t max_context_len, float scale,
+                                       int32_t partition_tokens, void* workspace,
+                                       size_t workspace_bytes, void* stream);
+
+/* The two launches paged_attention_decode makes, exposed separately so each kernel
+ * can be timed on its own.  paged_attention_partition writes `out` for sequences that
+ * fit one partition and the per-partition (max, sum, weighted values) state of the
+ * others into `workspace`; paged_attention_reduce merges that state into `out`.
+ * Arguments as for paged_attention_decode. */
+paged_kv_status paged_attention_partition(const paged_kv_pool_desc* desc, void* out,
+                                          int32_t out_dtype, const void* q, const void* k_pool,
+                                          const void* v_pool, const int32_t* block_tables,
+                                          int32_t max_blocks_per_seq, const int32_t* context_lens,
+                                          int32_t num_seqs, int32_t num_q_heads,
+                                          int32_t max_context_len, float scale,
+                                          int32_t partition_tokens, void* workspace,
+                                          size_t workspace_bytes, void* stream);
+paged_kv_status paged_attention_reduce(const paged_kv_pool_desc* desc, void* out, int32_t out_dtype,
+                                       const int32_t* context_lens, int32_t num_seqs,
+                                       int32_t num_q_heads, int32_t max_context_len,
+                                       int32_t partition_tokens, const void* workspace,
+                                       size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGED_KV_H */

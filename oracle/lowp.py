@@ -18,15 +18,20 @@ def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
     bfloat16 keeps the top 16 bits of the float32 pattern.  Adding 0x7FFF plus
     the lowest kept bit to the full pattern and truncating rounds to nearest
     with ties going to the even kept pattern.  NaNs stay NaN (quiet bit set).
+    (Only NaN patterns can wrap around 2**32 in the addition.)
     """
     x = np.ascontiguousarray(x, dtype=np.float32)
-    bits = x.view(np.uint32).astype(np.uint64)
-    keep_lsb = (bits >> 16) & 1
-    rounded = ((bits + 0x7FFF + keep_lsb) >> 16).astype(np.uint16)
+    bits = x.view(np.uint32)
+    t = bits >> 16
+    t &= 1
+    t += 0x7FFF
+    t += bits
+    t >>= 16
+    rounded = t.astype(np.uint16)
     is_nan = (bits & 0x7FFFFFFF) > 0x7F800000
     if np.any(is_nan):
-        rounded = np.where(is_nan, ((bits >> 16) | 0x0040).astype(np.uint16), rounded)
-    return rounded.astype(np.uint16)
+        rounded[is_nan] = ((bits[is_nan] >> 16) | 0x0040).astype(np.uint16)
+    return rounded
 
 
 def bf16_bits_to_f64(b: np.ndarray) -> np.ndarray:
@@ -44,7 +49,12 @@ def to_storage_bits(x: np.ndarray, dtype: str) -> np.ndarray:
         # numpy's float32 -> float16 conversion rounds to nearest even
         return x.astype(np.float16).view(np.uint16)
     if dtype == "bf16":
-        return f32_to_bf16_bits(x)
+        flat = x.reshape(-1)
+        out = np.empty(flat.shape, dtype=np.uint16)
+        step = 1 << 20            # cache-sized pieces; the result is the same
+        for i in range(0, flat.size, step):
+            out[i:i + step] = f32_to_bf16_bits(flat[i:i + step])
+        return out.reshape(x.shape)
     raise ValueError(dtype)
 
 

@@ -1,0 +1,338 @@
+"""ctypes binding of libpagedkv.so (include/paged_kv.h), argument marshalling only.
+
+Every function here has the name of the C entry point it calls.  Device buffers
+may be given as torch tensors (their data pointer is passed) or as raw integer
+addresses; streams as torch streams, raw hipStream_t addresses, or None for
+torch's current stream.  A non-OK status raises PagedKVError carrying the
+library's message.  There is no CPU fallback: if the library is not built, importing
+this module fails.
+"""
+import ctypes
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libpagedkv.so")
+
+PAGED_KV_OK = 0
+PAGED_KV_ERR_INVALID_ARG = 1
+PAGED_KV_ERR_OUT_OF_BLOCKS = 2
+PAGED_KV_ERR_UNSUPPORTED = 3
+PAGED_KV_ERR_HIP = 4
+PAGED_KV_ERR_NO_SUCH_SEQ = 5
+PAGED_KV_ERR_BUFFER_TOO_SMALL = 6
+
+PAGED_KV_F32, PAGED_KV_F16, PAGED_KV_BF16 = 0, 1, 2
+PAGED_KV_POOL_HOST_ONLY = 1
+DTYPE_CODES = {"f32": PAGED_KV_F32, "f16": PAGED_KV_F16, "bf16": PAGED_KV_BF16}
+
+
+class PagedKVError(RuntimeError):
+    def __init__(self, func, status, message):
+        super().__init__(f"{func}: {message} (status {status})")
+        self.status = status
+
+
+class paged_kv_pool_desc(ctypes.Structure):
+    _fields_ = [("num_blocks", ctypes.c_int32), ("block_size", ctypes.c_int32),
+                ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("dtype", ctypes.c_int32), ("flags", ctypes.c_int32)]
+
+
+def make_desc(num_blocks, block_size, num_kv_heads, head_dim, dtype, flags=0):
+    if isinstance(dtype, str):
+        dtype = DTYPE_CODES[dtype]
+    return paged_kv_pool_desc(int(num_blocks), int(block_size), int(num_kv_heads), int(head_dim),
+                              int(dtype), int(flags))
+
+
+_i32p = ctypes.POINTER(ctypes.c_int32)
+_i64p = ctypes.POINTER(ctypes.c_int64)
+_vp = ctypes.c_void_p
+_descp = ctypes.POINTER(paged_kv_pool_desc)
+_i32, _i64, _f32, _sz = ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
+
+_SIGNATURES = {
+    "paged_kv_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "paged_kv_last_error": (ctypes.c_char_p, []),
+    "paged_kv_bytes_per_token": (ctypes.c_uint64, [_i32, _i32, _i32, _i32]),
+    "paged_kv_pool_bytes": (_sz, [_descp]),
+    "paged_kv_pool_create": (ctypes.c_int, [_descp, _i32p, _vp, _vp, ctypes.POINTER(_vp)]),
+    "paged_kv_pool_destroy": (None, [_vp]),
+    "paged_kv_pool_buffers": (ctypes.c_int, [_vp, ctypes.POINTER(_vp), ctypes.POINTER(_vp)]),
+    "paged_kv_pool_get_desc": (ctypes.c_int, [_vp, _descp]),
+    "paged_kv_seq_create": (ctypes.c_int, [_vp, _i32p]),
+    "paged_kv_seq_fork": (ctypes.c_int, [_vp, _i32, _i32p]),
+    "paged_kv_seq_append": (ctypes.c_int, [_vp, _i32, _i32, _i32p, _i32p, _i32, _i32p]),
+    "paged_kv_append_batch": (ctypes.c_int, [_vp, _i32p, _i32p, _i32, _i32p, _i32p, _i32, _i32p,
+                                             _i32p]),
+    "paged_kv_seq_free": (ctypes.c_int, [_vp, _i32]),
+    "paged_kv_block_tables": (ctypes.c_int, [_vp, _i32p, _i32, _i32, _i32p, _i32p]),
+    "paged_kv_seq_info": (ctypes.c_int, [_vp, _i32, _i32p, _i32p]),
+    "paged_kv_block_refcount": (ctypes.c_int, [_vp, _i32, _i32p]),
+    "paged_kv_stats": (ctypes.c_int, [_vp, _i64p, _i64p, _i64p]),
+    "paged_kv_copy_blocks": (ctypes.c_int, [_descp, _vp, _vp, _vp, _i32, _vp]),
+    "reshape_and_cache": (ctypes.c_int, [_descp, _vp, _vp, _i64, _i64, _vp, _vp, _vp, _i32, _vp]),
+    "paged_attention_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32]),
+    "paged_attention_decode": (ctypes.c_int, [_descp, _vp, _i32, _vp, _vp, _vp, _vp, _i32, _vp,
+                                              _i32, _i32, _i32, _f32, _i32, _vp, _sz, _vp]),
+    "paged_attention_partition": (ctypes.c_int, [_descp, _vp, _i32, _vp, _vp, _vp, _vp, _i32, _vp,
+                                                 _i32, _i32, _i32, _f32, _i32, _vp, _sz, _vp]),
+    "paged_attention_reduce": (ctypes.c_int, [_descp, _vp, _i32, _vp, _i32, _i32, _i32, _i32, _vp,
+                                              _sz, _vp]),
+}
+
+
+def _load():
+    # The library must share torch's HIP runtime (torch's streams and device pointers
+    # are only valid there).  torch ships its own libamdhip64 with the same soname;
+    # loading torch first makes the dynamic linker bind libpagedkv.so to that copy
+    # instead of bringing a second HIP runtime into the process.
+    import torch  # noqa: F401
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built (python -m paged_kv_cache_15_amd.build); "
+                          "this package has no fallback implementation")
+    lib = ctypes.CDLL(LIB_PATH)
+    for name, (res, args) in _SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    return lib
+
+
+lib = _load()
+EXPORTED = tuple(_SIGNATURES)
+
+
+def _check(func, status):
+    if status != PAGED_KV_OK:
+        msg = lib.paged_kv_last_error().decode() or lib.paged_kv_status_string(status).decode()
+        raise PagedKVError(func, status, msg)
+
+
+def _ptr(x):
+    """Device or host address of a torch tensor / numpy array / int / None."""
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    if hasattr(x, "data_ptr"):
+        return x.data_ptr()
+    if isinstance(x, np.ndarray):
+        return x.ctypes.data
+    raise TypeError(f"cannot take the address of {type(x)}")
+
+
+def _stream(s):
+    if s is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(s, int):
+        return s
+    return s.cuda_stream
+
+
+def _i32_array(a):
+    a = np.ascontiguousarray(a, dtype=np.int32)
+    return a, a.ctypes.data_as(_i32p)
+
+
+# ------------------------------------------------------------------ misc ----
+def paged_kv_status_string(status):
+    return lib.paged_kv_status_string(status).decode()
+
+
+def paged_kv_last_error():
+    return lib.paged_kv_last_error().decode()
+
+
+def paged_kv_bytes_per_token(layers, kv_heads, head_dim, dtype_bytes):
+    return int(lib.paged_kv_bytes_per_token(layers, kv_heads, head_dim, dtype_bytes))
+
+
+def paged_kv_pool_bytes(desc):
+    return int(lib.paged_kv_pool_bytes(ctypes.byref(desc)))
+
+
+# -------------------------------------------------------- pool + allocator ----
+def paged_kv_pool_create(desc, free_order=None, k_pool=None, v_pool=None):
+    """Returns an opaque pool handle (int).  free_order: host int sequence or None."""
+    handle = _vp()
+    if free_order is not None:
+        arr, p = _i32_array(free_order)
+    else:
+        arr, p = None, None
+    _check("paged_kv_pool_create",
+           lib.paged_kv_pool_create(ctypes.byref(desc), p, _ptr(k_pool), _ptr(v_pool),
+                                    ctypes.byref(handle)))
+    return handle.value
+
+
+def paged_kv_pool_destroy(pool):
+    lib.paged_kv_pool_destroy(pool)
+
+
+def paged_kv_pool_buffers(pool):
+    k, v = _vp(), _vp()
+    _check("paged_kv_pool_buffers", lib.paged_kv_pool_buffers(pool, ctypes.byref(k), ctypes.byref(v)))
+    return k.value, v.value
+
+
+def paged_kv_pool_get_desc(pool):
+    d = paged_kv_pool_desc()
+    _check("paged_kv_pool_get_desc", lib.paged_kv_pool_get_desc(pool, ctypes.byref(d)))
+    return d
+
+
+def paged_kv_seq_create(pool):
+    sid = ctypes.c_int32()
+    _check("paged_kv_seq_create", lib.paged_kv_seq_create(pool, ctypes.byref(sid)))
+    return sid.value
+
+
+def paged_kv_seq_fork(pool, parent):
+    sid = ctypes.c_int32()
+    _check("paged_kv_seq_fork", lib.paged_kv_seq_fork(pool, parent, ctypes.byref(sid)))
+    return sid.value
+
+
+def paged_kv_seq_append(pool, seq, n_tokens):
+    """Returns (slots int32[n], copies int32[k][2])."""
+    slots = np.empty(max(n_tokens, 0), dtype=np.int32)
+    copies = np.empty(2, dtype=np.int32)
+    nc = ctypes.c_int32()
+    _check("paged_kv_seq_append",
+           lib.paged_kv_seq_append(pool, seq, n_tokens, slots.ctypes.data_as(_i32p),
+                                   copies.ctypes.data_as(_i32p), 1, ctypes.byref(nc)))
+    return slots, copies[:2 * nc.value].reshape(-1, 2)
+
+
+def paged_kv_append_batch(pool, seqs, counts):
+    """Returns (slots int32[sum(counts)], copies int32[k][2]).  On failure the
+    raised error carries .n_done (sequences appended before the failing one)."""
+    s_arr, s_p = _i32_array(seqs)
+    c_arr, c_p = _i32_array(counts)
+    slots = np.empty(int(c_arr.sum()), dtype=np.int32)
+    copies = np.empty(2 * max(1, len(s_arr)), dtype=np.int32)
+    nc, nd = ctypes.c_int32(), ctypes.c_int32()
+    st = lib.paged_kv_append_batch(pool, s_p, c_p, len(s_arr), slots.ctypes.data_as(_i32p),
+                                   copies.ctypes.data_as(_i32p), len(s_arr), ctypes.byref(nc),
+                                   ctypes.byref(nd))
+    try:
+        _check("paged_kv_append_batch", st)
+    except PagedKVError as e:
+        e.n_done = nd.value
+        raise
+    return slots, copies[:2 * nc.value].reshape(-1, 2)
+
+
+def paged_kv_seq_free(pool, seq):
+    _check("paged_kv_seq_free", lib.paged_kv_seq_free(pool, seq))
+
+
+def paged_kv_block_tables(pool, seq_ids, max_blocks=None):
+    """Returns (tables int32[n][max_blocks] padded with -1, context_lens int32[n])."""
+    ids, ids_p = _i32_array(seq_ids)
+    if max_blocks is None:
+        max_blocks = max([paged_kv_seq_info(pool, int(s))[1] for s in ids] + [1])
+    tables = np.empty((len(ids), max_blocks), dtype=np.int32)
+    lens = np.empty(len(ids), dtype=np.int32)
+    _check("paged_kv_block_tables",
+           lib.paged_kv_block_tables(pool, ids_p, len(ids), max_blocks,
+                                     tables.ctypes.data_as(_i32p), lens.ctypes.data_as(_i32p)))
+    return tables, lens
+
+
+def paged_kv_seq_info(pool, seq):
+    """Returns (context_len, num_blocks)."""
+    L, nb = ctypes.c_int32(), ctypes.c_int32()
+    _check("paged_kv_seq_info", lib.paged_kv_seq_info(pool, seq, ctypes.byref(L), ctypes.byref(nb)))
+    return L.value, nb.value
+
+
+def paged_kv_block_refcount(pool, block):
+    rc = ctypes.c_int32()
+    _check("paged_kv_block_refcount", lib.paged_kv_block_refcount(pool, block, ctypes.byref(rc)))
+    return rc.value
+
+
+def paged_kv_stats(pool):
+    """Returns (num_free, num_used, waste_slots)."""
+    f, u, w = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int64()
+    _check("paged_kv_stats", lib.paged_kv_stats(pool, ctypes.byref(f), ctypes.byref(u), ctypes.byref(w)))
+    return f.value, u.value, w.value
+
+
+# ------------------------------------------------------------ device ops ----
+def paged_kv_copy_blocks(desc, k_pool, v_pool, pairs, n, stream=None):
+    _check("paged_kv_copy_blocks",
+           lib.paged_kv_copy_blocks(ctypes.byref(desc), _ptr(k_pool), _ptr(v_pool), _ptr(pairs),
+                                    int(n), _stream(stream)))
+
+
+def reshape_and_cache(desc, key, value, k_pool, v_pool, slot_mapping, num_tokens=None,
+                      key_stride=None, value_stride=None, stream=None):
+    """key/value: [T][Hkv][d] tensors (token stride taken from the tensor unless given)."""
+    if num_tokens is None:
+        num_tokens = key.shape[0]
+    if key_stride is None:
+        key_stride = key.stride(0)
+    if value_stride is None:
+        value_stride = value.stride(0)
+    _check("reshape_and_cache",
+           lib.reshape_and_cache(ctypes.byref(desc), _ptr(key), _ptr(value), int(key_stride),
+                                 int(value_stride), _ptr(k_pool), _ptr(v_pool), _ptr(slot_mapping),
+                                 int(num_tokens), _stream(stream)))
+
+
+def paged_attention_workspace_bytes(num_seqs, num_q_heads, head_dim, max_context_len,
+                                    partition_tokens=0):
+    return int(lib.paged_attention_workspace_bytes(num_seqs, num_q_heads, head_dim,
+                                                   max_context_len, partition_tokens))
+
+
+def _attn_args(desc, out, out_dtype, q, k_pool, v_pool, block_tables, context_lens,
+               num_q_heads, max_context_len, scale, partition_tokens, workspace, stream):
+    if isinstance(out_dtype, str):
+        out_dtype = DTYPE_CODES[out_dtype]
+    ws_bytes = 0 if workspace is None else (workspace.numel() * workspace.element_size()
+                                            if hasattr(workspace, "numel") else 0)
+    return (ctypes.byref(desc), _ptr(out), int(out_dtype), _ptr(q), _ptr(k_pool), _ptr(v_pool),
+            _ptr(block_tables), int(block_tables.shape[1]), _ptr(context_lens),
+            int(context_lens.shape[0]), int(num_q_heads), int(max_context_len), float(scale),
+            int(partition_tokens), _ptr(workspace), ws_bytes, _stream(stream))
+
+
+def paged_attention_decode(desc, out, out_dtype, q, k_pool, v_pool, block_tables, context_lens,
+                           num_q_heads, max_context_len, scale, partition_tokens=0,
+                           workspace=None, stream=None):
+    """block_tables: int32 [B][max_blocks] device tensor; context_lens: int32 [B] device."""
+    _check("paged_attention_decode",
+           lib.paged_attention_decode(*_attn_args(desc, out, out_dtype, q, k_pool, v_pool,
+                                                  block_tables, context_lens, num_q_heads,
+                                                  max_context_len, scale, partition_tokens,
+                                                  workspace, stream)))
+
+
+def paged_attention_partition(desc, out, out_dtype, q, k_pool, v_pool, block_tables, context_lens,
+                              num_q_heads, max_context_len, scale, partition_tokens=0,
+                              workspace=None, stream=None):
+    _check("paged_attention_partition",
+           lib.paged_attention_partition(*_attn_args(desc, out, out_dtype, q, k_pool, v_pool,
+                                                     block_tables, context_lens, num_q_heads,
+                                                     max_context_len, scale, partition_tokens,
+                                                     workspace, stream)))
+
+
+def paged_attention_reduce(desc, out, out_dtype, context_lens, num_q_heads, max_context_len,
+                           partition_tokens=0, workspace=None, stream=None):
+    if isinstance(out_dtype, str):
+        out_dtype = DTYPE_CODES[out_dtype]
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check("paged_attention_reduce",
+           lib.paged_attention_reduce(ctypes.byref(desc), _ptr(out), int(out_dtype),
+                                      _ptr(context_lens), int(context_lens.shape[0]),
+                                      int(num_q_heads), int(max_context_len),
+                                      int(partition_tokens), _ptr(workspace), ws_bytes,
+                                      _stream(stream)))

@@ -1,0 +1,94 @@
+"""One decode step on the paged KV cache, driven from the host.
+
+A step (deepsonar "PagedAttention de vLLM …" §2.2 and §2.6; deeplearn.tn
+"PagedAttention : comment optimiser la mémoire GPU …", continuous batching) is:
+  1. the host allocator reserves a slot for each new token (taking a block only when
+     the previous one is full, copying a shared partial block first);
+  2. copy-on-write copies and the cache write run on the GPU;
+  3. the block tables go to the GPU and paged attention reads the pool through them.
+Every arithmetic step runs in libpagedkv.so; this module only moves arguments.
+The pool buffers are torch tensors owned by this object (PyTorch provides device
+memory and streams; the library never allocates them).
+"""
+import numpy as np
+import torch
+
+from . import binding as B
+
+TORCH_DTYPES = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
+BITS_DTYPES = {"f32": torch.int32, "f16": torch.int16, "bf16": torch.int16}
+
+
+class PagedKVCache:
+    def __init__(self, num_blocks, num_kv_heads, head_dim, dtype, block_size=16, free_order=None,
+                 device="cuda", poison=True):
+        self.dtype = dtype
+        self.device = torch.device(device)
+        self.desc = B.make_desc(num_blocks, block_size, num_kv_heads, head_dim, dtype)
+        x = 16 // torch.tensor([], dtype=TORCH_DTYPES[dtype]).element_size()
+        tdt = TORCH_DTYPES[dtype]
+        self.k_pool = torch.empty((num_blocks, num_kv_heads, head_dim // x, block_size, x),
+                                  dtype=tdt, device=self.device)
+        self.v_pool = torch.empty((num_blocks, num_kv_heads, head_dim, block_size), dtype=tdt,
+                                  device=self.device)
+        if poison:   # all-ones bytes: NaN in every supported type
+            self.k_pool.view(BITS_DTYPES[dtype]).fill_(-1)
+            self.v_pool.view(BITS_DTYPES[dtype]).fill_(-1)
+        self.pool = B.paged_kv_pool_create(self.desc, free_order, self.k_pool, self.v_pool)
+
+    def close(self):
+        if self.pool:
+            B.paged_kv_pool_destroy(self.pool)
+            self.pool = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    # -- allocator ---------------------------------------------------------
+    def create(self):
+        return B.paged_kv_seq_create(self.pool)
+
+    def fork(self, parent):
+        return B.paged_kv_seq_fork(self.pool, parent)
+
+    def free(self, seq):
+        B.paged_kv_seq_free(self.pool, seq)
+
+    def stats(self):
+        return B.paged_kv_stats(self.pool)
+
+    def block_tables(self, seqs, max_blocks=None):
+        return B.paged_kv_block_tables(self.pool, seqs, max_blocks)
+
+    # -- steps -------------------------------------------------------------
+    def append(self, seqs, counts, key, value, stream=None):
+        """Reserve slots for counts[i] new tokens of seqs[i], then copy shared tail
+        blocks and write key/value ([sum(counts)][Hkv][d] device tensors) into them.
+        Returns the host slot mapping and copy pairs."""
+        slots, copies = B.paged_kv_append_batch(self.pool, seqs, counts)
+        if len(copies):
+            pairs = torch.from_numpy(np.ascontiguousarray(copies)).to(self.device)
+            B.paged_kv_copy_blocks(self.desc, self.k_pool, self.v_pool, pairs, len(copies), stream)
+        if len(slots):
+            slot_d = torch.from_numpy(slots).to(self.device)
+            B.reshape_and_cache(self.desc, key, value, self.k_pool, self.v_pool, slot_d,
+                                stream=stream)
+        return slots, copies
+
+    def attend(self, seqs, q, scale, out_dtype=None, partition_tokens=0, stream=None):
+        """Decode attention of q ([len(seqs)][Hq][d] device tensor) over the sequences."""
+        tables, lens = self.block_tables(seqs)
+        out_dtype = out_dtype or self.dtype
+        max_ctx = int(lens.max()) if len(lens) else 1
+        tables_d = torch.from_numpy(tables).to(self.device)
+        lens_d = torch.from_numpy(lens).to(self.device)
+        hq, d = q.shape[1], q.shape[2]
+        out = torch.empty((len(seqs), hq, d), dtype=TORCH_DTYPES[out_dtype], device=self.device)
+        nbytes = B.paged_attention_workspace_bytes(len(seqs), hq, d, max_ctx, partition_tokens)
+        ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=self.device) if nbytes else None
+        B.paged_attention_decode(self.desc, out, out_dtype, q, self.k_pool, self.v_pool, tables_d,
+                                 lens_d, hq, max_ctx, scale, partition_tokens, ws, stream)
+        return out, tables, lens

@@ -1,0 +1,403 @@
+// Host block allocator of the paged KV cache and the pool object behind the C ABI.
+//
+// What it implements (deepsonar "PagedAttention de vLLM …"):
+//   §2.2  fixed-size physical blocks, a per-sequence table from logical to physical
+//         block, a new block only once the previous one is full;
+//   §2.3  reference counts on shared blocks, copy before writing into a shared one;
+//   §2.4  a FIFO free-block queue: allocation pops the head, release pushes the tail.
+// deeplearn.tn "PagedAttention : comment optimiser la mémoire GPU …", worked example:
+// the token that overflows a full block lands at offset 0 of a newly taken block.
+//
+// Readings where the pages are silent: the initial queue order is caller input;
+// released blocks go back in logical order; a copy-on-write copies a whole block and
+// the last holder writes in place; a failed append changes nothing; sequence ids are
+// sequential and never reused.
+
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <deque>
+#include <vector>
+
+#include "common.h"
+
+namespace pkv {
+
+static thread_local std::string g_last_error;
+
+void set_error(const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof(buf), fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+}
+
+void clear_error() { g_last_error.clear(); }
+
+bool valid_desc(const paged_kv_pool_desc* d) {
+    if (!d) { set_error("null pool descriptor"); return false; }
+    if (d->num_blocks < 1 || d->block_size < 1 || d->num_kv_heads < 1 || d->head_dim < 1) {
+        set_error("pool sizes must be >= 1 (blocks %d, block_size %d, kv_heads %d, head_dim %d)",
+                  d->num_blocks, d->block_size, d->num_kv_heads, d->head_dim);
+        return false;
+    }
+    int eb = elem_bytes(d->dtype);
+    if (!eb) { set_error("unknown dtype %d", d->dtype); return false; }
+    if ((d->head_dim * eb) % 16) {
+        set_error("head_dim %d is not a multiple of the 16-byte chunk", d->head_dim);
+        return false;
+    }
+    if ((int64_t)d->num_blocks * d->block_size > INT32_MAX) {
+        set_error("num_blocks * block_size does not fit an int32 slot id");
+        return false;
+    }
+    return true;
+}
+
+bool kernel_desc(const paged_kv_pool_desc* d, bool attention) {
+    if (!valid_desc(d)) return false;
+    if (d->block_size != kKernelBlockSize) {
+        set_error("device kernels need block_size %d (got %d)", kKernelBlockSize, d->block_size);
+        return false;
+    }
+    if (attention && d->head_dim != 64 && d->head_dim != 128) {
+        set_error("attention kernels support head_dim 64 and 128 (got %d)", d->head_dim);
+        return false;
+    }
+    return true;
+}
+
+}  // namespace pkv
+
+using namespace pkv;
+
+struct Sequence {
+    bool alive = false;
+    int32_t length = 0;
+    std::vector<int32_t> table;
+};
+
+struct paged_kv_pool {
+    paged_kv_pool_desc desc{};
+    void* k = nullptr;
+    void* v = nullptr;
+    bool owns_buffers = false;
+    std::deque<int32_t> free_queue;
+    std::vector<int32_t> refcount;
+    std::vector<Sequence> seqs;
+};
+
+static Sequence* find_seq(paged_kv_pool* p, int32_t id) {
+    if (!p || id < 0 || (size_t)id >= p->seqs.size() || !p->seqs[id].alive) return nullptr;
+    return &p->seqs[id];
+}
+
+static const Sequence* find_seq(const paged_kv_pool* p, int32_t id) {
+    return find_seq(const_cast<paged_kv_pool*>(p), id);
+}
+
+extern "C" {
+
+const char* paged_kv_status_string(paged_kv_status s) {
+    switch (s) {
+        case PAGED_KV_OK: return "ok";
+        case PAGED_KV_ERR_INVALID_ARG: return "invalid argument";
+        case PAGED_KV_ERR_OUT_OF_BLOCKS: return "out of blocks";
+        case PAGED_KV_ERR_UNSUPPORTED: return "unsupported";
+        case PAGED_KV_ERR_HIP: return "HIP runtime error";
+        case PAGED_KV_ERR_NO_SUCH_SEQ: return "no such sequence";
+        case PAGED_KV_ERR_BUFFER_TOO_SMALL: return "buffer too small";
+    }
+    return "unknown status";
+}
+
+const char* paged_kv_last_error(void) { return g_last_error.c_str(); }
+
+uint64_t paged_kv_bytes_per_token(int32_t layers, int32_t kv_heads, int32_t head_dim,
+                                  int32_t dtype_bytes) {
+    if (layers < 0 || kv_heads < 0 || head_dim < 0 || dtype_bytes < 0) return 0;
+    return 2ull * (uint64_t)layers * (uint64_t)kv_heads * (uint64_t)head_dim *
+           (uint64_t)dtype_bytes;
+}
+
+size_t paged_kv_pool_bytes(const paged_kv_pool_desc* d) {
+    if (!valid_desc(d)) return 0;
+    return (size_t)d->num_blocks * d->num_kv_heads * d->block_size * d->head_dim *
+           elem_bytes(d->dtype);
+}
+
+paged_kv_status paged_kv_pool_create(const paged_kv_pool_desc* desc, const int32_t* free_order,
+                                     void* k_pool, void* v_pool, paged_kv_pool** out) {
+    clear_error();
+    if (!out) { set_error("null output pointer"); return PAGED_KV_ERR_INVALID_ARG; }
+    *out = nullptr;
+    if (!valid_desc(desc)) return PAGED_KV_ERR_INVALID_ARG;
+    const bool host_only = desc->flags & PAGED_KV_POOL_HOST_ONLY;
+    if (!host_only && ((k_pool == nullptr) != (v_pool == nullptr))) {
+        set_error("give both k_pool and v_pool, or neither");
+        return PAGED_KV_ERR_INVALID_ARG;
+    }
+    const int32_t nb = desc->num_blocks;
+    std::vector<int32_t> order(nb);
+    if (free_order) {
+        std::vector<char> seen(nb, 0);
+        for (int32_t i = 0; i < nb; ++i) {
+            int32_t b = free_order[i];
+            if (b < 0 || b >= nb || seen[b]) {
+                set_error("free_order is not a permutation of 0..%d (entry %d = %d)", nb - 1, i, b);
+                return PAGED_KV_ERR_INVALID_ARG;
+            }
+            seen[b] = 1;
+            order[i] = b;
+        }
+    } else {
+        for (int32_t i = 0; i < nb; ++i) order[i] = i;
+    }
+    auto* p = new paged_kv_pool();
+    p->desc = *desc;
+    p->free_queue.assign(order.begin(), order.end());
+    p->refcount.assign(nb, 0);
+    if (!host_only) {
+        if (k_pool) {
+            p->k = k_pool;
+            p->v = v_pool;
+        } else {
+            size_t bytes = paged_kv_pool_bytes(desc);
+            hipError_t e1 = hipMalloc(&p->k, bytes);
+            hipError_t e2 = e1 == hipSuccess ? hipMalloc(&p->v, bytes) : e1;
+            if (e1 == hipSuccess && e2 == hipSuccess) {
+                e1 = hipMemset(p->k, 0xFF, bytes);
+                e2 = e1 == hipSuccess ? hipMemset(p->v, 0xFF, bytes) : e1;
+            }
+            if (e1 != hipSuccess || e2 != hipSuccess) {
+                set_error("pool allocation of 2 x %zu bytes failed: %s", bytes,
+                          hipGetErrorString(e1 != hipSuccess ? e1 : e2));
+                if (p->k) (void)hipFree(p->k);
+                if (p->v) (void)hipFree(p->v);
+                delete p;
+                return PAGED_KV_ERR_HIP;
+            }
+            p->owns_buffers = true;
+        }
+    }
+    *out = p;
+    return PAGED_KV_OK;
+}
+
+void paged_kv_pool_destroy(paged_kv_pool* p) {
+    if (!p) return;
+    if (p->owns_buffers) {
+        (void)hipFree(p->k);
+        (void)hipFree(p->v);
+    }
+    delete p;
+}
+
+paged_kv_status paged_kv_pool_buffers(const paged_kv_pool* p, void** k, void** v) {
+    clear_error();
+    if (!p || !k || !v) { set_error("null argument"); return PAGED_KV_ERR_INVALID_ARG; }
+    *k = p->k;
+    *v = p->v;
+    return PAGED_KV_OK;
+}
+
+paged_kv_status paged_kv_pool_get_desc(const paged_kv_pool* p, paged_kv_pool_desc* d) {
+    clear_error();
+    if (!p || !d) { set_error("null argument"); return PAGED_KV_ERR_INVALID_ARG; }
+    *d = p->desc;
+    return PAGED_KV_OK;
+}
+
+paged_kv_status paged_kv_seq_create(paged_kv_pool* p, int32_t* seq_id) {
+    clear_error();
+    if (!p || !seq_id) { set_error("null argument"); return PAGED_KV_ERR_INVALID_ARG; }
+    if (p->seqs.size() >= (size_t)INT32_MAX) { set_error("sequence ids exhausted"); return PAGED_KV_ERR_INVALID_ARG; }
+    p->seqs.emplace_back();
+    p->seqs.back().alive = true;
+    *seq_id = (int32_t)p->seqs.size() - 1;
+    return PAGED_KV_OK;
+}
+
+paged_kv_status paged_kv_seq_fork(paged_kv_pool* p, int32_t parent, int32_t* child) {
+    clear_error();
+    if (!p || !child) { set_error("null argument"); return PAGED_KV_ERR_INVALID_ARG; }
+    const Sequence* par = find_seq(p, parent);
+    if (!par) { set_error("no live sequence %d", parent); return PAGED_KV_ERR_NO_SUCH_SEQ; }
+    Sequence s;
+    s.alive = true;
+    s.length = par->length;
+    s.table = par->table;
+    for (int32_t b : s.table) p->refcount[b] += 1;
+    p->seqs.push_back(std::move(s));     // may reallocate: `par` is not used after this
+    *child = (int32_t)p->seqs.size() - 1;
+    return PAGED_KV_OK;
+}
+
+// Blocks an append of n tokens takes from the queue, and whether it copies the tail.
+static int64_t blocks_needed(const paged_kv_pool* p, const Sequence& s, int32_t n, bool* cow) {
+    const int64_t bs = p->desc.block_size, len = s.length;
+    int64_t fresh = (len + n + bs - 1) / bs - (len + bs - 1) / bs;   // offsets 0 in [len, len+n)
+    *cow = n > 0 && (len % bs) != 0 && p->refcount[s.table.back()] > 1;
+    return fresh + (*cow ? 1 : 0);
+}
+
+static paged_kv_status append_one(paged_kv_pool* p, int32_t seq, int32_t n, int32_t* slots_out,
+                                  int32_t* copies_out, int32_t max_copies, int32_t* n_copies) {
+    Sequence* s = find_seq(p, seq);
+    if (!s) { set_error("no live sequence %d", seq); return PAGED_KV_ERR_NO_SUCH_SEQ; }
+    if (n < 0) { set_error("n_tokens %d < 0", n); return PAGED_KV_ERR_INVALID_ARG; }
+    if ((int64_t)s->length + n > INT32_MAX) { set_error("sequence length overflow"); return PAGED_KV_ERR_INVALID_ARG; }
+    bool cow = false;
+    int64_t need = blocks_needed(p, *s, n, &cow);
+    if (need > (int64_t)p->free_queue.size()) {
+        set_error("sequence %d needs %lld blocks, %zu free", seq, (long long)need,
+                  p->free_queue.size());
+        return PAGED_KV_ERR_OUT_OF_BLOCKS;
+    }
+    if (cow && max_copies < 1) {
+        set_error("append of sequence %d copies a shared block; copies buffer holds %d pairs",
+                  seq, max_copies);
+        return PAGED_KV_ERR_BUFFER_TOO_SMALL;
+    }
+    *n_copies = 0;
+    const int32_t bs = p->desc.block_size;
+    if (cow) {
+        int32_t src = s->table.back();
+        int32_t dst = p->free_queue.front();
+        p->free_queue.pop_front();
+        p->refcount[src] -= 1;
+        p->refcount[dst] = 1;
+        s->table.back() = dst;
+        copies_out[0] = src;
+        copies_out[1] = dst;
+        *n_copies = 1;
+    }
+    for (int32_t i = 0; i < n; ++i) {
+        int32_t pos = s->length;
+        if (pos % bs == 0) {
+            int32_t b = p->free_queue.front();
+            p->free_queue.pop_front();
+            p->refcount[b] = 1;
+            s->table.push_back(b);
+        }
+        slots_out[i] = s->table[pos / bs] * bs + pos % bs;
+        s->length = pos + 1;
+    }
+    return PAGED_KV_OK;
+}
+
+paged_kv_status paged_kv_seq_append(paged_kv_pool* p, int32_t seq, int32_t n_tokens,
+                                    int32_t* slots_out, int32_t* copies_out, int32_t max_copies,
+                                    int32_t* n_copies) {
+    clear_error();
+    if (!p || !n_copies || (n_tokens > 0 && !slots_out) || (max_copies > 0 && !copies_out)) {
+        set_error("null argument");
+        return PAGED_KV_ERR_INVALID_ARG;
+    }
+    *n_copies = 0;
+    return append_one(p, seq, n_tokens, slots_out, copies_out, max_copies, n_copies);
+}
+
+paged_kv_status paged_kv_append_batch(paged_kv_pool* p, const int32_t* seqs, const int32_t* counts,
+                                      int32_t n_seqs, int32_t* slots_out, int32_t* copies_out,
+                                      int32_t max_copies, int32_t* n_copies, int32_t* n_done) {
+    clear_error();
+    if (!p || !n_copies || !n_done || n_seqs < 0 || (n_seqs > 0 && (!seqs || !counts)) ||
+        (max_copies > 0 && !copies_out)) {
+        set_error("null or invalid argument");
+        return PAGED_KV_ERR_INVALID_ARG;
+    }
+    *n_copies = 0;
+    *n_done = 0;
+    int64_t slot_pos = 0;
+    for (int32_t i = 0; i < n_seqs; ++i) {
+        if (counts[i] > 0 && !slots_out) { set_error("null slots_out"); return PAGED_KV_ERR_INVALID_ARG; }
+        int32_t nc = 0;
+        paged_kv_status st = append_one(p, seqs[i], counts[i], slots_out ? slots_out + slot_pos : nullptr,
+                                        copies_out ? copies_out + 2 * (*n_copies) : nullptr,
+                                        max_copies - *n_copies, &nc);
+        if (st != PAGED_KV_OK) return st;
+        slot_pos += counts[i];
+        *n_copies += nc;
+        *n_done = i + 1;
+    }
+    return PAGED_KV_OK;
+}
+
+paged_kv_status paged_kv_seq_free(paged_kv_pool* p, int32_t seq) {
+    clear_error();
+    Sequence* s = find_seq(p, seq);
+    if (!s) { set_error("no live sequence %d", seq); return PAGED_KV_ERR_NO_SUCH_SEQ; }
+    for (int32_t b : s->table) {
+        if (--p->refcount[b] == 0) p->free_queue.push_back(b);
+    }
+    s->alive = false;
+    s->length = 0;
+    std::vector<int32_t>().swap(s->table);
+    return PAGED_KV_OK;
+}
+
+paged_kv_status paged_kv_block_tables(const paged_kv_pool* p, const int32_t* ids, int32_t n,
+                                      int32_t max_blocks, int32_t* tables_out,
+                                      int32_t* lens_out) {
+    clear_error();
+    if (!p || n < 0 || max_blocks < 0 || (n > 0 && (!ids || !lens_out || (max_blocks > 0 && !tables_out)))) {
+        set_error("null or invalid argument");
+        return PAGED_KV_ERR_INVALID_ARG;
+    }
+    for (int32_t i = 0; i < n; ++i) {
+        const Sequence* s = find_seq(p, ids[i]);
+        if (!s) { set_error("no live sequence %d", ids[i]); return PAGED_KV_ERR_NO_SUCH_SEQ; }
+        if ((int64_t)s->table.size() > max_blocks) {
+            set_error("sequence %d has %zu blocks, table width %d", ids[i], s->table.size(), max_blocks);
+            return PAGED_KV_ERR_INVALID_ARG;
+        }
+    }
+    for (int32_t i = 0; i < n; ++i) {
+        const Sequence* s = find_seq(p, ids[i]);
+        int32_t* row = tables_out + (int64_t)i * max_blocks;
+        int32_t j = 0;
+        for (; j < (int32_t)s->table.size(); ++j) row[j] = s->table[j];
+        for (; j < max_blocks; ++j) row[j] = -1;
+        lens_out[i] = s->length;
+    }
+    return PAGED_KV_OK;
+}
+
+paged_kv_status paged_kv_seq_info(const paged_kv_pool* p, int32_t seq, int32_t* len,
+                                  int32_t* nblocks) {
+    clear_error();
+    if (!len || !nblocks) { set_error("null argument"); return PAGED_KV_ERR_INVALID_ARG; }
+    const Sequence* s = find_seq(p, seq);
+    if (!s) { set_error("no live sequence %d", seq); return PAGED_KV_ERR_NO_SUCH_SEQ; }
+    *len = s->length;
+    *nblocks = (int32_t)s->table.size();
+    return PAGED_KV_OK;
+}
+
+paged_kv_status paged_kv_block_refcount(const paged_kv_pool* p, int32_t block, int32_t* rc) {
+    clear_error();
+    if (!p || !rc || block < 0 || block >= p->desc.num_blocks) {
+        set_error("null argument or block %d out of range", block);
+        return PAGED_KV_ERR_INVALID_ARG;
+    }
+    *rc = p->refcount[block];
+    return PAGED_KV_OK;
+}
+
+paged_kv_status paged_kv_stats(const paged_kv_pool* p, int64_t* num_free, int64_t* num_used,
+                               int64_t* waste) {
+    clear_error();
+    if (!p || !num_free || !num_used || !waste) { set_error("null argument"); return PAGED_KV_ERR_INVALID_ARG; }
+    *num_free = (int64_t)p->free_queue.size();
+    *num_used = p->desc.num_blocks - *num_free;
+    int64_t w = 0;
+    for (const Sequence& s : p->seqs)
+        if (s.alive) w += (int64_t)p->desc.block_size * (int64_t)s.table.size() - s.length;
+    *waste = w;
+    return PAGED_KV_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,776 @@
+// Paged decode attention for gfx950: split-K partition kernels and the merge kernel.
+//
+// What is computed (deepsonar "PagedAttention de vLLM …" §2.2 and §2.6; chester-dev
+// "vLLM transforme la mémoire GPU …", PagedAttention section): one query per head per
+// sequence attends over that sequence's tokens, whose K/V blocks are gathered from
+// anywhere in the pool through the block table.  How (deeplearn.tn "PagedAttention :
+// comment optimiser la mémoire GPU …", PagedAttention vs. FlashAttention): tiles of K
+// and V are brought on chip and reduced with an incremental softmax, so nothing of
+// size context x heads goes back to HBM.
+//
+// Work decomposition: one workgroup of 4 wave64s per (sequence, KV head, partition of
+// `partition_tokens` tokens).  Wave w takes the partition's blocks w, w+4, w+8, ...
+// (16 tokens each), keeps its own running max / sum / weighted-V state, and the four
+// states are merged in LDS in fixed wave order.  A sequence that fits one partition
+// writes its output directly; longer ones leave (max, sum, weighted V) per partition
+// in the workspace and attn_reduce_kernel merges them (log-sum-exp, partition order).
+// Every summation order depends only on logical token positions, never on where a
+// block sits in the pool, so placement and sharing leave results bit-identical.
+//
+// Two partition kernels:
+//   attn_mfma_kernel  fp16/bf16 with >= 2 query heads per KV head: the group's
+//     queries form the N side of MFMA tiles, so the scores (16 tokens x group) and
+//     the value product (head_dim x group) are dense contractions on the matrix cores.
+//   attn_valu_kernel  one query head per workgroup (a group of 1, or fp32): q.k is a
+//     GEMV, done on the vector ALUs with cross-lane reductions.
+// Scores are kept in the base-2 domain: x = (scale * log2 e) * q.k, weights 2^(x - m).
+//
+// Pool layout (X = 16 bytes / element size):
+//   K [block][kv_head][head_dim / X][16][X]   V [block][kv_head][head_dim][16]
+// so one (block, KV head) tile is 16 * head_dim contiguous elements, and the MFMA
+// operand loads below are contiguous across the 64 lanes of each load instruction.
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <type_traits>
+
+#include "common.h"
+
+namespace {
+
+typedef __attribute__((__vector_size__(4 * sizeof(int)))) int i32x4;
+typedef __attribute__((__vector_size__(2 * sizeof(int)))) int i32x2;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(4 * sizeof(short)))) short s16x4;
+typedef __attribute__((__vector_size__(8 * sizeof(_Float16)))) _Float16 f16x8;
+typedef __attribute__((__vector_size__(4 * sizeof(_Float16)))) _Float16 f16x4;
+
+constexpr int kBS = pkv::kKernelBlockSize;  // tokens per block
+constexpr int kWaves = 4;                   // waves per partition workgroup
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kNegInf = -INFINITY;
+
+enum { DT_F32 = 0, DT_F16 = 1, DT_BF16 = 2 };
+
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// 16-bit storage bits -> float
+template <int DT>
+__device__ __forceinline__ float bits_to_f32(uint32_t b) {
+    if constexpr (DT == DT_BF16) return __uint_as_float(b << 16);
+    else if constexpr (DT == DT_F16) return (float)__builtin_bit_cast(_Float16, (uint16_t)b);
+    else return __uint_as_float(b);
+}
+
+// float -> 16-bit storage bits, round to nearest even
+template <int DT>
+__device__ __forceinline__ uint16_t f32_to_bits16(float f) {
+    if constexpr (DT == DT_BF16) return __builtin_bit_cast(uint16_t, (__bf16)f);
+    else return __builtin_bit_cast(uint16_t, (_Float16)f);
+}
+
+template <int OUT_DT>
+__device__ __forceinline__ void store_out(void* out, int64_t i, float v) {
+    if constexpr (OUT_DT == DT_F32) static_cast<float*>(out)[i] = v;
+    else static_cast<uint16_t*>(out)[i] = f32_to_bits16<OUT_DT>(v);
+}
+
+// max over the lanes that share lane % 16 (xor 16, 32)
+__device__ __forceinline__ float max_across_quads(float v) {
+    v = fmaxf(v, __shfl_xor(v, 16));
+    v = fmaxf(v, __shfl_xor(v, 32));
+    return v;
+}
+__device__ __forceinline__ float sum_across_quads(float v) {
+    v += __shfl_xor(v, 16);
+    v += __shfl_xor(v, 32);
+    return v;
+}
+
+struct PartitionArgs {
+    void* out;
+    const void* q;
+    const void* k_pool;
+    const void* v_pool;
+    const int32_t* block_tables;
+    const int32_t* context_lens;
+    float* ws_m;
+    float* ws_l;
+    float* ws_acc;
+    int32_t max_blocks_per_seq;
+    int32_t num_q_heads;
+    int32_t num_kv_heads;
+    int32_t group;
+    int32_t num_blocks;
+    int32_t max_context_len;
+    int32_t partition_tokens;
+    int32_t max_parts;
+    float scale_log2;  // scale * log2(e)
+};
+
+// Final write of a workgroup's merged state for query head h (index into the group gq):
+// normalised output for a one-partition sequence, raw state for the merge otherwise.
+template <int D, int OUT_DT>
+__device__ __forceinline__ void write_partition_result(const PartitionArgs& a, int s, int h,
+                                                       int p, int npart, int d, float m, float l,
+                                                       float acc, bool bad) {
+    if (bad) {
+        m = NAN;
+        l = NAN;
+        acc = NAN;
+    }
+    if (npart == 1) {
+        store_out<OUT_DT>(a.out, ((int64_t)s * a.num_q_heads + h) * D + d, acc / l);
+    } else {
+        const int64_t row = ((int64_t)s * a.num_q_heads + h) * a.max_parts + p;
+        a.ws_acc[row * D + d] = acc;
+        if (d == 0) {
+            a.ws_m[row] = m;
+            a.ws_l[row] = l;
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------------
+// MFMA partition kernel: fp16/bf16, group of 2..16 query heads per KV head.
+//
+// Per block of 16 tokens a wave computes S^T = K . Q^T with v_mfma_f32_16x16x32
+// (M = 16 tokens, N = 16 query-head slots, K = 32 dims per instruction; D/32 of
+// them), then O^T += V^T . P^T with v_mfma_f32_16x16x16 (M = 16 dims per instruction,
+// D/16 of them; N = head slots; K = the 16 tokens), P entering as a 16-bit head and a
+// 16-bit remainder (two MFMAs per tile).  Lane l works on head slot l % 16
+// and token quad l / 16, which is exactly the layout the score tile comes out in and
+// the layout the value product wants its B operand in, so P never leaves registers.
+// ---------------------------------------------------------------------------------
+template <int D, int DT, int OUT_DT>
+__global__ __launch_bounds__(kWaves * 64) void attn_mfma_kernel(PartitionArgs a) {
+    constexpr int KI = D / 32;   // QK MFMAs (and 16-byte K loads per lane) per block
+    constexpr int MT = D / 16;   // PV MFMAs (and 8-byte V loads per lane) per block
+    constexpr int TILE = kBS * D;  // elements of one (block, KV head) tile
+    using kvec = typename std::conditional<DT == DT_BF16, bf16x8, f16x8>::type;
+
+    const int s = blockIdx.z, g = blockIdx.y, p = blockIdx.x;
+    const int lane = threadIdx.x & 63;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int gq = lane & 15, quad = lane >> 4;
+    const int ctx = a.context_lens[s];
+    const bool bad_len = ctx < 1 || ctx > a.max_context_len;
+    const int start = p * a.partition_tokens;
+    if (bad_len) {
+        if (p == 0) {
+            for (int i = threadIdx.x; i < a.group * D; i += blockDim.x)
+                store_out<OUT_DT>(a.out, ((int64_t)s * a.num_q_heads + g * a.group + i / D) * D + i % D, NAN);
+        }
+        return;
+    }
+    if (start >= ctx) return;
+    const int end = min(start + a.partition_tokens, ctx);
+    const int npart = (ctx + a.partition_tokens - 1) / a.partition_tokens;
+    const int blk_begin = start / kBS, blk_end = (end + kBS - 1) / kBS;
+    const int32_t* trow = a.block_tables + (int64_t)s * a.max_blocks_per_seq;
+
+    // Query operand: lane holds q[head gq][32*kk + 8*quad .. +8] for each kk.
+    kvec qop[KI];
+    {
+        const uint16_t* qh = static_cast<const uint16_t*>(a.q) +
+                             ((int64_t)s * a.num_q_heads + g * a.group + gq) * D + 8 * quad;
+#pragma unroll
+        for (int kk = 0; kk < KI; ++kk) {
+            i32x4 v = {0, 0, 0, 0};
+            if (gq < a.group) v = *reinterpret_cast<const i32x4*>(qh + 32 * kk);
+            qop[kk] = __builtin_bit_cast(kvec, v);
+        }
+    }
+
+    const uint16_t* kbase = static_cast<const uint16_t*>(a.k_pool) + (int64_t)g * TILE;
+    const uint16_t* vbase = static_cast<const uint16_t*>(a.v_pool) + (int64_t)g * TILE;
+    const int64_t blk_stride = (int64_t)a.num_kv_heads * TILE;
+
+    f32x4 acc[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) acc[mt] = (f32x4){0.f, 0.f, 0.f, 0.f};
+    float m = kNegInf, lsum = 0.f;
+    bool bad_block = false;
+
+    i32x4 kA[KI], kB[KI];
+    i32x2 vA[MT], vB[MT];
+
+    auto load = [&](int b, i32x4 (&kr)[KI], i32x2 (&vr)[MT]) {
+        const int32_t bid = trow[b];
+        if ((uint32_t)bid >= (uint32_t)a.num_blocks) {
+            bad_block = true;
+#pragma unroll
+            for (int kk = 0; kk < KI; ++kk) kr[kk] = (i32x4){0, 0, 0, 0};
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) vr[mt] = (i32x2){0, 0};
+            return;
+        }
+        const i32x4* kt = reinterpret_cast<const i32x4*>(kbase + bid * blk_stride);
+        const i32x2* vt = reinterpret_cast<const i32x2*>(vbase + bid * blk_stride);
+#pragma unroll
+        for (int kk = 0; kk < KI; ++kk) kr[kk] = __builtin_nontemporal_load(kt + kk * 64 + lane);
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+            vr[mt] = __builtin_nontemporal_load(vt + (16 * mt + gq) * 4 + quad);
+    };
+
+    auto compute = [&](int b, i32x4 (&kr)[KI], i32x2 (&vr)[MT]) {
+        f32x4 sc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < KI; ++kk) {
+            if constexpr (DT == DT_BF16)
+                sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kr[kk]),
+                                                             qop[kk], sc, 0, 0, 0);
+            else
+                sc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, kr[kk]),
+                                                            qop[kk], sc, 0, 0, 0);
+        }
+        const int tok0 = b * kBS + 4 * quad;  // this lane's 4 tokens: tok0 .. tok0+3
+        float x[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) x[j] = (tok0 + j < end) ? sc[j] * a.scale_log2 : kNegInf;
+        float mb = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+        mb = max_across_quads(mb);
+        const float mnew = fmaxf(m, mb);
+        const float alpha = exp2_fast(m - mnew);
+        // The weights enter the value product as 16-bit MFMA operands.  One 16-bit
+        // rounding of p costs 2^-9 relative (bf16), which short contexts with spread-out
+        // values turn into ~1e-3 output error; so p is split into a 16-bit head and a
+        // 16-bit remainder (p = hi + lo to ~2^-17) and both are multiplied in.
+        s16x4 phi, plo;
+        float psum = 0.f;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const float pf = exp2_fast(x[j] - mnew);
+            const uint16_t hi = f32_to_bits16<DT>(pf);
+            const uint16_t lo = f32_to_bits16<DT>(pf - bits_to_f32<DT>(hi));
+            phi[j] = (short)hi;
+            plo[j] = (short)lo;
+            psum += pf;
+        }
+        lsum = lsum * alpha + psum;
+        m = mnew;
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) acc[mt] *= alpha;
+        if (b * kBS + kBS > end) {
+            // tail block: slots past the context may hold anything (NaN included);
+            // their weight is 0 but 0 * NaN is not, so clear those value elements
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) {
+                uint32_t lo = (uint32_t)vr[mt][0], hi = (uint32_t)vr[mt][1];
+                if (tok0 + 0 >= end) lo &= 0xFFFF0000u;
+                if (tok0 + 1 >= end) lo &= 0x0000FFFFu;
+                if (tok0 + 2 >= end) hi &= 0xFFFF0000u;
+                if (tok0 + 3 >= end) hi &= 0x0000FFFFu;
+                vr[mt][0] = (int)lo;
+                vr[mt][1] = (int)hi;
+            }
+        }
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+            if constexpr (DT == DT_BF16) {
+                const s16x4 va = __builtin_bit_cast(s16x4, vr[mt]);
+                acc[mt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, phi, acc[mt], 0, 0, 0);
+                acc[mt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, plo, acc[mt], 0, 0, 0);
+            } else {
+                const f16x4 va = __builtin_bit_cast(f16x4, vr[mt]);
+                acc[mt] = __builtin_amdgcn_mfma_f32_16x16x16f16(va, __builtin_bit_cast(f16x4, phi),
+                                                               acc[mt], 0, 0, 0);
+                acc[mt] = __builtin_amdgcn_mfma_f32_16x16x16f16(va, __builtin_bit_cast(f16x4, plo),
+                                                               acc[mt], 0, 0, 0);
+            }
+        }
+    };
+
+    // software pipeline: the next block's loads are in flight while this one computes
+    int b = blk_begin + w;
+    if (b < blk_end) load(b, kA, vA);
+    while (b < blk_end) {
+        if (b + kWaves < blk_end) load(b + kWaves, kB, vB);
+        compute(b, kA, vA);
+        b += kWaves;
+        if (b >= blk_end) break;
+        if (b + kWaves < blk_end) load(b + kWaves, kA, vA);
+        compute(b, kB, vB);
+        b += kWaves;
+    }
+
+    // ---- merge the four waves' states (fixed order) ----
+    __shared__ float sm_m[kWaves][16];
+    __shared__ float sm_l[kWaves][16];
+    __shared__ float sm_acc[16][D + 4];
+    const float lw = sum_across_quads(lsum);
+    if (lane < 16) {
+        sm_m[w][lane] = m;
+        sm_l[w][lane] = lw;
+    }
+    const bool any_bad = __syncthreads_or(bad_block);
+    float mmax = kNegInf;
+#pragma unroll
+    for (int ww = 0; ww < kWaves; ++ww) mmax = fmaxf(mmax, sm_m[ww][gq]);
+    const float f = (m == kNegInf) ? 0.f : exp2_fast(m - mmax);
+    for (int ww = 0; ww < kWaves; ++ww) {
+        if (ww == w && gq < a.group) {
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int d = 16 * mt + 4 * quad + r;
+                    const float v = acc[mt][r] * f;
+                    if (ww == 0) sm_acc[gq][d] = v;
+                    else sm_acc[gq][d] += v;
+                }
+            }
+        }
+        __syncthreads();
+    }
+    for (int i = threadIdx.x; i < a.group * D; i += blockDim.x) {
+        const int hg = i / D, d = i - hg * D;
+        float mm = kNegInf;
+#pragma unroll
+        for (int ww = 0; ww < kWaves; ++ww) mm = fmaxf(mm, sm_m[ww][hg]);
+        float l = 0.f;
+#pragma unroll
+        for (int ww = 0; ww < kWaves; ++ww)
+            if (sm_m[ww][hg] != kNegInf) l += exp2_fast(sm_m[ww][hg] - mm) * sm_l[ww][hg];
+        write_partition_result<D, OUT_DT>(a, s, g * a.group + hg, p, npart, d, mm, l,
+                                          sm_acc[hg][d], any_bad);
+    }
+}
+
+// ---------------------------------------------------------------------------------
+// VALU partition kernel: one query head per workgroup (grid.y = query head).
+//
+// K tile: load i of lane l covers 16-byte chunk 4*i + l/16 of token l % 16, so a lane
+// holds D/4 dims of one token; q.k is finished with two cross-lane adds (xor 16, 32).
+// V tile (dim-major): load i covers 16 bytes of row (64*i + l) / E (E = element bytes),
+// i.e. X consecutive tokens of one dim; the weights of those tokens are fetched from
+// the lanes that own them with ds_bpermute.
+// ---------------------------------------------------------------------------------
+template <int D, int DT, int OUT_DT>
+__global__ __launch_bounds__(kWaves * 64) void attn_valu_kernel(PartitionArgs a) {
+    using bits_t = typename std::conditional<DT == DT_F32, uint32_t, uint16_t>::type;
+    constexpr int E = sizeof(bits_t);
+    constexpr int X = 16 / E;           // elements per 16-byte chunk
+    constexpr int NI = kBS * D * E / 1024;  // 16-byte loads per lane per tile (K or V)
+    constexpr int TILE = kBS * D;
+
+    const int s = blockIdx.z, h = blockIdx.y, p = blockIdx.x;
+    const int g = h / a.group;
+    const int lane = threadIdx.x & 63;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int ctx = a.context_lens[s];
+    const bool bad_len = ctx < 1 || ctx > a.max_context_len;
+    const int start = p * a.partition_tokens;
+    if (bad_len) {
+        if (p == 0)
+            for (int i = threadIdx.x; i < D; i += blockDim.x)
+                store_out<OUT_DT>(a.out, ((int64_t)s * a.num_q_heads + h) * D + i, NAN);
+        return;
+    }
+    if (start >= ctx) return;
+    const int end = min(start + a.partition_tokens, ctx);
+    const int npart = (ctx + a.partition_tokens - 1) / a.partition_tokens;
+    const int blk_begin = start / kBS, blk_end = (end + kBS - 1) / kBS;
+    const int32_t* trow = a.block_tables + (int64_t)s * a.max_blocks_per_seq;
+
+    // scaled query in LDS, then the lane's D/4 dims in registers
+    __shared__ float sm_q[D];
+    {
+        const bits_t* qh = static_cast<const bits_t*>(a.q) + ((int64_t)s * a.num_q_heads + h) * D;
+        for (int i = threadIdx.x; i < D; i += blockDim.x)
+            sm_q[i] = bits_to_f32<DT>(qh[i]) * a.scale_log2;
+    }
+    __syncthreads();
+    const int tok = lane & 15;       // K: token of this lane
+    const int kq = lane >> 4;        // K: chunk quad
+    const int vpiece = lane % E;     // V: which X-token piece of a row this lane reads
+    float qr[NI][X];
+#pragma unroll
+    for (int i = 0; i < NI; ++i)
+#pragma unroll
+        for (int e = 0; e < X; ++e) qr[i][e] = sm_q[(4 * i + kq) * X + e];
+
+    const bits_t* kbase = static_cast<const bits_t*>(a.k_pool) + (int64_t)g * TILE;
+    const bits_t* vbase = static_cast<const bits_t*>(a.v_pool) + (int64_t)g * TILE;
+    const int64_t blk_stride = (int64_t)a.num_kv_heads * TILE;
+
+    float acc[NI];
+#pragma unroll
+    for (int i = 0; i < NI; ++i) acc[i] = 0.f;
+    float m = kNegInf, lsum = 0.f;
+    bool bad_block = false;
+    i32x4 kA[NI], kB[NI], vA[NI], vB[NI];
+
+    auto load = [&](int b, i32x4 (&kr)[NI], i32x4 (&vr)[NI]) {
+        const int32_t bid = trow[b];
+        if ((uint32_t)bid >= (uint32_t)a.num_blocks) {
+            bad_block = true;
+#pragma unroll
+            for (int i = 0; i < NI; ++i) kr[i] = vr[i] = (i32x4){0, 0, 0, 0};
+            return;
+        }
+        const i32x4* kt = reinterpret_cast<const i32x4*>(kbase + bid * blk_stride);
+        const i32x4* vt = reinterpret_cast<const i32x4*>(vbase + bid * blk_stride);
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+            kr[i] = __builtin_nontemporal_load(kt + i * 64 + lane);
+            vr[i] = __builtin_nontemporal_load(vt + i * 64 + lane);
+        }
+    };
+
+    auto compute = [&](int b, i32x4 (&kr)[NI], i32x4 (&vr)[NI]) {
+        float part = 0.f;
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+            bits_t kb[X];
+            __builtin_memcpy(kb, &kr[i], 16);
+#pragma unroll
+            for (int e = 0; e < X; ++e) part = fmaf(qr[i][e], bits_to_f32<DT>(kb[e]), part);
+        }
+        const float sc = sum_across_quads(part);
+        const int t = b * kBS + tok;
+        const float x = t < end ? sc : kNegInf;
+        float mb = x;
+        mb = fmaxf(mb, __shfl_xor(mb, 1));
+        mb = fmaxf(mb, __shfl_xor(mb, 2));
+        mb = fmaxf(mb, __shfl_xor(mb, 4));
+        mb = fmaxf(mb, __shfl_xor(mb, 8));
+        const float mnew = fmaxf(m, mb);
+        const float alpha = exp2_fast(m - mnew);
+        const float pt = exp2_fast(x - mnew);
+        lsum = lsum * alpha + pt;
+        m = mnew;
+        float pw[X];
+#pragma unroll
+        for (int e = 0; e < X; ++e) pw[e] = __shfl(pt, vpiece * X + e);
+        const int valid = end - b * kBS;   // tokens of this block inside the partition
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+            bits_t vb[X];
+            __builtin_memcpy(vb, &vr[i], 16);
+            float r = acc[i] * alpha;
+#pragma unroll
+            for (int e = 0; e < X; ++e) {
+                // slots past the context may hold NaN: select, never multiply by 0
+                const float v = (vpiece * X + e < valid) ? bits_to_f32<DT>(vb[e]) : 0.f;
+                r = fmaf(pw[e], v, r);
+            }
+            acc[i] = r;
+        }
+    };
+
+    int b = blk_begin + w;
+    if (b < blk_end) load(b, kA, vA);
+    while (b < blk_end) {
+        if (b + kWaves < blk_end) load(b + kWaves, kB, vB);
+        compute(b, kA, vA);
+        b += kWaves;
+        if (b >= blk_end) break;
+        if (b + kWaves < blk_end) load(b + kWaves, kA, vA);
+        compute(b, kB, vB);
+        b += kWaves;
+    }
+
+    // lane sums: each token's weight sits in its 16-lane row 4 times; take one row
+    float lw = lsum;
+    lw += __shfl_xor(lw, 1);
+    lw += __shfl_xor(lw, 2);
+    lw += __shfl_xor(lw, 4);
+    lw += __shfl_xor(lw, 8);
+    // value rows: the E lanes that share a row hold disjoint token pieces
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+        if constexpr (E >= 2) acc[i] += __shfl_xor(acc[i], 1);
+        if constexpr (E >= 4) acc[i] += __shfl_xor(acc[i], 2);
+    }
+
+    __shared__ float sm_m[kWaves], sm_l[kWaves];
+    __shared__ float sm_acc[D];
+    if (lane == 0) {
+        sm_m[w] = m;
+        sm_l[w] = lw;
+    }
+    const bool any_bad = __syncthreads_or(bad_block);
+    float mmax = kNegInf;
+#pragma unroll
+    for (int ww = 0; ww < kWaves; ++ww) mmax = fmaxf(mmax, sm_m[ww]);
+    const float f = (m == kNegInf) ? 0.f : exp2_fast(m - mmax);
+    for (int ww = 0; ww < kWaves; ++ww) {
+        if (ww == w && vpiece == 0) {
+#pragma unroll
+            for (int i = 0; i < NI; ++i) {
+                const int d = (64 * i + lane) / E;
+                const float v = acc[i] * f;
+                if (ww == 0) sm_acc[d] = v;
+                else sm_acc[d] += v;
+            }
+        }
+        __syncthreads();
+    }
+    float l = 0.f;
+#pragma unroll
+    for (int ww = 0; ww < kWaves; ++ww)
+        if (sm_m[ww] != kNegInf) l += exp2_fast(sm_m[ww] - mmax) * sm_l[ww];
+    for (int d = threadIdx.x; d < D; d += blockDim.x)
+        write_partition_result<D, OUT_DT>(a, s, h, p, npart, d, mmax, l, sm_acc[d], any_bad);
+}
+
+// ---------------------------------------------------------------------------------
+// Merge of the partitions of one (sequence, query head): with M the largest partition
+// max, out = sum_p 2^(m_p - M) acc_p / sum_p 2^(m_p - M) l_p, partitions in order.
+// ---------------------------------------------------------------------------------
+template <int D, int OUT_DT>
+__global__ __launch_bounds__(D) void attn_reduce_kernel(void* out, const int32_t* context_lens,
+                                                        int32_t num_q_heads, int32_t max_context_len,
+                                                        int32_t partition_tokens, int32_t max_parts,
+                                                        const float* ws_m, const float* ws_l,
+                                                        const float* ws_acc) {
+    const int s = blockIdx.y, h = blockIdx.x, d = threadIdx.x;
+    const int64_t o = ((int64_t)s * num_q_heads + h) * D + d;
+    const int ctx = context_lens[s];
+    if (ctx < 1 || ctx > max_context_len) {
+        store_out<OUT_DT>(out, o, NAN);
+        return;
+    }
+    const int np = (ctx + partition_tokens - 1) / partition_tokens;
+    if (np == 1) return;   // written by the partition kernel
+    const int64_t row = ((int64_t)s * num_q_heads + h) * max_parts;
+    float mm = kNegInf;
+    for (int i = 0; i < np; ++i) mm = fmaxf(mm, ws_m[row + i]);
+    float l = 0.f, acc = 0.f;
+    bool nan_seen = false;
+    for (int i = 0; i < np; ++i) {
+        const float mi = ws_m[row + i];
+        nan_seen |= mi != mi;
+        const float f = exp2_fast(mi - mm);
+        l += f * ws_l[row + i];
+        acc += f * ws_acc[(row + i) * D + d];
+    }
+    store_out<OUT_DT>(out, o, nan_seen ? NAN : acc / l);
+}
+
+// ---------------------------------------------------------------------------------
+// host side
+// ---------------------------------------------------------------------------------
+
+struct Plan {
+    PartitionArgs a;
+    int dtype, out_dtype, head_dim;
+    bool mfma;
+    dim3 grid;
+    size_t ws_needed;
+    hipStream_t stream;
+};
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+size_t workspace_for(int64_t num_seqs, int64_t hq, int64_t d, int64_t max_parts) {
+    if (max_parts <= 1) return 0;
+    const size_t rows = (size_t)num_seqs * hq * max_parts;
+    return 2 * align256(rows * sizeof(float)) + rows * d * sizeof(float);
+}
+
+paged_kv_status make_plan(Plan& pl, const paged_kv_pool_desc* desc, void* out, int32_t out_dtype,
+                          const void* q, const void* k_pool, const void* v_pool,
+                          const int32_t* tables, int32_t max_blocks, const int32_t* lens,
+                          int32_t num_seqs, int32_t hq, int32_t max_ctx, float scale,
+                          int32_t part_tokens, void* ws, size_t ws_bytes, void* stream,
+                          bool need_kv) {
+    if (!pkv::kernel_desc(desc, true)) return PAGED_KV_ERR_INVALID_ARG;
+    if (num_seqs < 0 || hq < 1) {
+        pkv::set_error("num_seqs %d < 0 or num_q_heads %d < 1", num_seqs, hq);
+        return PAGED_KV_ERR_INVALID_ARG;
+    }
+    if (hq % desc->num_kv_heads) {
+        pkv::set_error("num_q_heads %d is not a multiple of num_kv_heads %d", hq, desc->num_kv_heads);
+        return PAGED_KV_ERR_INVALID_ARG;
+    }
+    const int group = hq / desc->num_kv_heads;
+    if (group > 16) {
+        pkv::set_error("at most 16 query heads per KV head (got %d)", group);
+        return PAGED_KV_ERR_UNSUPPORTED;
+    }
+    if (out_dtype != desc->dtype && out_dtype != PAGED_KV_F32) {
+        pkv::set_error("out_dtype must be the pool dtype or fp32");
+        return PAGED_KV_ERR_INVALID_ARG;
+    }
+    if (max_ctx < 1) { pkv::set_error("max_context_len must be >= 1"); return PAGED_KV_ERR_INVALID_ARG; }
+    if (part_tokens == 0) part_tokens = pkv::kDefaultPartitionTokens;
+    if (part_tokens < 0 || part_tokens % kBS) {
+        pkv::set_error("partition_tokens %d must be a positive multiple of %d", part_tokens, kBS);
+        return PAGED_KV_ERR_INVALID_ARG;
+    }
+    if ((int64_t)max_blocks * kBS < max_ctx) {
+        pkv::set_error("max_blocks_per_seq %d cannot hold max_context_len %d", max_blocks, max_ctx);
+        return PAGED_KV_ERR_INVALID_ARG;
+    }
+    if (num_seqs > 65535) { pkv::set_error("at most 65535 sequences per launch"); return PAGED_KV_ERR_UNSUPPORTED; }
+    const int max_parts = (max_ctx + part_tokens - 1) / part_tokens;
+    pl.ws_needed = workspace_for(num_seqs, hq, desc->head_dim, max_parts);
+    if (num_seqs > 0) {
+        if (!out || !lens || (need_kv && (!q || !k_pool || !v_pool || !tables))) {
+            pkv::set_error("null pointer argument");
+            return PAGED_KV_ERR_INVALID_ARG;
+        }
+        if (pl.ws_needed > 0 && (!ws || ws_bytes < pl.ws_needed)) {
+            pkv::set_error("workspace of %zu bytes needed (%zu given)", pl.ws_needed, ws_bytes);
+            return PAGED_KV_ERR_BUFFER_TOO_SMALL;
+        }
+        if ((reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(k_pool) |
+             reinterpret_cast<uintptr_t>(v_pool) | reinterpret_cast<uintptr_t>(ws)) & 15) {
+            pkv::set_error("q, pools and workspace must be 16-byte aligned");
+            return PAGED_KV_ERR_INVALID_ARG;
+        }
+    }
+    PartitionArgs& a = pl.a;
+    a.out = out;
+    a.q = q;
+    a.k_pool = k_pool;
+    a.v_pool = v_pool;
+    a.block_tables = tables;
+    a.context_lens = lens;
+    const size_t rows = (size_t)num_seqs * hq * max_parts;
+    a.ws_m = static_cast<float*>(ws);
+    a.ws_l = pl.ws_needed ? reinterpret_cast<float*>(static_cast<char*>(ws) + align256(rows * 4)) : nullptr;
+    a.ws_acc = pl.ws_needed ? reinterpret_cast<float*>(static_cast<char*>(ws) + 2 * align256(rows * 4)) : nullptr;
+    a.max_blocks_per_seq = max_blocks;
+    a.num_q_heads = hq;
+    a.num_kv_heads = desc->num_kv_heads;
+    a.group = group;
+    a.num_blocks = desc->num_blocks;
+    a.max_context_len = max_ctx;
+    a.partition_tokens = part_tokens;
+    a.max_parts = max_parts;
+    a.scale_log2 = scale * kLog2e;
+    pl.dtype = desc->dtype;
+    pl.out_dtype = out_dtype;
+    pl.head_dim = desc->head_dim;
+    pl.mfma = desc->dtype != PAGED_KV_F32 && group >= 2;
+    pl.grid = dim3((unsigned)max_parts, (unsigned)(pl.mfma ? desc->num_kv_heads : hq), (unsigned)num_seqs);
+    pl.stream = reinterpret_cast<hipStream_t>(stream);
+    return PAGED_KV_OK;
+}
+
+template <int D, int DT, int OUT>
+void launch_partition_t(const Plan& pl) {
+    if constexpr (DT == DT_F32) {
+        attn_valu_kernel<D, DT, OUT><<<pl.grid, dim3(kWaves * 64), 0, pl.stream>>>(pl.a);
+    } else {
+        if (pl.mfma) attn_mfma_kernel<D, DT, OUT><<<pl.grid, dim3(kWaves * 64), 0, pl.stream>>>(pl.a);
+        else attn_valu_kernel<D, DT, OUT><<<pl.grid, dim3(kWaves * 64), 0, pl.stream>>>(pl.a);
+    }
+}
+
+template <int D, int DT>
+void launch_partition_d(const Plan& pl) {
+    if (pl.out_dtype == PAGED_KV_F32) launch_partition_t<D, DT, DT_F32>(pl);
+    else launch_partition_t<D, DT, DT>(pl);
+}
+
+template <int D>
+void launch_partition_dd(const Plan& pl) {
+    switch (pl.dtype) {
+        case PAGED_KV_F32: launch_partition_d<D, DT_F32>(pl); break;
+        case PAGED_KV_F16: launch_partition_d<D, DT_F16>(pl); break;
+        default: launch_partition_d<D, DT_BF16>(pl); break;
+    }
+}
+
+template <int D, int OUT>
+void launch_reduce_t(const Plan& pl, int num_seqs) {
+    attn_reduce_kernel<D, OUT><<<dim3((unsigned)pl.a.num_q_heads, (unsigned)num_seqs), dim3(D), 0,
+                                 pl.stream>>>(pl.a.out, pl.a.context_lens, pl.a.num_q_heads,
+                                              pl.a.max_context_len, pl.a.partition_tokens,
+                                              pl.a.max_parts, pl.a.ws_m, pl.a.ws_l, pl.a.ws_acc);
+}
+
+template <int D>
+void launch_reduce_d(const Plan& pl, int num_seqs) {
+    switch (pl.out_dtype) {
+        case PAGED_KV_F32: launch_reduce_t<D, DT_F32>(pl, num_seqs); break;
+        case PAGED_KV_F16: launch_reduce_t<D, DT_F16>(pl, num_seqs); break;
+        default: launch_reduce_t<D, DT_BF16>(pl, num_seqs); break;
+    }
+}
+
+paged_kv_status launch_status(const char* what) {
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) {
+        pkv::set_error("%s launch failed: %s", what, hipGetErrorString(e));
+        return PAGED_KV_ERR_HIP;
+    }
+    return PAGED_KV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t paged_attention_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
+                                       int32_t max_context_len, int32_t partition_tokens) {
+    if (num_seqs < 0 || num_q_heads < 1 || head_dim < 1 || max_context_len < 1) return 0;
+    if (partition_tokens == 0) partition_tokens = pkv::kDefaultPartitionTokens;
+    if (partition_tokens < 0) return 0;
+    const int64_t max_parts = (max_context_len + (int64_t)partition_tokens - 1) / partition_tokens;
+    return workspace_for(num_seqs, num_q_heads, head_dim, max_parts);
+}
+
+paged_kv_status paged_attention_partition(const paged_kv_pool_desc* desc, void* out,
+                                          int32_t out_dtype, const void* q, const void* k_pool,
+                                          const void* v_pool, const int32_t* block_tables,
+                                          int32_t max_blocks_per_seq, const int32_t* context_lens,
+                                          int32_t num_seqs, int32_t num_q_heads,
+                                          int32_t max_context_len, float scale,
+                                          int32_t partition_tokens, void* workspace,
+                                          size_t workspace_bytes, void* stream) {
+    pkv::clear_error();
+    Plan pl;
+    paged_kv_status st = make_plan(pl, desc, out, out_dtype, q, k_pool, v_pool, block_tables,
+                                   max_blocks_per_seq, context_lens, num_seqs, num_q_heads,
+                                   max_context_len, scale, partition_tokens, workspace,
+                                   workspace_bytes, stream, true);
+    if (st != PAGED_KV_OK || num_seqs == 0) return st;
+    if (pl.head_dim == 64) launch_partition_dd<64>(pl);
+    else launch_partition_dd<128>(pl);
+    return launch_status("paged attention partition kernel");
+}
+
+paged_kv_status paged_attention_reduce(const paged_kv_pool_desc* desc, void* out, int32_t out_dtype,
+                                       const int32_t* context_lens, int32_t num_seqs,
+                                       int32_t num_q_heads, int32_t max_context_len,
+                                       int32_t partition_tokens, const void* workspace,
+                                       size_t workspace_bytes, void* stream) {
+    pkv::clear_error();
+    Plan pl;
+    const int32_t max_blocks = (max_context_len + kBS - 1) / kBS;
+    paged_kv_status st = make_plan(pl, desc, out, out_dtype, nullptr, nullptr, nullptr, nullptr,
+                                   max_blocks, context_lens, num_seqs, num_q_heads, max_context_len,
+                                   1.f, partition_tokens, const_cast<void*>(workspace),
+                                   workspace_bytes, stream, false);
+    if (st != PAGED_KV_OK || num_seqs == 0 || pl.a.max_parts <= 1) return st;
+    if (pl.head_dim == 64) launch_reduce_d<64>(pl, num_seqs);
+    else launch_reduce_d<128>(pl, num_seqs);
+    return launch_status("paged attention reduce kernel");
+}
+
+paged_kv_status paged_attention_decode(const paged_kv_pool_desc* desc, void* out, int32_t out_dtype,
+                                       const void* q, const void* k_pool, const void* v_pool,
+                                       const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                       const int32_t* context_lens, int32_t num_seqs,
+                                       int32_t num_q_heads, int32_t max_context_len, float scale,
+                                       int32_t partition_tokens, void* workspace,
+                                       size_t workspace_bytes, void* stream) {
+    paged_kv_status st = paged_attention_partition(
+        desc, out, out_dtype, q, k_pool, v_pool, block_tables, max_blocks_per_seq, context_lens,
+        num_seqs, num_q_heads, max_context_len, scale, partition_tokens, workspace,
+        workspace_bytes, stream);
+    if (st != PAGED_KV_OK) return st;
+    return paged_attention_reduce(desc, out, out_dtype, context_lens, num_seqs, num_q_heads,
+                                  max_context_len, partition_tokens, workspace, workspace_bytes,
+                                  stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,219 @@
+"""Edge cases and invariances of the HIP path (GPU), checked against the oracle."""
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+from oracle import replay as oreplay
+from oracle import lowp
+from gpu_common import (TOL, say, assert_pools_equal, assert_bookkeeping_equal, max_err, out_f64,
+                        assert_close)
+
+pytestmark = pytest.mark.gpu
+
+BOUNDARY_LENS = [1, 2, 15, 16, 17, 31, 32, 33, 63, 64, 65, 511, 512, 513, 1024, 1025, 1100]
+
+# (dtype, q heads, kv heads, head_dim): VALU path (group 1, and fp32) and MFMA path
+SHAPES = [("f32", 4, 4, 64), ("f32", 8, 2, 128), ("f16", 4, 4, 128), ("bf16", 2, 2, 64),
+          ("bf16", 16, 2, 128), ("f16", 8, 4, 128), ("bf16", 8, 2, 64), ("bf16", 32, 2, 128),
+          ("f16", 12, 4, 64)]
+
+
+def _run(w, out_dtype="f32", pt=None):
+    from paged_kv_cache_15_amd.replay import run_workload
+    g = run_workload(w, "cuda", out_dtype=out_dtype, partition_tokens=pt)
+    torch.cuda.synchronize()
+    return g
+
+
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "-".join(map(str, s)))
+def test_boundary_lengths_every_path(shape):
+    dt, hq, hkv, d = shape
+    w = W.make_custom(BOUNDARY_LENS, hq, hkv, d, dt, seed=hq * 7 + d)
+    say(f"[edge] boundary lengths {shape}")
+    for out_dtype in ("f32", dt):
+        g = _run(w, out_dtype)
+        o = oreplay.run(w)
+        assert_bookkeeping_equal(g, o)
+        assert_pools_equal(g.cache, o, dt)
+        err = assert_close(g.outputs[0], o.outputs[0], dt, out_dtype)
+        say(f"   out={out_dtype} max|err| {err:.3e}")
+        g.cache.close()
+
+
+@pytest.mark.parametrize("shape", SHAPES[:6], ids=lambda s: "-".join(map(str, s)))
+def test_single_token_returns_its_value_exactly(shape):
+    dt, hq, hkv, d = shape
+    w = W.make_custom([1, 1, 1], hq, hkv, d, dt, seed=3)
+    g = _run(w, "f32")
+    k, v = w.kv[-1]
+    vb = lowp.storage_bits_to_f64(lowp.to_storage_bits(v, dt), dt)   # [3][hkv][d]
+    expect = np.repeat(vb, hq // hkv, axis=1)
+    assert np.array_equal(out_f64(g.outputs[0]), expect)
+    g.cache.close()
+
+
+@pytest.mark.parametrize("dt,hq,hkv", [("bf16", 64, 8), ("f16", 32, 32), ("f32", 4, 4)])
+def test_partition_size_invariance(dt, hq, hkv):
+    w = W.make_custom([5, 700, 1500, 2049], hq, hkv, 128 if dt != "f32" else 64, dt, seed=11)
+    o = oreplay.run(w)
+    outs = []
+    for pt in (16, 48, 512, 4096):
+        g = _run(w, "f32", pt)
+        err = max_err(g.outputs[0], o.outputs[0])
+        say(f"[edge] partition {pt}: max|err| {err:.3e}")
+        assert err <= TOL[dt]
+        outs.append(out_f64(g.outputs[0]))
+        g.cache.close()
+    for x in outs[1:]:
+        assert np.abs(x - outs[0]).max() <= TOL[dt]
+
+
+@pytest.mark.parametrize("dt,hq,hkv", [("bf16", 64, 8), ("f16", 32, 32), ("f32", 4, 4)])
+def test_placement_invariance_bitwise(dt, hq, hkv):
+    d = 128 if dt != "f32" else 64
+    base = W.make_custom([300, 1000, 17, 2500], hq, hkv, d, dt, seed=21)
+    outs = []
+    for perm_seed in (0, 1, 2):
+        w = W.make_custom([300, 1000, 17, 2500], hq, hkv, d, dt, seed=21,
+                          free_order=np.random.default_rng(50 + perm_seed).permutation(base.num_blocks))
+        g = _run(w, "f32")
+        outs.append((out_f64(g.outputs[0]), g.tables[0]))
+        g.cache.close()
+    assert not np.array_equal(outs[0][1], outs[1][1])
+    for o, _ in outs[1:]:
+        assert np.array_equal(o, outs[0][0])
+
+
+def test_shared_and_copied_prefix_bitwise():
+    shared, copied = W.configs.make_shared_prefix_pair(small=True)
+    gs = _run(shared, "f32")
+    gc = _run(copied, "f32")
+    assert sum(len(c) for c in gs.copies) == 2 * 7
+    assert sum(len(c) for c in gc.copies) == 0
+    assert np.array_equal(out_f64(gs.outputs[0]), out_f64(gc.outputs[0]))
+    os_ = oreplay.run(shared)
+    assert_pools_equal(gs.cache, os_, "bf16")
+    assert max_err(gs.outputs[0], os_.outputs[0]) <= TOL["bf16"]
+    fs, us, _ = gs.cache.stats()
+    fc, uc, _ = gc.cache.stats()
+    assert us < uc
+    gs.cache.close()
+    gc.cache.close()
+
+
+def test_gqa_matches_replicated_mha():
+    gqa = W.make_custom([40, 600, 1300], 16, 2, 128, "bf16", seed=31)
+    mha = W.make_custom([40, 600, 1300], 16, 16, 128, "bf16", seed=31)
+    # same draws, KV heads repeated 8x for the MHA twin
+    mha.kv = [(np.repeat(k, 8, axis=1), np.repeat(v, 8, axis=1)) for k, v in gqa.kv]
+    mha.q = gqa.q
+    mha.num_blocks = gqa.num_blocks
+    mha.free_order = gqa.free_order
+    a = _run(gqa, "f32")
+    b = _run(mha, "f32")
+    assert np.abs(out_f64(a.outputs[0]) - out_f64(b.outputs[0])).max() <= TOL["bf16"]
+    a.cache.close()
+    b.cache.close()
+
+
+def test_invalid_lengths_and_block_ids_give_nan_without_reading():
+    from paged_kv_cache_15_amd import binding as B
+    from paged_kv_cache_15_amd.replay import run_workload
+    for dt, hq, hkv, d in [("bf16", 16, 2, 128), ("f16", 4, 4, 128), ("f32", 4, 4, 64)]:
+        w = W.make_custom([100, 700, 30, 1200], hq, hkv, d, dt, seed=41)
+        g = run_workload(w, "cuda", out_dtype="f32")
+        o = oreplay.run(w)
+        c = g.cache
+        tables = g.tables[0].copy()
+        lens = g.context_lens[0].copy()
+        tables[1, 3] = c.desc.num_blocks + 5       # past the pool
+        tables[3, 0] = -7                          # negative id
+        lens[2] = 0                                # empty context
+        max_ctx = 1200
+        mb = tables.shape[1]
+        lens_d = torch.from_numpy(lens).cuda()
+        tab_d = torch.from_numpy(tables).cuda()
+        from paged_kv_cache_15_amd.cache import TORCH_DTYPES
+        q = torch.from_numpy(w.q[0]).cuda().to(TORCH_DTYPES[dt])
+        out = torch.zeros((4, hq, d), device="cuda")
+        for pt in (512, 2048):
+            nb = B.paged_attention_workspace_bytes(4, hq, d, max_ctx, pt)
+            ws = torch.empty(max(nb, 16), dtype=torch.uint8, device="cuda")
+            B.paged_attention_decode(c.desc, out, "f32", q, c.k_pool, c.v_pool, tab_d, lens_d, hq,
+                                     max_ctx, float(w.scale), pt, ws)
+            torch.cuda.synchronize()
+            r = out_f64(out)
+            assert np.isnan(r[1]).all() and np.isnan(r[2]).all() and np.isnan(r[3]).all()
+            assert np.abs(r[0] - o.outputs[0][0]).max() <= TOL[dt]
+        # a context longer than max_context_len is rejected the same way
+        lens2 = g.context_lens[0].copy()
+        lens_d2 = torch.from_numpy(lens2).cuda()
+        nb = B.paged_attention_workspace_bytes(4, hq, d, 1000, 512)
+        ws = torch.empty(nb, dtype=torch.uint8, device="cuda")
+        B.paged_attention_decode(c.desc, out, "f32", q, c.k_pool, c.v_pool,
+                                 torch.from_numpy(g.tables[0]).cuda(), lens_d2, hq, 1000,
+                                 float(w.scale), 512, ws)
+        torch.cuda.synchronize()
+        r = out_f64(out)
+        assert np.isnan(r[3]).all() and not np.isnan(r[:3]).any()
+        c.close()
+
+
+def test_padding_and_out_of_range_slots_are_not_written():
+    from paged_kv_cache_15_amd import binding as B
+    from paged_kv_cache_15_amd.cache import PagedKVCache
+    c = PagedKVCache(8, 2, 64, "bf16")
+    key = torch.randn(4, 2, 64, device="cuda").to(torch.bfloat16)
+    val = torch.randn(4, 2, 64, device="cuda").to(torch.bfloat16)
+    slots = torch.tensor([-1, 5, 8 * 16, 17], dtype=torch.int32, device="cuda")
+    B.reshape_and_cache(c.desc, key, val, c.k_pool, c.v_pool, slots)
+    pairs = torch.tensor([[1, 3], [9, 2], [1, -1]], dtype=torch.int32, device="cuda")
+    B.paged_kv_copy_blocks(c.desc, c.k_pool, c.v_pool, pairs, 3)
+    torch.cuda.synchronize()
+    kb = c.k_pool.view(torch.int16).cpu().numpy().view(np.uint16)
+    vb = c.v_pool.view(torch.int16).cpu().numpy().view(np.uint16)
+    kk = key.view(torch.int16).cpu().numpy().view(np.uint16)
+    vv = val.view(torch.int16).cpu().numpy().view(np.uint16)
+    poison = np.uint16(0xFFFF)
+    # slot 5 -> block 0 offset 5; slot 17 -> block 1 offset 1 (then copied to block 3)
+    assert np.array_equal(kb[0, :, :, 5, :].reshape(2, 64), kk[1])
+    assert np.array_equal(vb[0, :, :, 5], vv[1])
+    assert np.array_equal(kb[1, :, :, 1, :].reshape(2, 64), kk[3])
+    assert np.array_equal(kb[3], kb[1]) and np.array_equal(vb[3], vb[1])
+    written = np.zeros(kb.shape[:1] + (kb.shape[3],), bool)
+    written[0, 5] = written[1, 1] = written[3, 1] = True
+    for b in range(8):
+        for o in range(16):
+            if not written[b, o]:
+                assert np.all(kb[b, :, :, o, :] == poison) and np.all(vb[b, :, :, o] == poison)
+    c.close()
+
+
+def test_empty_batches_launch_nothing():
+    from paged_kv_cache_15_amd import binding as B
+    from paged_kv_cache_15_amd.cache import PagedKVCache
+    c = PagedKVCache(8, 2, 64, "f16")
+    e = torch.empty((0, 2, 64), dtype=torch.float16, device="cuda")
+    B.reshape_and_cache(c.desc, e, e, c.k_pool, c.v_pool, torch.empty(0, dtype=torch.int32, device="cuda"))
+    B.paged_kv_copy_blocks(c.desc, c.k_pool, c.v_pool, torch.empty((0, 2), dtype=torch.int32, device="cuda"), 0)
+    out = torch.empty((0, 4, 64), device="cuda")
+    B.paged_attention_decode(c.desc, out, "f32", torch.empty((0, 4, 64), dtype=torch.float16, device="cuda"),
+                             c.k_pool, c.v_pool, torch.empty((0, 1), dtype=torch.int32, device="cuda"),
+                             torch.empty(0, dtype=torch.int32, device="cuda"), 4, 16, 0.1)
+    torch.cuda.synchronize()
+    assert np.all(c.k_pool.view(torch.int16).cpu().numpy() == -1)
+    c.close()
+
+
+def test_decode_steps_append_and_attend():
+    """Config-5 shape in small: eight consecutive steps, each one token per sequence."""
+    w = W.make_config(5, small=True)
+    g = _run(w, "bf16")
+    o = oreplay.run(w)
+    assert len(g.outputs) == 8
+    assert_bookkeeping_equal(g, o)
+    assert_pools_equal(g.cache, o, "bf16")
+    for go, oo in zip(g.outputs, o.outputs):
+        assert_close(go, oo, "bf16", "bf16")
+    g.cache.close()

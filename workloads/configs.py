@@ -14,11 +14,14 @@ consume.  Operations, in the order they are to be executed:
 
 Values are float32 N(0, 1).  Casting them to the workload's storage type is
 left to each consumer.  Seeds: workload k draws from numpy
-``SeedSequence(k).spawn(3)`` = (lengths, free-queue order, values).
+``SeedSequence(k).spawn(3)`` = (lengths, free-queue order, values); the values
+sequence spawns one child per draw, in op order.
 """
 from __future__ import annotations
 
 import math
+import os
+from concurrent.futures import ThreadPoolExecutor
 from dataclasses import dataclass, field
 
 import numpy as np
@@ -75,8 +78,23 @@ class Workload:
         return lens
 
 
-def _normal(rng, shape):
-    return rng.standard_normal(shape, dtype=np.float32)
+_CHUNK = 1 << 22
+_POOL = ThreadPoolExecutor(max_workers=min(16, os.cpu_count() or 1))
+
+
+def _normal(ss, shape):
+    """float32 N(0, 1) of `shape` from SeedSequence `ss`: the flat array is cut into
+    chunks of 2**22 values, chunk i drawn from ss.spawn(n)[i] (filled in parallel
+    threads; the values do not depend on the thread count)."""
+    n = int(np.prod(shape))
+    out = np.empty(n, dtype=np.float32)
+    seeds = ss.spawn(max(1, -(-n // _CHUNK)))
+
+    def fill(i):
+        np.random.default_rng(seeds[i]).standard_normal(
+            out=out[i * _CHUNK:(i + 1) * _CHUNK], dtype=np.float32)
+    list(_POOL.map(fill, range(len(seeds))))
+    return out.reshape(shape)
 
 
 def _blocks(n_tokens: int, bs: int) -> int:
@@ -84,10 +102,11 @@ def _blocks(n_tokens: int, bs: int) -> int:
 
 
 class _Builder:
-    """Collects ops and draws their values in op order from one generator."""
+    """Collects ops; each draw (K, V of an append; q of an attend) takes the next
+    child of the values SeedSequence, in op order."""
 
-    def __init__(self, rng_val, hkv, hq, d, draw_values=True):
-        self.rng, self.hkv, self.hq, self.d = rng_val, hkv, hq, d
+    def __init__(self, ss_val, hkv, hq, d, draw_values=True):
+        self.ss, self.hkv, self.hq, self.d = ss_val, hkv, hq, d
         self.draw_values = draw_values
         self.ops, self.kv, self.q = [], [], []
         self.next_id = 0
@@ -106,16 +125,16 @@ class _Builder:
         seqs, counts = [int(s) for s in seqs], [int(c) for c in counts]
         total = sum(counts)
         if self.draw_values:
-            k = _normal(self.rng, (total, self.hkv, self.d))
-            v = _normal(self.rng, (total, self.hkv, self.d))
+            k = _normal(self.ss.spawn(1)[0], (total, self.hkv, self.d))
+            v = _normal(self.ss.spawn(1)[0], (total, self.hkv, self.d))
             self.kv.append((k, v))
         else:
             self.kv.append(None)
         self.ops.append(("append", seqs, counts, len(self.kv) - 1))
 
     def attend(self, seqs):
-        self.q.append(_normal(self.rng, (len(seqs), self.hq, self.d)) if self.draw_values
-                      else None)
+        self.q.append(_normal(self.ss.spawn(1)[0], (len(seqs), self.hq, self.d))
+                      if self.draw_values else None)
         self.ops.append(("attend", [int(s) for s in seqs], len(self.q) - 1))
 
     def free(self, seq):
@@ -155,7 +174,8 @@ def make_config(k: int, small: bool = False, draw_values: bool = True) -> Worklo
     only (lengths, pool order and operations are the same; kv and q hold None)."""
     dv = draw_values
     ss = np.random.SeedSequence(k + (100 if small else 0)).spawn(3)
-    rng_len, rng_pool, rng_val = (np.random.default_rng(s) for s in ss)
+    rng_len, rng_pool = (np.random.default_rng(s) for s in ss[:2])
+    rng_val = ss[2]           # values: SeedSequence, children spawned per draw
     name = CONFIG_NAMES[k] + ("_small" if small else "")
     if k == 1:
         lens = [7, 16, 33, 100]
@@ -236,7 +256,8 @@ def make_shared_prefix_pair(small: bool = True, prompt_len: int = 2056):
     out = []
     for share in (True, False):
         ss = np.random.SeedSequence(4 + (100 if small else 0)).spawn(3)
-        rng_len, rng_pool, rng_val = (np.random.default_rng(s) for s in ss)
+        rng_len, rng_pool = (np.random.default_rng(s) for s in ss[:2])
+        rng_val = ss[2]
         prompts = 2 if small else 32
         out.append(_shared_prefix(f"shared_prefix_share{int(share)}", prompts, 8, prompt_len,
                                   (64, 512), rng_len, rng_pool, rng_val, share=share))
@@ -247,7 +268,7 @@ def make_custom(lengths, num_q_heads, num_kv_heads, head_dim, dtype, seed=0, num
                 free_order=None, steps=1, block_size=16):
     """A prefill-then-decode workload with the given attention lengths (edge cases)."""
     ss = np.random.SeedSequence(1000 + seed).spawn(3)
-    _, rng_pool, rng_val = (np.random.default_rng(s) for s in ss)
+    rng_pool, rng_val = np.random.default_rng(ss[1]), ss[2]
     lens = [int(x) for x in lengths]
     if num_blocks is None:
         num_blocks = max(1, _pool_size(sum(_blocks(L + steps - 1, block_size) for L in lens)))
