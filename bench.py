@@ -42,7 +42,21 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="bound on the oracle's timed CPU work")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB (3 times) and exit: the "
+                         "known-size reference for scaling HBM byte counters")
     return ap.parse_args()
+
+
+def copy_calibration(mib):
+    import torch
+    n = mib * (1 << 20) // 4
+    x = torch.ones(n, dtype=torch.float32, device="cuda")
+    y = torch.empty_like(x)
+    for _ in range(3):
+        y.copy_(x)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": n * 4, "launches": 3}), flush=True)
 
 
 def attention_bytes(lens, nblocks, w, out_elem):
@@ -90,6 +104,9 @@ def cpu_baseline(w, seconds):
 
 def main():
     args = parse()
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
               "(the path shards by sequence or KV head with no exchange, but this build "

@@ -51,6 +51,7 @@ constexpr int kBS = pkv::kKernelBlockSize;  // tokens per block
 constexpr int kWaves = 4;                   // waves per partition workgroup
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kNegInf = -INFINITY;
+constexpr float kRescaleSlack = 8.f;        // log2 units: weights stay below 2^8
 
 enum { DT_F32 = 0, DT_F16 = 1, DT_BF16 = 2 };
 
@@ -145,13 +146,14 @@ __device__ __forceinline__ void write_partition_result(const PartitionArgs& a, i
 // the layout the value product wants its B operand in, so P never leaves registers.
 // ---------------------------------------------------------------------------------
 template <int D, int DT, int OUT_DT>
-__global__ __launch_bounds__(kWaves * 64) void attn_mfma_kernel(PartitionArgs a) {
+__global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(3))) void attn_mfma_kernel(PartitionArgs a) {
     constexpr int KI = D / 32;   // QK MFMAs (and 16-byte K loads per lane) per block
-    constexpr int MT = D / 16;   // PV MFMAs (and 8-byte V loads per lane) per block
+    constexpr int MT = D / 16;   // PV MFMA pairs (and 8-byte V loads per lane) per block
     constexpr int TILE = kBS * D;  // elements of one (block, KV head) tile
     using kvec = typename std::conditional<DT == DT_BF16, bf16x8, f16x8>::type;
 
-    const int s = blockIdx.z, g = blockIdx.y, p = blockIdx.x;
+    const int s = blockIdx.x / a.num_kv_heads, g = blockIdx.x - s * a.num_kv_heads;
+    const int p = blockIdx.y;
     const int lane = threadIdx.x & 63;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int gq = lane & 15, quad = lane >> 4;
@@ -187,6 +189,7 @@ __global__ __launch_bounds__(kWaves * 64) void attn_mfma_kernel(PartitionArgs a)
     const uint16_t* kbase = static_cast<const uint16_t*>(a.k_pool) + (int64_t)g * TILE;
     const uint16_t* vbase = static_cast<const uint16_t*>(a.v_pool) + (int64_t)g * TILE;
     const int64_t blk_stride = (int64_t)a.num_kv_heads * TILE;
+    const int voff = gq * 4 + quad;   // 8-byte unit of row gq, tokens 4*quad.. of a V^T tile
 
     f32x4 acc[MT];
 #pragma unroll
@@ -197,23 +200,16 @@ __global__ __launch_bounds__(kWaves * 64) void attn_mfma_kernel(PartitionArgs a)
     i32x4 kA[KI], kB[KI];
     i32x2 vA[MT], vB[MT];
 
-    auto load = [&](int b, i32x4 (&kr)[KI], i32x2 (&vr)[MT]) {
-        const int32_t bid = trow[b];
-        if ((uint32_t)bid >= (uint32_t)a.num_blocks) {
-            bad_block = true;
-#pragma unroll
-            for (int kk = 0; kk < KI; ++kk) kr[kk] = (i32x4){0, 0, 0, 0};
-#pragma unroll
-            for (int mt = 0; mt < MT; ++mt) vr[mt] = (i32x2){0, 0};
-            return;
-        }
+    // K tile: load kk of lane l is 16-byte chunk 4*kk + l/16 of token l%16, i.e. bytes
+    // [1024*kk + 16*l, +16): each load instruction reads 1 KiB contiguous.  V^T tile:
+    // load mt of lane l is row 16*mt + l%16, tokens 4*(l/16)..+3: 512 B contiguous.
+    auto load = [&](int32_t bid, i32x4 (&kr)[KI], i32x2 (&vr)[MT]) {
         const i32x4* kt = reinterpret_cast<const i32x4*>(kbase + bid * blk_stride);
         const i32x2* vt = reinterpret_cast<const i32x2*>(vbase + bid * blk_stride);
 #pragma unroll
         for (int kk = 0; kk < KI; ++kk) kr[kk] = __builtin_nontemporal_load(kt + kk * 64 + lane);
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
-            vr[mt] = __builtin_nontemporal_load(vt + (16 * mt + gq) * 4 + quad);
+        for (int mt = 0; mt < MT; ++mt) vr[mt] = __builtin_nontemporal_load(vt + mt * 64 + voff);
     };
 
     auto compute = [&](int b, i32x4 (&kr)[KI], i32x2 (&vr)[MT]) {
@@ -231,29 +227,32 @@ __global__ __launch_bounds__(kWaves * 64) void attn_mfma_kernel(PartitionArgs a)
         float x[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) x[j] = (tok0 + j < end) ? sc[j] * a.scale_log2 : kNegInf;
-        float mb = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
-        mb = max_across_quads(mb);
-        const float mnew = fmaxf(m, mb);
-        const float alpha = exp2_fast(m - mnew);
+        // Lazy rescaling: the reference max m only moves when a score exceeds it by more
+        // than kRescaleSlack (weights stay <= 2^kRescaleSlack); the softmax is the same
+        // for any reference, so most blocks skip the cross-lane max and the rescale.
+        const float xm = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+        if (__ballot(xm > m + kRescaleSlack)) {
+            const float mnew = fmaxf(m, max_across_quads(xm));
+            const float alpha = exp2_fast(m - mnew);
+            lsum *= alpha;
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) acc[mt] *= alpha;
+            m = mnew;
+        }
         // The weights enter the value product as 16-bit MFMA operands.  One 16-bit
         // rounding of p costs 2^-9 relative (bf16), which short contexts with spread-out
         // values turn into ~1e-3 output error; so p is split into a 16-bit head and a
         // 16-bit remainder (p = hi + lo to ~2^-17) and both are multiplied in.
         s16x4 phi, plo;
-        float psum = 0.f;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            const float pf = exp2_fast(x[j] - mnew);
+            const float pf = exp2_fast(x[j] - m);
             const uint16_t hi = f32_to_bits16<DT>(pf);
             const uint16_t lo = f32_to_bits16<DT>(pf - bits_to_f32<DT>(hi));
             phi[j] = (short)hi;
             plo[j] = (short)lo;
-            psum += pf;
+            lsum += pf;
         }
-        lsum = lsum * alpha + psum;
-        m = mnew;
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) acc[mt] *= alpha;
         if (b * kBS + kBS > end) {
             // tail block: slots past the context may hold anything (NaN included);
             // their weight is 0 but 0 * NaN is not, so clear those value elements
@@ -284,17 +283,36 @@ __global__ __launch_bounds__(kWaves * 64) void attn_mfma_kernel(PartitionArgs a)
         }
     };
 
-    // software pipeline: the next block's loads are in flight while this one computes
-    int b = blk_begin + w;
-    if (b < blk_end) load(b, kA, vA);
-    while (b < blk_end) {
-        if (b + kWaves < blk_end) load(b + kWaves, kB, vB);
-        compute(b, kA, vA);
-        b += kWaves;
-        if (b >= blk_end) break;
-        if (b + kWaves < blk_end) load(b + kWaves, kA, vA);
-        compute(b, kB, vB);
-        b += kWaves;
+    // Wave w takes the partition's blocks w, w+4, w+8, ...; lane i holds the id of the
+    // wave's i-th block (windows of 64).  Software pipeline, two register sets: the
+    // next block's loads are in flight while the current one is computed.  Every path
+    // through the loop issues the same loads, so the compiler waits for exactly the
+    // current block's loads and never drains the prefetch.
+    const int nblk = blk_end - blk_begin;
+    const int n_w = nblk > w ? (nblk - w + kWaves - 1) / kWaves : 0;
+    for (int base = 0; base < n_w; base += 64) {
+        const int cnt = min(64, n_w - base);
+        int id_v = 0;
+        if (lane < cnt) id_v = trow[blk_begin + w + kWaves * (base + lane)];
+        const bool id_ok = (uint32_t)id_v < (uint32_t)a.num_blocks;
+        if (__ballot(lane < cnt && !id_ok)) bad_block = true;
+        id_v = id_ok ? id_v : 0;
+        const int b0 = blk_begin + w + kWaves * base;
+        load(__builtin_amdgcn_readlane(id_v, 0), kA, vA);
+        int i = 0;
+        for (; i + 2 < cnt; i += 2) {
+            load(__builtin_amdgcn_readlane(id_v, i + 1), kB, vB);
+            compute(b0 + kWaves * i, kA, vA);
+            load(__builtin_amdgcn_readlane(id_v, i + 2), kA, vA);
+            compute(b0 + kWaves * (i + 1), kB, vB);
+        }
+        if (i + 1 < cnt) {
+            load(__builtin_amdgcn_readlane(id_v, i + 1), kB, vB);
+            compute(b0 + kWaves * i, kA, vA);
+            compute(b0 + kWaves * (i + 1), kB, vB);
+        } else {
+            compute(b0 + kWaves * i, kA, vA);
+        }
     }
 
     // ---- merge the four waves' states (fixed order) ----
@@ -357,7 +375,8 @@ __global__ __launch_bounds__(kWaves * 64) void attn_valu_kernel(PartitionArgs a)
     constexpr int NI = kBS * D * E / 1024;  // 16-byte loads per lane per tile (K or V)
     constexpr int TILE = kBS * D;
 
-    const int s = blockIdx.z, h = blockIdx.y, p = blockIdx.x;
+    const int s = blockIdx.x / a.num_q_heads, h = blockIdx.x - s * a.num_q_heads;
+    const int p = blockIdx.y;
     const int g = h / a.group;
     const int lane = threadIdx.x & 63;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -404,14 +423,7 @@ __global__ __launch_bounds__(kWaves * 64) void attn_valu_kernel(PartitionArgs a)
     bool bad_block = false;
     i32x4 kA[NI], kB[NI], vA[NI], vB[NI];
 
-    auto load = [&](int b, i32x4 (&kr)[NI], i32x4 (&vr)[NI]) {
-        const int32_t bid = trow[b];
-        if ((uint32_t)bid >= (uint32_t)a.num_blocks) {
-            bad_block = true;
-#pragma unroll
-            for (int i = 0; i < NI; ++i) kr[i] = vr[i] = (i32x4){0, 0, 0, 0};
-            return;
-        }
+    auto load = [&](int32_t bid, i32x4 (&kr)[NI], i32x4 (&vr)[NI]) {
         const i32x4* kt = reinterpret_cast<const i32x4*>(kbase + bid * blk_stride);
         const i32x4* vt = reinterpret_cast<const i32x4*>(vbase + bid * blk_stride);
 #pragma unroll
@@ -433,16 +445,22 @@ __global__ __launch_bounds__(kWaves * 64) void attn_valu_kernel(PartitionArgs a)
         const float sc = sum_across_quads(part);
         const int t = b * kBS + tok;
         const float x = t < end ? sc : kNegInf;
-        float mb = x;
-        mb = fmaxf(mb, __shfl_xor(mb, 1));
-        mb = fmaxf(mb, __shfl_xor(mb, 2));
-        mb = fmaxf(mb, __shfl_xor(mb, 4));
-        mb = fmaxf(mb, __shfl_xor(mb, 8));
-        const float mnew = fmaxf(m, mb);
-        const float alpha = exp2_fast(m - mnew);
-        const float pt = exp2_fast(x - mnew);
-        lsum = lsum * alpha + pt;
-        m = mnew;
+        // lazy rescaling, as in the MFMA kernel
+        if (__ballot(x > m + kRescaleSlack)) {
+            float mb = x;
+            mb = fmaxf(mb, __shfl_xor(mb, 1));
+            mb = fmaxf(mb, __shfl_xor(mb, 2));
+            mb = fmaxf(mb, __shfl_xor(mb, 4));
+            mb = fmaxf(mb, __shfl_xor(mb, 8));
+            const float mnew = fmaxf(m, mb);
+            const float alpha = exp2_fast(m - mnew);
+            lsum *= alpha;
+#pragma unroll
+            for (int i = 0; i < NI; ++i) acc[i] *= alpha;
+            m = mnew;
+        }
+        const float pt = exp2_fast(x - m);
+        lsum += pt;
         float pw[X];
 #pragma unroll
         for (int e = 0; e < X; ++e) pw[e] = __shfl(pt, vpiece * X + e);
@@ -451,7 +469,7 @@ __global__ __launch_bounds__(kWaves * 64) void attn_valu_kernel(PartitionArgs a)
         for (int i = 0; i < NI; ++i) {
             bits_t vb[X];
             __builtin_memcpy(vb, &vr[i], 16);
-            float r = acc[i] * alpha;
+            float r = acc[i];
 #pragma unroll
             for (int e = 0; e < X; ++e) {
                 // slots past the context may hold NaN: select, never multiply by 0
@@ -462,16 +480,32 @@ __global__ __launch_bounds__(kWaves * 64) void attn_valu_kernel(PartitionArgs a)
         }
     };
 
-    int b = blk_begin + w;
-    if (b < blk_end) load(b, kA, vA);
-    while (b < blk_end) {
-        if (b + kWaves < blk_end) load(b + kWaves, kB, vB);
-        compute(b, kA, vA);
-        b += kWaves;
-        if (b >= blk_end) break;
-        if (b + kWaves < blk_end) load(b + kWaves, kA, vA);
-        compute(b, kB, vB);
-        b += kWaves;
+    // same schedule and pipeline as the MFMA kernel
+    const int nblk = blk_end - blk_begin;
+    const int n_w = nblk > w ? (nblk - w + kWaves - 1) / kWaves : 0;
+    for (int base = 0; base < n_w; base += 64) {
+        const int cnt = min(64, n_w - base);
+        int id_v = 0;
+        if (lane < cnt) id_v = trow[blk_begin + w + kWaves * (base + lane)];
+        const bool id_ok = (uint32_t)id_v < (uint32_t)a.num_blocks;
+        if (__ballot(lane < cnt && !id_ok)) bad_block = true;
+        id_v = id_ok ? id_v : 0;
+        const int b0 = blk_begin + w + kWaves * base;
+        load(__builtin_amdgcn_readlane(id_v, 0), kA, vA);
+        int i = 0;
+        for (; i + 2 < cnt; i += 2) {
+            load(__builtin_amdgcn_readlane(id_v, i + 1), kB, vB);
+            compute(b0 + kWaves * i, kA, vA);
+            load(__builtin_amdgcn_readlane(id_v, i + 2), kA, vA);
+            compute(b0 + kWaves * (i + 1), kB, vB);
+        }
+        if (i + 1 < cnt) {
+            load(__builtin_amdgcn_readlane(id_v, i + 1), kB, vB);
+            compute(b0 + kWaves * i, kA, vA);
+            compute(b0 + kWaves * (i + 1), kB, vB);
+        } else {
+            compute(b0 + kWaves * i, kA, vA);
+        }
     }
 
     // lane sums: each token's weight sits in its 16-lane row 4 times; take one row
@@ -609,6 +643,7 @@ paged_kv_status make_plan(Plan& pl, const paged_kv_pool_desc* desc, void* out, i
     }
     if (num_seqs > 65535) { pkv::set_error("at most 65535 sequences per launch"); return PAGED_KV_ERR_UNSUPPORTED; }
     const int max_parts = (max_ctx + part_tokens - 1) / part_tokens;
+    if (max_parts > 65535) { pkv::set_error("at most 65535 partitions per sequence"); return PAGED_KV_ERR_UNSUPPORTED; }
     pl.ws_needed = workspace_for(num_seqs, hq, desc->head_dim, max_parts);
     if (num_seqs > 0) {
         if (!out || !lens || (need_kv && (!q || !k_pool || !v_pool || !tables))) {
@@ -649,7 +684,10 @@ paged_kv_status make_plan(Plan& pl, const paged_kv_pool_desc* desc, void* out, i
     pl.out_dtype = out_dtype;
     pl.head_dim = desc->head_dim;
     pl.mfma = desc->dtype != PAGED_KV_F32 && group >= 2;
-    pl.grid = dim3((unsigned)max_parts, (unsigned)(pl.mfma ? desc->num_kv_heads : hq), (unsigned)num_seqs);
+    // x: (sequence, head) pairs, y: partition.  All first partitions are dispatched
+    // first; the empty high partitions of short sequences come last and exit at once.
+    pl.grid = dim3((unsigned)((int64_t)num_seqs * (pl.mfma ? desc->num_kv_heads : hq)),
+                   (unsigned)max_parts);
     pl.stream = reinterpret_cast<hipStream_t>(stream);
     return PAGED_KV_OK;
 }
