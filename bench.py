@@ -38,7 +38,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", type=int, default=3, help="workload 1..5 (default 3: GQA 72B shape)")
-    ap.add_argument("--partition-tokens", type=int, default=512)
+    ap.add_argument("--partition-tokens", type=int, default=None,
+                    help="0: stream-K schedule; > 0: fixed partitions (default: the workload's)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="bound on the oracle's timed CPU work")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -159,8 +160,8 @@ def main():
     out_dtype = w.dtype
     out = torch.empty((len(seqs), w.num_q_heads, w.head_dim), dtype=TORCH_DTYPES[out_dtype], device=dev)
     max_ctx = int(lens.max())
-    pt = args.partition_tokens
-    ws_bytes = B.paged_attention_workspace_bytes(len(seqs), w.num_q_heads, w.head_dim, max_ctx, pt)
+    pt = w.partition_tokens if args.partition_tokens is None else args.partition_tokens
+    ws_bytes = B.paged_attention_workspace_bytes(cache.desc, len(seqs), w.num_q_heads, max_ctx, pt)
     ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
 

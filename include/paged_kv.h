@@ -196,10 +196,12 @@ paged_kv_status reshape_and_cache(const paged_kv_pool_desc* desc, const void* ke
                                   void* k_pool, void* v_pool, const int32_t* slot_mapping,
                                   int32_t num_tokens, void* stream);
 
-/* Bytes of workspace paged_attention_decode needs (0 when no sequence can span more
- * than one partition).  partition_tokens 0 = the default (512). */
-size_t paged_attention_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
-                                       int32_t max_context_len, int32_t partition_tokens);
+/* Bytes of workspace paged_attention_decode needs for this batch shape and pool (0 when
+ * nothing needs merging).  Same partition_tokens convention as paged_attention_decode.
+ * 0 if an argument is invalid. */
+size_t paged_attention_workspace_bytes(const paged_kv_pool_desc* desc, int32_t num_seqs,
+                                       int32_t num_q_heads, int32_t max_context_len,
+                                       int32_t partition_tokens);
 
 /* Paged decode attention ([DS] §2.2, §2.6; [CD]; [DL] PagedAttention vs.
  * FlashAttention): for every sequence s and query head h,
@@ -214,8 +216,13 @@ size_t paged_attention_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, in
  *                 sequence's last block are never read
  *   context_lens  device int32[num_seqs]
  *   max_context_len  host bound on every context_lens[s] (sizes the launch)
- *   partition_tokens tokens per split-K partition (multiple of 16; 0 = 512).  Sequences
- *                 longer than one partition are reduced by a log-sum-exp merge.
+ *   partition_tokens 0: stream-K schedule — the batch's (sequence, head unit,
+ *                 16-token block) tiles are split evenly over a fixed set of waves
+ *                 (3072 on MI355X, fewer for small batches) and the pieces of a
+ *                 sequence's head unit cut by those splits are merged by log-sum-exp
+ *                 (used for up to 8192 sequences; larger batches fall back to 512-token
+ *                 partitions).  > 0: fixed split-K partitions of that many tokens
+ *                 (multiple of 16), merged the same way.
  *   workspace     device buffer of paged_attention_workspace_bytes(...) bytes
  *                 (may be NULL when that is 0); contents on entry are ignored.
  * A sequence whose context_len is outside [1, max_context_len], or whose table holds

@@ -74,7 +74,7 @@ _SIGNATURES = {
     "paged_kv_stats": (ctypes.c_int, [_vp, _i64p, _i64p, _i64p]),
     "paged_kv_copy_blocks": (ctypes.c_int, [_descp, _vp, _vp, _vp, _i32, _vp]),
     "reshape_and_cache": (ctypes.c_int, [_descp, _vp, _vp, _i64, _i64, _vp, _vp, _vp, _i32, _vp]),
-    "paged_attention_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32]),
+    "paged_attention_workspace_bytes": (_sz, [_descp, _i32, _i32, _i32, _i32]),
     "paged_attention_decode": (ctypes.c_int, [_descp, _vp, _i32, _vp, _vp, _vp, _vp, _i32, _vp,
                                               _i32, _i32, _i32, _f32, _i32, _vp, _sz, _vp]),
     "paged_attention_partition": (ctypes.c_int, [_descp, _vp, _i32, _vp, _vp, _vp, _vp, _i32, _vp,
@@ -286,9 +286,9 @@ def reshape_and_cache(desc, key, value, k_pool, v_pool, slot_mapping, num_tokens
                                  int(num_tokens), _stream(stream)))
 
 
-def paged_attention_workspace_bytes(num_seqs, num_q_heads, head_dim, max_context_len,
+def paged_attention_workspace_bytes(desc, num_seqs, num_q_heads, max_context_len,
                                     partition_tokens=0):
-    return int(lib.paged_attention_workspace_bytes(num_seqs, num_q_heads, head_dim,
+    return int(lib.paged_attention_workspace_bytes(ctypes.byref(desc), num_seqs, num_q_heads,
                                                    max_context_len, partition_tokens))
 
 

@@ -1,0 +1,55 @@
+// Host-side plan of the stream-K decode attention launch (shared between the two
+// translation units that launch attention kernels).
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+
+#include "paged_kv.h"
+
+namespace pkv {
+
+// Stream-K decomposition: the (sequence, head unit, 16-token block) tiles of the
+// whole batch form one line; `waves` waves each take an equal contiguous slice of it.
+// 3072 = 256 CUs x 4 SIMDs x 3 resident waves of the MFMA kernel on MI355X.
+constexpr int kStreamMaxWaves = 3072;
+// The per-sequence tile prefix is built in LDS by every workgroup.
+constexpr int kStreamMaxSeqs = 8192;
+
+struct StreamPlan {
+    bool mfma;             // MFMA kernel (unit = KV head) or VALU kernel (unit = query head)
+    int32_t units;         // head units per sequence
+    int32_t heads_per_unit;
+    int32_t waves;         // W
+    int64_t max_pieces;    // W + num_seqs * units: upper bound on partial results
+    size_t meta_off, m_off, l_off, acc_off, ws_bytes;
+};
+
+// Plan for a batch; `ok` false when the shape is outside what stream-K serves.
+StreamPlan stream_plan(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                       int32_t dtype, int32_t head_dim, int32_t max_context_len, bool* ok);
+
+struct StreamLaunch {
+    void* out;
+    int32_t out_dtype;
+    const void* q;
+    const void* k_pool;
+    const void* v_pool;
+    const int32_t* block_tables;
+    int32_t max_blocks_per_seq;
+    const int32_t* context_lens;
+    int32_t num_seqs;
+    int32_t num_q_heads;
+    int32_t num_kv_heads;
+    int32_t num_blocks;
+    int32_t dtype;
+    int32_t head_dim;
+    int32_t max_context_len;
+    float scale;
+    void* workspace;
+};
+
+void launch_streamk_partition(const StreamLaunch& L, const StreamPlan& P, void* stream);
+void launch_streamk_reduce(const StreamLaunch& L, const StreamPlan& P, void* stream);
+
+}  // namespace pkv

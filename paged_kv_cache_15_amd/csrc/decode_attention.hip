@@ -30,65 +30,12 @@
 // so one (block, KV head) tile is 16 * head_dim contiguous elements, and the MFMA
 // operand loads below are contiguous across the 64 lanes of each load instruction.
 
-#include <hip/hip_runtime.h>
-
-#include <cmath>
-#include <type_traits>
-
-#include "common.h"
+#include "attention_common.h"
+#include "attention_host.h"
 
 namespace {
 
-typedef __attribute__((__vector_size__(4 * sizeof(int)))) int i32x4;
-typedef __attribute__((__vector_size__(2 * sizeof(int)))) int i32x2;
-typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
-typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
-typedef __attribute__((__vector_size__(4 * sizeof(short)))) short s16x4;
-typedef __attribute__((__vector_size__(8 * sizeof(_Float16)))) _Float16 f16x8;
-typedef __attribute__((__vector_size__(4 * sizeof(_Float16)))) _Float16 f16x4;
-
-constexpr int kBS = pkv::kKernelBlockSize;  // tokens per block
-constexpr int kWaves = 4;                   // waves per partition workgroup
-constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kNegInf = -INFINITY;
-constexpr float kRescaleSlack = 8.f;        // log2 units: weights stay below 2^8
-
-enum { DT_F32 = 0, DT_F16 = 1, DT_BF16 = 2 };
-
-__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
-
-// 16-bit storage bits -> float
-template <int DT>
-__device__ __forceinline__ float bits_to_f32(uint32_t b) {
-    if constexpr (DT == DT_BF16) return __uint_as_float(b << 16);
-    else if constexpr (DT == DT_F16) return (float)__builtin_bit_cast(_Float16, (uint16_t)b);
-    else return __uint_as_float(b);
-}
-
-// float -> 16-bit storage bits, round to nearest even
-template <int DT>
-__device__ __forceinline__ uint16_t f32_to_bits16(float f) {
-    if constexpr (DT == DT_BF16) return __builtin_bit_cast(uint16_t, (__bf16)f);
-    else return __builtin_bit_cast(uint16_t, (_Float16)f);
-}
-
-template <int OUT_DT>
-__device__ __forceinline__ void store_out(void* out, int64_t i, float v) {
-    if constexpr (OUT_DT == DT_F32) static_cast<float*>(out)[i] = v;
-    else static_cast<uint16_t*>(out)[i] = f32_to_bits16<OUT_DT>(v);
-}
-
-// max over the lanes that share lane % 16 (xor 16, 32)
-__device__ __forceinline__ float max_across_quads(float v) {
-    v = fmaxf(v, __shfl_xor(v, 16));
-    v = fmaxf(v, __shfl_xor(v, 32));
-    return v;
-}
-__device__ __forceinline__ float sum_across_quads(float v) {
-    v += __shfl_xor(v, 16);
-    v += __shfl_xor(v, 32);
-    return v;
-}
+using namespace pkv_dev;
 
 struct PartitionArgs {
     void* out;
@@ -594,10 +541,19 @@ struct Plan {
     PartitionArgs a;
     int dtype, out_dtype, head_dim;
     bool mfma;
+    bool streamk;              // stream-K schedule (partition_tokens 0) or fixed partitions
+    pkv::StreamPlan sp;
+    pkv::StreamLaunch sl;
     dim3 grid;
     size_t ws_needed;
     hipStream_t stream;
 };
+
+// partition_tokens 0 selects stream-K when the batch fits its limits, else the default
+// fixed partition size; workspace sizing and both launches apply the same rule.
+bool use_streamk(int32_t part_tokens, int32_t num_seqs) {
+    return part_tokens == 0 && num_seqs <= pkv::kStreamMaxSeqs;
+}
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
@@ -632,6 +588,7 @@ paged_kv_status make_plan(Plan& pl, const paged_kv_pool_desc* desc, void* out, i
         return PAGED_KV_ERR_INVALID_ARG;
     }
     if (max_ctx < 1) { pkv::set_error("max_context_len must be >= 1"); return PAGED_KV_ERR_INVALID_ARG; }
+    pl.streamk = use_streamk(part_tokens, num_seqs);
     if (part_tokens == 0) part_tokens = pkv::kDefaultPartitionTokens;
     if (part_tokens < 0 || part_tokens % kBS) {
         pkv::set_error("partition_tokens %d must be a positive multiple of %d", part_tokens, kBS);
@@ -644,7 +601,14 @@ paged_kv_status make_plan(Plan& pl, const paged_kv_pool_desc* desc, void* out, i
     if (num_seqs > 65535) { pkv::set_error("at most 65535 sequences per launch"); return PAGED_KV_ERR_UNSUPPORTED; }
     const int max_parts = (max_ctx + part_tokens - 1) / part_tokens;
     if (max_parts > 65535) { pkv::set_error("at most 65535 partitions per sequence"); return PAGED_KV_ERR_UNSUPPORTED; }
-    pl.ws_needed = workspace_for(num_seqs, hq, desc->head_dim, max_parts);
+    if (pl.streamk) {
+        bool ok = false;
+        pl.sp = pkv::stream_plan(num_seqs, hq, desc->num_kv_heads, desc->dtype, desc->head_dim,
+                                 max_ctx, &ok);
+        pl.ws_needed = pl.sp.ws_bytes;
+    } else {
+        pl.ws_needed = workspace_for(num_seqs, hq, desc->head_dim, max_parts);
+    }
     if (num_seqs > 0) {
         if (!out || !lens || (need_kv && (!q || !k_pool || !v_pool || !tables))) {
             pkv::set_error("null pointer argument");
@@ -689,6 +653,9 @@ paged_kv_status make_plan(Plan& pl, const paged_kv_pool_desc* desc, void* out, i
     pl.grid = dim3((unsigned)((int64_t)num_seqs * (pl.mfma ? desc->num_kv_heads : hq)),
                    (unsigned)max_parts);
     pl.stream = reinterpret_cast<hipStream_t>(stream);
+    pl.sl = pkv::StreamLaunch{out, out_dtype, q, k_pool, v_pool, tables, max_blocks, lens,
+                              num_seqs, hq, desc->num_kv_heads, desc->num_blocks, desc->dtype,
+                              desc->head_dim, max_ctx, scale, ws};
     return PAGED_KV_OK;
 }
 
@@ -747,13 +714,21 @@ paged_kv_status launch_status(const char* what) {
 
 extern "C" {
 
-size_t paged_attention_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
-                                       int32_t max_context_len, int32_t partition_tokens) {
-    if (num_seqs < 0 || num_q_heads < 1 || head_dim < 1 || max_context_len < 1) return 0;
+size_t paged_attention_workspace_bytes(const paged_kv_pool_desc* desc, int32_t num_seqs,
+                                       int32_t num_q_heads, int32_t max_context_len,
+                                       int32_t partition_tokens) {
+    if (!pkv::valid_desc(desc) || num_seqs < 0 || num_q_heads < 1 || max_context_len < 1 ||
+        partition_tokens < 0 || num_q_heads % desc->num_kv_heads)
+        return 0;
+    if (use_streamk(partition_tokens, num_seqs)) {
+        bool ok = false;
+        pkv::StreamPlan p = pkv::stream_plan(num_seqs, num_q_heads, desc->num_kv_heads, desc->dtype,
+                                             desc->head_dim, max_context_len, &ok);
+        return ok ? p.ws_bytes : 0;
+    }
     if (partition_tokens == 0) partition_tokens = pkv::kDefaultPartitionTokens;
-    if (partition_tokens < 0) return 0;
     const int64_t max_parts = (max_context_len + (int64_t)partition_tokens - 1) / partition_tokens;
-    return workspace_for(num_seqs, num_q_heads, head_dim, max_parts);
+    return workspace_for(num_seqs, num_q_heads, desc->head_dim, max_parts);
 }
 
 paged_kv_status paged_attention_partition(const paged_kv_pool_desc* desc, void* out,
@@ -771,7 +746,8 @@ paged_kv_status paged_attention_partition(const paged_kv_pool_desc* desc, void* 
                                    max_context_len, scale, partition_tokens, workspace,
                                    workspace_bytes, stream, true);
     if (st != PAGED_KV_OK || num_seqs == 0) return st;
-    if (pl.head_dim == 64) launch_partition_dd<64>(pl);
+    if (pl.streamk) pkv::launch_streamk_partition(pl.sl, pl.sp, stream);
+    else if (pl.head_dim == 64) launch_partition_dd<64>(pl);
     else launch_partition_dd<128>(pl);
     return launch_status("paged attention partition kernel");
 }
@@ -788,7 +764,12 @@ paged_kv_status paged_attention_reduce(const paged_kv_pool_desc* desc, void* out
                                    max_blocks, context_lens, num_seqs, num_q_heads, max_context_len,
                                    1.f, partition_tokens, const_cast<void*>(workspace),
                                    workspace_bytes, stream, false);
-    if (st != PAGED_KV_OK || num_seqs == 0 || pl.a.max_parts <= 1) return st;
+    if (st != PAGED_KV_OK || num_seqs == 0) return st;
+    if (pl.streamk) {
+        pkv::launch_streamk_reduce(pl.sl, pl.sp, stream);
+        return launch_status("paged attention merge kernel");
+    }
+    if (pl.a.max_parts <= 1) return st;
     if (pl.head_dim == 64) launch_reduce_d<64>(pl, num_seqs);
     else launch_reduce_d<128>(pl, num_seqs);
     return launch_status("paged attention reduce kernel");

@@ -1,0 +1,737 @@
+// Stream-K paged decode attention for gfx950.
+//
+// Same computation as the fixed-partition kernels (deepsonar "PagedAttention de vLLM
+// …" §2.2/§2.6: gather a sequence's blocks through its table; deeplearn.tn
+// "PagedAttention : comment optimiser la mémoire GPU …", PagedAttention vs.
+// FlashAttention: stream K/V tiles through on-chip memory with an incremental
+// softmax), scheduled differently:
+//
+// Every (sequence, head unit, 16-token block) of the batch is a tile; tiles are laid on
+// one line ordered by sequence, then unit, then block.  A fixed number W of waves each
+// take an equal contiguous slice of the line (to within one tile) and stream it with a
+// two-deep load pipeline that never restarts at sequence or head boundaries.  When a
+// wave's slice covers a whole (sequence, unit) the wave writes the normalised output;
+// otherwise it writes the piece's (max, sum, weighted values) and the merge kernel
+// combines the pieces of that (sequence, unit) in slice order (log-sum-exp).  Piece
+// index = wave index + (sequence, unit) index: along the line every wave boundary and
+// every unit boundary starts a new piece, so this numbering is dense and collision-free.
+//
+// Units: the MFMA kernel's unit is a KV head with its group of query heads (fp16/bf16,
+// group >= 2); the VALU kernel's unit is one query head.
+//
+// Results depend only on the logical token order and on W, never on where blocks sit
+// in the pool: placement and sharing leave them bit-identical.
+
+#include "attention_common.h"
+#include "attention_host.h"
+
+namespace {
+
+using namespace pkv_dev;
+
+struct StreamArgs {
+    void* out;
+    const void* q;
+    const void* k_pool;
+    const void* v_pool;
+    const int32_t* block_tables;
+    const int32_t* context_lens;
+    int32_t* meta;     // per-sequence tile prefix, written by workgroup 0 for the merge
+    float* ws_m;
+    float* ws_l;
+    float* ws_acc;
+    int32_t num_seqs;
+    int32_t max_blocks_per_seq;
+    int32_t num_q_heads;
+    int32_t num_kv_heads;
+    int32_t group;           // query heads per KV head
+    int32_t units;           // head units per sequence
+    int32_t heads_per_unit;  // query heads per unit
+    int32_t num_blocks;
+    int32_t max_context_len;
+    int32_t waves;           // W
+    float scale_log2;
+};
+
+// Read-only int32 through the scalar data cache: block tables and context lengths are
+// never written while a kernel runs, and a scalar load keeps the per-tile lookups off the
+// vector memory counter, so they never force a wait on the K/V loads in flight.
+__device__ __forceinline__ int32_t sload(const int32_t* p, int64_t i) {
+    return ((const __attribute__((address_space(4))) int32_t*)p)[i];
+}
+
+__device__ __forceinline__ int tiles_of(int ctx, int max_ctx) {
+    return (ctx >= 1 && ctx <= max_ctx) ? (ctx + kBS - 1) / kBS : 0;
+}
+
+// Exclusive prefix of per-sequence tile counts (per unit) into s_pref[0..B]; returns
+// s_pref[B].  Called by every thread of the workgroup.
+__device__ int build_prefix(const StreamArgs& a, int* s_pref) {
+    __shared__ int s_wsum[kWaves];
+    const int B = a.num_seqs, tid = threadIdx.x, nthr = blockDim.x;
+    const int lane = tid & 63, w = tid >> 6;
+    const int chunk = (B + nthr - 1) / nthr;
+    const int lo = min(B, tid * chunk), hi = min(B, lo + chunk);
+    int sum = 0;
+    for (int i = lo; i < hi; ++i) sum += tiles_of(a.context_lens[i], a.max_context_len);
+    int incl = sum;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int v = __shfl_up(incl, o);
+        if (lane >= o) incl += v;
+    }
+    if (lane == 63) s_wsum[w] = incl;
+    __syncthreads();
+    int off = 0;
+    for (int ww = 0; ww < w; ++ww) off += s_wsum[ww];
+    int run = off + incl - sum;
+    for (int i = lo; i < hi; ++i) {
+        s_pref[i] = run;
+        run += tiles_of(a.context_lens[i], a.max_context_len);
+    }
+    if (tid == nthr - 1) s_pref[B] = off + incl;
+    __syncthreads();
+    return s_pref[B];
+}
+
+// Position on the tile line, kept in scalar registers (every value is wave-uniform).
+struct Cursor {
+    int s, u, it, nt, ctx;
+};
+
+__device__ __forceinline__ int uni(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+// Cursor of tile t: sequence = the last s with units * pref[s] <= t (it has >= 1 tile).
+__device__ Cursor locate(const StreamArgs& a, const int* s_pref, int64_t t) {
+    int lo = 0, hi = a.num_seqs - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if ((int64_t)a.units * uni(s_pref[mid]) <= t) lo = mid;
+        else hi = mid - 1;
+    }
+    Cursor c;
+    c.s = lo;
+    const int base = uni(s_pref[lo]);
+    c.nt = uni(s_pref[lo + 1]) - base;
+    const int64_t o = t - (int64_t)a.units * base;
+    c.u = (int)(o / c.nt);
+    c.it = (int)(o - (int64_t)c.u * c.nt);
+    c.ctx = sload(a.context_lens, lo);
+    return c;
+}
+
+// Next tile on the line (only called while one exists).
+__device__ __forceinline__ void advance(const StreamArgs& a, Cursor& c) {
+    if (++c.it < c.nt) return;
+    c.it = 0;
+    if (++c.u < a.units) return;
+    c.u = 0;
+    do {
+        ++c.s;
+        c.ctx = sload(a.context_lens, c.s);
+        c.nt = tiles_of(c.ctx, a.max_context_len);
+    } while (c.nt == 0 && c.s < a.num_seqs - 1);
+}
+
+// Physical block of the cursor's tile; out-of-range ids read block 0 and flag the unit.
+__device__ __forceinline__ int32_t tile_block(const StreamArgs& a, const Cursor& c, bool& bad) {
+    const int32_t bid = sload(a.block_tables, (int64_t)c.s * a.max_blocks_per_seq + c.it);
+    bad = (uint32_t)bid >= (uint32_t)a.num_blocks;
+    return bad ? 0 : bid;
+}
+
+__device__ __forceinline__ void wave_slice(const StreamArgs& a, int64_t T, int j, int64_t& t0,
+                                           int64_t& t1) {
+    t0 = (int64_t)j * T / a.waves;
+    t1 = (int64_t)(j + 1) * T / a.waves;
+}
+
+// ---------------------------------------------------------------------------------
+// MFMA stream-K kernel (fp16/bf16, 2..16 query heads per KV head).  The per-tile math
+// is the fixed-partition MFMA kernel's: S^T = K.Q^T with 16x16x32 MFMAs, lazy-rescaled
+// base-2 softmax, O^T += V^T.P^T with P split into 16-bit head + remainder.
+// ---------------------------------------------------------------------------------
+template <int D, int DT, int OUT_DT>
+__global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(3)))
+void attn_mfma_streamk(StreamArgs a) {
+    constexpr int KI = D / 32;
+    constexpr int MT = D / 16;
+    constexpr int TILE = kBS * D;
+    using kvec = typename std::conditional<DT == DT_BF16, bf16x8, f16x8>::type;
+
+    extern __shared__ int s_pref[];
+    const int tiles_per_unit = build_prefix(a, s_pref);
+    if (blockIdx.x == 0)
+        for (int i = threadIdx.x; i <= a.num_seqs; i += blockDim.x) a.meta[i] = s_pref[i];
+    const int lane = threadIdx.x & 63;
+    const int j = uni(blockIdx.x * kWaves + (threadIdx.x >> 6));
+    if (j >= a.waves) return;
+    const int64_t T = (int64_t)a.units * tiles_per_unit;
+    int64_t t0, t1;
+    wave_slice(a, T, j, t0, t1);
+    if (t0 >= t1) return;
+    const int n = (int)(t1 - t0);
+    const int gq = lane & 15, quad = lane >> 4;
+    const int G = a.heads_per_unit;
+    // Padded head slots (gq >= G) reuse head G-1's query: their score and value columns
+    // are computed and never written.  (Zeroing them would need a wait on the query
+    // load right where it is issued, draining the K/V prefetch.)
+    const int gqc = min(gq, G - 1);
+    const int64_t blk_stride = (int64_t)a.num_kv_heads * TILE;
+    const int voff = gq * 4 + quad;
+    const uint16_t* kpool = static_cast<const uint16_t*>(a.k_pool);
+    const uint16_t* vpool = static_cast<const uint16_t*>(a.v_pool);
+
+    Cursor lc = locate(a, s_pref, t0);   // tile being loaded (one ahead)
+    Cursor cc = lc;                       // tile being computed
+
+    kvec qop[KI];
+    auto load_q = [&](const Cursor& c) {
+        const uint16_t* qh = static_cast<const uint16_t*>(a.q) +
+                             ((int64_t)c.s * a.num_q_heads + c.u * G + gqc) * D + 8 * quad;
+#pragma unroll
+        for (int kk = 0; kk < KI; ++kk)
+            qop[kk] = __builtin_bit_cast(kvec, *reinterpret_cast<const i32x4*>(qh + 32 * kk));
+    };
+    auto load_kv = [&](const Cursor& c, i32x4 (&kr)[KI], i32x2 (&vr)[MT], bool& bad) {
+        const int32_t bid = tile_block(a, c, bad);
+        const int64_t base = (int64_t)c.u * TILE + bid * blk_stride;
+        const i32x4* kt = reinterpret_cast<const i32x4*>(kpool + base);
+        const i32x2* vt = reinterpret_cast<const i32x2*>(vpool + base);
+#pragma unroll
+        for (int kk = 0; kk < KI; ++kk) kr[kk] = __builtin_nontemporal_load(kt + kk * 64 + lane);
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) vr[mt] = __builtin_nontemporal_load(vt + mt * 64 + voff);
+    };
+
+    f32x4 acc[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) acc[mt] = (f32x4){0.f, 0.f, 0.f, 0.f};
+    float m = kNegInf, lsum = 0.f;
+    bool unit_bad = false;
+    bool first_here = cc.it == 0;
+
+    // Write the finished (or slice-cut) unit of cursor c, then reset the state.
+    auto finish = [&](const Cursor& c) {
+        const bool direct = first_here && c.it == c.nt - 1;
+        const float lw = sum_across_quads(lsum);
+        const int q = c.s * a.units + c.u;
+        if (gq < G) {
+            if (direct) {
+                const int64_t ob = ((int64_t)c.s * a.num_q_heads + c.u * G + gq) * D;
+                const float inv = 1.f / lw;
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        store_out<OUT_DT>(a.out, ob + 16 * mt + 4 * quad + r,
+                                          unit_bad ? NAN : acc[mt][r] * inv);
+            } else {
+                const int64_t piece = ((int64_t)j + q) * G + gq;
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt)
+                    *reinterpret_cast<f32x4*>(a.ws_acc + piece * D + 16 * mt + 4 * quad) =
+                        unit_bad ? (f32x4){NAN, NAN, NAN, NAN} : acc[mt];
+                if (quad == 0) {
+                    a.ws_m[piece] = unit_bad ? NAN : m;
+                    a.ws_l[piece] = unit_bad ? NAN : lw;
+                }
+            }
+        }
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) acc[mt] = (f32x4){0.f, 0.f, 0.f, 0.f};
+        m = kNegInf;
+        lsum = 0.f;
+        unit_bad = false;
+        first_here = true;
+    };
+
+    // Compute the tile of cc from registers kr/vr.  If the next tile (nc) starts a new
+    // unit, its queries are loaded into qop once the score MFMAs have read them.
+    auto compute = [&](i32x4 (&kr)[KI], i32x2 (&vr)[MT], bool bad, bool next_unit,
+                       const Cursor& nc) {
+        f32x4 sc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < KI; ++kk) {
+            if constexpr (DT == DT_BF16)
+                sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kr[kk]),
+                                                             qop[kk], sc, 0, 0, 0);
+            else
+                sc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, kr[kk]),
+                                                            qop[kk], sc, 0, 0, 0);
+        }
+        if (next_unit) load_q(nc);
+        const int valid = min(kBS, cc.ctx - cc.it * kBS);   // tokens of this tile in the context
+        const int tok0 = 4 * quad;
+        float x[4];
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) x[jj] = (tok0 + jj < valid) ? sc[jj] * a.scale_log2 : kNegInf;
+        const float xm = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+        if (__ballot(xm > m + kRescaleSlack)) {
+            const float mnew = fmaxf(m, max_across_quads(xm));
+            const float alpha = exp2_fast(m - mnew);
+            lsum *= alpha;
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) acc[mt] *= alpha;
+            m = mnew;
+        }
+        s16x4 phi, plo;
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+            const float pf = exp2_fast(x[jj] - m);
+            const uint16_t hi = f32_to_bits16<DT>(pf);
+            const uint16_t lo = f32_to_bits16<DT>(pf - bits_to_f32<DT>(hi));
+            phi[jj] = (short)hi;
+            plo[jj] = (short)lo;
+            lsum += pf;
+        }
+        if (valid < kBS) {
+            // slots past the context may hold anything (NaN included): clear them
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) {
+                uint32_t lo = (uint32_t)vr[mt][0], hi = (uint32_t)vr[mt][1];
+                if (tok0 + 0 >= valid) lo &= 0xFFFF0000u;
+                if (tok0 + 1 >= valid) lo &= 0x0000FFFFu;
+                if (tok0 + 2 >= valid) hi &= 0xFFFF0000u;
+                if (tok0 + 3 >= valid) hi &= 0x0000FFFFu;
+                vr[mt][0] = (int)lo;
+                vr[mt][1] = (int)hi;
+            }
+        }
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+            if constexpr (DT == DT_BF16) {
+                const s16x4 va = __builtin_bit_cast(s16x4, vr[mt]);
+                acc[mt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, phi, acc[mt], 0, 0, 0);
+                acc[mt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, plo, acc[mt], 0, 0, 0);
+            } else {
+                const f16x4 va = __builtin_bit_cast(f16x4, vr[mt]);
+                acc[mt] = __builtin_amdgcn_mfma_f32_16x16x16f16(va, __builtin_bit_cast(f16x4, phi),
+                                                               acc[mt], 0, 0, 0);
+                acc[mt] = __builtin_amdgcn_mfma_f32_16x16x16f16(va, __builtin_bit_cast(f16x4, plo),
+                                                               acc[mt], 0, 0, 0);
+            }
+        }
+        unit_bad |= bad;
+    };
+
+    i32x4 kA[KI], kB[KI];
+    i32x2 vA[MT], vB[MT];
+    bool bA = false, bB = false;
+
+    // one pipeline step: load tile k+1 into (kn, vn), compute tile k from (kc, vc)
+    auto step = [&](i32x4 (&kc)[KI], i32x2 (&vc)[MT], bool bc, i32x4 (&kn)[KI],
+                    i32x2 (&vn)[MT], bool& bn) {
+        advance(a, lc);
+        load_kv(lc, kn, vn, bn);
+        const bool next_unit = lc.s != cc.s || lc.u != cc.u;
+        compute(kc, vc, bc, next_unit, lc);
+        if (next_unit) finish(cc);
+        cc = lc;
+    };
+
+    load_q(cc);
+    load_kv(lc, kA, vA, bA);
+    int k = 0;
+    for (; k + 2 < n; k += 2) {
+        step(kA, vA, bA, kB, vB, bB);
+        step(kB, vB, bB, kA, vA, bA);
+    }
+    if (k + 1 < n) {
+        step(kA, vA, bA, kB, vB, bB);
+        compute(kB, vB, bB, false, cc);
+    } else {
+        compute(kA, vA, bA, false, cc);
+    }
+    finish(cc);
+}
+
+// ---------------------------------------------------------------------------------
+// VALU stream-K kernel: unit = one query head (a group of 1, or fp32).  The per-tile
+// math is the fixed-partition VALU kernel's.
+// ---------------------------------------------------------------------------------
+template <int D, int DT, int OUT_DT>
+__global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(3)))
+void attn_valu_streamk(StreamArgs a) {
+    using bits_t = typename std::conditional<DT == DT_F32, uint32_t, uint16_t>::type;
+    constexpr int E = sizeof(bits_t);
+    constexpr int X = 16 / E;
+    constexpr int NI = kBS * D * E / 1024;
+    constexpr int TILE = kBS * D;
+
+    extern __shared__ int s_pref[];
+    const int tiles_per_unit = build_prefix(a, s_pref);
+    if (blockIdx.x == 0)
+        for (int i = threadIdx.x; i <= a.num_seqs; i += blockDim.x) a.meta[i] = s_pref[i];
+    const int lane = threadIdx.x & 63;
+    const int j = uni(blockIdx.x * kWaves + (threadIdx.x >> 6));
+    if (j >= a.waves) return;
+    const int64_t T = (int64_t)a.units * tiles_per_unit;
+    int64_t t0, t1;
+    wave_slice(a, T, j, t0, t1);
+    if (t0 >= t1) return;
+    const int n = (int)(t1 - t0);
+    const int tok = lane & 15, kq = lane >> 4, vpiece = lane % E;
+    const int64_t blk_stride = (int64_t)a.num_kv_heads * TILE;
+    const bits_t* kpool = static_cast<const bits_t*>(a.k_pool);
+    const bits_t* vpool = static_cast<const bits_t*>(a.v_pool);
+
+    Cursor lc = locate(a, s_pref, t0);
+    Cursor cc = lc;
+
+    // query: raw bits of the lane's D/4 dims (chunks 4*i + kq), converted on unit change
+    i32x4 qraw[NI];
+    float qr[NI][X];
+    auto load_q = [&](const Cursor& c) {
+        const i32x4* qh = reinterpret_cast<const i32x4*>(
+            static_cast<const bits_t*>(a.q) + ((int64_t)c.s * a.num_q_heads + c.u) * D);
+#pragma unroll
+        for (int i = 0; i < NI; ++i) qraw[i] = qh[4 * i + kq];
+    };
+    auto convert_q = [&]() {
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+            bits_t qb[X];
+            __builtin_memcpy(qb, &qraw[i], 16);
+#pragma unroll
+            for (int e = 0; e < X; ++e) qr[i][e] = bits_to_f32<DT>(qb[e]) * a.scale_log2;
+        }
+    };
+    auto load_kv = [&](const Cursor& c, i32x4 (&kr)[NI], i32x4 (&vr)[NI], bool& bad) {
+        const int32_t bid = tile_block(a, c, bad);
+        const int64_t base = (int64_t)(c.u / a.group) * TILE + bid * blk_stride;
+        const i32x4* kt = reinterpret_cast<const i32x4*>(kpool + base);
+        const i32x4* vt = reinterpret_cast<const i32x4*>(vpool + base);
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+            kr[i] = __builtin_nontemporal_load(kt + i * 64 + lane);
+            vr[i] = __builtin_nontemporal_load(vt + i * 64 + lane);
+        }
+    };
+
+    float acc[NI];
+#pragma unroll
+    for (int i = 0; i < NI; ++i) acc[i] = 0.f;
+    float m = kNegInf, lsum = 0.f;
+    bool unit_bad = false;
+    bool first_here = cc.it == 0;
+    bool q_stale = false;    // qraw holds the next unit's query, not yet converted
+
+    auto finish = [&](const Cursor& c) {
+        const bool direct = first_here && c.it == c.nt - 1;
+        float lw = lsum;
+        lw += __shfl_xor(lw, 1);
+        lw += __shfl_xor(lw, 2);
+        lw += __shfl_xor(lw, 4);
+        lw += __shfl_xor(lw, 8);
+        float rows[NI];
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+            float r = acc[i];
+            if constexpr (E >= 2) r += __shfl_xor(r, 1);
+            if constexpr (E >= 4) r += __shfl_xor(r, 2);
+            rows[i] = r;
+        }
+        const int q = c.s * a.units + c.u;
+        if (vpiece == 0) {
+            if (direct) {
+                const int64_t ob = ((int64_t)c.s * a.num_q_heads + c.u) * D;
+                const float inv = 1.f / lw;
+#pragma unroll
+                for (int i = 0; i < NI; ++i)
+                    store_out<OUT_DT>(a.out, ob + (64 * i + lane) / E, unit_bad ? NAN : rows[i] * inv);
+            } else {
+                const int64_t piece = (int64_t)j + q;
+#pragma unroll
+                for (int i = 0; i < NI; ++i)
+                    a.ws_acc[piece * D + (64 * i + lane) / E] = unit_bad ? NAN : rows[i];
+                if (lane == 0) {
+                    a.ws_m[piece] = unit_bad ? NAN : m;
+                    a.ws_l[piece] = unit_bad ? NAN : lw;
+                }
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < NI; ++i) acc[i] = 0.f;
+        m = kNegInf;
+        lsum = 0.f;
+        unit_bad = false;
+        first_here = true;
+    };
+
+    auto compute = [&](i32x4 (&kr)[NI], i32x4 (&vr)[NI], bool bad, bool next_unit,
+                       const Cursor& nc) {
+        if (q_stale) {
+            convert_q();
+            q_stale = false;
+        }
+        float part = 0.f;
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+            bits_t kb[X];
+            __builtin_memcpy(kb, &kr[i], 16);
+#pragma unroll
+            for (int e = 0; e < X; ++e) part = fmaf(qr[i][e], bits_to_f32<DT>(kb[e]), part);
+        }
+        if (next_unit) {
+            load_q(nc);
+            q_stale = true;
+        }
+        const float sc = sum_across_quads(part);
+        const int valid = min(kBS, cc.ctx - cc.it * kBS);
+        const float x = tok < valid ? sc : kNegInf;
+        if (__ballot(x > m + kRescaleSlack)) {
+            float mb = x;
+            mb = fmaxf(mb, __shfl_xor(mb, 1));
+            mb = fmaxf(mb, __shfl_xor(mb, 2));
+            mb = fmaxf(mb, __shfl_xor(mb, 4));
+            mb = fmaxf(mb, __shfl_xor(mb, 8));
+            const float mnew = fmaxf(m, mb);
+            const float alpha = exp2_fast(m - mnew);
+            lsum *= alpha;
+#pragma unroll
+            for (int i = 0; i < NI; ++i) acc[i] *= alpha;
+            m = mnew;
+        }
+        const float pt = exp2_fast(x - m);
+        lsum += pt;
+        float pw[X];
+#pragma unroll
+        for (int e = 0; e < X; ++e) pw[e] = __shfl(pt, vpiece * X + e);
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+            bits_t vb[X];
+            __builtin_memcpy(vb, &vr[i], 16);
+            float r = acc[i];
+#pragma unroll
+            for (int e = 0; e < X; ++e) {
+                const float v = (vpiece * X + e < valid) ? bits_to_f32<DT>(vb[e]) : 0.f;
+                r = fmaf(pw[e], v, r);
+            }
+            acc[i] = r;
+        }
+        unit_bad |= bad;
+    };
+
+    i32x4 kA[NI], kB[NI], vA[NI], vB[NI];
+    bool bA = false, bB = false;
+    auto step = [&](i32x4 (&kc)[NI], i32x4 (&vc)[NI], bool bc, i32x4 (&kn)[NI],
+                    i32x4 (&vn)[NI], bool& bn) {
+        advance(a, lc);
+        load_kv(lc, kn, vn, bn);
+        const bool next_unit = lc.s != cc.s || lc.u != cc.u;
+        compute(kc, vc, bc, next_unit, lc);
+        if (next_unit) finish(cc);
+        cc = lc;
+    };
+
+    load_q(cc);
+    q_stale = true;
+    load_kv(lc, kA, vA, bA);
+    int k = 0;
+    for (; k + 2 < n; k += 2) {
+        step(kA, vA, bA, kB, vB, bB);
+        step(kB, vB, bB, kA, vA, bA);
+    }
+    if (k + 1 < n) {
+        step(kA, vA, bA, kB, vB, bB);
+        compute(kB, vB, bB, false, cc);
+    } else {
+        compute(kA, vA, bA, false, cc);
+    }
+    finish(cc);
+}
+
+// ---------------------------------------------------------------------------------
+// Merge.  Units that one wave covered entirely were written by that wave; the others
+// combine their pieces in slice order:
+// out = sum_p 2^(m_p - M) acc_p / sum_p 2^(m_p - M) l_p, M = max_p m_p.
+// ---------------------------------------------------------------------------------
+__device__ __forceinline__ int wave_of(int64_t t, int64_t T, int W) {
+    return (int)(((t + 1) * W - 1) / T);   // the wave whose slice holds tile t
+}
+
+// With fewer tiles than waves some slices are empty; those waves wrote no piece.
+__device__ __forceinline__ bool slice_empty(int j, int64_t T, int W) {
+    return (int64_t)(j + 1) * T / W == (int64_t)j * T / W;
+}
+
+// One wave per (sequence, unit, query head of the unit).  Lanes first hold one piece
+// each (its max and sum), then one or two head dims each for the weighted sum over the
+// pieces, taken in slice order.
+template <int D, int OUT_DT>
+__global__ __launch_bounds__(kWaves * 64) void attn_streamk_reduce(StreamArgs a) {
+    constexpr int DPL = D / 64;   // head dims per lane
+    const int lane = threadIdx.x & 63;
+    const int G = a.heads_per_unit;
+    const int64_t job = (int64_t)blockIdx.x * kWaves + (threadIdx.x >> 6);
+    if (job >= (int64_t)a.num_seqs * a.units * G) return;
+    const int q = (int)(job / G), gq = (int)(job - (int64_t)q * G);
+    const int s = q / a.units, u = q - s * a.units;
+    const int64_t ob = ((int64_t)s * a.num_q_heads + u * G + gq) * D + lane;
+    const int ctx = sload(a.context_lens, s);
+    if (ctx < 1 || ctx > a.max_context_len) {
+#pragma unroll
+        for (int i = 0; i < DPL; ++i) store_out<OUT_DT>(a.out, ob + 64 * i, NAN);
+        return;
+    }
+    const int nt = (ctx + kBS - 1) / kBS;
+    const int64_t T = (int64_t)a.units * sload(a.meta, a.num_seqs);
+    const int64_t ta = (int64_t)a.units * sload(a.meta, s) + (int64_t)u * nt;
+    const int jf = wave_of(ta, T, a.waves), jl = wave_of(ta + nt - 1, T, a.waves);
+    if (jf == jl) return;   // one wave held the whole unit and wrote the output
+
+    float mm = kNegInf;
+    bool nan_seen = false;
+    for (int j0 = jf; j0 <= jl; j0 += 64) {
+        const int jj = j0 + lane;
+        if (jj <= jl && !slice_empty(jj, T, a.waves)) {
+            const float mj = a.ws_m[((int64_t)jj + q) * G + gq];
+            nan_seen |= mj != mj;
+            mm = fmaxf(mm, mj);
+        }
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) mm = fmaxf(mm, __shfl_xor(mm, o));
+    nan_seen = __ballot(nan_seen) != 0;
+
+    float l = 0.f, acc[DPL];
+#pragma unroll
+    for (int i = 0; i < DPL; ++i) acc[i] = 0.f;
+    for (int j0 = jf; j0 <= jl; j0 += 64) {
+        const int jj = j0 + lane;
+        float wgt = 0.f;
+        bool have = false;
+        if (jj <= jl && !slice_empty(jj, T, a.waves)) {
+            const int64_t piece = ((int64_t)jj + q) * G + gq;
+            wgt = exp2_fast(a.ws_m[piece] - mm);
+            l += wgt * a.ws_l[piece];
+            have = true;
+        }
+        const uint64_t mask = __ballot(have);
+        const int cnt = min(64, jl - j0 + 1);
+        for (int k = 0; k < cnt; ++k) {
+            if (!((mask >> k) & 1)) continue;            // empty slice: no piece
+            const float wk = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wgt), k));
+            const float* src = a.ws_acc + (((int64_t)j0 + k + q) * G + gq) * D + lane;
+#pragma unroll
+            for (int i = 0; i < DPL; ++i) acc[i] = fmaf(wk, src[64 * i], acc[i]);
+        }
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) l += __shfl_xor(l, o);
+    const float inv = 1.f / l;
+#pragma unroll
+    for (int i = 0; i < DPL; ++i) store_out<OUT_DT>(a.out, ob + 64 * i, nan_seen ? NAN : acc[i] * inv);
+}
+
+StreamArgs make_args(const pkv::StreamLaunch& L, const pkv::StreamPlan& P) {
+    StreamArgs a;
+    char* ws = static_cast<char*>(L.workspace);
+    a.out = L.out;
+    a.q = L.q;
+    a.k_pool = L.k_pool;
+    a.v_pool = L.v_pool;
+    a.block_tables = L.block_tables;
+    a.context_lens = L.context_lens;
+    a.meta = reinterpret_cast<int32_t*>(ws + P.meta_off);
+    a.ws_m = reinterpret_cast<float*>(ws + P.m_off);
+    a.ws_l = reinterpret_cast<float*>(ws + P.l_off);
+    a.ws_acc = reinterpret_cast<float*>(ws + P.acc_off);
+    a.num_seqs = L.num_seqs;
+    a.max_blocks_per_seq = L.max_blocks_per_seq;
+    a.num_q_heads = L.num_q_heads;
+    a.num_kv_heads = L.num_kv_heads;
+    a.group = L.num_q_heads / L.num_kv_heads;
+    a.units = P.units;
+    a.heads_per_unit = P.heads_per_unit;
+    a.num_blocks = L.num_blocks;
+    a.max_context_len = L.max_context_len;
+    a.waves = P.waves;
+    a.scale_log2 = L.scale * kLog2e;
+    return a;
+}
+
+template <int D, int DT, int OUT>
+void launch_part_t(const StreamArgs& a, bool mfma, hipStream_t st) {
+    const dim3 grid((unsigned)((a.waves + kWaves - 1) / kWaves));
+    const size_t lds = (size_t)(a.num_seqs + 1) * sizeof(int);
+    if constexpr (DT == DT_F32) {
+        attn_valu_streamk<D, DT, OUT><<<grid, dim3(kWaves * 64), lds, st>>>(a);
+    } else {
+        if (mfma) attn_mfma_streamk<D, DT, OUT><<<grid, dim3(kWaves * 64), lds, st>>>(a);
+        else attn_valu_streamk<D, DT, OUT><<<grid, dim3(kWaves * 64), lds, st>>>(a);
+    }
+}
+
+template <int D, int DT>
+void launch_part_d(const StreamArgs& a, int out_dtype, bool mfma, hipStream_t st) {
+    if (out_dtype == PAGED_KV_F32) launch_part_t<D, DT, DT_F32>(a, mfma, st);
+    else launch_part_t<D, DT, DT>(a, mfma, st);
+}
+
+template <int D>
+void launch_part_dd(const StreamArgs& a, int dtype, int out_dtype, bool mfma, hipStream_t st) {
+    switch (dtype) {
+        case PAGED_KV_F32: launch_part_d<D, DT_F32>(a, out_dtype, mfma, st); break;
+        case PAGED_KV_F16: launch_part_d<D, DT_F16>(a, out_dtype, mfma, st); break;
+        default: launch_part_d<D, DT_BF16>(a, out_dtype, mfma, st); break;
+    }
+}
+
+template <int D>
+void launch_reduce_dd(const StreamArgs& a, int out_dtype, hipStream_t st) {
+    const int64_t jobs = (int64_t)a.num_seqs * a.units * a.heads_per_unit;
+    const dim3 grid((unsigned)((jobs + kWaves - 1) / kWaves));
+    const dim3 block(kWaves * 64);
+    switch (out_dtype) {
+        case PAGED_KV_F32: attn_streamk_reduce<D, DT_F32><<<grid, block, 0, st>>>(a); break;
+        case PAGED_KV_F16: attn_streamk_reduce<D, DT_F16><<<grid, block, 0, st>>>(a); break;
+        default: attn_streamk_reduce<D, DT_BF16><<<grid, block, 0, st>>>(a); break;
+    }
+}
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+}  // namespace
+
+namespace pkv {
+
+StreamPlan stream_plan(int32_t num_seqs, int32_t hq, int32_t hkv, int32_t dtype, int32_t head_dim,
+                       int32_t max_ctx, bool* ok) {
+    StreamPlan p{};
+    *ok = num_seqs >= 0 && num_seqs <= kStreamMaxSeqs && hq >= 1 && hkv >= 1 && hq % hkv == 0 &&
+          max_ctx >= 1 && head_dim >= 1;
+    if (!*ok) return p;
+    const int group = hq / hkv;
+    p.mfma = dtype != PAGED_KV_F32 && group >= 2;
+    p.units = p.mfma ? hkv : hq;
+    p.heads_per_unit = p.mfma ? group : 1;
+    const int64_t max_tiles = (int64_t)((max_ctx + kKernelBlockSize - 1) / kKernelBlockSize) *
+                              num_seqs * p.units;
+    p.waves = (int32_t)std::max<int64_t>(1, std::min<int64_t>(kStreamMaxWaves, max_tiles));
+    p.max_pieces = (int64_t)p.waves + (int64_t)num_seqs * p.units;
+    const size_t rows = (size_t)p.max_pieces * p.heads_per_unit;
+    p.meta_off = 0;
+    p.m_off = align256((size_t)(num_seqs + 1) * sizeof(int32_t));
+    p.l_off = p.m_off + align256(rows * sizeof(float));
+    p.acc_off = p.l_off + align256(rows * sizeof(float));
+    p.ws_bytes = p.acc_off + rows * head_dim * sizeof(float);
+    return p;
+}
+
+void launch_streamk_partition(const StreamLaunch& L, const StreamPlan& P, void* stream) {
+    const StreamArgs a = make_args(L, P);
+    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    if (L.head_dim == 64) launch_part_dd<64>(a, L.dtype, L.out_dtype, P.mfma, st);
+    else launch_part_dd<128>(a, L.dtype, L.out_dtype, P.mfma, st);
+}
+
+void launch_streamk_reduce(const StreamLaunch& L, const StreamPlan& P, void* stream) {
+    const StreamArgs a = make_args(L, P);
+    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    if (L.head_dim == 64) launch_reduce_dd<64>(a, L.out_dtype, st);
+    else launch_reduce_dd<128>(a, L.out_dtype, st);
+}
+
+}  // namespace pkv

@@ -288,7 +288,11 @@ def test_device_op_validation_without_gpu():
     with pytest.raises(B.PagedKVError):
         _attn(good, out_dtype="f16")                                        # neither pool nor fp32
     with pytest.raises(B.PagedKVError) as e:
-        _attn(good, block_tables=_FakeTensor((2, 40)), max_context_len=600)  # needs workspace
+        _attn(good, block_tables=_FakeTensor((2, 40)), max_context_len=600,
+              partition_tokens=512)                                         # needs workspace
+    assert e.value.status == B.PAGED_KV_ERR_BUFFER_TOO_SMALL
+    with pytest.raises(B.PagedKVError) as e:
+        _attn(good)                                                         # stream-K workspace
     assert e.value.status == B.PAGED_KV_ERR_BUFFER_TOO_SMALL
     with pytest.raises(B.PagedKVError):
         _attn(good, q=_FakeTensor((2, 8, 128), addr=4098))                  # misaligned q
@@ -300,6 +304,11 @@ def test_device_op_validation_without_gpu():
         B.reshape_and_cache(good, _FakeTensor((3, 2, 128)), _FakeTensor((3, 2, 128)),
                             _FakeTensor((1,)), _FakeTensor((1,)), _FakeTensor((3,)),
                             key_stride=100, stream=0)                        # stride < heads*dim
-    assert B.paged_attention_workspace_bytes(2, 8, 128, 512) == 0
-    ws = B.paged_attention_workspace_bytes(2, 8, 128, 513)
+    assert B.paged_attention_workspace_bytes(good, 2, 8, 512, 512) == 0
+    ws = B.paged_attention_workspace_bytes(good, 2, 8, 513, 512)
     assert ws >= 2 * 8 * 2 * (128 + 2) * 4
+    # stream-K (partition_tokens 0): meta + (waves + seqs*units) pieces of group x (d + 2)
+    wsk = B.paged_attention_workspace_bytes(good, 2, 8, 64, 0)
+    waves = min(3072, 4 * 2 * 2)            # 4 blocks x 2 seqs x 2 KV heads
+    assert wsk >= (waves + 2 * 2) * 4 * (128 + 2) * 4
+    assert B.paged_attention_workspace_bytes(good, 2, 7, 64, 0) == 0     # 7 % 2 != 0

@@ -26,13 +26,14 @@ def _run(w, out_dtype="f32", pt=None):
     return g
 
 
+@pytest.mark.parametrize("pt", [0, 512], ids=["streamk", "pt512"])
 @pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "-".join(map(str, s)))
-def test_boundary_lengths_every_path(shape):
+def test_boundary_lengths_every_path(shape, pt):
     dt, hq, hkv, d = shape
     w = W.make_custom(BOUNDARY_LENS, hq, hkv, d, dt, seed=hq * 7 + d)
-    say(f"[edge] boundary lengths {shape}")
+    say(f"[edge] boundary lengths {shape} partition_tokens={pt}")
     for out_dtype in ("f32", dt):
-        g = _run(w, out_dtype)
+        g = _run(w, out_dtype, pt)
         o = oreplay.run(w)
         assert_bookkeeping_equal(g, o)
         assert_pools_equal(g.cache, o, dt)
@@ -58,7 +59,7 @@ def test_partition_size_invariance(dt, hq, hkv):
     w = W.make_custom([5, 700, 1500, 2049], hq, hkv, 128 if dt != "f32" else 64, dt, seed=11)
     o = oreplay.run(w)
     outs = []
-    for pt in (16, 48, 512, 4096):
+    for pt in (16, 48, 512, 4096, 0):
         g = _run(w, "f32", pt)
         err = max_err(g.outputs[0], o.outputs[0])
         say(f"[edge] partition {pt}: max|err| {err:.3e}")
@@ -69,15 +70,16 @@ def test_partition_size_invariance(dt, hq, hkv):
         assert np.abs(x - outs[0]).max() <= TOL[dt]
 
 
+@pytest.mark.parametrize("pt", [0, 512], ids=["streamk", "pt512"])
 @pytest.mark.parametrize("dt,hq,hkv", [("bf16", 64, 8), ("f16", 32, 32), ("f32", 4, 4)])
-def test_placement_invariance_bitwise(dt, hq, hkv):
+def test_placement_invariance_bitwise(dt, hq, hkv, pt):
     d = 128 if dt != "f32" else 64
     base = W.make_custom([300, 1000, 17, 2500], hq, hkv, d, dt, seed=21)
     outs = []
     for perm_seed in (0, 1, 2):
         w = W.make_custom([300, 1000, 17, 2500], hq, hkv, d, dt, seed=21,
                           free_order=np.random.default_rng(50 + perm_seed).permutation(base.num_blocks))
-        g = _run(w, "f32")
+        g = _run(w, "f32", pt)
         outs.append((out_f64(g.outputs[0]), g.tables[0]))
         g.cache.close()
     assert not np.array_equal(outs[0][1], outs[1][1])
@@ -85,10 +87,11 @@ def test_placement_invariance_bitwise(dt, hq, hkv):
         assert np.array_equal(o, outs[0][0])
 
 
-def test_shared_and_copied_prefix_bitwise():
+@pytest.mark.parametrize("pt", [0, 512], ids=["streamk", "pt512"])
+def test_shared_and_copied_prefix_bitwise(pt):
     shared, copied = W.configs.make_shared_prefix_pair(small=True)
-    gs = _run(shared, "f32")
-    gc = _run(copied, "f32")
+    gs = _run(shared, "f32", pt)
+    gc = _run(copied, "f32", pt)
     assert sum(len(c) for c in gs.copies) == 2 * 7
     assert sum(len(c) for c in gc.copies) == 0
     assert np.array_equal(out_f64(gs.outputs[0]), out_f64(gc.outputs[0]))
@@ -137,8 +140,8 @@ def test_invalid_lengths_and_block_ids_give_nan_without_reading():
         from paged_kv_cache_15_amd.cache import TORCH_DTYPES
         q = torch.from_numpy(w.q[0]).cuda().to(TORCH_DTYPES[dt])
         out = torch.zeros((4, hq, d), device="cuda")
-        for pt in (512, 2048):
-            nb = B.paged_attention_workspace_bytes(4, hq, d, max_ctx, pt)
+        for pt in (512, 2048, 0):
+            nb = B.paged_attention_workspace_bytes(c.desc, 4, hq, max_ctx, pt)
             ws = torch.empty(max(nb, 16), dtype=torch.uint8, device="cuda")
             B.paged_attention_decode(c.desc, out, "f32", q, c.k_pool, c.v_pool, tab_d, lens_d, hq,
                                      max_ctx, float(w.scale), pt, ws)
@@ -149,14 +152,15 @@ def test_invalid_lengths_and_block_ids_give_nan_without_reading():
         # a context longer than max_context_len is rejected the same way
         lens2 = g.context_lens[0].copy()
         lens_d2 = torch.from_numpy(lens2).cuda()
-        nb = B.paged_attention_workspace_bytes(4, hq, d, 1000, 512)
-        ws = torch.empty(nb, dtype=torch.uint8, device="cuda")
-        B.paged_attention_decode(c.desc, out, "f32", q, c.k_pool, c.v_pool,
-                                 torch.from_numpy(g.tables[0]).cuda(), lens_d2, hq, 1000,
-                                 float(w.scale), 512, ws)
-        torch.cuda.synchronize()
-        r = out_f64(out)
-        assert np.isnan(r[3]).all() and not np.isnan(r[:3]).any()
+        for pt in (512, 0):
+            nb = B.paged_attention_workspace_bytes(c.desc, 4, hq, 1000, pt)
+            ws = torch.empty(nb, dtype=torch.uint8, device="cuda")
+            B.paged_attention_decode(c.desc, out, "f32", q, c.k_pool, c.v_pool,
+                                     torch.from_numpy(g.tables[0]).cuda(), lens_d2, hq, 1000,
+                                     float(w.scale), pt, ws)
+            torch.cuda.synchronize()
+            r = out_f64(out)
+            assert np.isnan(r[3]).all() and not np.isnan(r[:3]).any()
         c.close()
 
 

@@ -24,13 +24,14 @@ def _run_both(w, out_dtype=None, attend_rows=None, partition_tokens=None):
     return g, o
 
 
+@pytest.mark.parametrize("pt", [0, 512], ids=["streamk", "pt512"])
 @pytest.mark.parametrize("k", [1, 2, 3, 4, 5])
 @pytest.mark.parametrize("out", ["f32", "pool"])
-def test_small_configs(k, out):
+def test_small_configs(k, out, pt):
     w = W.make_config(k, small=(k != 1))
     out_dtype = "f32" if out == "f32" else w.dtype
-    say(f"[parity] config {k} {w.name} out={out_dtype}")
-    g, o = _run_both(w, out_dtype)
+    say(f"[parity] config {k} {w.name} out={out_dtype} partition_tokens={pt}")
+    g, o = _run_both(w, out_dtype, partition_tokens=pt)
     assert_bookkeeping_equal(g, o)
     assert_pools_equal(g.cache, o, w.dtype)
     for go, oo in zip(g.outputs, o.outputs):
@@ -49,7 +50,8 @@ def _sample_rows(lens, n, seed):
 
 @pytest.mark.parametrize("k", [2, 3, 4, 5])
 def test_full_size_configs(k):
-    """Full sizes, the launch configuration the bench times (512-token partitions):
+    """Full sizes, in the launch configuration the bench times (the workload's own
+    partition setting: stream-K, or 512-token partitions for the long-context one):
     whole pools bit-exact, attention on sampled sequences."""
     from paged_kv_cache_15_amd.replay import run_workload
     w = W.make_config(k)
