@@ -162,7 +162,7 @@ def main():
     max_ctx = int(lens.max())
     pt = w.partition_tokens if args.partition_tokens is None else args.partition_tokens
     ws_bytes = B.paged_attention_workspace_bytes(cache.desc, len(seqs), w.num_q_heads, max_ctx, pt)
-    ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
+    ws = torch.zeros(max(ws_bytes, 16), dtype=torch.uint8, device=dev)   # zero before first use
     stream = torch.cuda.current_stream(dev)
 
     def step(ev=None):

@@ -223,8 +223,11 @@ size_t paged_attention_workspace_bytes(const paged_kv_pool_desc* desc, int32_t n
  *                 (used for up to 8192 sequences; larger batches fall back to 512-token
  *                 partitions).  > 0: fixed split-K partitions of that many tokens
  *                 (multiple of 16), merged the same way.
- *   workspace     device buffer of paged_attention_workspace_bytes(...) bytes
- *                 (may be NULL when that is 0); contents on entry are ignored.
+ *   workspace     device buffer of paged_attention_workspace_bytes(...) bytes (may be
+ *                 NULL when that is 0).  Zero-fill it once before its first use (e.g.
+ *                 hipMemsetAsync): the stream-K schedule keeps per-(sequence, head unit)
+ *                 merge counters in it, and every call leaves them at zero again.  The
+ *                 rest is scratch.  Calls sharing one workspace must not overlap.
  * A sequence whose context_len is outside [1, max_context_len], or whose table holds
  * an id outside [0, num_blocks) below its length, gets NaN outputs; nothing outside
  * the buffers is read.  Requires block_size 16, head_dim 64 or 128,
@@ -239,10 +242,12 @@ paged_kv_status paged_attention_decode(const paged_kv_pool_desc* desc, void* out
                                        int32_t partition_tokens, void* workspace,
                                        size_t workspace_bytes, void* stream);
 
-/* The two launches paged_attention_decode makes, exposed separately so each kernel
- * can be timed on its own.  paged_attention_partition writes `out` for sequences that
+/* The two halves of paged_attention_decode, exposed so each kernel can be timed on its
+ * own.  With fixed partitions, paged_attention_partition writes `out` for sequences that
  * fit one partition and the per-partition (max, sum, weighted values) state of the
- * others into `workspace`; paged_attention_reduce merges that state into `out`.
+ * others into `workspace`, and paged_attention_reduce merges that state into `out`.
+ * With the stream-K schedule the partition launch merges in-kernel and writes all of
+ * `out`; paged_attention_reduce then only validates its arguments.
  * Arguments as for paged_attention_decode. */
 paged_kv_status paged_attention_partition(const paged_kv_pool_desc* desc, void* out,
                                           int32_t out_dtype, const void* q, const void* k_pool,

@@ -13,7 +13,8 @@ import os
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libpagedkv.so")
+# PAGED_KV_LIBRARY may name another build of the same library (same ABI).
+LIB_PATH = os.environ.get("PAGED_KV_LIBRARY") or os.path.join(_HERE, "libpagedkv.so")
 
 PAGED_KV_OK = 0
 PAGED_KV_ERR_INVALID_ARG = 1

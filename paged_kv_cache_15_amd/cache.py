@@ -89,7 +89,8 @@ class PagedKVCache:
         out = torch.empty((len(seqs), hq, d), dtype=TORCH_DTYPES[out_dtype], device=self.device)
         nbytes = B.paged_attention_workspace_bytes(self.desc, len(seqs), hq, max_ctx,
                                                    partition_tokens)
-        ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=self.device) if nbytes else None
+        # zero-filled: the stream-K schedule keeps per-unit counters in the workspace
+        ws = torch.zeros(max(nbytes, 1), dtype=torch.uint8, device=self.device) if nbytes else None
         B.paged_attention_decode(self.desc, out, out_dtype, q, self.k_pool, self.v_pool, tables_d,
                                  lens_d, hq, max_ctx, scale, partition_tokens, ws, stream)
         return out, tables, lens

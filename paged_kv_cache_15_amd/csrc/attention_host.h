@@ -22,7 +22,7 @@ struct StreamPlan {
     int32_t heads_per_unit;
     int32_t waves;         // W
     int64_t max_pieces;    // W + num_seqs * units: upper bound on partial results
-    size_t meta_off, m_off, l_off, acc_off, ws_bytes;
+    size_t meta_off, cnt_off, m_off, l_off, acc_off, ws_bytes;
 };
 
 // Plan for a batch; `ok` false when the shape is outside what stream-K serves.
@@ -49,7 +49,7 @@ struct StreamLaunch {
     void* workspace;
 };
 
+// One launch: partition work and the merge of multi-piece units.
 void launch_streamk_partition(const StreamLaunch& L, const StreamPlan& P, void* stream);
-void launch_streamk_reduce(const StreamLaunch& L, const StreamPlan& P, void* stream);
 
 }  // namespace pkv

@@ -765,10 +765,7 @@ paged_kv_status paged_attention_reduce(const paged_kv_pool_desc* desc, void* out
                                    1.f, partition_tokens, const_cast<void*>(workspace),
                                    workspace_bytes, stream, false);
     if (st != PAGED_KV_OK || num_seqs == 0) return st;
-    if (pl.streamk) {
-        pkv::launch_streamk_reduce(pl.sl, pl.sp, stream);
-        return launch_status("paged attention merge kernel");
-    }
+    if (pl.streamk) return st;   // the stream-K launch merges in-kernel
     if (pl.a.max_parts <= 1) return st;
     if (pl.head_dim == 64) launch_reduce_d<64>(pl, num_seqs);
     else launch_reduce_d<128>(pl, num_seqs);

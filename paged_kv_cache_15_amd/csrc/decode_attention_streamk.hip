@@ -11,10 +11,11 @@
 // take an equal contiguous slice of the line (to within one tile) and stream it with a
 // two-deep load pipeline that never restarts at sequence or head boundaries.  When a
 // wave's slice covers a whole (sequence, unit) the wave writes the normalised output;
-// otherwise it writes the piece's (max, sum, weighted values) and the merge kernel
-// combines the pieces of that (sequence, unit) in slice order (log-sum-exp).  Piece
-// index = wave index + (sequence, unit) index: along the line every wave boundary and
-// every unit boundary starts a new piece, so this numbering is dense and collision-free.
+// otherwise it writes the piece's (max, sum, weighted values), counts it in a per-unit
+// counter, and the wave that completes the count merges the unit's pieces in slice
+// order (log-sum-exp) — no second kernel.  Piece index = wave index + (sequence, unit)
+// index: along the line every wave boundary and every unit boundary starts a new piece,
+// so this numbering is dense and collision-free.
 //
 // Units: the MFMA kernel's unit is a KV head with its group of query heads (fp16/bf16,
 // group >= 2); the VALU kernel's unit is one query head.
@@ -36,7 +37,8 @@ struct StreamArgs {
     const void* v_pool;
     const int32_t* block_tables;
     const int32_t* context_lens;
-    int32_t* meta;     // per-sequence tile prefix, written by workgroup 0 for the merge
+    int32_t* meta;     // per-sequence tile prefix (written by workgroup 0)
+    int32_t* counters; // per unit: pieces written so far; zero on entry, left zero
     float* ws_m;
     float* ws_l;
     float* ws_acc;
@@ -146,6 +148,177 @@ __device__ __forceinline__ void wave_slice(const StreamArgs& a, int64_t T, int j
     t1 = (int64_t)(j + 1) * T / a.waves;
 }
 
+__device__ __forceinline__ int wave_of(int64_t t, int64_t T, int W) {
+    return (int)(((t + 1) * W - 1) / T);   // the wave whose slice holds tile t
+}
+
+// With fewer tiles than waves some slices are empty; those waves wrote no piece.
+__device__ __forceinline__ bool slice_empty(int j, int64_t T, int W) {
+    return (int64_t)(j + 1) * T / W == (int64_t)j * T / W;
+}
+
+// Number of pieces unit q was cut into (its tiles start at line position ta).
+__device__ __forceinline__ int unit_pieces(int64_t ta, int nt, int64_t T, int W, int& jf, int& jl) {
+    jf = wave_of(ta, T, W);
+    jl = wave_of(ta + nt - 1, T, W);
+    if (T >= W) return jl - jf + 1;
+    int cnt = 0;
+    for (int jj = jf; jj <= jl; ++jj) cnt += !slice_empty(jj, T, W);
+    return cnt;
+}
+
+// Pieces cross XCDs, whose L2 caches are not kept coherent with each other inside a
+// kernel.  They are written and read with agent-scope relaxed atomics, which the
+// compiler emits as write-through stores and coherent loads (sc1), so publishing a
+// piece only needs its stores to have completed before the counter is bumped.  An
+// agent-scope release fence would instead write back the XCD's whole L2, and those
+// write-backs serialise across the thousands of pieces of one launch.
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+constexpr int kPolicySc1 = 1 << 4;   // cache-policy operand bit of sc1 on gfx94x/gfx950
+__device__ __forceinline__ void put_coherent(float* p, float v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float get_coherent(const float* p) {
+    return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// 16-byte form of put_coherent for a wave-uniform region of `bytes` bytes at `base`
+// (a buffer store with the same sc1 policy); lanes whose offset falls outside the
+// region write nothing (the buffer's range check drops them).
+__device__ __forceinline__ void put_coherent4(float* base, uint32_t bytes, uint32_t off_bytes,
+                                              f32x4 v) {
+    // third descriptor word 0x00020000: raw 32-bit data format on gfx9-family chips
+    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(base, 0, (int)bytes, 0x00020000);
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, v), r, off_bytes, 0,
+                                           kPolicySc1);
+}
+// Every vector memory operation this wave issued has completed (vmcnt counts stores
+// too on this architecture); the clobber keeps the compiler from moving memory
+// operations across it.
+__device__ __forceinline__ void wait_memory_done() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// Log-sum-exp merge of all pieces of unit q (written by waves jf..jl; empty slices wrote
+// none), in slice order, into the unit's G query-head output rows.  One wave, heads in
+// groups of HC: lane h < HC keeps head g0+h's running max M and sum L, and every lane
+// holds the group's output elements idx = lane + 64 i (head 64 i / D, uniform).
+// Pieces are folded in online, PC at a time, all loads of a chunk in flight together:
+//   M' = max(M, m_p), L' = L 2^(M - M') + l_p 2^(m_p - M'), acc likewise; out = acc / L.
+// The code is kept small on purpose: every wave reaches it at the end of the launch
+// with a cold instruction cache.
+template <int D, int OUT_DT, int HC, int PC>
+__device__ void merge_unit(const StreamArgs& a, int q, int s, int u, int jf, int jl, int64_t T,
+                           int lane) {
+    constexpr int EC = HC * D / 64;       // outputs per lane per head group
+    const int G = a.heads_per_unit;
+    const int W = a.waves;
+#pragma unroll 1
+    for (int g0 = 0; g0 < G; g0 += HC) {
+        float Ml = kNegInf, Ll = 0.f, acc[EC];
+#pragma unroll
+        for (int i = 0; i < EC; ++i) acc[i] = 0.f;
+        bool bad = false;
+        const int hl = min(g0 + min(lane, HC - 1), G - 1);
+#pragma unroll 1
+        for (int k0 = jf; k0 <= jl; k0 += PC) {
+            // Loads first, with no branch between them: slots past jl re-read piece jl
+            // and padded heads re-read head G-1; neither is folded in.
+            float pm[PC], pl[PC], pa[PC][EC];
+#pragma unroll
+            for (int p = 0; p < PC; ++p) {
+                const int64_t pr = ((int64_t)min(k0 + p, jl) + q) * G;
+                pm[p] = get_coherent(a.ws_m + pr + hl);
+                pl[p] = get_coherent(a.ws_l + pr + hl);
+#pragma unroll
+                for (int i = 0; i < EC; ++i) {
+                    const int hi = min(g0 + 64 * i / D, G - 1);
+                    pa[p][i] = get_coherent(a.ws_acc + (pr + hi) * D + (64 * i) % D + lane);
+                }
+            }
+#pragma unroll
+            for (int p = 0; p < PC; ++p) {
+                const int jj = k0 + p;
+                // with at least as many tiles as waves no slice is empty
+                if (jj > jl || (T < W && slice_empty(jj, T, W))) continue;
+                bad |= __ballot(pm[p] != pm[p]) != 0;
+                const float mn = fmaxf(Ml, pm[p]);
+                const float sc = exp2_fast(Ml - mn), wt = exp2_fast(pm[p] - mn);
+                Ll = Ll * sc + wt * pl[p];
+                Ml = mn;
+#pragma unroll
+                for (int i = 0; i < EC; ++i) {
+                    const int h = 64 * i / D;
+                    const float sh = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sc), h));
+                    const float wh = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wt), h));
+                    acc[i] = acc[i] * sh + wh * pa[p][i];
+                }
+            }
+        }
+        const int64_t ob = ((int64_t)s * a.num_q_heads + u * G + g0) * D + lane;
+        const float inv = 1.f / Ll;
+#pragma unroll
+        for (int i = 0; i < EC; ++i) {
+            const int h = 64 * i / D;
+            const float ih = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(inv), h));
+            if (g0 + h < G) store_out<OUT_DT>(a.out, ob + 64 * i, bad ? NAN : acc[i] * ih);
+        }
+    }
+}
+
+// Units this wave wrote a piece of (at most two: the first unit of its slice, if it
+// began in an earlier slice, and the last, if it goes on into a later one).
+struct Pending {
+    int n = 0;
+    int s0 = 0, u0 = 0, nt0 = 0, s1 = 0, u1 = 0, nt1 = 0;
+    __device__ void add(int s, int u, int nt) {
+        if (n == 0) { s0 = s; u0 = u; nt0 = nt; }
+        else { s1 = s; u1 = u; nt1 = nt; }
+        ++n;
+    }
+};
+
+// End of a wave's slice: once its pieces (written with put_coherent) have completed, it
+// counts them in their units' counters; for each unit it counted last, it merges the
+// pieces (reading with get_coherent, after the count came back) and resets the
+// counter for the next call.  Counting only here keeps the wait for the piece stores
+// out of the load pipeline.
+template <int D, int OUT_DT, int HC, int PC>
+__device__ void publish_pieces(const StreamArgs& a, const int* s_pref, const Pending& pd,
+                               int64_t T, int lane) {
+    if (pd.n == 0) return;
+    wait_memory_done();
+    const int q0 = pd.s0 * a.units + pd.u0, q1 = pd.s1 * a.units + pd.u1;
+    int old0 = 0, old1 = 0;
+    if (lane == 0) {
+        old0 = __hip_atomic_fetch_add(a.counters + q0, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (pd.n > 1)
+            old1 = __hip_atomic_fetch_add(a.counters + q1, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    old0 = __shfl(old0, 0);
+    old1 = __shfl(old1, 0);
+#pragma unroll 1
+    for (int e = 0; e < pd.n; ++e) {
+        const int s = e ? pd.s1 : pd.s0, u = e ? pd.u1 : pd.u0, nt = e ? pd.nt1 : pd.nt0;
+        const int q = e ? q1 : q0, old = e ? old1 : old0;
+        int jf, jl;
+        const int64_t ta = (int64_t)a.units * uni(s_pref[s]) + (int64_t)u * nt;
+        if (old != unit_pieces(ta, nt, T, a.waves, jf, jl) - 1) continue;
+        merge_unit<D, OUT_DT, HC, PC>(a, q, s, u, jf, jl, T, lane);
+        if (lane == 0) __hip_atomic_store(a.counters + q, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+}
+
+// Workgroup 0 gives every sequence with an invalid length NaN outputs (no tile covers it).
+template <int D, int OUT_DT>
+__device__ void nan_invalid_sequences(const StreamArgs& a) {
+    if (blockIdx.x != 0) return;
+    for (int s = 0; s < a.num_seqs; ++s) {
+        const int ctx = a.context_lens[s];
+        if (ctx >= 1 && ctx <= a.max_context_len) continue;
+        const int64_t ob = (int64_t)s * a.num_q_heads * D;
+        for (int i = threadIdx.x; i < a.num_q_heads * D; i += blockDim.x)
+            store_out<OUT_DT>(a.out, ob + i, NAN);
+    }
+}
+
 // ---------------------------------------------------------------------------------
 // MFMA stream-K kernel (fp16/bf16, 2..16 query heads per KV head).  The per-tile math
 // is the fixed-partition MFMA kernel's: S^T = K.Q^T with 16x16x32 MFMAs, lazy-rescaled
@@ -163,6 +336,7 @@ void attn_mfma_streamk(StreamArgs a) {
     const int tiles_per_unit = build_prefix(a, s_pref);
     if (blockIdx.x == 0)
         for (int i = threadIdx.x; i <= a.num_seqs; i += blockDim.x) a.meta[i] = s_pref[i];
+    nan_invalid_sequences<D, OUT_DT>(a);
     const int lane = threadIdx.x & 63;
     const int j = uni(blockIdx.x * kWaves + (threadIdx.x >> 6));
     if (j >= a.waves) return;
@@ -210,6 +384,7 @@ void attn_mfma_streamk(StreamArgs a) {
     float m = kNegInf, lsum = 0.f;
     bool unit_bad = false;
     bool first_here = cc.it == 0;
+    Pending pend;
 
     // Write the finished (or slice-cut) unit of cursor c, then reset the state.
     auto finish = [&](const Cursor& c) {
@@ -228,16 +403,21 @@ void attn_mfma_streamk(StreamArgs a) {
                                           unit_bad ? NAN : acc[mt][r] * inv);
             } else {
                 const int64_t piece = ((int64_t)j + q) * G + gq;
+                // the unit's G x D piece is one contiguous region: 16-byte stores, each
+                // head row written as 64-byte runs
+                float* region = a.ws_acc + ((int64_t)j + q) * G * D;
 #pragma unroll
                 for (int mt = 0; mt < MT; ++mt)
-                    *reinterpret_cast<f32x4*>(a.ws_acc + piece * D + 16 * mt + 4 * quad) =
-                        unit_bad ? (f32x4){NAN, NAN, NAN, NAN} : acc[mt];
+                    put_coherent4(region, (uint32_t)(G * D * 4),
+                                  (uint32_t)((gq * D + 16 * mt + 4 * quad) * 4),
+                                  unit_bad ? (f32x4){NAN, NAN, NAN, NAN} : acc[mt]);
                 if (quad == 0) {
-                    a.ws_m[piece] = unit_bad ? NAN : m;
-                    a.ws_l[piece] = unit_bad ? NAN : lw;
+                    put_coherent(a.ws_m + piece, unit_bad ? NAN : m);
+                    put_coherent(a.ws_l + piece, unit_bad ? NAN : lw);
                 }
             }
         }
+        if (!direct) pend.add(c.s, c.u, c.nt);
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) acc[mt] = (f32x4){0.f, 0.f, 0.f, 0.f};
         m = kNegInf;
@@ -320,8 +500,20 @@ void attn_mfma_streamk(StreamArgs a) {
     bool bA = false, bB = false;
 
     // one pipeline step: load tile k+1 into (kn, vn), compute tile k from (kc, vc)
+    int done = 0;
     auto step = [&](i32x4 (&kc)[KI], i32x2 (&vc)[MT], bool bc, i32x4 (&kn)[KI],
                     i32x2 (&vn)[MT], bool& bn) {
+        // Waves with more of their slice left get issue priority: co-resident waves share
+        // the CU's memory pipe unevenly (oldest first), and a slice split is only balanced
+        // if the waves progress together.
+        {
+            const int pr = ((n - done) * 4) / (n + 1);
+            if (pr >= 3) __builtin_amdgcn_s_setprio(3);
+            else if (pr == 2) __builtin_amdgcn_s_setprio(2);
+            else if (pr == 1) __builtin_amdgcn_s_setprio(1);
+            else __builtin_amdgcn_s_setprio(0);
+            ++done;
+        }
         advance(a, lc);
         load_kv(lc, kn, vn, bn);
         const bool next_unit = lc.s != cc.s || lc.u != cc.u;
@@ -344,6 +536,8 @@ void attn_mfma_streamk(StreamArgs a) {
         compute(kA, vA, bA, false, cc);
     }
     finish(cc);
+    __builtin_amdgcn_s_setprio(0);
+    publish_pieces<D, OUT_DT, 8, (D == 64 ? 8 : 4)>(a, s_pref, pend, T, lane);
 }
 
 // ---------------------------------------------------------------------------------
@@ -363,6 +557,7 @@ void attn_valu_streamk(StreamArgs a) {
     const int tiles_per_unit = build_prefix(a, s_pref);
     if (blockIdx.x == 0)
         for (int i = threadIdx.x; i <= a.num_seqs; i += blockDim.x) a.meta[i] = s_pref[i];
+    nan_invalid_sequences<D, OUT_DT>(a);
     const int lane = threadIdx.x & 63;
     const int j = uni(blockIdx.x * kWaves + (threadIdx.x >> 6));
     if (j >= a.waves) return;
@@ -416,6 +611,7 @@ void attn_valu_streamk(StreamArgs a) {
     bool unit_bad = false;
     bool first_here = cc.it == 0;
     bool q_stale = false;    // qraw holds the next unit's query, not yet converted
+    Pending pend;
 
     auto finish = [&](const Cursor& c) {
         const bool direct = first_here && c.it == c.nt - 1;
@@ -444,13 +640,14 @@ void attn_valu_streamk(StreamArgs a) {
                 const int64_t piece = (int64_t)j + q;
 #pragma unroll
                 for (int i = 0; i < NI; ++i)
-                    a.ws_acc[piece * D + (64 * i + lane) / E] = unit_bad ? NAN : rows[i];
+                    put_coherent(a.ws_acc + piece * D + (64 * i + lane) / E, unit_bad ? NAN : rows[i]);
                 if (lane == 0) {
-                    a.ws_m[piece] = unit_bad ? NAN : m;
-                    a.ws_l[piece] = unit_bad ? NAN : lw;
+                    put_coherent(a.ws_m + piece, unit_bad ? NAN : m);
+                    put_coherent(a.ws_l + piece, unit_bad ? NAN : lw);
                 }
             }
         }
+        if (!direct) pend.add(c.s, c.u, c.nt);
 #pragma unroll
         for (int i = 0; i < NI; ++i) acc[i] = 0.f;
         m = kNegInf;
@@ -515,8 +712,18 @@ void attn_valu_streamk(StreamArgs a) {
 
     i32x4 kA[NI], kB[NI], vA[NI], vB[NI];
     bool bA = false, bB = false;
+    int done = 0;
     auto step = [&](i32x4 (&kc)[NI], i32x4 (&vc)[NI], bool bc, i32x4 (&kn)[NI],
                     i32x4 (&vn)[NI], bool& bn) {
+        // issue priority to the waves with more of their slice left (see the MFMA kernel)
+        {
+            const int pr = ((n - done) * 4) / (n + 1);
+            if (pr >= 3) __builtin_amdgcn_s_setprio(3);
+            else if (pr == 2) __builtin_amdgcn_s_setprio(2);
+            else if (pr == 1) __builtin_amdgcn_s_setprio(1);
+            else __builtin_amdgcn_s_setprio(0);
+            ++done;
+        }
         advance(a, lc);
         load_kv(lc, kn, vn, bn);
         const bool next_unit = lc.s != cc.s || lc.u != cc.u;
@@ -540,6 +747,8 @@ void attn_valu_streamk(StreamArgs a) {
         compute(kA, vA, bA, false, cc);
     }
     finish(cc);
+    __builtin_amdgcn_s_setprio(0);
+    publish_pieces<D, OUT_DT, 1, 8>(a, s_pref, pend, T, lane);
 }
 
 // ---------------------------------------------------------------------------------
@@ -547,84 +756,6 @@ void attn_valu_streamk(StreamArgs a) {
 // combine their pieces in slice order:
 // out = sum_p 2^(m_p - M) acc_p / sum_p 2^(m_p - M) l_p, M = max_p m_p.
 // ---------------------------------------------------------------------------------
-__device__ __forceinline__ int wave_of(int64_t t, int64_t T, int W) {
-    return (int)(((t + 1) * W - 1) / T);   // the wave whose slice holds tile t
-}
-
-// With fewer tiles than waves some slices are empty; those waves wrote no piece.
-__device__ __forceinline__ bool slice_empty(int j, int64_t T, int W) {
-    return (int64_t)(j + 1) * T / W == (int64_t)j * T / W;
-}
-
-// One wave per (sequence, unit, query head of the unit).  Lanes first hold one piece
-// each (its max and sum), then one or two head dims each for the weighted sum over the
-// pieces, taken in slice order.
-template <int D, int OUT_DT>
-__global__ __launch_bounds__(kWaves * 64) void attn_streamk_reduce(StreamArgs a) {
-    constexpr int DPL = D / 64;   // head dims per lane
-    const int lane = threadIdx.x & 63;
-    const int G = a.heads_per_unit;
-    const int64_t job = (int64_t)blockIdx.x * kWaves + (threadIdx.x >> 6);
-    if (job >= (int64_t)a.num_seqs * a.units * G) return;
-    const int q = (int)(job / G), gq = (int)(job - (int64_t)q * G);
-    const int s = q / a.units, u = q - s * a.units;
-    const int64_t ob = ((int64_t)s * a.num_q_heads + u * G + gq) * D + lane;
-    const int ctx = sload(a.context_lens, s);
-    if (ctx < 1 || ctx > a.max_context_len) {
-#pragma unroll
-        for (int i = 0; i < DPL; ++i) store_out<OUT_DT>(a.out, ob + 64 * i, NAN);
-        return;
-    }
-    const int nt = (ctx + kBS - 1) / kBS;
-    const int64_t T = (int64_t)a.units * sload(a.meta, a.num_seqs);
-    const int64_t ta = (int64_t)a.units * sload(a.meta, s) + (int64_t)u * nt;
-    const int jf = wave_of(ta, T, a.waves), jl = wave_of(ta + nt - 1, T, a.waves);
-    if (jf == jl) return;   // one wave held the whole unit and wrote the output
-
-    float mm = kNegInf;
-    bool nan_seen = false;
-    for (int j0 = jf; j0 <= jl; j0 += 64) {
-        const int jj = j0 + lane;
-        if (jj <= jl && !slice_empty(jj, T, a.waves)) {
-            const float mj = a.ws_m[((int64_t)jj + q) * G + gq];
-            nan_seen |= mj != mj;
-            mm = fmaxf(mm, mj);
-        }
-    }
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) mm = fmaxf(mm, __shfl_xor(mm, o));
-    nan_seen = __ballot(nan_seen) != 0;
-
-    float l = 0.f, acc[DPL];
-#pragma unroll
-    for (int i = 0; i < DPL; ++i) acc[i] = 0.f;
-    for (int j0 = jf; j0 <= jl; j0 += 64) {
-        const int jj = j0 + lane;
-        float wgt = 0.f;
-        bool have = false;
-        if (jj <= jl && !slice_empty(jj, T, a.waves)) {
-            const int64_t piece = ((int64_t)jj + q) * G + gq;
-            wgt = exp2_fast(a.ws_m[piece] - mm);
-            l += wgt * a.ws_l[piece];
-            have = true;
-        }
-        const uint64_t mask = __ballot(have);
-        const int cnt = min(64, jl - j0 + 1);
-        for (int k = 0; k < cnt; ++k) {
-            if (!((mask >> k) & 1)) continue;            // empty slice: no piece
-            const float wk = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wgt), k));
-            const float* src = a.ws_acc + (((int64_t)j0 + k + q) * G + gq) * D + lane;
-#pragma unroll
-            for (int i = 0; i < DPL; ++i) acc[i] = fmaf(wk, src[64 * i], acc[i]);
-        }
-    }
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) l += __shfl_xor(l, o);
-    const float inv = 1.f / l;
-#pragma unroll
-    for (int i = 0; i < DPL; ++i) store_out<OUT_DT>(a.out, ob + 64 * i, nan_seen ? NAN : acc[i] * inv);
-}
-
 StreamArgs make_args(const pkv::StreamLaunch& L, const pkv::StreamPlan& P) {
     StreamArgs a;
     char* ws = static_cast<char*>(L.workspace);
@@ -635,6 +766,7 @@ StreamArgs make_args(const pkv::StreamLaunch& L, const pkv::StreamPlan& P) {
     a.block_tables = L.block_tables;
     a.context_lens = L.context_lens;
     a.meta = reinterpret_cast<int32_t*>(ws + P.meta_off);
+    a.counters = reinterpret_cast<int32_t*>(ws + P.cnt_off);
     a.ws_m = reinterpret_cast<float*>(ws + P.m_off);
     a.ws_l = reinterpret_cast<float*>(ws + P.l_off);
     a.ws_acc = reinterpret_cast<float*>(ws + P.acc_off);
@@ -679,18 +811,6 @@ void launch_part_dd(const StreamArgs& a, int dtype, int out_dtype, bool mfma, hi
     }
 }
 
-template <int D>
-void launch_reduce_dd(const StreamArgs& a, int out_dtype, hipStream_t st) {
-    const int64_t jobs = (int64_t)a.num_seqs * a.units * a.heads_per_unit;
-    const dim3 grid((unsigned)((jobs + kWaves - 1) / kWaves));
-    const dim3 block(kWaves * 64);
-    switch (out_dtype) {
-        case PAGED_KV_F32: attn_streamk_reduce<D, DT_F32><<<grid, block, 0, st>>>(a); break;
-        case PAGED_KV_F16: attn_streamk_reduce<D, DT_F16><<<grid, block, 0, st>>>(a); break;
-        default: attn_streamk_reduce<D, DT_BF16><<<grid, block, 0, st>>>(a); break;
-    }
-}
-
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 }  // namespace
@@ -713,7 +833,8 @@ StreamPlan stream_plan(int32_t num_seqs, int32_t hq, int32_t hkv, int32_t dtype,
     p.max_pieces = (int64_t)p.waves + (int64_t)num_seqs * p.units;
     const size_t rows = (size_t)p.max_pieces * p.heads_per_unit;
     p.meta_off = 0;
-    p.m_off = align256((size_t)(num_seqs + 1) * sizeof(int32_t));
+    p.cnt_off = align256((size_t)(num_seqs + 1) * sizeof(int32_t));
+    p.m_off = p.cnt_off + align256((size_t)num_seqs * p.units * sizeof(int32_t));
     p.l_off = p.m_off + align256(rows * sizeof(float));
     p.acc_off = p.l_off + align256(rows * sizeof(float));
     p.ws_bytes = p.acc_off + rows * head_dim * sizeof(float);
@@ -725,13 +846,6 @@ void launch_streamk_partition(const StreamLaunch& L, const StreamPlan& P, void* 
     hipStream_t st = reinterpret_cast<hipStream_t>(stream);
     if (L.head_dim == 64) launch_part_dd<64>(a, L.dtype, L.out_dtype, P.mfma, st);
     else launch_part_dd<128>(a, L.dtype, L.out_dtype, P.mfma, st);
-}
-
-void launch_streamk_reduce(const StreamLaunch& L, const StreamPlan& P, void* stream) {
-    const StreamArgs a = make_args(L, P);
-    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-    if (L.head_dim == 64) launch_reduce_dd<64>(a, L.out_dtype, st);
-    else launch_reduce_dd<128>(a, L.out_dtype, st);
 }
 
 }  // namespace pkv

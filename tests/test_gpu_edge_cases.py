@@ -142,7 +142,7 @@ def test_invalid_lengths_and_block_ids_give_nan_without_reading():
         out = torch.zeros((4, hq, d), device="cuda")
         for pt in (512, 2048, 0):
             nb = B.paged_attention_workspace_bytes(c.desc, 4, hq, max_ctx, pt)
-            ws = torch.empty(max(nb, 16), dtype=torch.uint8, device="cuda")
+            ws = torch.zeros(max(nb, 16), dtype=torch.uint8, device="cuda")
             B.paged_attention_decode(c.desc, out, "f32", q, c.k_pool, c.v_pool, tab_d, lens_d, hq,
                                      max_ctx, float(w.scale), pt, ws)
             torch.cuda.synchronize()
@@ -154,7 +154,7 @@ def test_invalid_lengths_and_block_ids_give_nan_without_reading():
         lens_d2 = torch.from_numpy(lens2).cuda()
         for pt in (512, 0):
             nb = B.paged_attention_workspace_bytes(c.desc, 4, hq, 1000, pt)
-            ws = torch.empty(nb, dtype=torch.uint8, device="cuda")
+            ws = torch.zeros(nb, dtype=torch.uint8, device="cuda")
             B.paged_attention_decode(c.desc, out, "f32", q, c.k_pool, c.v_pool,
                                      torch.from_numpy(g.tables[0]).cuda(), lens_d2, hq, 1000,
                                      float(w.scale), pt, ws)
