@@ -3,9 +3,12 @@
 
 A step is one pass of the decode hot path over one batch already resident in HBM:
   reshape_and_cache  (write each sequence's new token into its slot)
-  paged attention    (partition kernel over 512-token partitions)
-  partition merge    (log-sum-exp reduce of multi-partition sequences)
-for the GQA workload of 128 sequences, 64 query heads over 8 KV heads, head_dim 128,
+  paged attention    (the partition launch: by default the stream-K schedule, which
+                      also merges split (sequence, KV head) units in-kernel; with fixed
+                      partitions, one workgroup per (sequence, head, partition))
+  partition merge    (the reduce launch: log-sum-exp merge of fixed partitions; it only
+                      validates its arguments under the stream-K schedule)
+for, by default, the GQA workload of 128 sequences, 64 query heads over 8 KV heads, head_dim 128,
 bf16 KV, 16-token blocks scattered through a pool 1.25x the need, context lengths
 lognormal around 2048 (capped at 8192).  The host allocator's work for the step
 (slot reservation) happens before timing; the step re-writes the same slots, so every
@@ -13,9 +16,13 @@ step is the same work.
 
 Prints one JSON line: decode KV GB/s over the whole step (algorithmic bytes / step
 time), seq-tokens/s, the partition kernel against the HBM roofline (HIP events on the
-launch stream), and the CPU oracle timed on the host cores as a baseline.
+launch stream), the kernel's measured HBM traffic when a committed counter summary
+under profiles/ matches the current kernel sources, and the CPU oracle timed on the
+host cores as a baseline.
 """
 import argparse
+import glob
+import hashlib
 import json
 import os
 import sys
@@ -40,7 +47,7 @@ def parse():
     ap.add_argument("--config", type=int, default=3, help="workload 1..5 (default 3: GQA 72B shape)")
     ap.add_argument("--partition-tokens", type=int, default=None,
                     help="0: stream-K schedule; > 0: fixed partitions (default: the workload's)")
-    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="bound on the oracle's timed CPU work")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -58,6 +65,41 @@ def copy_calibration(mib):
         y.copy_(x)
     torch.cuda.synchronize()
     print(json.dumps({"copy_calibration_bytes": n * 4, "launches": 3}), flush=True)
+
+
+# Sources that determine the attention kernels' code and launch shape; a counter summary
+# records their digest, and its traffic figure is only reported while they match.
+KERNEL_SOURCES = ("paged_kv_cache_15_amd/csrc/attention_common.h",
+                  "paged_kv_cache_15_amd/csrc/attention_host.h",
+                  "paged_kv_cache_15_amd/csrc/decode_attention.hip",
+                  "paged_kv_cache_15_amd/csrc/decode_attention_streamk.hip")
+
+
+def kernel_source_digest():
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload, partition_tokens):
+    """HBM bytes per launch of the partition kernel from a committed counter summary
+    (profiles/*_hbm_bytes.txt: FETCH_SIZE and WRITE_SIZE scaled by a plain copy's
+    readings) for this workload and schedule, or None if none matches the current
+    kernel sources."""
+    digest = kernel_source_digest()
+    for path in sorted(glob.glob(os.path.join(ROOT, "profiles", "*_hbm_bytes.txt"))):
+        kv = {}
+        with open(path) as f:
+            for line in f:
+                if ":" in line and not line.startswith((" ", "#", "|")):
+                    k, v = line.split(":", 1)
+                    kv[k.strip()] = v.strip()
+        if (kv.get("workload") == workload and kv.get("partition_tokens") == str(partition_tokens)
+                and kv.get("kernel_source_sha256") == digest and "traffic_bytes_per_launch" in kv):
+            return int(kv["traffic_bytes_per_launch"]), os.path.relpath(path, ROOT)
+    return None, None
 
 
 def attention_bytes(lens, nblocks, w, out_elem):
@@ -85,12 +127,15 @@ def cpu_baseline(w, seconds):
     qidx = attends[-1][2]
     tables, lens = r.tables[-1], r.context_lens[-1]
     q = storage_bits_to_f64(to_storage_bits(w.q[qidx], w.dtype), w.dtype)
-    done, kv_bytes = 0, 0
+    # sequences in batch order, wrapping round, until `seconds` of CPU work are spent
+    done, kv_bytes, ctx_tokens = 0, 0, 0
     t0 = time.perf_counter()
-    while done < len(lens) and time.perf_counter() - t0 < seconds:
+    while time.perf_counter() - t0 < seconds:
+        i = done % len(lens)
         paged_decode(q, r.k_pool, r.v_pool, tables, lens, w.scale, w.dtype, w.block_size,
-                     seqs=[done])
-        kv_bytes += int(lens[done]) * 2 * w.num_kv_heads * w.head_dim * w.elem_bytes
+                     seqs=[i])
+        kv_bytes += int(lens[i]) * 2 * w.num_kv_heads * w.head_dim * w.elem_bytes
+        ctx_tokens += int(lens[i])
         done += 1
     dt = time.perf_counter() - t0
     cores = len(os.sched_getaffinity(0))
@@ -98,8 +143,9 @@ def cpu_baseline(w, seconds):
         "value": round(kv_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": cores,
         "blas_threads": blas_threads, "kind": "oracle",
         "seq_tokens_per_s": round(done / dt, 3),
-        "sample": f"fp64 NumPy oracle attention for the first {done} of {len(lens)} sequences "
-                  f"of the same step ({int(lens[:done].sum())} context tokens), {dt:.1f} s",
+        "sample": f"fp64 NumPy oracle attention over {done} sequence decodes of the same step "
+                  f"({done / len(lens):.2f} passes over its {len(lens)} sequences, "
+                  f"{ctx_tokens} context tokens), {dt:.1f} s",
     }
 
 
@@ -203,6 +249,7 @@ def main():
     write_bytes = 2 * 2 * n_app * w.num_kv_heads * w.head_dim * w.elem_bytes + 4 * n_app
     step_bytes = attn_bytes + write_bytes
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
+    traffic, traffic_src = measured_traffic(w.name, pt)
     achieved = attn_bytes / (part_ms * 1e-3) / 1e9
     res = {
         "metric": "decode KV GB/s (% of HBM peak) + seq-tokens/s, paged attention, 1 MI355X",
@@ -234,8 +281,9 @@ def main():
         "roofline": {
             "kernel": "paged_attention_partition",
             "bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
             "algorithmic_bytes_per_launch": attn_bytes,
+            "traffic_source": traffic_src,
         },
         "cpu_baseline": None,
     }
