@@ -72,10 +72,14 @@ __device__ int build_prefix(const StreamArgs& a, int* s_pref) {
     __shared__ int s_wsum[kWaves];
     const int B = a.num_seqs, tid = threadIdx.x, nthr = blockDim.x;
     const int lane = tid & 63, w = tid >> 6;
+    // tile counts into LDS with coalesced loads, several in flight per thread
+#pragma unroll 8
+    for (int i = tid; i < B; i += nthr) s_pref[i] = tiles_of(a.context_lens[i], a.max_context_len);
+    __syncthreads();
     const int chunk = (B + nthr - 1) / nthr;
     const int lo = min(B, tid * chunk), hi = min(B, lo + chunk);
     int sum = 0;
-    for (int i = lo; i < hi; ++i) sum += tiles_of(a.context_lens[i], a.max_context_len);
+    for (int i = lo; i < hi; ++i) sum += s_pref[i];
     int incl = sum;
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
@@ -88,8 +92,9 @@ __device__ int build_prefix(const StreamArgs& a, int* s_pref) {
     for (int ww = 0; ww < w; ++ww) off += s_wsum[ww];
     int run = off + incl - sum;
     for (int i = lo; i < hi; ++i) {
+        const int v = s_pref[i];
         s_pref[i] = run;
-        run += tiles_of(a.context_lens[i], a.max_context_len);
+        run += v;
     }
     if (tid == nthr - 1) s_pref[B] = off + incl;
     __syncthreads();
@@ -306,13 +311,13 @@ __device__ void publish_pieces(const StreamArgs& a, const int* s_pref, const Pen
     }
 }
 
-// Workgroup 0 gives every sequence with an invalid length NaN outputs (no tile covers it).
+// Sequences with an invalid length (no tiles: s_pref[s + 1] == s_pref[s]) get NaN
+// outputs; workgroup b takes sequences b, b + grid, ...  Only LDS is read, so no
+// workgroup's own slice is held up by this.
 template <int D, int OUT_DT>
-__device__ void nan_invalid_sequences(const StreamArgs& a) {
-    if (blockIdx.x != 0) return;
-    for (int s = 0; s < a.num_seqs; ++s) {
-        const int ctx = a.context_lens[s];
-        if (ctx >= 1 && ctx <= a.max_context_len) continue;
+__device__ void nan_invalid_sequences(const StreamArgs& a, const int* s_pref) {
+    for (int s = blockIdx.x; s < a.num_seqs; s += gridDim.x) {
+        if (s_pref[s + 1] != s_pref[s]) continue;
         const int64_t ob = (int64_t)s * a.num_q_heads * D;
         for (int i = threadIdx.x; i < a.num_q_heads * D; i += blockDim.x)
             store_out<OUT_DT>(a.out, ob + i, NAN);
@@ -336,7 +341,7 @@ void attn_mfma_streamk(StreamArgs a) {
     const int tiles_per_unit = build_prefix(a, s_pref);
     if (blockIdx.x == 0)
         for (int i = threadIdx.x; i <= a.num_seqs; i += blockDim.x) a.meta[i] = s_pref[i];
-    nan_invalid_sequences<D, OUT_DT>(a);
+    nan_invalid_sequences<D, OUT_DT>(a, s_pref);
     const int lane = threadIdx.x & 63;
     const int j = uni(blockIdx.x * kWaves + (threadIdx.x >> 6));
     if (j >= a.waves) return;
@@ -516,6 +521,11 @@ void attn_mfma_streamk(StreamArgs a) {
         }
         advance(a, lc);
         load_kv(lc, kn, vn, bn);
+        // Keep the next tile's loads ahead of everything that waits on the current one:
+        // left alone, the scheduler hoists the first score product (and with it a wait
+        // on the current tile's loads) into the block-id lookup's latency, which leaves
+        // one tile in flight instead of two.
+        __builtin_amdgcn_sched_barrier(0);
         const bool next_unit = lc.s != cc.s || lc.u != cc.u;
         compute(kc, vc, bc, next_unit, lc);
         if (next_unit) finish(cc);
@@ -557,7 +567,7 @@ void attn_valu_streamk(StreamArgs a) {
     const int tiles_per_unit = build_prefix(a, s_pref);
     if (blockIdx.x == 0)
         for (int i = threadIdx.x; i <= a.num_seqs; i += blockDim.x) a.meta[i] = s_pref[i];
-    nan_invalid_sequences<D, OUT_DT>(a);
+    nan_invalid_sequences<D, OUT_DT>(a, s_pref);
     const int lane = threadIdx.x & 63;
     const int j = uni(blockIdx.x * kWaves + (threadIdx.x >> 6));
     if (j >= a.waves) return;
@@ -726,6 +736,11 @@ void attn_valu_streamk(StreamArgs a) {
         }
         advance(a, lc);
         load_kv(lc, kn, vn, bn);
+        // Keep the next tile's loads ahead of everything that waits on the current one:
+        // left alone, the scheduler hoists the first score product (and with it a wait
+        // on the current tile's loads) into the block-id lookup's latency, which leaves
+        // one tile in flight instead of two.
+        __builtin_amdgcn_sched_barrier(0);
         const bool next_unit = lc.s != cc.s || lc.u != cc.u;
         compute(kc, vc, bc, next_unit, lc);
         if (next_unit) finish(cc);
