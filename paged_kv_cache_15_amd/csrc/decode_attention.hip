@@ -503,34 +503,76 @@ __global__ __launch_bounds__(kWaves * 64) void attn_valu_kernel(PartitionArgs a)
 // Merge of the partitions of one (sequence, query head): with M the largest partition
 // max, out = sum_p 2^(m_p - M) acc_p / sum_p 2^(m_p - M) l_p, partitions in order.
 // ---------------------------------------------------------------------------------
+constexpr int kReduceMaxGroups = 8;
+
 template <int D, int OUT_DT>
-__global__ __launch_bounds__(D) void attn_reduce_kernel(void* out, const int32_t* context_lens,
-                                                        int32_t num_q_heads, int32_t max_context_len,
-                                                        int32_t partition_tokens, int32_t max_parts,
-                                                        const float* ws_m, const float* ws_l,
-                                                        const float* ws_acc) {
-    const int s = blockIdx.y, h = blockIdx.x, d = threadIdx.x;
+__global__ __launch_bounds__(D * kReduceMaxGroups) void attn_reduce_kernel(
+        void* out, const int32_t* context_lens, int32_t num_q_heads, int32_t max_context_len,
+        int32_t partition_tokens, int32_t max_parts, const float* ws_m, const float* ws_l,
+        const float* ws_acc) {
+    // One workgroup per (query head, sequence) of R = blockDim.x / D groups of D threads
+    // (one thread per head dim).  Group g folds partitions [g*per, (g+1)*per) in order,
+    // eight per memory round trip, by an online log-sum-exp:
+    //   M' = max(M, m_i), L' = L 2^(M - M') + l_i 2^(m_i - M'), acc likewise;
+    // group 0 then folds the groups' states in group order.
+    __shared__ float s_acc[kReduceMaxGroups][D];
+    __shared__ float s_ml[kReduceMaxGroups][2];
+    __shared__ int s_bad[kReduceMaxGroups];
+    const int R = blockDim.x / D, g = threadIdx.x / D, d = threadIdx.x % D;
+    const int s = blockIdx.y, h = blockIdx.x;
     const int64_t o = ((int64_t)s * num_q_heads + h) * D + d;
     const int ctx = context_lens[s];
     if (ctx < 1 || ctx > max_context_len) {
-        store_out<OUT_DT>(out, o, NAN);
+        if (g == 0) store_out<OUT_DT>(out, o, NAN);
         return;
     }
     const int np = (ctx + partition_tokens - 1) / partition_tokens;
     if (np == 1) return;   // written by the partition kernel
     const int64_t row = ((int64_t)s * num_q_heads + h) * max_parts;
-    float mm = kNegInf;
-    for (int i = 0; i < np; ++i) mm = fmaxf(mm, ws_m[row + i]);
-    float l = 0.f, acc = 0.f;
-    bool nan_seen = false;
-    for (int i = 0; i < np; ++i) {
-        const float mi = ws_m[row + i];
-        nan_seen |= mi != mi;
-        const float f = exp2_fast(mi - mm);
-        l += f * ws_l[row + i];
-        acc += f * ws_acc[(row + i) * D + d];
+    const int per = (np + R - 1) / R;
+    const int i_lo = min(np, g * per), i_hi = min(np, i_lo + per);
+    float M = kNegInf, l = 0.f, acc = 0.f;
+    bool bad = false;
+    for (int i0 = i_lo; i0 < i_hi; i0 += 8) {
+        float mv[8], lv[8], av[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {   // slots past the range re-read its last partition
+            const int64_t r = row + min(i0 + k, i_hi - 1);
+            mv[k] = ws_m[r];
+            lv[k] = ws_l[r];
+            av[k] = ws_acc[r * D + d];
+        }
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            if (i0 + k >= i_hi) break;
+            bad |= mv[k] != mv[k];
+            const float mn = fmaxf(M, mv[k]);
+            const float sc = exp2_fast(M - mn), w = exp2_fast(mv[k] - mn);
+            l = l * sc + w * lv[k];
+            acc = acc * sc + w * av[k];
+            M = mn;
+        }
     }
-    store_out<OUT_DT>(out, o, nan_seen ? NAN : acc / l);
+    if (R > 1) {
+        s_acc[g][d] = acc;
+        if (d == 0) {
+            s_ml[g][0] = M;
+            s_ml[g][1] = l;
+            s_bad[g] = bad;
+        }
+        __syncthreads();
+        if (g != 0) return;
+        for (int gg = 1; gg < R; ++gg) {   // group 0 has partitions, so M is finite here
+            const float mg = s_ml[gg][0];
+            bad |= s_bad[gg] != 0;
+            const float mn = fmaxf(M, mg);
+            const float sc = exp2_fast(M - mn), w = exp2_fast(mg - mn);   // empty group: w = 0
+            l = l * sc + w * s_ml[gg][1];
+            acc = acc * sc + w * s_acc[gg][d];
+            M = mn;
+        }
+    }
+    store_out<OUT_DT>(out, o, bad ? NAN : acc / l);
 }
 
 // ---------------------------------------------------------------------------------
@@ -686,7 +728,10 @@ void launch_partition_dd(const Plan& pl) {
 
 template <int D, int OUT>
 void launch_reduce_t(const Plan& pl, int num_seqs) {
-    attn_reduce_kernel<D, OUT><<<dim3((unsigned)pl.a.num_q_heads, (unsigned)num_seqs), dim3(D), 0,
+    // about 16 partitions per thread group, at most kReduceMaxGroups groups
+    const int groups = std::max(1, std::min(kReduceMaxGroups, (pl.a.max_parts + 15) / 16));
+    attn_reduce_kernel<D, OUT><<<dim3((unsigned)pl.a.num_q_heads, (unsigned)num_seqs),
+                                 dim3(D * groups), 0,
                                  pl.stream>>>(pl.a.out, pl.a.context_lens, pl.a.num_q_heads,
                                               pl.a.max_context_len, pl.a.partition_tokens,
                                               pl.a.max_parts, pl.a.ws_m, pl.a.ws_l, pl.a.ws_acc);
