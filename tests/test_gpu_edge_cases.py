@@ -221,3 +221,48 @@ def test_decode_steps_append_and_attend():
     for go, oo in zip(g.outputs, o.outputs):
         assert_close(go, oo, "bf16", "bf16")
     g.cache.close()
+
+
+@pytest.mark.parametrize("pt", [0, 512], ids=["streamk", "pt512"])
+def test_workspace_reused_across_calls_bitwise(pt):
+    """The stream-K schedule keeps per-unit merge counters in the workspace and every call
+    must leave them at zero: one zero-filled workspace reused across calls with different
+    batches gives the same bits as a fresh zero-filled workspace per call."""
+    from paged_kv_cache_15_amd import binding as B
+    from paged_kv_cache_15_amd.replay import to_device
+    lens = [300, 1000, 17, 2500, 64, 4000, 1]
+    w = W.make_custom(lens, 64, 8, 128, "bf16", seed=31)
+    g = _run(w, "f32", pt)
+    cache = g.cache
+    seqs, qidx = w.attend_ops()[-1][1], w.attend_ops()[-1][2]
+    q_all = to_device(w.q[qidx], w.dtype, "cuda")
+    batches = [list(range(len(lens))), [1, 3, 5], [2, 6], [5, 4, 3, 2, 1, 0], [0]]
+
+    def args(rows):
+        tables, blens = cache.block_tables([seqs[i] for i in rows])
+        return (torch.from_numpy(tables).cuda(), torch.from_numpy(blens).cuda(),
+                int(blens.max()), q_all[rows].contiguous())
+
+    need = max(B.paged_attention_workspace_bytes(cache.desc, len(r), 64, args(r)[2], pt)
+               for r in batches)
+    shared = torch.zeros(max(need, 16), dtype=torch.uint8, device="cuda")
+    say(f"[edge] workspace reuse, partition_tokens={pt}, {need} bytes")
+    for rep in range(2):
+        for rows in batches:
+            tab, bl, mx, q = args(rows)
+            outs = []
+            for ws in (shared, None):
+                if ws is None:
+                    nb = B.paged_attention_workspace_bytes(cache.desc, len(rows), 64, mx, pt)
+                    ws = torch.zeros(max(nb, 16), dtype=torch.uint8, device="cuda")
+                out = torch.empty((len(rows), 64, 128), dtype=torch.float32, device="cuda")
+                B.paged_attention_decode(cache.desc, out, "f32", q, cache.k_pool, cache.v_pool,
+                                         tab, bl, 64, mx, float(w.scale), pt, ws)
+                outs.append(out)
+            torch.cuda.synchronize()
+            assert torch.equal(outs[0], outs[1]), (rep, rows)
+            if rows == batches[0]:   # the replay's own call on the full batch
+                assert torch.equal(outs[0], g.outputs[0])
+    o = oreplay.run(w)
+    assert_close(g.outputs[0], o.outputs[0], "bf16", "f32")
+    cache.close()
