@@ -149,6 +149,46 @@ def cpu_baseline(w, seconds):
     }
 
 
+def prefix_cache_host(seconds_cap=5.0):
+    """Host cost of prefix caching (deepsonar §2.4 hash chain) on the shared-prefix shape:
+    32 prompts of 2056 token ids, each requested 8 times; a request matches its prompt
+    against the cache, appends the uncached rest with token ids and is then released.
+    Library (C++ SHA-256 + allocator) and oracle (Python) do the same requests."""
+    import numpy as np
+    from paged_kv_cache_15_amd import binding as B
+    from oracle import prefix_cache as opc
+    rng = np.random.default_rng(4)
+    prompts = [rng.integers(0, 50000, 2056).tolist() for _ in range(32)]
+    order = [p for p in prompts for _ in range(8)]
+    nb, bs = 32 * 129 * 2, 16
+    desc = B.make_desc(nb, bs, 8, 128, "bf16", B.PAGED_KV_POOL_HOST_ONLY | B.PAGED_KV_POOL_PREFIX_CACHE)
+    pool = B.paged_kv_pool_create(desc)
+    hit_tokens = 0
+    t0 = time.perf_counter()
+    for pr in order:
+        s, n = B.paged_kv_seq_create_prefix(pool, pr)
+        B.paged_kv_seq_append_tokens(pool, s, pr[n:])
+        B.paged_kv_seq_free(pool, s)
+        hit_tokens += n
+    t_lib = time.perf_counter() - t0
+    B.paged_kv_pool_destroy(pool)
+    al = opc.PrefixCachingAllocator(nb, bs)
+    t0, done = time.perf_counter(), 0
+    for pr in order:
+        s, n = al.create_prefix(pr)
+        al.append_tokens(s, pr[n:])
+        al.release(s)
+        done += 1
+        if time.perf_counter() - t0 > seconds_cap:
+            break
+    t_orc = time.perf_counter() - t0
+    hashed = sum((len(p) - 1) // bs for p in order) + sum(len(p) // bs for p in prompts)
+    return {"requests": len(order), "prompt_tokens": 2056, "hit_tokens": hit_tokens,
+            "library_us_per_request": round(t_lib / len(order) * 1e6, 2),
+            "library_block_hashes_per_s": round(hashed / t_lib, 1),
+            "oracle_us_per_request": round(t_orc / done * 1e6, 2), "oracle_requests": done}
+
+
 def main():
     args = parse()
     if args.copy_calibration:
@@ -290,6 +330,7 @@ def main():
     if not args.no_cpu_baseline:
         del new_k, new_v
         res["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+    res["prefix_cache_host"] = prefix_cache_host()
     print(json.dumps(res), flush=True)
 
 

@@ -73,6 +73,10 @@ typedef struct {
 
 /* Allocator only: no device memory is allocated or referenced by the pool object. */
 #define PAGED_KV_POOL_HOST_ONLY 1
+/* Prefix caching ([DS] §2.4, block pool and hash chain of V1; §VII step 5): the pool
+ * keeps a map from chained block hash to physical block for full blocks written with
+ * paged_kv_seq_append_tokens, and paged_kv_seq_create_prefix takes cached blocks over. */
+#define PAGED_KV_POOL_PREFIX_CACHE 2
 
 typedef struct paged_kv_pool paged_kv_pool; /* opaque host-side object */
 
@@ -172,6 +176,43 @@ paged_kv_status paged_kv_block_refcount(const paged_kv_pool* pool, int32_t block
  * live sequences (block_size * blocks - tokens, < block_size per sequence: [DS] §2.2). */
 paged_kv_status paged_kv_stats(const paged_kv_pool* pool, int64_t* num_free, int64_t* num_used,
                                int64_t* waste_slots);
+
+/* ------------------------------------------------------- prefix caching ---- */
+
+/* Chained block hash ([DS] §2.4): SHA-256 (FIPS 180-4) over the parent block's 32-byte
+ * hash (NULL: 32 zero bytes, a sequence's first block), the n token ids as
+ * little-endian int32 and extra_key as a little-endian int64, into out[32].  One
+ * differing token changes the hash of its block and, through the parent, of every
+ * later block. */
+paged_kv_status paged_kv_block_hash(const uint8_t* parent, const int32_t* tokens, int32_t n,
+                                    int64_t extra_key, uint8_t* out);
+
+/* New sequence for a prompt of n token ids ([DS] §2.4, comparison block by block along
+ * the hash chain; §VII step 5).  Walks the prompt's full blocks that lie inside its
+ * first n-1 tokens (the last prompt token is always recomputed); each block whose
+ * chained hash (with extra_key) is in the pool's map is taken over: its reference
+ * count goes up and, if it was waiting in the free queue, it leaves the queue.  The
+ * walk stops at the first miss.  *n_cached = tokens now held (a multiple of
+ * block_size); the caller writes the rest with paged_kv_seq_append_tokens.  Errors:
+ * PAGED_KV_ERR_UNSUPPORTED without PAGED_KV_POOL_PREFIX_CACHE; the pool is unchanged
+ * on any error. */
+paged_kv_status paged_kv_seq_create_prefix(paged_kv_pool* pool, const int32_t* prompt, int32_t n,
+                                           int64_t extra_key, int32_t* seq_id, int32_t* n_cached);
+
+/* paged_kv_seq_append with the new tokens' ids: on a prefix-caching pool, each block of
+ * a sequence made by paged_kv_seq_create_prefix that this append fills gets its chained
+ * hash and enters the map (unless the hash is already there).  A plain
+ * paged_kv_seq_append to such a sequence stops its registration for good.  Taking a
+ * block from the queue head evicts its cached hash first ([DS] §2.4: the queue order is
+ * the LRU order).  Arguments and errors as paged_kv_seq_append. */
+paged_kv_status paged_kv_seq_append_tokens(paged_kv_pool* pool, int32_t seq, const int32_t* tokens,
+                                           int32_t n_tokens, int32_t* slots_out,
+                                           int32_t* copies_out, int32_t max_copies,
+                                           int32_t* n_copies);
+
+/* Blocks in the hash map, blocks taken over by prompts so far, cached blocks evicted. */
+paged_kv_status paged_kv_prefix_stats(const paged_kv_pool* pool, int64_t* cached_blocks,
+                                      int64_t* hit_blocks, int64_t* evictions);
 
 /* ------------------------------------------------------------ device ops ---- */
 

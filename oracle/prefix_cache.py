@@ -108,9 +108,11 @@ class PrefixCachingAllocator(BlockAllocator):
         return sid, self.lengths[sid]
 
     def append(self, seq: int, n: int):
-        """Append without token ids: the sequence stops registering blocks."""
+        """Append without token ids: the sequence stops registering blocks (once the
+        append succeeded: a failed append changes nothing)."""
+        out = self._append(seq, n)
         self.tokens[seq] = None
-        return self._append(seq, n)
+        return out
 
     def append_tokens(self, seq: int, tokens):
         """Append with token ids: every block this fills is hashed and registered."""

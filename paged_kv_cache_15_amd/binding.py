@@ -26,6 +26,7 @@ PAGED_KV_ERR_BUFFER_TOO_SMALL = 6
 
 PAGED_KV_F32, PAGED_KV_F16, PAGED_KV_BF16 = 0, 1, 2
 PAGED_KV_POOL_HOST_ONLY = 1
+PAGED_KV_POOL_PREFIX_CACHE = 2
 DTYPE_CODES = {"f32": PAGED_KV_F32, "f16": PAGED_KV_F16, "bf16": PAGED_KV_BF16}
 
 
@@ -73,6 +74,11 @@ _SIGNATURES = {
     "paged_kv_seq_info": (ctypes.c_int, [_vp, _i32, _i32p, _i32p]),
     "paged_kv_block_refcount": (ctypes.c_int, [_vp, _i32, _i32p]),
     "paged_kv_stats": (ctypes.c_int, [_vp, _i64p, _i64p, _i64p]),
+    "paged_kv_block_hash": (ctypes.c_int, [_vp, _i32p, _i32, _i64, _vp]),
+    "paged_kv_seq_create_prefix": (ctypes.c_int, [_vp, _i32p, _i32, _i64, _i32p, _i32p]),
+    "paged_kv_seq_append_tokens": (ctypes.c_int, [_vp, _i32, _i32p, _i32, _i32p, _i32p, _i32,
+                                                  _i32p]),
+    "paged_kv_prefix_stats": (ctypes.c_int, [_vp, _i64p, _i64p, _i64p]),
     "paged_kv_copy_blocks": (ctypes.c_int, [_descp, _vp, _vp, _vp, _i32, _vp]),
     "reshape_and_cache": (ctypes.c_int, [_descp, _vp, _vp, _i64, _i64, _vp, _vp, _vp, _i32, _vp]),
     "paged_attention_workspace_bytes": (_sz, [_descp, _i32, _i32, _i32, _i32]),
@@ -263,6 +269,48 @@ def paged_kv_stats(pool):
     f, u, w = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int64()
     _check("paged_kv_stats", lib.paged_kv_stats(pool, ctypes.byref(f), ctypes.byref(u), ctypes.byref(w)))
     return f.value, u.value, w.value
+
+
+# -------------------------------------------------------- prefix caching ----
+def paged_kv_block_hash(parent, tokens, extra_key=0):
+    """Chained block hash: 32 bytes from parent (32 bytes or None) and token ids."""
+    toks = np.ascontiguousarray(np.asarray(tokens, dtype=np.int32))
+    out = ctypes.create_string_buffer(32)
+    par = None if parent is None else ctypes.create_string_buffer(bytes(parent), 32)
+    _check("paged_kv_block_hash",
+           lib.paged_kv_block_hash(par, toks.ctypes.data_as(_i32p), len(toks), int(extra_key), out))
+    return out.raw
+
+
+def paged_kv_seq_create_prefix(pool, prompt, extra_key=0):
+    """Returns (seq id, number of prompt tokens taken over from cached blocks)."""
+    toks = np.ascontiguousarray(np.asarray(prompt, dtype=np.int32))
+    sid, nc = ctypes.c_int32(), ctypes.c_int32()
+    _check("paged_kv_seq_create_prefix",
+           lib.paged_kv_seq_create_prefix(pool, toks.ctypes.data_as(_i32p), len(toks), int(extra_key),
+                                          ctypes.byref(sid), ctypes.byref(nc)))
+    return sid.value, nc.value
+
+
+def paged_kv_seq_append_tokens(pool, seq, tokens):
+    """Returns (slots int32[n], copies int32[k][2])."""
+    toks = np.ascontiguousarray(np.asarray(tokens, dtype=np.int32))
+    slots = np.empty(max(len(toks), 1), dtype=np.int32)
+    copies = np.empty(2, dtype=np.int32)
+    nc = ctypes.c_int32()
+    _check("paged_kv_seq_append_tokens",
+           lib.paged_kv_seq_append_tokens(pool, seq, toks.ctypes.data_as(_i32p), len(toks),
+                                          slots.ctypes.data_as(_i32p), copies.ctypes.data_as(_i32p),
+                                          1, ctypes.byref(nc)))
+    return slots[:len(toks)], copies[:2 * nc.value].reshape(-1, 2)
+
+
+def paged_kv_prefix_stats(pool):
+    """Returns (cached_blocks, hit_blocks, evictions)."""
+    c, h, e = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int64()
+    _check("paged_kv_prefix_stats",
+           lib.paged_kv_prefix_stats(pool, ctypes.byref(c), ctypes.byref(h), ctypes.byref(e)))
+    return c.value, h.value, e.value
 
 
 # ------------------------------------------------------------ device ops ----

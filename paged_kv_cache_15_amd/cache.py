@@ -21,10 +21,11 @@ BITS_DTYPES = {"f32": torch.int32, "f16": torch.int16, "bf16": torch.int16}
 
 class PagedKVCache:
     def __init__(self, num_blocks, num_kv_heads, head_dim, dtype, block_size=16, free_order=None,
-                 device="cuda", poison=True):
+                 device="cuda", poison=True, prefix_cache=False):
         self.dtype = dtype
         self.device = torch.device(device)
-        self.desc = B.make_desc(num_blocks, block_size, num_kv_heads, head_dim, dtype)
+        self.desc = B.make_desc(num_blocks, block_size, num_kv_heads, head_dim, dtype,
+                                B.PAGED_KV_POOL_PREFIX_CACHE if prefix_cache else 0)
         x = 16 // torch.tensor([], dtype=TORCH_DTYPES[dtype]).element_size()
         tdt = TORCH_DTYPES[dtype]
         self.k_pool = torch.empty((num_blocks, num_kv_heads, head_dim // x, block_size, x),
@@ -59,6 +60,29 @@ class PagedKVCache:
 
     def stats(self):
         return B.paged_kv_stats(self.pool)
+
+    # -- prefix caching (pool made with prefix_cache=True) ----------------------
+    def create_prefix(self, prompt, extra_key=0):
+        """New sequence for a prompt of token ids; returns (seq, tokens already cached)."""
+        return B.paged_kv_seq_create_prefix(self.pool, prompt, extra_key)
+
+    def append_tokens(self, seqs, token_lists, key, value, stream=None):
+        """Like append, with the new tokens' ids (full blocks enter the hash map); key and
+        value hold the rows of all sequences' new tokens in order."""
+        slots, copies = [], []
+        for sq, toks in zip(seqs, token_lists):
+            s_, c_ = B.paged_kv_seq_append_tokens(self.pool, sq, toks)
+            slots.append(s_)
+            copies.extend(tuple(x) for x in c_)
+        slots = np.concatenate(slots) if slots else np.empty(0, np.int32)
+        if copies:
+            pairs = torch.from_numpy(np.asarray(copies, dtype=np.int32)).to(self.device)
+            B.paged_kv_copy_blocks(self.desc, self.k_pool, self.v_pool, pairs, len(copies), stream)
+        if len(slots):
+            slot_d = torch.from_numpy(slots).to(self.device)
+            B.reshape_and_cache(self.desc, key, value, self.k_pool, self.v_pool, slot_d,
+                                stream=stream)
+        return slots, copies
 
     def block_tables(self, seqs, max_blocks=None):
         return B.paged_kv_block_tables(self.pool, seqs, max_blocks)

@@ -8,18 +8,33 @@
 // deeplearn.tn "PagedAttention : comment optimiser la mémoire GPU …", worked example:
 // the token that overflows a full block lands at offset 0 of a newly taken block.
 //
+// With PAGED_KV_POOL_PREFIX_CACHE (§2.4, hash chain of V1; §VII step 5): every full
+// block written through paged_kv_seq_append_tokens gets a chained hash,
+// SHA-256(parent block's hash, its token ids, an extra key); a map from hash to block
+// lets a new prompt take over the cached blocks its chain matches (all but the last
+// prompt token, which is always recomputed); released blocks keep their hash while
+// they wait in the free queue, and a cached block is evicted from the map when
+// allocation takes it from the queue head, so the queue order is the LRU order.
+//
 // Readings where the pages are silent: the initial queue order is caller input;
 // released blocks go back in logical order; a copy-on-write copies a whole block and
 // the last holder writes in place; a failed append changes nothing; sequence ids are
-// sequential and never reused.
+// sequential and never reused.  Hash input: parent digest (32 zero bytes for the first
+// block), token ids as little-endian int32, extra key as little-endian int64; only full
+// blocks are hashed; a hash already in the map keeps its older block; a matched block
+// waiting in the free queue leaves the queue; a sequence appended to without token ids
+// registers no blocks.
 
 #include <hip/hip_runtime.h>
 
+#include <array>
 #include <cstdarg>
-#include <deque>
+#include <cstring>
+#include <unordered_map>
 #include <vector>
 
 #include "common.h"
+#include "sha256.h"
 
 namespace pkv {
 
@@ -73,10 +88,90 @@ bool kernel_desc(const paged_kv_pool_desc* d, bool attention) {
 
 using namespace pkv;
 
+using Digest = std::array<uint8_t, 32>;
+
+struct DigestHash {
+    size_t operator()(const Digest& d) const {
+        size_t h;
+        std::memcpy(&h, d.data(), sizeof(h));   // SHA-256 output bits are uniform
+        return h;
+    }
+};
+
+// SHA-256(parent || tokens as little-endian int32 || extra as little-endian int64),
+// the message assembled in one buffer.
+static void chain_hash(const Digest& parent, const int32_t* tokens, int32_t n, int64_t extra,
+                       Digest& out) {
+    thread_local std::vector<uint8_t> msg;
+    msg.resize(32 + 4 * (size_t)n + 8);
+    std::memcpy(msg.data(), parent.data(), 32);
+    uint8_t* q = msg.data() + 32;
+    for (int32_t i = 0; i < n; ++i, q += 4) {
+        const uint32_t t = (uint32_t)tokens[i];
+        q[0] = (uint8_t)t;
+        q[1] = (uint8_t)(t >> 8);
+        q[2] = (uint8_t)(t >> 16);
+        q[3] = (uint8_t)(t >> 24);
+    }
+    for (int i = 0; i < 8; ++i) q[i] = (uint8_t)((uint64_t)extra >> (8 * i));
+    Sha256 h;
+    h.update(msg.data(), msg.size());
+    h.final(out.data());
+}
+
+// The free-block queue: a doubly linked list threaded through per-block links, so a
+// cached block that a new prompt matches can leave from the middle in O(1).
+struct FreeQueue {
+    std::vector<int32_t> prev, next;
+    std::vector<char> queued;
+    int32_t head = -1, tail = -1;
+    int64_t count = 0;
+
+    void init(const std::vector<int32_t>& order, int32_t nb) {
+        prev.assign(nb, -1);
+        next.assign(nb, -1);
+        queued.assign(nb, 0);
+        head = tail = -1;
+        count = 0;
+        for (int32_t b : order) push_back(b);
+    }
+    int64_t size() const { return count; }
+    int32_t front() const { return head; }
+    void push_back(int32_t b) {
+        prev[b] = tail;
+        next[b] = -1;
+        if (tail >= 0) next[tail] = b;
+        else head = b;
+        tail = b;
+        queued[b] = 1;
+        ++count;
+    }
+    void remove(int32_t b) {
+        if (prev[b] >= 0) next[prev[b]] = next[b];
+        else head = next[b];
+        if (next[b] >= 0) prev[next[b]] = prev[b];
+        else tail = prev[b];
+        prev[b] = next[b] = -1;
+        queued[b] = 0;
+        --count;
+    }
+    int32_t pop_front() {
+        const int32_t b = head;
+        remove(b);
+        return b;
+    }
+};
+
 struct Sequence {
     bool alive = false;
     int32_t length = 0;
     std::vector<int32_t> table;
+    // prefix caching: token ids of the partly filled last block, the hash of the last
+    // full block, the extra key; `tracked` false once tokens went in without ids
+    bool tracked = false;
+    std::vector<int32_t> partial;
+    Digest last{};
+    int64_t extra = 0;
 };
 
 struct paged_kv_pool {
@@ -84,10 +179,27 @@ struct paged_kv_pool {
     void* k = nullptr;
     void* v = nullptr;
     bool owns_buffers = false;
-    std::deque<int32_t> free_queue;
+    FreeQueue free_queue;
     std::vector<int32_t> refcount;
     std::vector<Sequence> seqs;
+    // prefix caching
+    bool prefix = false;
+    std::vector<char> has_hash;
+    std::vector<Digest> block_digest;
+    std::unordered_map<Digest, int32_t, DigestHash> cached;
+    int64_t hit_blocks = 0, evictions = 0;
 };
+
+// Take the block at the queue head; cached content there leaves the map first.
+static int32_t take_free(paged_kv_pool* p) {
+    const int32_t b = p->free_queue.pop_front();
+    if (p->prefix && p->has_hash[b]) {
+        p->cached.erase(p->block_digest[b]);
+        p->has_hash[b] = 0;
+        ++p->evictions;
+    }
+    return b;
+}
 
 static Sequence* find_seq(paged_kv_pool* p, int32_t id) {
     if (!p || id < 0 || (size_t)id >= p->seqs.size() || !p->seqs[id].alive) return nullptr;
@@ -157,8 +269,13 @@ paged_kv_status paged_kv_pool_create(const paged_kv_pool_desc* desc, const int32
     }
     auto* p = new paged_kv_pool();
     p->desc = *desc;
-    p->free_queue.assign(order.begin(), order.end());
+    p->free_queue.init(order, nb);
     p->refcount.assign(nb, 0);
+    p->prefix = (desc->flags & PAGED_KV_POOL_PREFIX_CACHE) != 0;
+    if (p->prefix) {
+        p->has_hash.assign(nb, 0);
+        p->block_digest.assign(nb, Digest{});
+    }
     if (!host_only) {
         if (k_pool) {
             p->k = k_pool;
@@ -225,10 +342,7 @@ paged_kv_status paged_kv_seq_fork(paged_kv_pool* p, int32_t parent, int32_t* chi
     if (!p || !child) { set_error("null argument"); return PAGED_KV_ERR_INVALID_ARG; }
     const Sequence* par = find_seq(p, parent);
     if (!par) { set_error("no live sequence %d", parent); return PAGED_KV_ERR_NO_SUCH_SEQ; }
-    Sequence s;
-    s.alive = true;
-    s.length = par->length;
-    s.table = par->table;
+    Sequence s = *par;
     for (int32_t b : s.table) p->refcount[b] += 1;
     p->seqs.push_back(std::move(s));     // may reallocate: `par` is not used after this
     *child = (int32_t)p->seqs.size() - 1;
@@ -244,7 +358,8 @@ static int64_t blocks_needed(const paged_kv_pool* p, const Sequence& s, int32_t 
 }
 
 static paged_kv_status append_one(paged_kv_pool* p, int32_t seq, int32_t n, int32_t* slots_out,
-                                  int32_t* copies_out, int32_t max_copies, int32_t* n_copies) {
+                                  int32_t* copies_out, int32_t max_copies, int32_t* n_copies,
+                                  const int32_t* tokens = nullptr) {
     Sequence* s = find_seq(p, seq);
     if (!s) { set_error("no live sequence %d", seq); return PAGED_KV_ERR_NO_SUCH_SEQ; }
     if (n < 0) { set_error("n_tokens %d < 0", n); return PAGED_KV_ERR_INVALID_ARG; }
@@ -252,8 +367,8 @@ static paged_kv_status append_one(paged_kv_pool* p, int32_t seq, int32_t n, int3
     bool cow = false;
     int64_t need = blocks_needed(p, *s, n, &cow);
     if (need > (int64_t)p->free_queue.size()) {
-        set_error("sequence %d needs %lld blocks, %zu free", seq, (long long)need,
-                  p->free_queue.size());
+        set_error("sequence %d needs %lld blocks, %lld free", seq, (long long)need,
+                  (long long)p->free_queue.size());
         return PAGED_KV_ERR_OUT_OF_BLOCKS;
     }
     if (cow && max_copies < 1) {
@@ -263,10 +378,10 @@ static paged_kv_status append_one(paged_kv_pool* p, int32_t seq, int32_t n, int3
     }
     *n_copies = 0;
     const int32_t bs = p->desc.block_size;
+    if (!tokens) s->tracked = false;
     if (cow) {
         int32_t src = s->table.back();
-        int32_t dst = p->free_queue.front();
-        p->free_queue.pop_front();
+        int32_t dst = take_free(p);
         p->refcount[src] -= 1;
         p->refcount[dst] = 1;
         s->table.back() = dst;
@@ -277,13 +392,25 @@ static paged_kv_status append_one(paged_kv_pool* p, int32_t seq, int32_t n, int3
     for (int32_t i = 0; i < n; ++i) {
         int32_t pos = s->length;
         if (pos % bs == 0) {
-            int32_t b = p->free_queue.front();
-            p->free_queue.pop_front();
+            int32_t b = take_free(p);
             p->refcount[b] = 1;
             s->table.push_back(b);
         }
         slots_out[i] = s->table[pos / bs] * bs + pos % bs;
         s->length = pos + 1;
+        if (s->tracked) {
+            s->partial.push_back(tokens[i]);
+            if ((int32_t)s->partial.size() == bs) {   // the block just became full
+                chain_hash(s->last, s->partial.data(), bs, s->extra, s->last);
+                s->partial.clear();
+                const int32_t b = s->table[pos / bs];
+                if (!p->has_hash[b] && p->cached.find(s->last) == p->cached.end()) {
+                    p->cached.emplace(s->last, b);
+                    p->block_digest[b] = s->last;
+                    p->has_hash[b] = 1;
+                }
+            }
+        }
     }
     return PAGED_KV_OK;
 }
@@ -323,6 +450,76 @@ paged_kv_status paged_kv_append_batch(paged_kv_pool* p, const int32_t* seqs, con
         *n_copies += nc;
         *n_done = i + 1;
     }
+    return PAGED_KV_OK;
+}
+
+paged_kv_status paged_kv_block_hash(const uint8_t* parent, const int32_t* tokens, int32_t n,
+                                    int64_t extra_key, uint8_t* out) {
+    clear_error();
+    if (!out || n < 0 || (n > 0 && !tokens)) { set_error("null or invalid argument"); return PAGED_KV_ERR_INVALID_ARG; }
+    Digest par{}, d;
+    if (parent) std::memcpy(par.data(), parent, 32);
+    chain_hash(par, tokens, n, extra_key, d);
+    std::memcpy(out, d.data(), 32);
+    return PAGED_KV_OK;
+}
+
+paged_kv_status paged_kv_seq_create_prefix(paged_kv_pool* p, const int32_t* prompt, int32_t n,
+                                           int64_t extra_key, int32_t* seq_id, int32_t* n_cached) {
+    clear_error();
+    if (!p || !seq_id || !n_cached || n < 0 || (n > 0 && !prompt)) {
+        set_error("null or invalid argument");
+        return PAGED_KV_ERR_INVALID_ARG;
+    }
+    if (!p->prefix) { set_error("pool was created without PAGED_KV_POOL_PREFIX_CACHE"); return PAGED_KV_ERR_UNSUPPORTED; }
+    if (p->seqs.size() >= (size_t)INT32_MAX) { set_error("sequence ids exhausted"); return PAGED_KV_ERR_INVALID_ARG; }
+    Sequence s;
+    s.alive = true;
+    s.tracked = true;
+    s.extra = extra_key;
+    const int32_t bs = p->desc.block_size;
+    const int32_t full = n > 0 ? (n - 1) / bs : 0;      // the last prompt token is recomputed
+    for (int32_t i = 0; i < full; ++i) {
+        Digest h;
+        chain_hash(s.last, prompt + (int64_t)i * bs, bs, extra_key, h);
+        auto it = p->cached.find(h);
+        if (it == p->cached.end()) break;
+        const int32_t b = it->second;
+        if (p->refcount[b] == 0) p->free_queue.remove(b);
+        p->refcount[b] += 1;
+        s.table.push_back(b);
+        s.length += bs;
+        s.last = h;
+        ++p->hit_blocks;
+    }
+    p->seqs.push_back(std::move(s));
+    *seq_id = (int32_t)p->seqs.size() - 1;
+    *n_cached = p->seqs.back().length;
+    return PAGED_KV_OK;
+}
+
+paged_kv_status paged_kv_seq_append_tokens(paged_kv_pool* p, int32_t seq, const int32_t* tokens,
+                                           int32_t n_tokens, int32_t* slots_out,
+                                           int32_t* copies_out, int32_t max_copies,
+                                           int32_t* n_copies) {
+    clear_error();
+    if (!p || !n_copies || (n_tokens > 0 && (!slots_out || !tokens)) || (max_copies > 0 && !copies_out)) {
+        set_error("null argument");
+        return PAGED_KV_ERR_INVALID_ARG;
+    }
+    *n_copies = 0;
+    static const int32_t none = 0;
+    return append_one(p, seq, n_tokens, slots_out, copies_out, max_copies, n_copies,
+                      n_tokens > 0 ? tokens : &none);
+}
+
+paged_kv_status paged_kv_prefix_stats(const paged_kv_pool* p, int64_t* cached_blocks,
+                                      int64_t* hit_blocks, int64_t* evictions) {
+    clear_error();
+    if (!p || !cached_blocks || !hit_blocks || !evictions) { set_error("null argument"); return PAGED_KV_ERR_INVALID_ARG; }
+    *cached_blocks = (int64_t)p->cached.size();
+    *hit_blocks = p->hit_blocks;
+    *evictions = p->evictions;
     return PAGED_KV_OK;
 }
 

@@ -266,3 +266,49 @@ def test_workspace_reused_across_calls_bitwise(pt):
     o = oreplay.run(w)
     assert_close(g.outputs[0], o.outputs[0], "bf16", "f32")
     cache.close()
+
+
+@pytest.mark.parametrize("keep_first", [True, False], ids=["shared", "from-free-queue"])
+def test_prefix_cache_hit_gives_the_same_attention_bitwise(keep_first):
+    """A prompt that takes over cached prefix blocks ([DS] §2.4 hash chain) attends to the
+    same K/V as one that writes the prefix itself: outputs are bit-identical, and match
+    the oracle."""
+    from paged_kv_cache_15_amd.cache import PagedKVCache
+    from paged_kv_cache_15_amd.replay import to_device
+    rng = np.random.default_rng(41)
+    hq, hkv, d, dt, bs = 32, 8, 128, "bf16", 16
+    pa = rng.integers(0, 50000, 2056).tolist()
+    pb = pa[:2048] + rng.integers(0, 50000, 100).tolist()
+    kva = rng.standard_normal((2, 2056, hkv, d)).astype(np.float32)
+    kvb = np.concatenate([kva[:, :2048], rng.standard_normal((2, 100, hkv, d)).astype(np.float32)], 1)
+    q = rng.standard_normal((1, hq, d)).astype(np.float32)
+    scale = 1.0 / np.sqrt(d)
+    qd = to_device(q, dt, "cuda")
+
+    c = PagedKVCache(400, hkv, d, dt, bs, np.random.default_rng(2).permutation(400), prefix_cache=True)
+    sa, na = c.create_prefix(pa)
+    assert na == 0
+    c.append_tokens([sa], [pa], to_device(kva[0], dt, "cuda"), to_device(kva[1], dt, "cuda"))
+    if not keep_first:
+        c.free(sa)
+    sb, nb = c.create_prefix(pb)
+    assert nb == 2048
+    c.append_tokens([sb], [pb[nb:]], to_device(kvb[0, nb:], dt, "cuda"), to_device(kvb[1, nb:], dt, "cuda"))
+    out_hit, tables_hit, _ = c.attend([sb], qd, scale, "f32")
+
+    r = PagedKVCache(400, hkv, d, dt, bs, np.random.default_rng(3).permutation(400))
+    sr = r.create()
+    r.append([sr], [len(pb)], to_device(kvb[0], dt, "cuda"), to_device(kvb[1], dt, "cuda"))
+    out_ref, _, _ = r.attend([sr], qd, scale, "f32")
+    torch.cuda.synchronize()
+    say(f"[edge] prefix hit {nb} tokens, keep_first={keep_first}")
+    assert torch.equal(out_hit, out_ref)
+    # the oracle on the dense K/V of prompt b
+    kb = lowp.storage_bits_to_f64(lowp.to_storage_bits(kvb[0], dt), dt)
+    vb = lowp.storage_bits_to_f64(lowp.to_storage_bits(kvb[1], dt), dt)
+    qb = lowp.storage_bits_to_f64(lowp.to_storage_bits(q, dt), dt)[0]
+    from oracle.attention import dense_decode
+    want = dense_decode(qb, kb, vb, scale)
+    assert np.abs(out_f64(out_hit)[0] - want).max() <= TOL[dt]
+    c.close()
+    r.close()
