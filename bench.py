@@ -189,6 +189,45 @@ def prefix_cache_host(seconds_cap=5.0):
             "oracle_us_per_request": round(t_orc / done * 1e6, 2), "oracle_requests": done}
 
 
+def decode_graph_timing(layers=32, reps=20):
+    """Launch cost of a small decode batch: one step of `layers` layers (cache write +
+    paged attention each) over 8 sequences of the GQA shape (64 q / 8 kv heads, d 128,
+    bf16, contexts 256..2048), launched eagerly vs replayed from a HIP graph.  The same
+    step is re-run (idempotent), HIP events around `reps` repetitions."""
+    import numpy as np
+    import torch
+    from paged_kv_cache_15_amd.graph import LayeredKV, DecodeStep
+    from paged_kv_cache_15_amd.replay import to_device
+    rng = np.random.default_rng(9)
+    lens = rng.integers(256, 2049, 8).tolist()
+    nb = sum((n + 16) // 16 + 1 for n in lens) + 8
+    kv = LayeredKV(layers, nb, 8, 128, "bf16", 16, rng.permutation(nb), poison=False)
+    seqs = [kv.cache.create() for _ in lens]
+    keys = [to_device(rng.standard_normal((sum(lens), 8, 128)).astype(np.float32), "bf16", "cuda")] * layers
+    kv.append(seqs, lens, keys, keys)
+    mx = max(lens) + 1
+    st = DecodeStep(kv, len(lens), 64, (mx + 15) // 16, mx, 1 / np.sqrt(128.0), 0, "bf16")
+    nk = to_device(rng.standard_normal((layers, len(lens), 8, 128)).astype(np.float32), "bf16", "cuda")
+    q = to_device(rng.standard_normal((layers, len(lens), 64, 128)).astype(np.float32), "bf16", "cuda")
+    st.set_step(seqs, nk, nk, q)
+    st.capture()
+    res = {}
+    for name, fn in (("eager", st.launch), ("graph", st.replay)):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        res[name] = e0.elapsed_time(e1) * 1e3 / reps
+    kv.close()
+    return {"layers": layers, "batch": len(lens), "launches_per_step": 2 * layers,
+            "eager_us_per_step": round(res["eager"], 1), "graph_us_per_step": round(res["graph"], 1)}
+
+
 def main():
     args = parse()
     if args.copy_calibration:
@@ -331,6 +370,8 @@ def main():
         del new_k, new_v
         res["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
     res["prefix_cache_host"] = prefix_cache_host()
+    if not args.no_cpu_baseline:
+        res["decode_graph"] = decode_graph_timing()
     print(json.dumps(res), flush=True)
 
 

@@ -15,6 +15,8 @@ namespace pkv {
 constexpr int kStreamMaxWaves = 3072;
 // The per-sequence tile prefix is built in LDS by every workgroup.
 constexpr int kStreamMaxSeqs = 8192;
+// Fewest tiles per wave the plan aims for (small batches get fewer waves).
+constexpr int kStreamMinSlice = 16;
 
 struct StreamPlan {
     bool mfma;             // MFMA kernel (unit = KV head) or VALU kernel (unit = query head)

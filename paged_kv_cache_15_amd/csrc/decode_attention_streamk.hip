@@ -844,7 +844,10 @@ StreamPlan stream_plan(int32_t num_seqs, int32_t hq, int32_t hkv, int32_t dtype,
     p.heads_per_unit = p.mfma ? group : 1;
     const int64_t max_tiles = (int64_t)((max_ctx + kKernelBlockSize - 1) / kKernelBlockSize) *
                               num_seqs * p.units;
-    p.waves = (int32_t)std::max<int64_t>(1, std::min<int64_t>(kStreamMaxWaves, max_tiles));
+    // at least kStreamMinSlice tiles per wave (on the bound max_tiles): thinner slices cut
+    // every unit into many pieces, and the merge's round trips grow with their number
+    p.waves = (int32_t)std::max<int64_t>(
+        1, std::min<int64_t>(kStreamMaxWaves, (max_tiles + kStreamMinSlice - 1) / kStreamMinSlice));
     p.max_pieces = (int64_t)p.waves + (int64_t)num_seqs * p.units;
     const size_t rows = (size_t)p.max_pieces * p.heads_per_unit;
     p.meta_off = 0;

@@ -1,0 +1,73 @@
+"""Graph-captured multi-layer decode step (GPU): every replay matches the eager step bit
+for bit, with the host's own work and synchronisations between replays, and one
+layer's attention matches the oracle."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import lowp
+from oracle.attention import dense_decode
+from gpu_common import TOL, say, out_f64
+
+pytestmark = pytest.mark.gpu
+
+
+def _bits(x, dt):
+    return lowp.storage_bits_to_f64(lowp.to_storage_bits(x, dt), dt)
+
+
+@pytest.mark.parametrize("pt", [0, 512], ids=["streamk", "pt512"])
+def test_decode_step_graph_matches_eager_bitwise(pt):
+    from paged_kv_cache_15_amd.graph import LayeredKV, DecodeStep
+    from paged_kv_cache_15_amd.replay import to_device
+    L, hq, hkv, d, dt = 4, 32, 8, 128, "bf16"
+    lens0 = [5, 17, 100, 257, 1000, 33, 64, 511]
+    nsteps = 6
+    rng = np.random.default_rng(55)
+    order = rng.permutation(600)
+    kvs = [LayeredKV(L, 600, hkv, d, dt, 16, order) for _ in range(2)]
+    seqs = [[kv.cache.create() for _ in lens0] for kv in kvs]
+    # prefill: the same rows in both, per layer
+    rows = [[rng.standard_normal((2, n, hkv, d)).astype(np.float32) for n in lens0] for _ in range(L)]
+    for kv, ss in zip(kvs, seqs):
+        keys = [to_device(np.concatenate([r[0] for r in rows[l]]), dt, "cuda") for l in range(L)]
+        vals = [to_device(np.concatenate([r[1] for r in rows[l]]), dt, "cuda") for l in range(L)]
+        kv.append(ss, lens0, keys, vals)
+    max_ctx = max(lens0) + nsteps
+    steps = [DecodeStep(kv, len(lens0), hq, (max_ctx + 15) // 16, max_ctx, 1 / np.sqrt(d), pt, "f32")
+             for kv in kvs]
+    history = [[list(r) for r in rows[l]] for l in range(L)]     # per layer, per seq: [k, v]
+    for step in range(nsteps):
+        nk = rng.standard_normal((L, len(lens0), hkv, d)).astype(np.float32)
+        nv = rng.standard_normal((L, len(lens0), hkv, d)).astype(np.float32)
+        q = rng.standard_normal((L, len(lens0), hq, d)).astype(np.float32)
+        dk, dv, dq = to_device(nk, dt, "cuda"), to_device(nv, dt, "cuda"), to_device(q, dt, "cuda")
+        for i, (st, ss) in enumerate(zip(steps, seqs)):
+            st.set_step(ss, dk, dv, dq)
+            if i == 0:
+                if step == 0:
+                    st.capture()          # its warm-up runs this step once
+                else:
+                    st.replay()
+            else:
+                st.launch()
+        torch.cuda.synchronize()
+        say(f"[graph] step {step} partition_tokens={pt}")
+        assert torch.equal(steps[0].out, steps[1].out), step
+        for l in range(L):
+            for s in range(len(lens0)):
+                history[l][s][0] = np.concatenate([history[l][s][0], nk[l, s][None]])
+                history[l][s][1] = np.concatenate([history[l][s][1], nv[l, s][None]])
+    # pools of every layer identical
+    for l in range(L):
+        assert torch.equal(kvs[0].k[l].view(torch.int16), kvs[1].k[l].view(torch.int16))
+        assert torch.equal(kvs[0].v[l].view(torch.int16), kvs[1].v[l].view(torch.int16))
+    # last step of layer 2 against the oracle's dense attention
+    l = 2
+    got = out_f64(steps[0].out[l])
+    for s in range(len(lens0)):
+        want = dense_decode(_bits(q[l, s], dt), _bits(history[l][s][0], dt), _bits(history[l][s][1], dt),
+                            float(np.float32(1 / np.sqrt(d))))
+        assert np.abs(got[s] - want).max() <= TOL[dt], s
+    for kv in kvs:
+        kv.close()
