@@ -59,9 +59,10 @@ typedef enum {
 
 typedef enum { PAGED_KV_F32 = 0, PAGED_KV_F16 = 1, PAGED_KV_BF16 = 2 } paged_kv_dtype;
 
-/* Pool shape.  block_size: tokens per block (any >= 1 for the allocator; 16 for the
- * device kernels, [DS] §2.2 "often 16 tokens").  dtype: element type of K and V (and
- * of the queries given to paged_attention_decode). */
+/* Pool shape.  block_size: tokens per block (any >= 1 for the allocator; 1, 16 or 32
+ * for the device kernels: [DS] §2.2 gives 16 as the usual size, [DL] page-size section
+ * of SGLang weighs 16/32 against 1).  dtype: element type of K and V (and of the
+ * queries given to paged_attention_decode). */
 typedef struct {
     int32_t num_blocks;
     int32_t block_size;
@@ -229,8 +230,8 @@ paged_kv_status paged_kv_copy_blocks(const paged_kv_pool_desc* desc, void* k_poo
  *                heads and dims contiguous).
  *   slot_mapping device int32[num_tokens]; -1 = padding, not written; slots outside
  *                [0, num_blocks * block_size) are not written either.
- * Layout of the destination: see the top of this file.  Requires block_size 16 and
- * head_dim a multiple of X.  num_tokens == 0 launches nothing.  Two tokens with one
+ * Layout of the destination: see the top of this file.  Requires block_size 1, 16 or
+ * 32 and head_dim a multiple of X.  num_tokens == 0 launches nothing.  Two tokens with one
  * slot in a call: the surviving value is unspecified. */
 paged_kv_status reshape_and_cache(const paged_kv_pool_desc* desc, const void* key,
                                   const void* value, int64_t key_stride, int64_t value_stride,
@@ -258,8 +259,8 @@ size_t paged_attention_workspace_bytes(const paged_kv_pool_desc* desc, int32_t n
  *   context_lens  device int32[num_seqs]
  *   max_context_len  host bound on every context_lens[s] (sizes the launch)
  *   partition_tokens 0: stream-K schedule — the batch's (sequence, head unit,
- *                 16-token block) tiles are split evenly over a fixed set of waves
- *                 (3072 on MI355X, fewer for small batches) and the pieces of a
+ *                 16-token tile) tiles are split evenly over a fixed set of waves
+ *                 (3072 on MI355X up to head_dim 128, fewer for small batches) and the pieces of a
  *                 sequence's head unit cut by those splits are merged by log-sum-exp
  *                 (used for up to 8192 sequences; larger batches fall back to 512-token
  *                 partitions).  > 0: fixed split-K partitions of that many tokens
@@ -271,7 +272,7 @@ size_t paged_attention_workspace_bytes(const paged_kv_pool_desc* desc, int32_t n
  *                 rest is scratch.  Calls sharing one workspace must not overlap.
  * A sequence whose context_len is outside [1, max_context_len], or whose table holds
  * an id outside [0, num_blocks) below its length, gets NaN outputs; nothing outside
- * the buffers is read.  Requires block_size 16, head_dim 64 or 128,
+ * the buffers is read.  Requires block_size 1, 16 or 32, head_dim 64, 128 or 256,
  * num_q_heads % num_kv_heads == 0 and a group of at most 16 query heads.
  * Results do not depend on where blocks sit in the pool, nor on whether a block is
  * shared: the summation order follows logical token positions only. */

@@ -10,6 +10,7 @@ import os
 import subprocess
 import sys
 import time
+from concurrent.futures import ThreadPoolExecutor
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
@@ -33,11 +34,16 @@ def build(verbose=False):
              "-Wall", "-Wno-unused-result",
              "-I", os.path.join(ROOT, "include"), "-I", CSRC]
     t0 = time.time()
+    cmds = []
     for src in SOURCES:
         obj = os.path.join(CSRC, src.rsplit(".", 1)[0] + ".o")
-        cmd = [hipcc(), *flags, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
-        _run(cmd, verbose)
+        cmds.append([hipcc(), *flags, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj])
         objs.append(obj)
+    # the translation units are independent: compile them side by side
+    jobs = max(1, min(len(cmds), int(os.environ.get("MAX_JOBS", "8"))))
+    with ThreadPoolExecutor(jobs) as ex:
+        for f in [ex.submit(_run, c, verbose) for c in cmds]:
+            f.result()
     tmp = LIB + ".tmp"
     _run([hipcc(), "-shared", f"--offload-arch={ARCH}", "-o", tmp, *objs], verbose)
     os.replace(tmp, LIB)

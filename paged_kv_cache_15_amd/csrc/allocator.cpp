@@ -73,12 +73,12 @@ bool valid_desc(const paged_kv_pool_desc* d) {
 
 bool kernel_desc(const paged_kv_pool_desc* d, bool attention) {
     if (!valid_desc(d)) return false;
-    if (d->block_size != kKernelBlockSize) {
-        set_error("device kernels need block_size %d (got %d)", kKernelBlockSize, d->block_size);
+    if (d->block_size != 1 && d->block_size != 16 && d->block_size != 32) {
+        set_error("device kernels need block_size 1, 16 or 32 (got %d)", d->block_size);
         return false;
     }
-    if (attention && d->head_dim != 64 && d->head_dim != 128) {
-        set_error("attention kernels support head_dim 64 and 128 (got %d)", d->head_dim);
+    if (attention && d->head_dim != 64 && d->head_dim != 128 && d->head_dim != 256) {
+        set_error("attention kernels support head_dim 64, 128 and 256 (got %d)", d->head_dim);
         return false;
     }
     return true;

@@ -19,7 +19,7 @@ typedef __attribute__((__vector_size__(4 * sizeof(short)))) short s16x4;
 typedef __attribute__((__vector_size__(8 * sizeof(_Float16)))) _Float16 f16x8;
 typedef __attribute__((__vector_size__(4 * sizeof(_Float16)))) _Float16 f16x4;
 
-constexpr int kBS = pkv::kKernelBlockSize;  // tokens per block
+constexpr int kTile = 16;                   // tokens per tile: the 16 rows of one MFMA block
 constexpr int kWaves = 4;                   // waves per partition workgroup
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kNegInf = -INFINITY;
@@ -60,6 +60,55 @@ __device__ __forceinline__ float sum_across_quads(float v) {
     v += __shfl_xor(v, 16);
     v += __shfl_xor(v, 32);
     return v;
+}
+
+// Read-only int32 through the scalar data cache: block tables and context lengths are
+// never written while a kernel runs, and a scalar load keeps the per-tile lookups off the
+// vector memory counter, so waiting for one never waits for the K/V loads in flight.
+__device__ __forceinline__ int32_t sload(const int32_t* p, int64_t i) {
+    return ((const __attribute__((address_space(4))) int32_t*)p)[i];
+}
+
+// Waves per SIMD the attention kernels are compiled for (a wave's registers must fit in
+// 512 / waves): two tiles of K/V in flight plus the accumulators and the query.  The
+// host plans stream-K launches with the same numbers (pkv::kernel_waves_per_simd).
+template <int D>
+constexpr int mfma_waves_per_simd() { return pkv::kernel_waves_per_simd(D, 2, true); }
+template <int D, int E>
+constexpr int valu_waves_per_simd() { return pkv::kernel_waves_per_simd(D, E, false); }
+
+// Block size 1: every token of a tile sits in its own block.  Lane l gets the block of
+// token 16*it + (l & 15) of the table row (ids read through the scalar cache; tokens at
+// or past ctx, which must be >= 1, take the id of token ctx - 1).  An id outside
+// [0, num_blocks) sets `bad` and reads block 0.
+__device__ __forceinline__ int32_t lane_block_bs1(const int32_t* row, int it, int ctx,
+                                                  int num_blocks, int lane, bool& bad) {
+    int32_t ids[kTile];
+#pragma unroll
+    for (int j = 0; j < kTile; ++j) ids[j] = sload(row, min(kTile * it + j, ctx - 1));
+    bool any = false;
+#pragma unroll
+    for (int j = 0; j < kTile; ++j) any |= (uint32_t)ids[j] >= (uint32_t)num_blocks;
+    bad = any;
+    const int tok = lane & (kTile - 1);
+    int32_t id = ids[0];
+#pragma unroll
+    for (int j = 1; j < kTile; ++j) id = tok == j ? ids[j] : id;
+    return (uint32_t)id < (uint32_t)num_blocks ? id : 0;
+}
+
+// Block size 1 stores V token-major (a block's [head_dim][1] is one token's row), while
+// the value products want each lane to hold several tokens of one dim.  A wave passes its
+// tile through its own LDS rows of `ldw` elements: lane l wrote 16-byte chunks
+// 4*i + l/16 of token l & 15 (the K-style load), then reads single elements back.
+// LDS operations of one wave complete in order, so no barrier is needed; rows are padded
+// by 16 bytes so that the element reads of one instruction hit distinct banks.
+template <typename T, int NCH>
+__device__ __forceinline__ void lds_put_rows(T* rows, int ldw, int lane, const i32x4 (&raw)[NCH]) {
+    constexpr int X = 16 / sizeof(T);
+#pragma unroll
+    for (int i = 0; i < NCH; ++i)
+        *reinterpret_cast<i32x4*>(rows + (lane & 15) * ldw + (4 * i + (lane >> 4)) * X) = raw[i];
 }
 
 }  // namespace pkv_dev

@@ -5,14 +5,19 @@
 #include <cstddef>
 #include <cstdint>
 
+#include "common.h"
 #include "paged_kv.h"
 
 namespace pkv {
 
-// Stream-K decomposition: the (sequence, head unit, 16-token block) tiles of the
-// whole batch form one line; `waves` waves each take an equal contiguous slice of it.
-// 3072 = 256 CUs x 4 SIMDs x 3 resident waves of the MFMA kernel on MI355X.
+// Stream-K decomposition: the (sequence, head unit, 16-token tile) tiles of the whole
+// batch form one line; `waves` waves each take an equal contiguous slice of it.
+// At most one wave per resident slot: 256 CUs x 4 SIMDs x the kernel's waves per SIMD
+// on MI355X (3072 for the MFMA kernel up to head_dim 128).
 constexpr int kStreamMaxWaves = 3072;
+inline int stream_max_waves(int head_dim, int elem_bytes, bool mfma) {
+    return 256 * 4 * kernel_waves_per_simd(head_dim, elem_bytes, mfma);
+}
 // The per-sequence tile prefix is built in LDS by every workgroup.
 constexpr int kStreamMaxSeqs = 8192;
 // Fewest tiles per wave the plan aims for (small batches get fewer waves).
@@ -46,6 +51,7 @@ struct StreamLaunch {
     int32_t num_blocks;
     int32_t dtype;
     int32_t head_dim;
+    int32_t block_size;
     int32_t max_context_len;
     float scale;
     void* workspace;

@@ -6,8 +6,8 @@
 // GPU …", worked example: the token written after a full block goes to offset 0 of
 // a freshly taken block anywhere in the pool.
 //
-// Pool layout (chunk X = 16 bytes / element size):
-//   K [block][kv_head][head_dim / X][16][X]     V [block][kv_head][head_dim][16]
+// Pool layout (chunk X = 16 bytes / element size, BS = block size 1, 16 or 32):
+//   K [block][kv_head][head_dim / X][BS][X]     V [block][kv_head][head_dim][BS]
 
 #include <hip/hip_runtime.h>
 
@@ -19,15 +19,14 @@ typedef __attribute__((__vector_size__(4 * sizeof(int)))) int i32x4;
 
 // One thread per (token, KV head, 16-byte chunk of head_dim).  The key chunk is one
 // 16-byte store; the value chunk scatters its X elements down X rows of the
-// transposed V tile (stride 16 elements).
-template <typename T>
+// transposed V tile (stride BS elements; one 16-byte store when BS is 1).
+template <typename T, int BS>
 __global__ __launch_bounds__(256) void reshape_and_cache_kernel(
     const T* __restrict__ key, const T* __restrict__ value, int64_t key_stride,
     int64_t value_stride, T* __restrict__ k_pool, T* __restrict__ v_pool,
     const int32_t* __restrict__ slot_mapping, int32_t num_tokens, int32_t kv_heads,
     int32_t head_dim, int64_t num_slots) {
     constexpr int X = 16 / sizeof(T);
-    constexpr int BS = pkv::kKernelBlockSize;
     const int chunks = head_dim / X;
     const int64_t per_token = (int64_t)kv_heads * chunks;
     const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -46,11 +45,15 @@ __global__ __launch_bounds__(256) void reshape_and_cache_kernel(
     T* kdst = k_pool + (((blk * kv_heads + h) * chunks + c) * BS + off) * X;
     *reinterpret_cast<i32x4*>(kdst) = kc;
 
-    T ve[X];
-    __builtin_memcpy(ve, &vc, 16);
     T* vdst = v_pool + ((blk * kv_heads + h) * head_dim + (int64_t)c * X) * BS + off;
+    if constexpr (BS == 1) {
+        *reinterpret_cast<i32x4*>(vdst) = vc;
+    } else {
+        T ve[X];
+        __builtin_memcpy(ve, &vc, 16);
 #pragma unroll
-    for (int e = 0; e < X; ++e) vdst[e * BS] = ve[e];
+        for (int e = 0; e < X; ++e) vdst[e * BS] = ve[e];
+    }
 }
 
 // One workgroup per (pair, K or V): copies a whole block (all heads, all slots).
@@ -65,6 +68,32 @@ __global__ __launch_bounds__(256) void copy_blocks_kernel(char* __restrict__ k_p
     i32x4* d = reinterpret_cast<i32x4*>(base + dst * block_bytes);
     const int64_t n = block_bytes / 16;
     for (int64_t i = threadIdx.x; i < n; i += blockDim.x) d[i] = s[i];
+}
+
+template <typename T>
+void launch_reshape(const paged_kv_pool_desc* desc, const void* key, const void* value,
+                    int64_t key_stride, int64_t value_stride, void* k_pool, void* v_pool,
+                    const int32_t* slot_mapping, int32_t num_tokens, int64_t num_slots,
+                    int64_t grid, hipStream_t st) {
+    const T* k = static_cast<const T*>(key);
+    const T* v = static_cast<const T*>(value);
+    T* kp = static_cast<T*>(k_pool);
+    T* vp = static_cast<T*>(v_pool);
+    const dim3 g((unsigned)grid), b(256);
+    switch (desc->block_size) {
+        case 1:
+            reshape_and_cache_kernel<T, 1><<<g, b, 0, st>>>(k, v, key_stride, value_stride, kp, vp,
+                slot_mapping, num_tokens, desc->num_kv_heads, desc->head_dim, num_slots);
+            break;
+        case 32:
+            reshape_and_cache_kernel<T, 32><<<g, b, 0, st>>>(k, v, key_stride, value_stride, kp, vp,
+                slot_mapping, num_tokens, desc->num_kv_heads, desc->head_dim, num_slots);
+            break;
+        default:
+            reshape_and_cache_kernel<T, 16><<<g, b, 0, st>>>(k, v, key_stride, value_stride, kp, vp,
+                slot_mapping, num_tokens, desc->num_kv_heads, desc->head_dim, num_slots);
+            break;
+    }
 }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
@@ -110,17 +139,10 @@ paged_kv_status reshape_and_cache(const paged_kv_pool_desc* desc, const void* ke
     if (grid > INT32_MAX) { pkv::set_error("too many tokens for one launch"); return PAGED_KV_ERR_UNSUPPORTED; }
     const int64_t num_slots = (int64_t)desc->num_blocks * desc->block_size;
     hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-    if (eb == 4) {
-        reshape_and_cache_kernel<uint32_t><<<dim3((unsigned)grid), dim3(256), 0, st>>>(
-            (const uint32_t*)key, (const uint32_t*)value, key_stride, value_stride,
-            (uint32_t*)k_pool, (uint32_t*)v_pool, slot_mapping, num_tokens, desc->num_kv_heads,
-            desc->head_dim, num_slots);
-    } else {
-        reshape_and_cache_kernel<uint16_t><<<dim3((unsigned)grid), dim3(256), 0, st>>>(
-            (const uint16_t*)key, (const uint16_t*)value, key_stride, value_stride,
-            (uint16_t*)k_pool, (uint16_t*)v_pool, slot_mapping, num_tokens, desc->num_kv_heads,
-            desc->head_dim, num_slots);
-    }
+    if (eb == 4) launch_reshape<uint32_t>(desc, key, value, key_stride, value_stride, k_pool, v_pool,
+                                          slot_mapping, num_tokens, num_slots, grid, st);
+    else launch_reshape<uint16_t>(desc, key, value, key_stride, value_stride, k_pool, v_pool,
+                                  slot_mapping, num_tokens, num_slots, grid, st);
     return launch_status("reshape_and_cache");
 }
 

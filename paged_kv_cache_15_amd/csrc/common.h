@@ -26,10 +26,19 @@ inline int elem_bytes(int32_t dtype) {
 // Checks every field of a descriptor; on failure records why and returns false.
 bool valid_desc(const paged_kv_pool_desc* d);
 
-// Extra conditions the device kernels need (block size 16, supported head dims).
+// Extra conditions the device kernels need (block size 1, 16 or 32; for attention,
+// head_dim 64, 128 or 256).
 bool kernel_desc(const paged_kv_pool_desc* d, bool attention);
 
-constexpr int kKernelBlockSize = 16;
+constexpr int kTileTokens = 16;   // attention works on 16-token tiles of a sequence
+
+// Resident waves per SIMD of the attention kernels for head_dim d, element bytes e: the
+// MFMA kernels hold 3 up to head_dim 128 and 2 at 256; the VALU kernels, whose registers
+// grow with the bytes of a tile (16-byte loads per lane, ni), 3 up to 4 loads, 2 up to 8
+// and 1 beyond.
+constexpr int kernel_waves_per_simd(int d, int e, bool mfma) {
+    return mfma ? (d > 128 ? 2 : 3) : (d * e / 64 <= 4 ? 3 : d * e / 64 <= 8 ? 2 : 1);
+}
 constexpr int kDefaultPartitionTokens = 512;
 
 }  // namespace pkv

@@ -9,8 +9,8 @@
 // size context x heads goes back to HBM.
 //
 // Work decomposition: one workgroup of 4 wave64s per (sequence, KV head, partition of
-// `partition_tokens` tokens).  Wave w takes the partition's blocks w, w+4, w+8, ...
-// (16 tokens each), keeps its own running max / sum / weighted-V state, and the four
+// `partition_tokens` tokens).  Wave w takes the partition's 16-token tiles w, w+4,
+// w+8, ..., keeps its own running max / sum / weighted-V state, and the four
 // states are merged in LDS in fixed wave order.  A sequence that fits one partition
 // writes its output directly; longer ones leave (max, sum, weighted V) per partition
 // in the workspace and attn_reduce_kernel merges them (log-sum-exp, partition order).
@@ -25,10 +25,13 @@
 //     GEMV, done on the vector ALUs with cross-lane reductions.
 // Scores are kept in the base-2 domain: x = (scale * log2 e) * q.k, weights 2^(x - m).
 //
-// Pool layout (X = 16 bytes / element size):
-//   K [block][kv_head][head_dim / X][16][X]   V [block][kv_head][head_dim][16]
-// so one (block, KV head) tile is 16 * head_dim contiguous elements, and the MFMA
-// operand loads below are contiguous across the 64 lanes of each load instruction.
+// Pool layout (X = 16 bytes / element size, BS = block size):
+//   K [block][kv_head][head_dim / X][BS][X]   V [block][kv_head][head_dim][BS]
+// so one (block, KV head) region is BS * head_dim contiguous elements.  With BS = 16 a
+// tile is one block and every operand load instruction reads one contiguous run across
+// its 64 lanes; with BS = 32 a tile is half a block (runs of 256 bytes); with BS = 1 a
+// tile gathers 16 blocks, each lane loading from its own token's block, and V (stored
+// token-major at that size) is turned into the V^T operand through LDS.
 
 #include "attention_common.h"
 #include "attention_host.h"
@@ -92,12 +95,17 @@ __device__ __forceinline__ void write_partition_result(const PartitionArgs& a, i
 // and token quad l / 16, which is exactly the layout the score tile comes out in and
 // the layout the value product wants its B operand in, so P never leaves registers.
 // ---------------------------------------------------------------------------------
-template <int D, int DT, int OUT_DT>
-__global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(3))) void attn_mfma_kernel(PartitionArgs a) {
-    constexpr int KI = D / 32;   // QK MFMAs (and 16-byte K loads per lane) per block
-    constexpr int MT = D / 16;   // PV MFMA pairs (and 8-byte V loads per lane) per block
-    constexpr int TILE = kBS * D;  // elements of one (block, KV head) tile
+template <int D, int DT, int OUT_DT, int BS>
+__global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(mfma_waves_per_simd<D>())))
+void attn_mfma_kernel(PartitionArgs a) {
+    constexpr int KI = D / 32;   // QK MFMAs (and 16-byte K loads per lane) per tile
+    constexpr int MT = D / 16;   // PV MFMA pairs (and 8-byte V loads per lane) per tile
+    constexpr int TILE = BS * D;  // elements of one (block, KV head) region
+    constexpr int TPB = BS >= kTile ? BS / kTile : 1;   // tiles per block
+    constexpr int LDW = D + 8;    // block size 1: LDS row of one token's values
     using kvec = typename std::conditional<DT == DT_BF16, bf16x8, f16x8>::type;
+    using vbuf = typename std::conditional<BS == 1, i32x4[KI], i32x2[MT]>::type;
+    __shared__ uint16_t s_vt[BS == 1 ? kWaves * kTile * LDW : 1];
 
     const int s = blockIdx.x / a.num_kv_heads, g = blockIdx.x - s * a.num_kv_heads;
     const int p = blockIdx.y;
@@ -117,7 +125,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(3))
     if (start >= ctx) return;
     const int end = min(start + a.partition_tokens, ctx);
     const int npart = (ctx + a.partition_tokens - 1) / a.partition_tokens;
-    const int blk_begin = start / kBS, blk_end = (end + kBS - 1) / kBS;
+    const int blk_begin = start / kTile, blk_end = (end + kTile - 1) / kTile;   // tiles
     const int32_t* trow = a.block_tables + (int64_t)s * a.max_blocks_per_seq;
 
     // Query operand: lane holds q[head gq][32*kk + 8*quad .. +8] for each kk.
@@ -133,10 +141,12 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(3))
         }
     }
 
-    const uint16_t* kbase = static_cast<const uint16_t*>(a.k_pool) + (int64_t)g * TILE;
-    const uint16_t* vbase = static_cast<const uint16_t*>(a.v_pool) + (int64_t)g * TILE;
+    const uint16_t* kbase = static_cast<const uint16_t*>(a.k_pool) + (int64_t)g * (BS == 1 ? D : TILE);
+    const uint16_t* vbase = static_cast<const uint16_t*>(a.v_pool) + (int64_t)g * (BS == 1 ? D : TILE);
     const int64_t blk_stride = (int64_t)a.num_kv_heads * TILE;
-    const int voff = gq * 4 + quad;   // 8-byte unit of row gq, tokens 4*quad.. of a V^T tile
+    const int koff = (lane >> 4) * BS + (lane & 15);   // 16-byte unit: chunk l/16 of token l%16
+    const int voff = gq * (BS / 4) + quad;   // 8-byte unit of row gq, tokens 4*quad.. of V^T
+    uint16_t* vrows = s_vt + w * kTile * LDW;
 
     f32x4 acc[MT];
 #pragma unroll
@@ -145,21 +155,51 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(3))
     bool bad_block = false;
 
     i32x4 kA[KI], kB[KI];
-    i32x2 vA[MT], vB[MT];
+    vbuf vA, vB;
+    int id_v = 0;    // block size >= 16: lane i holds the block of the wave's i-th tile
 
-    // K tile: load kk of lane l is 16-byte chunk 4*kk + l/16 of token l%16, i.e. bytes
-    // [1024*kk + 16*l, +16): each load instruction reads 1 KiB contiguous.  V^T tile:
-    // load mt of lane l is row 16*mt + l%16, tokens 4*(l/16)..+3: 512 B contiguous.
-    auto load = [&](int32_t bid, i32x4 (&kr)[KI], i32x2 (&vr)[MT]) {
-        const i32x4* kt = reinterpret_cast<const i32x4*>(kbase + bid * blk_stride);
-        const i32x2* vt = reinterpret_cast<const i32x2*>(vbase + bid * blk_stride);
+    // K tile: load kk of lane l is 16-byte chunk 4*kk + l/16 of token l%16 (block size
+    // 16: bytes [1024*kk + 16*l, +16), each load instruction reads 1 KiB contiguous).
+    // V^T tile: load mt of lane l is row 16*mt + l%16, tokens 4*(l/16)..+3.
+    auto load = [&](int idx, int b, i32x4 (&kr)[KI], vbuf& vr) {
+        if constexpr (BS == 1) {
+            bool bad;
+            const int32_t bid = lane_block_bs1(trow, b, ctx, a.num_blocks, lane, bad);
+            bad_block |= bad;
+            const i32x4* kt = reinterpret_cast<const i32x4*>(kbase + bid * blk_stride) + (lane >> 4);
+            const i32x4* vt = reinterpret_cast<const i32x4*>(vbase + bid * blk_stride) + (lane >> 4);
 #pragma unroll
-        for (int kk = 0; kk < KI; ++kk) kr[kk] = __builtin_nontemporal_load(kt + kk * 64 + lane);
+            for (int kk = 0; kk < KI; ++kk) kr[kk] = __builtin_nontemporal_load(kt + 4 * kk);
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) vr[mt] = __builtin_nontemporal_load(vt + mt * 64 + voff);
+            for (int kk = 0; kk < KI; ++kk) vr[kk] = __builtin_nontemporal_load(vt + 4 * kk);
+        } else {
+            const int32_t bid = __builtin_amdgcn_readlane(id_v, idx);
+            const int h = b & (TPB - 1);
+            const i32x4* kt = reinterpret_cast<const i32x4*>(kbase + bid * blk_stride) + koff + kTile * h;
+            const i32x2* vt = reinterpret_cast<const i32x2*>(vbase + bid * blk_stride) + voff + 4 * h;
+#pragma unroll
+            for (int kk = 0; kk < KI; ++kk) kr[kk] = __builtin_nontemporal_load(kt + kk * 4 * BS);
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) vr[mt] = __builtin_nontemporal_load(vt + mt * 4 * BS);
+        }
     };
 
-    auto compute = [&](int b, i32x4 (&kr)[KI], i32x2 (&vr)[MT]) {
+    auto compute = [&](int b, i32x4 (&kr)[KI], vbuf& vin) {
+        i32x2 vr[MT];
+        if constexpr (BS == 1) {
+            lds_put_rows<uint16_t, KI>(vrows, LDW, lane, vin);
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) {
+                uint32_t e[4];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) e[j] = vrows[(4 * quad + j) * LDW + 16 * mt + gq];
+                vr[mt][0] = (int)(e[0] | e[1] << 16);
+                vr[mt][1] = (int)(e[2] | e[3] << 16);
+            }
+        } else {
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) vr[mt] = vin[mt];
+        }
         f32x4 sc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kk = 0; kk < KI; ++kk) {
@@ -170,7 +210,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(3))
                 sc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, kr[kk]),
                                                             qop[kk], sc, 0, 0, 0);
         }
-        const int tok0 = b * kBS + 4 * quad;  // this lane's 4 tokens: tok0 .. tok0+3
+        const int tok0 = b * kTile + 4 * quad;  // this lane's 4 tokens: tok0 .. tok0+3
         float x[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) x[j] = (tok0 + j < end) ? sc[j] * a.scale_log2 : kNegInf;
@@ -200,7 +240,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(3))
             plo[j] = (short)lo;
             lsum += pf;
         }
-        if (b * kBS + kBS > end) {
+        if (b * kTile + kTile > end) {
             // tail block: slots past the context may hold anything (NaN included);
             // their weight is 0 but 0 * NaN is not, so clear those value elements
 #pragma unroll
@@ -239,22 +279,24 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(3))
     const int n_w = nblk > w ? (nblk - w + kWaves - 1) / kWaves : 0;
     for (int base = 0; base < n_w; base += 64) {
         const int cnt = min(64, n_w - base);
-        int id_v = 0;
-        if (lane < cnt) id_v = trow[blk_begin + w + kWaves * (base + lane)];
-        const bool id_ok = (uint32_t)id_v < (uint32_t)a.num_blocks;
-        if (__ballot(lane < cnt && !id_ok)) bad_block = true;
-        id_v = id_ok ? id_v : 0;
         const int b0 = blk_begin + w + kWaves * base;
-        load(__builtin_amdgcn_readlane(id_v, 0), kA, vA);
+        if constexpr (BS != 1) {
+            id_v = 0;
+            if (lane < cnt) id_v = trow[(b0 + kWaves * lane) / TPB];
+            const bool id_ok = (uint32_t)id_v < (uint32_t)a.num_blocks;
+            if (__ballot(lane < cnt && !id_ok)) bad_block = true;
+            id_v = id_ok ? id_v : 0;
+        }
+        load(0, b0, kA, vA);
         int i = 0;
         for (; i + 2 < cnt; i += 2) {
-            load(__builtin_amdgcn_readlane(id_v, i + 1), kB, vB);
+            load(i + 1, b0 + kWaves * (i + 1), kB, vB);
             compute(b0 + kWaves * i, kA, vA);
-            load(__builtin_amdgcn_readlane(id_v, i + 2), kA, vA);
+            load(i + 2, b0 + kWaves * (i + 2), kA, vA);
             compute(b0 + kWaves * (i + 1), kB, vB);
         }
         if (i + 1 < cnt) {
-            load(__builtin_amdgcn_readlane(id_v, i + 1), kB, vB);
+            load(i + 1, b0 + kWaves * (i + 1), kB, vB);
             compute(b0 + kWaves * i, kA, vA);
             compute(b0 + kWaves * (i + 1), kB, vB);
         } else {
@@ -314,13 +356,18 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(3))
 // i.e. X consecutive tokens of one dim; the weights of those tokens are fetched from
 // the lanes that own them with ds_bpermute.
 // ---------------------------------------------------------------------------------
-template <int D, int DT, int OUT_DT>
-__global__ __launch_bounds__(kWaves * 64) void attn_valu_kernel(PartitionArgs a) {
+template <int D, int DT, int OUT_DT, int BS>
+__global__ __launch_bounds__(kWaves * 64)
+__attribute__((amdgpu_waves_per_eu(valu_waves_per_simd<D, DT == DT_F32 ? 4 : 2>())))
+void attn_valu_kernel(PartitionArgs a) {
     using bits_t = typename std::conditional<DT == DT_F32, uint32_t, uint16_t>::type;
     constexpr int E = sizeof(bits_t);
     constexpr int X = 16 / E;           // elements per 16-byte chunk
-    constexpr int NI = kBS * D * E / 1024;  // 16-byte loads per lane per tile (K or V)
-    constexpr int TILE = kBS * D;
+    constexpr int NI = kTile * D * E / 1024;  // 16-byte loads per lane per tile (K or V)
+    constexpr int TILE = BS * D;
+    constexpr int TPB = BS >= kTile ? BS / kTile : 1;
+    constexpr int LDW = D + X;
+    __shared__ bits_t s_vt[BS == 1 ? kWaves * kTile * LDW : 1];
 
     const int s = blockIdx.x / a.num_q_heads, h = blockIdx.x - s * a.num_q_heads;
     const int p = blockIdx.y;
@@ -339,7 +386,7 @@ __global__ __launch_bounds__(kWaves * 64) void attn_valu_kernel(PartitionArgs a)
     if (start >= ctx) return;
     const int end = min(start + a.partition_tokens, ctx);
     const int npart = (ctx + a.partition_tokens - 1) / a.partition_tokens;
-    const int blk_begin = start / kBS, blk_end = (end + kBS - 1) / kBS;
+    const int blk_begin = start / kTile, blk_end = (end + kTile - 1) / kTile;   // tiles
     const int32_t* trow = a.block_tables + (int64_t)s * a.max_blocks_per_seq;
 
     // scaled query in LDS, then the lane's D/4 dims in registers
@@ -359,9 +406,11 @@ __global__ __launch_bounds__(kWaves * 64) void attn_valu_kernel(PartitionArgs a)
 #pragma unroll
         for (int e = 0; e < X; ++e) qr[i][e] = sm_q[(4 * i + kq) * X + e];
 
-    const bits_t* kbase = static_cast<const bits_t*>(a.k_pool) + (int64_t)g * TILE;
-    const bits_t* vbase = static_cast<const bits_t*>(a.v_pool) + (int64_t)g * TILE;
+    const bits_t* kbase = static_cast<const bits_t*>(a.k_pool) + (int64_t)g * (BS == 1 ? D : TILE);
+    const bits_t* vbase = static_cast<const bits_t*>(a.v_pool) + (int64_t)g * (BS == 1 ? D : TILE);
     const int64_t blk_stride = (int64_t)a.num_kv_heads * TILE;
+    const int koff = kq * BS + tok;
+    bits_t* vrows = s_vt + w * kTile * LDW;
 
     float acc[NI];
 #pragma unroll
@@ -369,18 +418,48 @@ __global__ __launch_bounds__(kWaves * 64) void attn_valu_kernel(PartitionArgs a)
     float m = kNegInf, lsum = 0.f;
     bool bad_block = false;
     i32x4 kA[NI], kB[NI], vA[NI], vB[NI];
+    int id_v = 0;
 
-    auto load = [&](int32_t bid, i32x4 (&kr)[NI], i32x4 (&vr)[NI]) {
-        const i32x4* kt = reinterpret_cast<const i32x4*>(kbase + bid * blk_stride);
-        const i32x4* vt = reinterpret_cast<const i32x4*>(vbase + bid * blk_stride);
+    auto load = [&](int idx, int b, i32x4 (&kr)[NI], i32x4 (&vr)[NI]) {
+        if constexpr (BS == 1) {
+            bool bad;
+            const int32_t bid = lane_block_bs1(trow, b, ctx, a.num_blocks, lane, bad);
+            bad_block |= bad;
+            const i32x4* kt = reinterpret_cast<const i32x4*>(kbase + bid * blk_stride) + kq;
+            const i32x4* vt = reinterpret_cast<const i32x4*>(vbase + bid * blk_stride) + kq;
 #pragma unroll
-        for (int i = 0; i < NI; ++i) {
-            kr[i] = __builtin_nontemporal_load(kt + i * 64 + lane);
-            vr[i] = __builtin_nontemporal_load(vt + i * 64 + lane);
+            for (int i = 0; i < NI; ++i) {
+                kr[i] = __builtin_nontemporal_load(kt + 4 * i);
+                vr[i] = __builtin_nontemporal_load(vt + 4 * i);
+            }
+        } else {
+            const int32_t bid = __builtin_amdgcn_readlane(id_v, idx);
+            const int h = b & (TPB - 1);
+            const i32x4* kt = reinterpret_cast<const i32x4*>(kbase + bid * blk_stride) + koff + kTile * h;
+            const i32x4* vt = reinterpret_cast<const i32x4*>(vbase + bid * blk_stride) + E * h + vpiece;
+#pragma unroll
+            for (int i = 0; i < NI; ++i) {
+                kr[i] = __builtin_nontemporal_load(kt + i * 4 * BS);
+                vr[i] = __builtin_nontemporal_load(vt + ((64 * i + lane) / E) * (BS / X));
+            }
         }
     };
 
-    auto compute = [&](int b, i32x4 (&kr)[NI], i32x4 (&vr)[NI]) {
+    auto compute = [&](int b, i32x4 (&kr)[NI], i32x4 (&vin)[NI]) {
+        i32x4 vr[NI];
+        if constexpr (BS == 1) {
+            lds_put_rows<bits_t, NI>(vrows, LDW, lane, vin);
+#pragma unroll
+            for (int i = 0; i < NI; ++i) {
+                bits_t vb[X];
+#pragma unroll
+                for (int e = 0; e < X; ++e) vb[e] = vrows[(vpiece * X + e) * LDW + (64 * i + lane) / E];
+                __builtin_memcpy(&vr[i], vb, 16);
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < NI; ++i) vr[i] = vin[i];
+        }
         float part = 0.f;
 #pragma unroll
         for (int i = 0; i < NI; ++i) {
@@ -390,7 +469,7 @@ __global__ __launch_bounds__(kWaves * 64) void attn_valu_kernel(PartitionArgs a)
             for (int e = 0; e < X; ++e) part = fmaf(qr[i][e], bits_to_f32<DT>(kb[e]), part);
         }
         const float sc = sum_across_quads(part);
-        const int t = b * kBS + tok;
+        const int t = b * kTile + tok;
         const float x = t < end ? sc : kNegInf;
         // lazy rescaling, as in the MFMA kernel
         if (__ballot(x > m + kRescaleSlack)) {
@@ -411,7 +490,7 @@ __global__ __launch_bounds__(kWaves * 64) void attn_valu_kernel(PartitionArgs a)
         float pw[X];
 #pragma unroll
         for (int e = 0; e < X; ++e) pw[e] = __shfl(pt, vpiece * X + e);
-        const int valid = end - b * kBS;   // tokens of this block inside the partition
+        const int valid = end - b * kTile;   // tokens of this tile inside the partition
 #pragma unroll
         for (int i = 0; i < NI; ++i) {
             bits_t vb[X];
@@ -432,22 +511,24 @@ __global__ __launch_bounds__(kWaves * 64) void attn_valu_kernel(PartitionArgs a)
     const int n_w = nblk > w ? (nblk - w + kWaves - 1) / kWaves : 0;
     for (int base = 0; base < n_w; base += 64) {
         const int cnt = min(64, n_w - base);
-        int id_v = 0;
-        if (lane < cnt) id_v = trow[blk_begin + w + kWaves * (base + lane)];
-        const bool id_ok = (uint32_t)id_v < (uint32_t)a.num_blocks;
-        if (__ballot(lane < cnt && !id_ok)) bad_block = true;
-        id_v = id_ok ? id_v : 0;
         const int b0 = blk_begin + w + kWaves * base;
-        load(__builtin_amdgcn_readlane(id_v, 0), kA, vA);
+        if constexpr (BS != 1) {
+            id_v = 0;
+            if (lane < cnt) id_v = trow[(b0 + kWaves * lane) / TPB];
+            const bool id_ok = (uint32_t)id_v < (uint32_t)a.num_blocks;
+            if (__ballot(lane < cnt && !id_ok)) bad_block = true;
+            id_v = id_ok ? id_v : 0;
+        }
+        load(0, b0, kA, vA);
         int i = 0;
         for (; i + 2 < cnt; i += 2) {
-            load(__builtin_amdgcn_readlane(id_v, i + 1), kB, vB);
+            load(i + 1, b0 + kWaves * (i + 1), kB, vB);
             compute(b0 + kWaves * i, kA, vA);
-            load(__builtin_amdgcn_readlane(id_v, i + 2), kA, vA);
+            load(i + 2, b0 + kWaves * (i + 2), kA, vA);
             compute(b0 + kWaves * (i + 1), kB, vB);
         }
         if (i + 1 < cnt) {
-            load(__builtin_amdgcn_readlane(id_v, i + 1), kB, vB);
+            load(i + 1, b0 + kWaves * (i + 1), kB, vB);
             compute(b0 + kWaves * i, kA, vA);
             compute(b0 + kWaves * (i + 1), kB, vB);
         } else {
@@ -504,9 +585,12 @@ __global__ __launch_bounds__(kWaves * 64) void attn_valu_kernel(PartitionArgs a)
 // max, out = sum_p 2^(m_p - M) acc_p / sum_p 2^(m_p - M) l_p, partitions in order.
 // ---------------------------------------------------------------------------------
 constexpr int kReduceMaxGroups = 8;
+// groups of D threads per workgroup: at most 8, and at most 1024 threads
+template <int D>
+constexpr int reduce_groups_max() { return 1024 / D < kReduceMaxGroups ? 1024 / D : kReduceMaxGroups; }
 
 template <int D, int OUT_DT>
-__global__ __launch_bounds__(D * kReduceMaxGroups) void attn_reduce_kernel(
+__global__ __launch_bounds__(D * reduce_groups_max<D>()) void attn_reduce_kernel(
         void* out, const int32_t* context_lens, int32_t num_q_heads, int32_t max_context_len,
         int32_t partition_tokens, int32_t max_parts, const float* ws_m, const float* ws_l,
         const float* ws_acc) {
@@ -581,7 +665,7 @@ __global__ __launch_bounds__(D * kReduceMaxGroups) void attn_reduce_kernel(
 
 struct Plan {
     PartitionArgs a;
-    int dtype, out_dtype, head_dim;
+    int dtype, out_dtype, head_dim, block_size;
     bool mfma;
     bool streamk;              // stream-K schedule (partition_tokens 0) or fixed partitions
     pkv::StreamPlan sp;
@@ -632,11 +716,11 @@ paged_kv_status make_plan(Plan& pl, const paged_kv_pool_desc* desc, void* out, i
     if (max_ctx < 1) { pkv::set_error("max_context_len must be >= 1"); return PAGED_KV_ERR_INVALID_ARG; }
     pl.streamk = use_streamk(part_tokens, num_seqs);
     if (part_tokens == 0) part_tokens = pkv::kDefaultPartitionTokens;
-    if (part_tokens < 0 || part_tokens % kBS) {
-        pkv::set_error("partition_tokens %d must be a positive multiple of %d", part_tokens, kBS);
+    if (part_tokens < 0 || part_tokens % kTile) {
+        pkv::set_error("partition_tokens %d must be a positive multiple of %d", part_tokens, kTile);
         return PAGED_KV_ERR_INVALID_ARG;
     }
-    if ((int64_t)max_blocks * kBS < max_ctx) {
+    if ((int64_t)max_blocks * desc->block_size < max_ctx) {
         pkv::set_error("max_blocks_per_seq %d cannot hold max_context_len %d", max_blocks, max_ctx);
         return PAGED_KV_ERR_INVALID_ARG;
     }
@@ -689,6 +773,7 @@ paged_kv_status make_plan(Plan& pl, const paged_kv_pool_desc* desc, void* out, i
     pl.dtype = desc->dtype;
     pl.out_dtype = out_dtype;
     pl.head_dim = desc->head_dim;
+    pl.block_size = desc->block_size;
     pl.mfma = desc->dtype != PAGED_KV_F32 && group >= 2;
     // x: (sequence, head) pairs, y: partition.  All first partitions are dispatched
     // first; the empty high partitions of short sequences come last and exit at once.
@@ -697,39 +782,48 @@ paged_kv_status make_plan(Plan& pl, const paged_kv_pool_desc* desc, void* out, i
     pl.stream = reinterpret_cast<hipStream_t>(stream);
     pl.sl = pkv::StreamLaunch{out, out_dtype, q, k_pool, v_pool, tables, max_blocks, lens,
                               num_seqs, hq, desc->num_kv_heads, desc->num_blocks, desc->dtype,
-                              desc->head_dim, max_ctx, scale, ws};
+                              desc->head_dim, desc->block_size, max_ctx, scale, ws};
     return PAGED_KV_OK;
 }
 
-template <int D, int DT, int OUT>
+template <int D, int DT, int OUT, int BS>
 void launch_partition_t(const Plan& pl) {
     if constexpr (DT == DT_F32) {
-        attn_valu_kernel<D, DT, OUT><<<pl.grid, dim3(kWaves * 64), 0, pl.stream>>>(pl.a);
+        attn_valu_kernel<D, DT, OUT, BS><<<pl.grid, dim3(kWaves * 64), 0, pl.stream>>>(pl.a);
     } else {
-        if (pl.mfma) attn_mfma_kernel<D, DT, OUT><<<pl.grid, dim3(kWaves * 64), 0, pl.stream>>>(pl.a);
-        else attn_valu_kernel<D, DT, OUT><<<pl.grid, dim3(kWaves * 64), 0, pl.stream>>>(pl.a);
+        if (pl.mfma) attn_mfma_kernel<D, DT, OUT, BS><<<pl.grid, dim3(kWaves * 64), 0, pl.stream>>>(pl.a);
+        else attn_valu_kernel<D, DT, OUT, BS><<<pl.grid, dim3(kWaves * 64), 0, pl.stream>>>(pl.a);
     }
 }
 
-template <int D, int DT>
+template <int D, int DT, int BS>
 void launch_partition_d(const Plan& pl) {
-    if (pl.out_dtype == PAGED_KV_F32) launch_partition_t<D, DT, DT_F32>(pl);
-    else launch_partition_t<D, DT, DT>(pl);
+    if (pl.out_dtype == PAGED_KV_F32) launch_partition_t<D, DT, DT_F32, BS>(pl);
+    else launch_partition_t<D, DT, DT, BS>(pl);
+}
+
+template <int D, int BS>
+void launch_partition_dd(const Plan& pl) {
+    switch (pl.dtype) {
+        case PAGED_KV_F32: launch_partition_d<D, DT_F32, BS>(pl); break;
+        case PAGED_KV_F16: launch_partition_d<D, DT_F16, BS>(pl); break;
+        default: launch_partition_d<D, DT_BF16, BS>(pl); break;
+    }
 }
 
 template <int D>
-void launch_partition_dd(const Plan& pl) {
-    switch (pl.dtype) {
-        case PAGED_KV_F32: launch_partition_d<D, DT_F32>(pl); break;
-        case PAGED_KV_F16: launch_partition_d<D, DT_F16>(pl); break;
-        default: launch_partition_d<D, DT_BF16>(pl); break;
+void launch_partition_b(const Plan& pl) {
+    switch (pl.block_size) {
+        case 1: launch_partition_dd<D, 1>(pl); break;
+        case 32: launch_partition_dd<D, 32>(pl); break;
+        default: launch_partition_dd<D, 16>(pl); break;
     }
 }
 
 template <int D, int OUT>
 void launch_reduce_t(const Plan& pl, int num_seqs) {
-    // about 16 partitions per thread group, at most kReduceMaxGroups groups
-    const int groups = std::max(1, std::min(kReduceMaxGroups, (pl.a.max_parts + 15) / 16));
+    // about 16 partitions per thread group, at most reduce_groups_max<D>() groups
+    const int groups = std::max(1, std::min(reduce_groups_max<D>(), (pl.a.max_parts + 15) / 16));
     attn_reduce_kernel<D, OUT><<<dim3((unsigned)pl.a.num_q_heads, (unsigned)num_seqs),
                                  dim3(D * groups), 0,
                                  pl.stream>>>(pl.a.out, pl.a.context_lens, pl.a.num_q_heads,
@@ -792,8 +886,9 @@ paged_kv_status paged_attention_partition(const paged_kv_pool_desc* desc, void* 
                                    workspace_bytes, stream, true);
     if (st != PAGED_KV_OK || num_seqs == 0) return st;
     if (pl.streamk) pkv::launch_streamk_partition(pl.sl, pl.sp, stream);
-    else if (pl.head_dim == 64) launch_partition_dd<64>(pl);
-    else launch_partition_dd<128>(pl);
+    else if (pl.head_dim == 64) launch_partition_b<64>(pl);
+    else if (pl.head_dim == 256) launch_partition_b<256>(pl);
+    else launch_partition_b<128>(pl);
     return launch_status("paged attention partition kernel");
 }
 
@@ -804,7 +899,7 @@ paged_kv_status paged_attention_reduce(const paged_kv_pool_desc* desc, void* out
                                        size_t workspace_bytes, void* stream) {
     pkv::clear_error();
     Plan pl;
-    const int32_t max_blocks = (max_context_len + kBS - 1) / kBS;
+    const int32_t max_blocks = desc ? (max_context_len + desc->block_size - 1) / std::max(1, desc->block_size) : 0;
     paged_kv_status st = make_plan(pl, desc, out, out_dtype, nullptr, nullptr, nullptr, nullptr,
                                    max_blocks, context_lens, num_seqs, num_q_heads, max_context_len,
                                    1.f, partition_tokens, const_cast<void*>(workspace),
@@ -813,6 +908,7 @@ paged_kv_status paged_attention_reduce(const paged_kv_pool_desc* desc, void* out
     if (pl.streamk) return st;   // the stream-K launch merges in-kernel
     if (pl.a.max_parts <= 1) return st;
     if (pl.head_dim == 64) launch_reduce_d<64>(pl, num_seqs);
+    else if (pl.head_dim == 256) launch_reduce_d<256>(pl, num_seqs);
     else launch_reduce_d<128>(pl, num_seqs);
     return launch_status("paged attention reduce kernel");
 }

@@ -6,7 +6,7 @@
 // FlashAttention: stream K/V tiles through on-chip memory with an incremental
 // softmax), scheduled differently:
 //
-// Every (sequence, head unit, 16-token block) of the batch is a tile; tiles are laid on
+// Every (sequence, head unit, 16-token tile) of the batch is a tile; tiles are laid on
 // one line ordered by sequence, then unit, then block.  A fixed number W of waves each
 // take an equal contiguous slice of the line (to within one tile) and stream it with a
 // two-deep load pipeline that never restarts at sequence or head boundaries.  When a
@@ -19,6 +19,10 @@
 //
 // Units: the MFMA kernel's unit is a KV head with its group of query heads (fp16/bf16,
 // group >= 2); the VALU kernel's unit is one query head.
+//
+// Block sizes: with 16 or 32 tokens per block a tile is one block or one half of one; with
+// 1 token per block a tile gathers 16 blocks (per-lane addresses, and V transposed
+// through LDS, since such a pool stores each token's values as one row).
 //
 // Results depend only on the logical token order and on W, never on where blocks sit
 // in the pool: placement and sharing leave them bit-identical.
@@ -55,15 +59,8 @@ struct StreamArgs {
     float scale_log2;
 };
 
-// Read-only int32 through the scalar data cache: block tables and context lengths are
-// never written while a kernel runs, and a scalar load keeps the per-tile lookups off the
-// vector memory counter, so they never force a wait on the K/V loads in flight.
-__device__ __forceinline__ int32_t sload(const int32_t* p, int64_t i) {
-    return ((const __attribute__((address_space(4))) int32_t*)p)[i];
-}
-
 __device__ __forceinline__ int tiles_of(int ctx, int max_ctx) {
-    return (ctx >= 1 && ctx <= max_ctx) ? (ctx + kBS - 1) / kBS : 0;
+    return (ctx >= 1 && ctx <= max_ctx) ? (ctx + kTile - 1) / kTile : 0;
 }
 
 // Exclusive prefix of per-sequence tile counts (per unit) into s_pref[0..B]; returns
@@ -140,9 +137,11 @@ __device__ __forceinline__ void advance(const StreamArgs& a, Cursor& c) {
     } while (c.nt == 0 && c.s < a.num_seqs - 1);
 }
 
-// Physical block of the cursor's tile; out-of-range ids read block 0 and flag the unit.
+// Physical block of the cursor's tile (block size BS >= 16: the tile is part TPB of
+// block it / TPB); out-of-range ids read block 0 and flag the unit.
+template <int BS>
 __device__ __forceinline__ int32_t tile_block(const StreamArgs& a, const Cursor& c, bool& bad) {
-    const int32_t bid = sload(a.block_tables, (int64_t)c.s * a.max_blocks_per_seq + c.it);
+    const int32_t bid = sload(a.block_tables, (int64_t)c.s * a.max_blocks_per_seq + c.it / (BS / kTile));
     bad = (uint32_t)bid >= (uint32_t)a.num_blocks;
     return bad ? 0 : bid;
 }
@@ -329,13 +328,18 @@ __device__ void nan_invalid_sequences(const StreamArgs& a, const int* s_pref) {
 // is the fixed-partition MFMA kernel's: S^T = K.Q^T with 16x16x32 MFMAs, lazy-rescaled
 // base-2 softmax, O^T += V^T.P^T with P split into 16-bit head + remainder.
 // ---------------------------------------------------------------------------------
-template <int D, int DT, int OUT_DT>
-__global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(3)))
+template <int D, int DT, int OUT_DT, int BS>
+__global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(mfma_waves_per_simd<D>())))
 void attn_mfma_streamk(StreamArgs a) {
     constexpr int KI = D / 32;
     constexpr int MT = D / 16;
-    constexpr int TILE = kBS * D;
+    constexpr int TILE = BS * D;          // elements of one (block, KV head) region
+    constexpr int TPB = BS >= kTile ? BS / kTile : 1;   // tiles per block
+    constexpr int LDW = D + 8;            // block size 1: LDS row of one token's values
     using kvec = typename std::conditional<DT == DT_BF16, bf16x8, f16x8>::type;
+    // V registers as loaded: a V^T operand per 16 dims, or (block size 1) token rows
+    using vbuf = typename std::conditional<BS == 1, i32x4[KI], i32x2[MT]>::type;
+    __shared__ uint16_t s_vt[BS == 1 ? kWaves * kTile * LDW : 1];
 
     extern __shared__ int s_pref[];
     const int tiles_per_unit = build_prefix(a, s_pref);
@@ -357,9 +361,13 @@ void attn_mfma_streamk(StreamArgs a) {
     // load right where it is issued, draining the K/V prefetch.)
     const int gqc = min(gq, G - 1);
     const int64_t blk_stride = (int64_t)a.num_kv_heads * TILE;
-    const int voff = gq * 4 + quad;
+    // K: load kk of lane l is chunk 4*kk + l/16 of token l%16 of the tile;
+    // V^T: load mt of lane l is dim 16*mt + l%16, tokens 4*(l/16)..+3
+    const int koff = (lane >> 4) * BS + (lane & 15);
+    const int voff = gq * (BS / 4) + quad;
     const uint16_t* kpool = static_cast<const uint16_t*>(a.k_pool);
     const uint16_t* vpool = static_cast<const uint16_t*>(a.v_pool);
+    uint16_t* vrows = s_vt + (threadIdx.x >> 6) * kTile * LDW;
 
     Cursor lc = locate(a, s_pref, t0);   // tile being loaded (one ahead)
     Cursor cc = lc;                       // tile being computed
@@ -372,15 +380,28 @@ void attn_mfma_streamk(StreamArgs a) {
         for (int kk = 0; kk < KI; ++kk)
             qop[kk] = __builtin_bit_cast(kvec, *reinterpret_cast<const i32x4*>(qh + 32 * kk));
     };
-    auto load_kv = [&](const Cursor& c, i32x4 (&kr)[KI], i32x2 (&vr)[MT], bool& bad) {
-        const int32_t bid = tile_block(a, c, bad);
-        const int64_t base = (int64_t)c.u * TILE + bid * blk_stride;
-        const i32x4* kt = reinterpret_cast<const i32x4*>(kpool + base);
-        const i32x2* vt = reinterpret_cast<const i32x2*>(vpool + base);
+    auto load_kv = [&](const Cursor& c, i32x4 (&kr)[KI], vbuf& vr, bool& bad) {
+        if constexpr (BS == 1) {
+            const int32_t bid = lane_block_bs1(a.block_tables + (int64_t)c.s * a.max_blocks_per_seq,
+                                               c.it, c.ctx, a.num_blocks, lane, bad);
+            const int64_t base = bid * blk_stride + (int64_t)c.u * D;
+            const i32x4* kt = reinterpret_cast<const i32x4*>(kpool + base) + (lane >> 4);
+            const i32x4* vt = reinterpret_cast<const i32x4*>(vpool + base) + (lane >> 4);
 #pragma unroll
-        for (int kk = 0; kk < KI; ++kk) kr[kk] = __builtin_nontemporal_load(kt + kk * 64 + lane);
+            for (int kk = 0; kk < KI; ++kk) kr[kk] = __builtin_nontemporal_load(kt + 4 * kk);
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) vr[mt] = __builtin_nontemporal_load(vt + mt * 64 + voff);
+            for (int kk = 0; kk < KI; ++kk) vr[kk] = __builtin_nontemporal_load(vt + 4 * kk);
+        } else {
+            const int32_t bid = tile_block<BS>(a, c, bad);
+            const int h = c.it & (TPB - 1);
+            const int64_t base = (int64_t)c.u * TILE + bid * blk_stride;
+            const i32x4* kt = reinterpret_cast<const i32x4*>(kpool + base) + koff + kTile * h;
+            const i32x2* vt = reinterpret_cast<const i32x2*>(vpool + base) + voff + 4 * h;
+#pragma unroll
+            for (int kk = 0; kk < KI; ++kk) kr[kk] = __builtin_nontemporal_load(kt + kk * 4 * BS);
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) vr[mt] = __builtin_nontemporal_load(vt + mt * 4 * BS);
+        }
     };
 
     f32x4 acc[MT];
@@ -433,8 +454,23 @@ void attn_mfma_streamk(StreamArgs a) {
 
     // Compute the tile of cc from registers kr/vr.  If the next tile (nc) starts a new
     // unit, its queries are loaded into qop once the score MFMAs have read them.
-    auto compute = [&](i32x4 (&kr)[KI], i32x2 (&vr)[MT], bool bad, bool next_unit,
+    auto compute = [&](i32x4 (&kr)[KI], vbuf& vin, bool bad, bool next_unit,
                        const Cursor& nc) {
+        i32x2 vr[MT];
+        if constexpr (BS == 1) {
+            lds_put_rows<uint16_t, KI>(vrows, LDW, lane, vin);
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) {
+                uint32_t e[4];
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj) e[jj] = vrows[(4 * quad + jj) * LDW + 16 * mt + gq];
+                vr[mt][0] = (int)(e[0] | e[1] << 16);
+                vr[mt][1] = (int)(e[2] | e[3] << 16);
+            }
+        } else {
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) vr[mt] = vin[mt];
+        }
         f32x4 sc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kk = 0; kk < KI; ++kk) {
@@ -446,7 +482,7 @@ void attn_mfma_streamk(StreamArgs a) {
                                                             qop[kk], sc, 0, 0, 0);
         }
         if (next_unit) load_q(nc);
-        const int valid = min(kBS, cc.ctx - cc.it * kBS);   // tokens of this tile in the context
+        const int valid = min(kTile, cc.ctx - cc.it * kTile);   // tokens of this tile in the context
         const int tok0 = 4 * quad;
         float x[4];
 #pragma unroll
@@ -470,7 +506,7 @@ void attn_mfma_streamk(StreamArgs a) {
             plo[jj] = (short)lo;
             lsum += pf;
         }
-        if (valid < kBS) {
+        if (valid < kTile) {
             // slots past the context may hold anything (NaN included): clear them
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt) {
@@ -501,13 +537,12 @@ void attn_mfma_streamk(StreamArgs a) {
     };
 
     i32x4 kA[KI], kB[KI];
-    i32x2 vA[MT], vB[MT];
+    vbuf vA, vB;
     bool bA = false, bB = false;
 
     // one pipeline step: load tile k+1 into (kn, vn), compute tile k from (kc, vc)
     int done = 0;
-    auto step = [&](i32x4 (&kc)[KI], i32x2 (&vc)[MT], bool bc, i32x4 (&kn)[KI],
-                    i32x2 (&vn)[MT], bool& bn) {
+    auto step = [&](i32x4 (&kc)[KI], vbuf& vc, bool bc, i32x4 (&kn)[KI], vbuf& vn, bool& bn) {
         // Waves with more of their slice left get issue priority: co-resident waves share
         // the CU's memory pipe unevenly (oldest first), and a slice split is only balanced
         // if the waves progress together.
@@ -554,14 +589,18 @@ void attn_mfma_streamk(StreamArgs a) {
 // VALU stream-K kernel: unit = one query head (a group of 1, or fp32).  The per-tile
 // math is the fixed-partition VALU kernel's.
 // ---------------------------------------------------------------------------------
-template <int D, int DT, int OUT_DT>
-__global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(3)))
+template <int D, int DT, int OUT_DT, int BS>
+__global__ __launch_bounds__(kWaves * 64)
+__attribute__((amdgpu_waves_per_eu(valu_waves_per_simd<D, DT == DT_F32 ? 4 : 2>())))
 void attn_valu_streamk(StreamArgs a) {
     using bits_t = typename std::conditional<DT == DT_F32, uint32_t, uint16_t>::type;
     constexpr int E = sizeof(bits_t);
     constexpr int X = 16 / E;
-    constexpr int NI = kBS * D * E / 1024;
-    constexpr int TILE = kBS * D;
+    constexpr int NI = kTile * D * E / 1024;
+    constexpr int TILE = BS * D;
+    constexpr int TPB = BS >= kTile ? BS / kTile : 1;
+    constexpr int LDW = D + X;
+    __shared__ bits_t s_vt[BS == 1 ? kWaves * kTile * LDW : 1];
 
     extern __shared__ int s_pref[];
     const int tiles_per_unit = build_prefix(a, s_pref);
@@ -578,8 +617,12 @@ void attn_valu_streamk(StreamArgs a) {
     const int n = (int)(t1 - t0);
     const int tok = lane & 15, kq = lane >> 4, vpiece = lane % E;
     const int64_t blk_stride = (int64_t)a.num_kv_heads * TILE;
+    // K: load i of lane l is chunk 4*i + l/16 of token l%16; V (dim-major): load i is
+    // dim (64*i + l)/E, tokens X*(l%E)..+X
+    const int koff = kq * BS + tok;
     const bits_t* kpool = static_cast<const bits_t*>(a.k_pool);
     const bits_t* vpool = static_cast<const bits_t*>(a.v_pool);
+    bits_t* vrows = s_vt + (threadIdx.x >> 6) * kTile * LDW;
 
     Cursor lc = locate(a, s_pref, t0);
     Cursor cc = lc;
@@ -603,14 +646,28 @@ void attn_valu_streamk(StreamArgs a) {
         }
     };
     auto load_kv = [&](const Cursor& c, i32x4 (&kr)[NI], i32x4 (&vr)[NI], bool& bad) {
-        const int32_t bid = tile_block(a, c, bad);
-        const int64_t base = (int64_t)(c.u / a.group) * TILE + bid * blk_stride;
-        const i32x4* kt = reinterpret_cast<const i32x4*>(kpool + base);
-        const i32x4* vt = reinterpret_cast<const i32x4*>(vpool + base);
+        if constexpr (BS == 1) {
+            const int32_t bid = lane_block_bs1(a.block_tables + (int64_t)c.s * a.max_blocks_per_seq,
+                                               c.it, c.ctx, a.num_blocks, lane, bad);
+            const int64_t base = bid * blk_stride + (int64_t)(c.u / a.group) * D;
+            const i32x4* kt = reinterpret_cast<const i32x4*>(kpool + base) + kq;
+            const i32x4* vt = reinterpret_cast<const i32x4*>(vpool + base) + kq;
 #pragma unroll
-        for (int i = 0; i < NI; ++i) {
-            kr[i] = __builtin_nontemporal_load(kt + i * 64 + lane);
-            vr[i] = __builtin_nontemporal_load(vt + i * 64 + lane);
+            for (int i = 0; i < NI; ++i) {
+                kr[i] = __builtin_nontemporal_load(kt + 4 * i);
+                vr[i] = __builtin_nontemporal_load(vt + 4 * i);
+            }
+        } else {
+            const int32_t bid = tile_block<BS>(a, c, bad);
+            const int h = c.it & (TPB - 1);
+            const int64_t base = (int64_t)(c.u / a.group) * TILE + bid * blk_stride;
+            const i32x4* kt = reinterpret_cast<const i32x4*>(kpool + base) + koff + kTile * h;
+            const i32x4* vt = reinterpret_cast<const i32x4*>(vpool + base) + E * h + vpiece;
+#pragma unroll
+            for (int i = 0; i < NI; ++i) {
+                kr[i] = __builtin_nontemporal_load(kt + i * 4 * BS);
+                vr[i] = __builtin_nontemporal_load(vt + ((64 * i + lane) / E) * (BS / X));
+            }
         }
     };
 
@@ -666,8 +723,22 @@ void attn_valu_streamk(StreamArgs a) {
         first_here = true;
     };
 
-    auto compute = [&](i32x4 (&kr)[NI], i32x4 (&vr)[NI], bool bad, bool next_unit,
+    auto compute = [&](i32x4 (&kr)[NI], i32x4 (&vin)[NI], bool bad, bool next_unit,
                        const Cursor& nc) {
+        i32x4 vr[NI];
+        if constexpr (BS == 1) {
+            lds_put_rows<bits_t, NI>(vrows, LDW, lane, vin);
+#pragma unroll
+            for (int i = 0; i < NI; ++i) {
+                bits_t vb[X];
+#pragma unroll
+                for (int e = 0; e < X; ++e) vb[e] = vrows[(vpiece * X + e) * LDW + (64 * i + lane) / E];
+                __builtin_memcpy(&vr[i], vb, 16);
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < NI; ++i) vr[i] = vin[i];
+        }
         if (q_stale) {
             convert_q();
             q_stale = false;
@@ -685,7 +756,7 @@ void attn_valu_streamk(StreamArgs a) {
             q_stale = true;
         }
         const float sc = sum_across_quads(part);
-        const int valid = min(kBS, cc.ctx - cc.it * kBS);
+        const int valid = min(kTile, cc.ctx - cc.it * kTile);
         const float x = tok < valid ? sc : kNegInf;
         if (__ballot(x > m + kRescaleSlack)) {
             float mb = x;
@@ -799,30 +870,40 @@ StreamArgs make_args(const pkv::StreamLaunch& L, const pkv::StreamPlan& P) {
     return a;
 }
 
-template <int D, int DT, int OUT>
+template <int D, int DT, int OUT, int BS>
 void launch_part_t(const StreamArgs& a, bool mfma, hipStream_t st) {
     const dim3 grid((unsigned)((a.waves + kWaves - 1) / kWaves));
     const size_t lds = (size_t)(a.num_seqs + 1) * sizeof(int);
     if constexpr (DT == DT_F32) {
-        attn_valu_streamk<D, DT, OUT><<<grid, dim3(kWaves * 64), lds, st>>>(a);
+        attn_valu_streamk<D, DT, OUT, BS><<<grid, dim3(kWaves * 64), lds, st>>>(a);
     } else {
-        if (mfma) attn_mfma_streamk<D, DT, OUT><<<grid, dim3(kWaves * 64), lds, st>>>(a);
-        else attn_valu_streamk<D, DT, OUT><<<grid, dim3(kWaves * 64), lds, st>>>(a);
+        if (mfma) attn_mfma_streamk<D, DT, OUT, BS><<<grid, dim3(kWaves * 64), lds, st>>>(a);
+        else attn_valu_streamk<D, DT, OUT, BS><<<grid, dim3(kWaves * 64), lds, st>>>(a);
     }
 }
 
-template <int D, int DT>
+template <int D, int DT, int BS>
 void launch_part_d(const StreamArgs& a, int out_dtype, bool mfma, hipStream_t st) {
-    if (out_dtype == PAGED_KV_F32) launch_part_t<D, DT, DT_F32>(a, mfma, st);
-    else launch_part_t<D, DT, DT>(a, mfma, st);
+    if (out_dtype == PAGED_KV_F32) launch_part_t<D, DT, DT_F32, BS>(a, mfma, st);
+    else launch_part_t<D, DT, DT, BS>(a, mfma, st);
+}
+
+template <int D, int BS>
+void launch_part_dd(const StreamArgs& a, int dtype, int out_dtype, bool mfma, hipStream_t st) {
+    switch (dtype) {
+        case PAGED_KV_F32: launch_part_d<D, DT_F32, BS>(a, out_dtype, mfma, st); break;
+        case PAGED_KV_F16: launch_part_d<D, DT_F16, BS>(a, out_dtype, mfma, st); break;
+        default: launch_part_d<D, DT_BF16, BS>(a, out_dtype, mfma, st); break;
+    }
 }
 
 template <int D>
-void launch_part_dd(const StreamArgs& a, int dtype, int out_dtype, bool mfma, hipStream_t st) {
-    switch (dtype) {
-        case PAGED_KV_F32: launch_part_d<D, DT_F32>(a, out_dtype, mfma, st); break;
-        case PAGED_KV_F16: launch_part_d<D, DT_F16>(a, out_dtype, mfma, st); break;
-        default: launch_part_d<D, DT_BF16>(a, out_dtype, mfma, st); break;
+void launch_part_b(const StreamArgs& a, int block_size, int dtype, int out_dtype, bool mfma,
+                   hipStream_t st) {
+    switch (block_size) {
+        case 1: launch_part_dd<D, 1>(a, dtype, out_dtype, mfma, st); break;
+        case 32: launch_part_dd<D, 32>(a, dtype, out_dtype, mfma, st); break;
+        default: launch_part_dd<D, 16>(a, dtype, out_dtype, mfma, st); break;
     }
 }
 
@@ -842,12 +923,12 @@ StreamPlan stream_plan(int32_t num_seqs, int32_t hq, int32_t hkv, int32_t dtype,
     p.mfma = dtype != PAGED_KV_F32 && group >= 2;
     p.units = p.mfma ? hkv : hq;
     p.heads_per_unit = p.mfma ? group : 1;
-    const int64_t max_tiles = (int64_t)((max_ctx + kKernelBlockSize - 1) / kKernelBlockSize) *
-                              num_seqs * p.units;
+    const int64_t max_tiles = (int64_t)((max_ctx + kTile - 1) / kTile) * num_seqs * p.units;
     // at least kStreamMinSlice tiles per wave (on the bound max_tiles): thinner slices cut
     // every unit into many pieces, and the merge's round trips grow with their number
     p.waves = (int32_t)std::max<int64_t>(
-        1, std::min<int64_t>(kStreamMaxWaves, (max_tiles + kStreamMinSlice - 1) / kStreamMinSlice));
+        1, std::min<int64_t>(stream_max_waves(head_dim, elem_bytes(dtype), p.mfma),
+                             (max_tiles + kStreamMinSlice - 1) / kStreamMinSlice));
     p.max_pieces = (int64_t)p.waves + (int64_t)num_seqs * p.units;
     const size_t rows = (size_t)p.max_pieces * p.heads_per_unit;
     p.meta_off = 0;
@@ -862,8 +943,11 @@ StreamPlan stream_plan(int32_t num_seqs, int32_t hq, int32_t hkv, int32_t dtype,
 void launch_streamk_partition(const StreamLaunch& L, const StreamPlan& P, void* stream) {
     const StreamArgs a = make_args(L, P);
     hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-    if (L.head_dim == 64) launch_part_dd<64>(a, L.dtype, L.out_dtype, P.mfma, st);
-    else launch_part_dd<128>(a, L.dtype, L.out_dtype, P.mfma, st);
+    switch (L.head_dim) {
+        case 64: launch_part_b<64>(a, L.block_size, L.dtype, L.out_dtype, P.mfma, st); break;
+        case 256: launch_part_b<256>(a, L.block_size, L.dtype, L.out_dtype, P.mfma, st); break;
+        default: launch_part_b<128>(a, L.block_size, L.dtype, L.out_dtype, P.mfma, st); break;
+    }
 }
 
 }  // namespace pkv

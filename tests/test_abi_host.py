@@ -276,6 +276,15 @@ def test_device_op_validation_without_gpu():
     assert e.value.status == B.PAGED_KV_ERR_INVALID_ARG
     with pytest.raises(B.PagedKVError):
         _attn(B.make_desc(64, 16, 2, 96, "bf16"))                           # head_dim 96
+    # block sizes 1 and 32 and head_dim 256 pass validation (and stop at the workspace)
+    for bs, d, width in [(1, 128, 64), (32, 128, 2), (16, 256, 4), (1, 256, 64)]:
+        with pytest.raises(B.PagedKVError) as e:
+            _attn(B.make_desc(64, bs, 2, d, "bf16"), block_tables=_FakeTensor((2, width)),
+                  q=_FakeTensor((2, 8, d)))
+        assert e.value.status == B.PAGED_KV_ERR_BUFFER_TOO_SMALL, (bs, d)
+    with pytest.raises(B.PagedKVError) as e:
+        _attn(B.make_desc(64, 1, 2, 128, "bf16"), block_tables=_FakeTensor((2, 63)))  # 63 < 64 tokens
+    assert e.value.status == B.PAGED_KV_ERR_INVALID_ARG
     with pytest.raises(B.PagedKVError):
         _attn(good, num_q_heads=7)                                          # 7 % 2 != 0
     with pytest.raises(B.PagedKVError) as e:
