@@ -287,10 +287,15 @@ def test_copy_on_write_counts_shared_prefix():
 
 
 # ------------------------------------------------------------------- pool ----
-def test_pool_layout_element_by_element():
-    rng = np.random.default_rng(4)
+@pytest.mark.parametrize("bs", [4, 1, 32])
+def test_pool_layout_element_by_element(bs):
+    """The ABI layout, element by element: a block of more than 16 tokens is 16-token
+    sub-blocks one after the other, each laid out like a 16-token block."""
+    rng = np.random.default_rng(4 + bs)
+    tb = min(bs, 16)
+    ns = bs // tb
     for dt, d in (("f32", 8), ("bf16", 16), ("f16", 32)):
-        nb, hkv, bs = 5, 3, 4
+        nb, hkv = (5 if bs > 1 else 12), 3
         x = P.chunk_elems(dt)
         kp, vp = P.new_pool(nb, hkv, bs, d, dt)
         T = 7
@@ -302,10 +307,12 @@ def test_pool_layout_element_by_element():
         written_k, written_v = set(), set()
         for t in range(T):
             b, o = divmod(int(slots[t]), bs)
+            sub, o = divmod(o, tb)
             for h in range(hkv):
                 for e in range(d):
-                    ik = (((b * hkv + h) * (d // x) + e // x) * bs + o) * x + e % x
-                    iv = ((b * hkv + h) * d + e) * bs + o
+                    r = (b * hkv + h) * ns + sub
+                    ik = ((r * (d // x) + e // x) * tb + o) * x + e % x
+                    iv = (r * d + e) * tb + o
                     assert flat_k[ik] == kbits[t, h, e]
                     assert flat_v[iv] == vbits[t, h, e]
                     written_k.add(ik)
@@ -316,6 +323,38 @@ def test_pool_layout_element_by_element():
         rest_v = np.ones(flat_v.size, bool)
         rest_v[list(written_v)] = False
         assert np.all(flat_k[rest_k] == poison) and np.all(flat_v[rest_v] == poison)
+
+
+def test_block_of_32_is_two_blocks_of_16_side_by_side():
+    """Per KV head, a 32-token-block pool holds the bytes of a 16-token-block pool whose
+    blocks 2b and 2b + 1 are block b's two halves: the same slot numbers land in the
+    same places, and reading back through either table gives the same tokens."""
+    rng = np.random.default_rng(12)
+    nb, hkv, d, dt = 6, 2, 16, "bf16"
+    k32, v32 = P.new_pool(nb, hkv, 32, d, dt)
+    k16, v16 = P.new_pool(2 * nb, hkv, 16, d, dt)
+    T = 90
+    slots = rng.choice(nb * 32, size=T, replace=False)
+    kbits = lowp.to_storage_bits(rng.standard_normal((T, hkv, d)).astype(np.float32), dt)
+    vbits = lowp.to_storage_bits(rng.standard_normal((T, hkv, d)).astype(np.float32), dt)
+    P.reshape_and_cache(k32, v32, kbits, vbits, slots, 32)
+    P.reshape_and_cache(k16, v16, kbits, vbits, slots, 16)
+    for h in range(hkv):
+        assert np.array_equal(k32[:, h].reshape(-1), k16[:, h].reshape(nb, -1).reshape(-1))
+        assert np.array_equal(v32[:, h].reshape(-1), v16[:, h].reshape(nb, -1).reshape(-1))
+    full = np.arange(nb * 32)
+    kall = lowp.to_storage_bits(rng.standard_normal((nb * 32, hkv, d)).astype(np.float32), dt)
+    vall = lowp.to_storage_bits(rng.standard_normal((nb * 32, hkv, d)).astype(np.float32), dt)
+    P.reshape_and_cache(k32, v32, kall, vall, full, 32)
+    table32 = rng.permutation(nb)
+    table16 = np.stack([2 * table32, 2 * table32 + 1], 1).reshape(-1)
+    n = nb * 32 - 5
+    ka, va = P.gather_sequence(k32, v32, table32, n, 32)
+    order = (table32[np.arange(n) // 32] * 32 + np.arange(n) % 32)
+    assert np.array_equal(ka, kall[order]) and np.array_equal(va, vall[order])
+    P.reshape_and_cache(k16, v16, kall, vall, full, 16)
+    kb, vb = P.gather_sequence(k16, v16, table16, n, 16)
+    assert np.array_equal(ka, kb) and np.array_equal(va, vb)
 
 
 def test_padding_slot_is_skipped_and_copy_is_exact():
