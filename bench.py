@@ -45,6 +45,10 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", type=int, default=3, help="workload 1..5 (default 3: GQA 72B shape)")
+    ap.add_argument("--block-size", type=int, default=16,
+                    help="tokens per block of the pool (1, 16 or 32; workloads 2, 3 and 5)")
+    ap.add_argument("--head-dim", type=int, default=None,
+                    help="head size of the workload's heads (64, 128 or 256; workloads 2, 3, 5)")
     ap.add_argument("--partition-tokens", type=int, default=None,
                     help="0: stream-K schedule; > 0: fixed partitions (default: the workload's)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
@@ -248,7 +252,7 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     log(f"[bench] building workload {args.config}")
-    w = W.make_config(args.config)
+    w = W.make_config(args.config, block_size=args.block_size, head_dim=args.head_dim)
     cache = PagedKVCache(w.num_blocks, w.num_kv_heads, w.head_dim, w.dtype, w.block_size,
                          w.free_order, device=dev)
     last_append = last_attend = None

@@ -30,12 +30,16 @@
  *   - A pool object is not thread-safe; calls on distinct pools may run concurrently.
  *
  * Memory layout of the KV pool (the pages leave it open; this is the library's):
- *   X = 16 / element bytes (8 for fp16/bf16, 4 for fp32); BS = block size.
- *   K pool: [num_blocks][num_kv_heads][head_dim / X][BS][X]
- *   V pool: [num_blocks][num_kv_heads][head_dim][BS]
+ *   X = 16 / element bytes (8 for fp16/bf16, 4 for fp32); BS = block size.  A block of
+ *   more than 16 tokens (BS a multiple of 16) is NS = BS / 16 sub-blocks of TB = 16
+ *   tokens stored one after the other; up to 16 tokens NS = 1 and TB = BS.
+ *   K pool: [num_blocks][num_kv_heads][NS][head_dim / X][TB][X]
+ *   V pool: [num_blocks][num_kv_heads][NS][head_dim][TB]
  *   Element d of the key (value) of the token in slot `slot` = block * BS + offset,
- *   KV head h, is K[block][h][d / X][offset][d % X] (V[block][h][d][offset]).
- *   One (block, KV head) tile of K or of V is BS * head_dim contiguous elements.
+ *   KV head h, is K[block][h][offset / TB][d / X][offset % TB][d % X]
+ *   (V[block][h][offset / TB][d][offset % TB]).
+ *   One (block, KV head) region of K or of V is BS * head_dim contiguous elements, and
+ *   each 16-token sub-block of it 16 * head_dim.
  */
 #ifndef PAGED_KV_H
 #define PAGED_KV_H

@@ -28,9 +28,13 @@ class PagedKVCache:
                                 B.PAGED_KV_POOL_PREFIX_CACHE if prefix_cache else 0)
         x = 16 // torch.tensor([], dtype=TORCH_DTYPES[dtype]).element_size()
         tdt = TORCH_DTYPES[dtype]
-        self.k_pool = torch.empty((num_blocks, num_kv_heads, head_dim // x, block_size, x),
+        # a block of more than 16 tokens is stored as 16-token sub-blocks, one after the
+        # other: [block][kv_head][sub-block * head_dim / X][16][X] (V: [.][.][sub * d][16])
+        tb = min(block_size, 16)
+        ns = block_size // tb
+        self.k_pool = torch.empty((num_blocks, num_kv_heads, ns * head_dim // x, tb, x),
                                   dtype=tdt, device=self.device)
-        self.v_pool = torch.empty((num_blocks, num_kv_heads, head_dim, block_size), dtype=tdt,
+        self.v_pool = torch.empty((num_blocks, num_kv_heads, ns * head_dim, tb), dtype=tdt,
                                   device=self.device)
         if poison:   # all-ones bytes: NaN in every supported type
             self.k_pool.view(BITS_DTYPES[dtype]).fill_(-1)

@@ -6,8 +6,9 @@
 // GPU …", worked example: the token written after a full block goes to offset 0 of
 // a freshly taken block anywhere in the pool.
 //
-// Pool layout (chunk X = 16 bytes / element size, BS = block size 1, 16 or 32):
-//   K [block][kv_head][head_dim / X][BS][X]     V [block][kv_head][head_dim][BS]
+// Pool layout (chunk X = 16 bytes / element size, BS = block size 1, 16 or 32; a block of
+// 32 tokens is two 16-token sub-blocks one after the other, TB = min(BS, 16) tokens each):
+//   K [block][kv_head][BS / TB][head_dim / X][TB][X]   V [block][kv_head][BS / TB][head_dim][TB]
 
 #include <hip/hip_runtime.h>
 
@@ -19,7 +20,7 @@ typedef __attribute__((__vector_size__(4 * sizeof(int)))) int i32x4;
 
 // One thread per (token, KV head, 16-byte chunk of head_dim).  The key chunk is one
 // 16-byte store; the value chunk scatters its X elements down X rows of the
-// transposed V tile (stride BS elements; one 16-byte store when BS is 1).
+// transposed V tile (stride TB elements; one 16-byte store when BS is 1).
 template <typename T, int BS>
 __global__ __launch_bounds__(256) void reshape_and_cache_kernel(
     const T* __restrict__ key, const T* __restrict__ value, int64_t key_stride,
@@ -36,23 +37,25 @@ __global__ __launch_bounds__(256) void reshape_and_cache_kernel(
     const int32_t h = r / chunks, c = r - h * chunks;
     const int32_t slot = slot_mapping[t];
     if (slot < 0 || (int64_t)slot >= num_slots) return;
+    constexpr int TB = BS < 16 ? BS : 16;   // tokens per sub-block
     const int64_t blk = slot / BS;
-    const int32_t off = slot % BS;
+    const int32_t sub = (slot % BS) / TB, off = slot % TB;
 
     const i32x4 kc = *reinterpret_cast<const i32x4*>(key + t * key_stride + (int64_t)h * head_dim + c * X);
     const i32x4 vc = *reinterpret_cast<const i32x4*>(value + t * value_stride + (int64_t)h * head_dim + c * X);
 
-    T* kdst = k_pool + (((blk * kv_heads + h) * chunks + c) * BS + off) * X;
+    const int64_t region = (blk * kv_heads + h) * (BS / TB) + sub;   // (block, head, sub-block)
+    T* kdst = k_pool + ((region * chunks + c) * TB + off) * X;
     *reinterpret_cast<i32x4*>(kdst) = kc;
 
-    T* vdst = v_pool + ((blk * kv_heads + h) * head_dim + (int64_t)c * X) * BS + off;
+    T* vdst = v_pool + (region * head_dim + (int64_t)c * X) * TB + off;
     if constexpr (BS == 1) {
         *reinterpret_cast<i32x4*>(vdst) = vc;
     } else {
         T ve[X];
         __builtin_memcpy(ve, &vc, 16);
 #pragma unroll
-        for (int e = 0; e < X; ++e) vdst[e * BS] = ve[e];
+        for (int e = 0; e < X; ++e) vdst[e * TB] = ve[e];
     }
 }
 

@@ -27,11 +27,13 @@
 //
 // Pool layout (X = 16 bytes / element size, BS = block size):
 //   K [block][kv_head][head_dim / X][BS][X]   V [block][kv_head][head_dim][BS]
-// so one (block, KV head) region is BS * head_dim contiguous elements.  With BS = 16 a
-// tile is one block and every operand load instruction reads one contiguous run across
-// its 64 lanes; with BS = 32 a tile is half a block (runs of 256 bytes); with BS = 1 a
-// tile gathers 16 blocks, each lane loading from its own token's block, and V (stored
-// token-major at that size) is turned into the V^T operand through LDS.
+// except that a block of 32 tokens is stored as two 16-token sub-blocks one after the
+// other (K [block][kv_head][2][head_dim / X][16][X], V [block][kv_head][2][head_dim][16]),
+// so a (block, KV head) region is BS * head_dim contiguous elements and a 16-token tile
+// is always 16 * head_dim contiguous elements when BS >= 16: every operand load
+// instruction reads one contiguous run across its 64 lanes.  With BS = 1 a tile gathers
+// 16 blocks, each lane loading from its own token's block, and V (stored token-major at
+// that size) is turned into the V^T operand through LDS.
 
 #include "attention_common.h"
 #include "attention_host.h"
@@ -144,8 +146,7 @@ void attn_mfma_kernel(PartitionArgs a) {
     const uint16_t* kbase = static_cast<const uint16_t*>(a.k_pool) + (int64_t)g * (BS == 1 ? D : TILE);
     const uint16_t* vbase = static_cast<const uint16_t*>(a.v_pool) + (int64_t)g * (BS == 1 ? D : TILE);
     const int64_t blk_stride = (int64_t)a.num_kv_heads * TILE;
-    const int koff = (lane >> 4) * BS + (lane & 15);   // 16-byte unit: chunk l/16 of token l%16
-    const int voff = gq * (BS / 4) + quad;   // 8-byte unit of row gq, tokens 4*quad.. of V^T
+    const int voff = gq * 4 + quad;   // 8-byte unit of row gq, tokens 4*quad.. of a V^T tile
     uint16_t* vrows = s_vt + w * kTile * LDW;
 
     f32x4 acc[MT];
@@ -161,7 +162,7 @@ void attn_mfma_kernel(PartitionArgs a) {
     // K tile: load kk of lane l is 16-byte chunk 4*kk + l/16 of token l%16 (block size
     // 16: bytes [1024*kk + 16*l, +16), each load instruction reads 1 KiB contiguous).
     // V^T tile: load mt of lane l is row 16*mt + l%16, tokens 4*(l/16)..+3.
-    auto load = [&](int idx, int b, i32x4 (&kr)[KI], vbuf& vr) {
+    auto load = [&](int idx, int b, i32x4 (&kr)[KI], vbuf& vr) __attribute__((always_inline)) {
         if constexpr (BS == 1) {
             bool bad;
             const int32_t bid = lane_block_bs1(trow, b, ctx, a.num_blocks, lane, bad);
@@ -174,17 +175,17 @@ void attn_mfma_kernel(PartitionArgs a) {
             for (int kk = 0; kk < KI; ++kk) vr[kk] = __builtin_nontemporal_load(vt + 4 * kk);
         } else {
             const int32_t bid = __builtin_amdgcn_readlane(id_v, idx);
-            const int h = b & (TPB - 1);
-            const i32x4* kt = reinterpret_cast<const i32x4*>(kbase + bid * blk_stride) + koff + kTile * h;
-            const i32x2* vt = reinterpret_cast<const i32x2*>(vbase + bid * blk_stride) + voff + 4 * h;
+            const int64_t sub = (b & (TPB - 1)) * (kTile * D);   // 16-token sub-block
+            const i32x4* kt = reinterpret_cast<const i32x4*>(kbase + bid * blk_stride + sub) + lane;
+            const i32x2* vt = reinterpret_cast<const i32x2*>(vbase + bid * blk_stride + sub) + voff;
 #pragma unroll
-            for (int kk = 0; kk < KI; ++kk) kr[kk] = __builtin_nontemporal_load(kt + kk * 4 * BS);
+            for (int kk = 0; kk < KI; ++kk) kr[kk] = __builtin_nontemporal_load(kt + kk * 64);
 #pragma unroll
-            for (int mt = 0; mt < MT; ++mt) vr[mt] = __builtin_nontemporal_load(vt + mt * 4 * BS);
+            for (int mt = 0; mt < MT; ++mt) vr[mt] = __builtin_nontemporal_load(vt + mt * 64);
         }
     };
 
-    auto compute = [&](int b, i32x4 (&kr)[KI], vbuf& vin) {
+    auto compute = [&](int b, i32x4 (&kr)[KI], vbuf& vin) __attribute__((always_inline)) {
         i32x2 vr[MT];
         if constexpr (BS == 1) {
             lds_put_rows<uint16_t, KI>(vrows, LDW, lane, vin);
@@ -409,7 +410,6 @@ void attn_valu_kernel(PartitionArgs a) {
     const bits_t* kbase = static_cast<const bits_t*>(a.k_pool) + (int64_t)g * (BS == 1 ? D : TILE);
     const bits_t* vbase = static_cast<const bits_t*>(a.v_pool) + (int64_t)g * (BS == 1 ? D : TILE);
     const int64_t blk_stride = (int64_t)a.num_kv_heads * TILE;
-    const int koff = kq * BS + tok;
     bits_t* vrows = s_vt + w * kTile * LDW;
 
     float acc[NI];
@@ -420,7 +420,7 @@ void attn_valu_kernel(PartitionArgs a) {
     i32x4 kA[NI], kB[NI], vA[NI], vB[NI];
     int id_v = 0;
 
-    auto load = [&](int idx, int b, i32x4 (&kr)[NI], i32x4 (&vr)[NI]) {
+    auto load = [&](int idx, int b, i32x4 (&kr)[NI], i32x4 (&vr)[NI]) __attribute__((always_inline)) {
         if constexpr (BS == 1) {
             bool bad;
             const int32_t bid = lane_block_bs1(trow, b, ctx, a.num_blocks, lane, bad);
@@ -434,18 +434,18 @@ void attn_valu_kernel(PartitionArgs a) {
             }
         } else {
             const int32_t bid = __builtin_amdgcn_readlane(id_v, idx);
-            const int h = b & (TPB - 1);
-            const i32x4* kt = reinterpret_cast<const i32x4*>(kbase + bid * blk_stride) + koff + kTile * h;
-            const i32x4* vt = reinterpret_cast<const i32x4*>(vbase + bid * blk_stride) + E * h + vpiece;
+            const int64_t sub = (b & (TPB - 1)) * (kTile * D);   // 16-token sub-block
+            const i32x4* kt = reinterpret_cast<const i32x4*>(kbase + bid * blk_stride + sub) + lane;
+            const i32x4* vt = reinterpret_cast<const i32x4*>(vbase + bid * blk_stride + sub) + lane;
 #pragma unroll
             for (int i = 0; i < NI; ++i) {
-                kr[i] = __builtin_nontemporal_load(kt + i * 4 * BS);
-                vr[i] = __builtin_nontemporal_load(vt + ((64 * i + lane) / E) * (BS / X));
+                kr[i] = __builtin_nontemporal_load(kt + i * 64);
+                vr[i] = __builtin_nontemporal_load(vt + i * 64);
             }
         }
     };
 
-    auto compute = [&](int b, i32x4 (&kr)[NI], i32x4 (&vin)[NI]) {
+    auto compute = [&](int b, i32x4 (&kr)[NI], i32x4 (&vin)[NI]) __attribute__((always_inline)) {
         i32x4 vr[NI];
         if constexpr (BS == 1) {
             lds_put_rows<bits_t, NI>(vrows, LDW, lane, vin);

@@ -20,8 +20,9 @@
 // Units: the MFMA kernel's unit is a KV head with its group of query heads (fp16/bf16,
 // group >= 2); the VALU kernel's unit is one query head.
 //
-// Block sizes: with 16 or 32 tokens per block a tile is one block or one half of one; with
-// 1 token per block a tile gathers 16 blocks (per-lane addresses, and V transposed
+// Block sizes: with 16 or 32 tokens per block a tile is one block or one of its two
+// 16-token sub-blocks (stored one after the other, each laid out like a 16-token block);
+// with 1 token per block a tile gathers 16 blocks (per-lane addresses, and V transposed
 // through LDS, since such a pool stores each token's values as one row).
 //
 // Results depend only on the logical token order and on W, never on where blocks sit
@@ -137,8 +138,8 @@ __device__ __forceinline__ void advance(const StreamArgs& a, Cursor& c) {
     } while (c.nt == 0 && c.s < a.num_seqs - 1);
 }
 
-// Physical block of the cursor's tile (block size BS >= 16: the tile is part TPB of
-// block it / TPB); out-of-range ids read block 0 and flag the unit.
+// Physical block of the cursor's tile (block size BS >= 16: the tile is sub-block
+// it % TPB of block it / TPB); out-of-range ids read block 0 and flag the unit.
 template <int BS>
 __device__ __forceinline__ int32_t tile_block(const StreamArgs& a, const Cursor& c, bool& bad) {
     const int32_t bid = sload(a.block_tables, (int64_t)c.s * a.max_blocks_per_seq + c.it / (BS / kTile));
@@ -361,10 +362,10 @@ void attn_mfma_streamk(StreamArgs a) {
     // load right where it is issued, draining the K/V prefetch.)
     const int gqc = min(gq, G - 1);
     const int64_t blk_stride = (int64_t)a.num_kv_heads * TILE;
-    // K: load kk of lane l is chunk 4*kk + l/16 of token l%16 of the tile;
-    // V^T: load mt of lane l is dim 16*mt + l%16, tokens 4*(l/16)..+3
-    const int koff = (lane >> 4) * BS + (lane & 15);
-    const int voff = gq * (BS / 4) + quad;
+    // K: load kk of lane l is chunk 4*kk + l/16 of token l%16 of the tile (1 KiB
+    // contiguous per load instruction); V^T: load mt of lane l is dim 16*mt + l%16,
+    // tokens 4*(l/16)..+3 (512 bytes contiguous)
+    const int voff = gq * 4 + quad;
     const uint16_t* kpool = static_cast<const uint16_t*>(a.k_pool);
     const uint16_t* vpool = static_cast<const uint16_t*>(a.v_pool);
     uint16_t* vrows = s_vt + (threadIdx.x >> 6) * kTile * LDW;
@@ -373,14 +374,14 @@ void attn_mfma_streamk(StreamArgs a) {
     Cursor cc = lc;                       // tile being computed
 
     kvec qop[KI];
-    auto load_q = [&](const Cursor& c) {
+    auto load_q = [&](const Cursor& c) __attribute__((always_inline)) {
         const uint16_t* qh = static_cast<const uint16_t*>(a.q) +
                              ((int64_t)c.s * a.num_q_heads + c.u * G + gqc) * D + 8 * quad;
 #pragma unroll
         for (int kk = 0; kk < KI; ++kk)
             qop[kk] = __builtin_bit_cast(kvec, *reinterpret_cast<const i32x4*>(qh + 32 * kk));
     };
-    auto load_kv = [&](const Cursor& c, i32x4 (&kr)[KI], vbuf& vr, bool& bad) {
+    auto load_kv = [&](const Cursor& c, i32x4 (&kr)[KI], vbuf& vr, bool& bad) __attribute__((always_inline)) {
         if constexpr (BS == 1) {
             const int32_t bid = lane_block_bs1(a.block_tables + (int64_t)c.s * a.max_blocks_per_seq,
                                                c.it, c.ctx, a.num_blocks, lane, bad);
@@ -393,14 +394,13 @@ void attn_mfma_streamk(StreamArgs a) {
             for (int kk = 0; kk < KI; ++kk) vr[kk] = __builtin_nontemporal_load(vt + 4 * kk);
         } else {
             const int32_t bid = tile_block<BS>(a, c, bad);
-            const int h = c.it & (TPB - 1);
-            const int64_t base = (int64_t)c.u * TILE + bid * blk_stride;
-            const i32x4* kt = reinterpret_cast<const i32x4*>(kpool + base) + koff + kTile * h;
-            const i32x2* vt = reinterpret_cast<const i32x2*>(vpool + base) + voff + 4 * h;
+            const int64_t base = (int64_t)c.u * TILE + bid * blk_stride + (c.it & (TPB - 1)) * (kTile * D);
+            const i32x4* kt = reinterpret_cast<const i32x4*>(kpool + base) + lane;
+            const i32x2* vt = reinterpret_cast<const i32x2*>(vpool + base) + voff;
 #pragma unroll
-            for (int kk = 0; kk < KI; ++kk) kr[kk] = __builtin_nontemporal_load(kt + kk * 4 * BS);
+            for (int kk = 0; kk < KI; ++kk) kr[kk] = __builtin_nontemporal_load(kt + kk * 64);
 #pragma unroll
-            for (int mt = 0; mt < MT; ++mt) vr[mt] = __builtin_nontemporal_load(vt + mt * 4 * BS);
+            for (int mt = 0; mt < MT; ++mt) vr[mt] = __builtin_nontemporal_load(vt + mt * 64);
         }
     };
 
@@ -413,7 +413,7 @@ void attn_mfma_streamk(StreamArgs a) {
     Pending pend;
 
     // Write the finished (or slice-cut) unit of cursor c, then reset the state.
-    auto finish = [&](const Cursor& c) {
+    auto finish = [&](const Cursor& c) __attribute__((always_inline)) {
         const bool direct = first_here && c.it == c.nt - 1;
         const float lw = sum_across_quads(lsum);
         const int q = c.s * a.units + c.u;
@@ -455,7 +455,7 @@ void attn_mfma_streamk(StreamArgs a) {
     // Compute the tile of cc from registers kr/vr.  If the next tile (nc) starts a new
     // unit, its queries are loaded into qop once the score MFMAs have read them.
     auto compute = [&](i32x4 (&kr)[KI], vbuf& vin, bool bad, bool next_unit,
-                       const Cursor& nc) {
+                       const Cursor& nc) __attribute__((always_inline)) {
         i32x2 vr[MT];
         if constexpr (BS == 1) {
             lds_put_rows<uint16_t, KI>(vrows, LDW, lane, vin);
@@ -542,7 +542,7 @@ void attn_mfma_streamk(StreamArgs a) {
 
     // one pipeline step: load tile k+1 into (kn, vn), compute tile k from (kc, vc)
     int done = 0;
-    auto step = [&](i32x4 (&kc)[KI], vbuf& vc, bool bc, i32x4 (&kn)[KI], vbuf& vn, bool& bn) {
+    auto step = [&](i32x4 (&kc)[KI], vbuf& vc, bool bc, i32x4 (&kn)[KI], vbuf& vn, bool& bn) __attribute__((always_inline)) {
         // Waves with more of their slice left get issue priority: co-resident waves share
         // the CU's memory pipe unevenly (oldest first), and a slice split is only balanced
         // if the waves progress together.
@@ -619,7 +619,6 @@ void attn_valu_streamk(StreamArgs a) {
     const int64_t blk_stride = (int64_t)a.num_kv_heads * TILE;
     // K: load i of lane l is chunk 4*i + l/16 of token l%16; V (dim-major): load i is
     // dim (64*i + l)/E, tokens X*(l%E)..+X
-    const int koff = kq * BS + tok;
     const bits_t* kpool = static_cast<const bits_t*>(a.k_pool);
     const bits_t* vpool = static_cast<const bits_t*>(a.v_pool);
     bits_t* vrows = s_vt + (threadIdx.x >> 6) * kTile * LDW;
@@ -630,13 +629,13 @@ void attn_valu_streamk(StreamArgs a) {
     // query: raw bits of the lane's D/4 dims (chunks 4*i + kq), converted on unit change
     i32x4 qraw[NI];
     float qr[NI][X];
-    auto load_q = [&](const Cursor& c) {
+    auto load_q = [&](const Cursor& c) __attribute__((always_inline)) {
         const i32x4* qh = reinterpret_cast<const i32x4*>(
             static_cast<const bits_t*>(a.q) + ((int64_t)c.s * a.num_q_heads + c.u) * D);
 #pragma unroll
         for (int i = 0; i < NI; ++i) qraw[i] = qh[4 * i + kq];
     };
-    auto convert_q = [&]() {
+    auto convert_q = [&]() __attribute__((always_inline)) {
 #pragma unroll
         for (int i = 0; i < NI; ++i) {
             bits_t qb[X];
@@ -645,7 +644,7 @@ void attn_valu_streamk(StreamArgs a) {
             for (int e = 0; e < X; ++e) qr[i][e] = bits_to_f32<DT>(qb[e]) * a.scale_log2;
         }
     };
-    auto load_kv = [&](const Cursor& c, i32x4 (&kr)[NI], i32x4 (&vr)[NI], bool& bad) {
+    auto load_kv = [&](const Cursor& c, i32x4 (&kr)[NI], i32x4 (&vr)[NI], bool& bad) __attribute__((always_inline)) {
         if constexpr (BS == 1) {
             const int32_t bid = lane_block_bs1(a.block_tables + (int64_t)c.s * a.max_blocks_per_seq,
                                                c.it, c.ctx, a.num_blocks, lane, bad);
@@ -659,14 +658,14 @@ void attn_valu_streamk(StreamArgs a) {
             }
         } else {
             const int32_t bid = tile_block<BS>(a, c, bad);
-            const int h = c.it & (TPB - 1);
-            const int64_t base = (int64_t)(c.u / a.group) * TILE + bid * blk_stride;
-            const i32x4* kt = reinterpret_cast<const i32x4*>(kpool + base) + koff + kTile * h;
-            const i32x4* vt = reinterpret_cast<const i32x4*>(vpool + base) + E * h + vpiece;
+            const int64_t base = (int64_t)(c.u / a.group) * TILE + bid * blk_stride +
+                                 (c.it & (TPB - 1)) * (kTile * D);
+            const i32x4* kt = reinterpret_cast<const i32x4*>(kpool + base) + lane;
+            const i32x4* vt = reinterpret_cast<const i32x4*>(vpool + base) + lane;
 #pragma unroll
             for (int i = 0; i < NI; ++i) {
-                kr[i] = __builtin_nontemporal_load(kt + i * 4 * BS);
-                vr[i] = __builtin_nontemporal_load(vt + ((64 * i + lane) / E) * (BS / X));
+                kr[i] = __builtin_nontemporal_load(kt + i * 64);
+                vr[i] = __builtin_nontemporal_load(vt + i * 64);
             }
         }
     };
@@ -680,7 +679,7 @@ void attn_valu_streamk(StreamArgs a) {
     bool q_stale = false;    // qraw holds the next unit's query, not yet converted
     Pending pend;
 
-    auto finish = [&](const Cursor& c) {
+    auto finish = [&](const Cursor& c) __attribute__((always_inline)) {
         const bool direct = first_here && c.it == c.nt - 1;
         float lw = lsum;
         lw += __shfl_xor(lw, 1);
@@ -724,7 +723,7 @@ void attn_valu_streamk(StreamArgs a) {
     };
 
     auto compute = [&](i32x4 (&kr)[NI], i32x4 (&vin)[NI], bool bad, bool next_unit,
-                       const Cursor& nc) {
+                       const Cursor& nc) __attribute__((always_inline)) {
         i32x4 vr[NI];
         if constexpr (BS == 1) {
             lds_put_rows<bits_t, NI>(vrows, LDW, lane, vin);
@@ -795,7 +794,7 @@ void attn_valu_streamk(StreamArgs a) {
     bool bA = false, bB = false;
     int done = 0;
     auto step = [&](i32x4 (&kc)[NI], i32x4 (&vc)[NI], bool bc, i32x4 (&kn)[NI],
-                    i32x4 (&vn)[NI], bool& bn) {
+                    i32x4 (&vn)[NI], bool& bn) __attribute__((always_inline)) {
         // issue priority to the waves with more of their slice left (see the MFMA kernel)
         {
             const int pr = ((n - done) * 4) / (n + 1);

@@ -167,16 +167,30 @@ def _pool_size(logical_blocks: int) -> int:
     return int(math.ceil(1.25 * logical_blocks))
 
 
-def make_config(k: int, small: bool = False, draw_values: bool = True) -> Workload:
+def make_config(k: int, small: bool = False, draw_values: bool = True, block_size: int = 16,
+                head_dim: int = None) -> Workload:
     """Workload k in 1..5.  small=True keeps heads, head_dim, type and block size
     but shrinks batch and lengths so the oracle finishes in seconds (still several
     512-token partitions with ragged tails).  draw_values=False builds the script
-    only (lengths, pool order and operations are the same; kv and q hold None)."""
+    only (lengths, pool order and operations are the same; kv and q hold None).
+    block_size / head_dim (workloads 2, 3 and 5) give the same lengths over a pool of
+    another block size (sized 1.25x its own need) or heads of another size."""
     dv = draw_values
     ss = np.random.SeedSequence(k + (100 if small else 0)).spawn(3)
     rng_len, rng_pool = (np.random.default_rng(s) for s in ss[:2])
     rng_val = ss[2]           # values: SeedSequence, children spawned per draw
     name = CONFIG_NAMES[k] + ("_small" if small else "")
+    bs = int(block_size)
+    if (bs != 16 or head_dim is not None) and k not in (2, 3, 5):
+        raise ValueError(f"workload {k} has no block-size or head-size variants")
+    if bs != 16:
+        name += f"_bs{bs}"
+    if head_dim is not None:
+        name += f"_d{int(head_dim)}"
+
+    def variant(w):
+        w.block_size = bs
+        return w
     if k == 1:
         lens = [7, 16, 33, 100]
         return _prefill_then_decode(name, lens, 4, 4, 64, "f32", 64, rng_pool, rng_val,
@@ -184,16 +198,16 @@ def make_config(k: int, small: bool = False, draw_values: bool = True) -> Worklo
     if k == 2:
         B, lo, hi = (4, 512, 1500) if small else (64, 512, 4096)
         lens = rng_len.integers(lo, hi, size=B, endpoint=True)
-        nb = _pool_size(sum(_blocks(L, 16) for L in lens))
-        return _prefill_then_decode(name, lens, 32, 32, 128, "f16", nb, rng_pool, rng_val,
-                                    draw_values=dv)
+        nb = _pool_size(sum(_blocks(L, bs) for L in lens))
+        return variant(_prefill_then_decode(name, lens, 32, 32, head_dim or 128, "f16", nb,
+                                            rng_pool, rng_val, draw_values=dv))
     if k == 3:
         B, med, cap = (6, 600, 2048) if small else (128, 2048, 8192)
         raw = rng_len.lognormal(mean=math.log(med), sigma=0.6, size=B)
         lens = np.clip(np.rint(raw), 1, cap).astype(np.int64)
-        nb = _pool_size(sum(_blocks(L, 16) for L in lens))
-        return _prefill_then_decode(name, lens, 64, 8, 128, "bf16", nb, rng_pool, rng_val,
-                                    draw_values=dv)
+        nb = _pool_size(sum(_blocks(L, bs) for L in lens))
+        return variant(_prefill_then_decode(name, lens, 64, 8, head_dim or 128, "bf16", nb,
+                                            rng_pool, rng_val, draw_values=dv))
     if k == 4:
         prompts = 2 if small else 32
         w = _shared_prefix(name, prompts, 8, 2056, (64, 512), rng_len, rng_pool, rng_val,
@@ -206,9 +220,9 @@ def make_config(k: int, small: bool = False, draw_values: bool = True) -> Worklo
     if k == 5:
         B, lo, hi = (2, 1500, 2500) if small else (16, 16384, 32768)
         L0 = rng_len.integers(lo, hi, size=B, endpoint=True)
-        nb = _pool_size(sum(_blocks(L + 8, 16) for L in L0))
-        w = _prefill_then_decode(name, L0, 64, 8, 128, "bf16", nb, rng_pool, rng_val,
-                                 steps=8, prefill_excludes=0, draw_values=dv)
+        nb = _pool_size(sum(_blocks(L + 8, bs) for L in L0))
+        w = variant(_prefill_then_decode(name, L0, 64, 8, head_dim or 128, "bf16", nb, rng_pool,
+                                         rng_val, steps=8, prefill_excludes=0, draw_values=dv))
         w.partition_tokens = 512     # the long-context workload is defined with 512-token partitions
         return w
     raise ValueError(f"no workload {k}")
