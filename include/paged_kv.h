@@ -264,7 +264,8 @@ size_t paged_attention_workspace_bytes(const paged_kv_pool_desc* desc, int32_t n
  *   max_context_len  host bound on every context_lens[s] (sizes the launch)
  *   partition_tokens 0: stream-K schedule — the batch's (sequence, head unit,
  *                 16-token tile) tiles are split evenly over a fixed set of waves
- *                 (3072 on MI355X up to head_dim 128, fewer for small batches) and the pieces of a
+ *                 (one per resident wave slot on MI355X: 1024 or 3072 by kernel, fewer
+ *                 for small batches) and the pieces of a
  *                 sequence's head unit cut by those splits are merged by log-sum-exp
  *                 (used for up to 8192 sequences; larger batches fall back to 512-token
  *                 partitions).  > 0: fixed split-K partitions of that many tokens

@@ -72,10 +72,16 @@ __device__ __forceinline__ int32_t sload(const int32_t* p, int64_t i) {
 // Waves per SIMD the attention kernels are compiled for (a wave's registers must fit in
 // 512 / waves): two tiles of K/V in flight plus the accumulators and the query.  The
 // host plans stream-K launches with the same numbers (pkv::kernel_waves_per_simd).
+template <int D, bool STREAMK>
+constexpr int mfma_waves_per_simd() { return pkv::kernel_waves_per_simd(D, 2, true, STREAMK); }
+template <int D, int E, bool STREAMK>
+constexpr int valu_waves_per_simd() { return pkv::kernel_waves_per_simd(D, E, false, STREAMK); }
+
+// Tiles in flight per wave in the stream-K MFMA kernel (ring of load buffers).  Two:
+// rings of 3 and 4 measured no faster at one wave per SIMD (the tiles in flight per CU
+// are not what limits the stream).
 template <int D>
-constexpr int mfma_waves_per_simd() { return pkv::kernel_waves_per_simd(D, 2, true); }
-template <int D, int E>
-constexpr int valu_waves_per_simd() { return pkv::kernel_waves_per_simd(D, E, false); }
+constexpr int stream_depth() { return 2; }
 
 // Block size 1: every token of a tile sits in its own block.  Lane l gets the block of
 // token 16*it + (l & 15) of the table row (ids read through the scalar cache; tokens at

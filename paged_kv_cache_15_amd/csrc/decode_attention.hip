@@ -98,7 +98,7 @@ __device__ __forceinline__ void write_partition_result(const PartitionArgs& a, i
 // the layout the value product wants its B operand in, so P never leaves registers.
 // ---------------------------------------------------------------------------------
 template <int D, int DT, int OUT_DT, int BS>
-__global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(mfma_waves_per_simd<D>())))
+__global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(mfma_waves_per_simd<D, false>())))
 void attn_mfma_kernel(PartitionArgs a) {
     constexpr int KI = D / 32;   // QK MFMAs (and 16-byte K loads per lane) per tile
     constexpr int MT = D / 16;   // PV MFMA pairs (and 8-byte V loads per lane) per tile
@@ -359,7 +359,7 @@ void attn_mfma_kernel(PartitionArgs a) {
 // ---------------------------------------------------------------------------------
 template <int D, int DT, int OUT_DT, int BS>
 __global__ __launch_bounds__(kWaves * 64)
-__attribute__((amdgpu_waves_per_eu(valu_waves_per_simd<D, DT == DT_F32 ? 4 : 2>())))
+__attribute__((amdgpu_waves_per_eu(valu_waves_per_simd<D, DT == DT_F32 ? 4 : 2, false>())))
 void attn_valu_kernel(PartitionArgs a) {
     using bits_t = typename std::conditional<DT == DT_F32, uint32_t, uint16_t>::type;
     constexpr int E = sizeof(bits_t);

@@ -330,7 +330,7 @@ __device__ void nan_invalid_sequences(const StreamArgs& a, const int* s_pref) {
 // base-2 softmax, O^T += V^T.P^T with P split into 16-bit head + remainder.
 // ---------------------------------------------------------------------------------
 template <int D, int DT, int OUT_DT, int BS>
-__global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(mfma_waves_per_simd<D>())))
+__global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(mfma_waves_per_simd<D, true>())))
 void attn_mfma_streamk(StreamArgs a) {
     constexpr int KI = D / 32;
     constexpr int MT = D / 16;
@@ -536,49 +536,86 @@ void attn_mfma_streamk(StreamArgs a) {
         unit_bad |= bad;
     };
 
-    i32x4 kA[KI], kB[KI];
-    vbuf vA, vB;
-    bool bA = false, bB = false;
+    // Ring of R tile buffers: while tile k is computed, tiles k+1 .. k+R-1 are in flight.
+    constexpr int R = stream_depth<D>();
+    i32x4 kbuf[R][KI];
+    vbuf vbufs[R];
+    bool bbuf[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) bbuf[r] = false;
 
-    // one pipeline step: load tile k+1 into (kn, vn), compute tile k from (kc, vc)
     int done = 0;
-    auto step = [&](i32x4 (&kc)[KI], vbuf& vc, bool bc, i32x4 (&kn)[KI], vbuf& vn, bool& bn) __attribute__((always_inline)) {
-        // Waves with more of their slice left get issue priority: co-resident waves share
-        // the CU's memory pipe unevenly (oldest first), and a slice split is only balanced
-        // if the waves progress together.
-        {
-            const int pr = ((n - done) * 4) / (n + 1);
-            if (pr >= 3) __builtin_amdgcn_s_setprio(3);
-            else if (pr == 2) __builtin_amdgcn_s_setprio(2);
-            else if (pr == 1) __builtin_amdgcn_s_setprio(1);
-            else __builtin_amdgcn_s_setprio(0);
-            ++done;
-        }
+    // Waves with more of their slice left get issue priority: co-resident waves share
+    // the CU's memory pipe unevenly (oldest first), and a slice split is only balanced
+    // if the waves progress together.
+    auto prio = [&]() __attribute__((always_inline)) {
+        const int pr = ((n - done) * 4) / (n + 1);
+        if (pr >= 3) __builtin_amdgcn_s_setprio(3);
+        else if (pr == 2) __builtin_amdgcn_s_setprio(2);
+        else if (pr == 1) __builtin_amdgcn_s_setprio(1);
+        else __builtin_amdgcn_s_setprio(0);
+        ++done;
+    };
+    // load the tile after the last one loaded into slot sl
+    auto produce = [&](int sl) __attribute__((always_inline)) {
         advance(a, lc);
-        load_kv(lc, kn, vn, bn);
-        // Keep the next tile's loads ahead of everything that waits on the current one:
-        // left alone, the scheduler hoists the first score product (and with it a wait
-        // on the current tile's loads) into the block-id lookup's latency, which leaves
-        // one tile in flight instead of two.
+        load_kv(lc, kbuf[sl], vbufs[sl], bbuf[sl]);
+        // Keep these loads ahead of everything that waits on the tile about to be
+        // computed: left alone, the scheduler hoists the first score product (and with
+        // it a wait on that tile's loads) into the block-id lookup's latency, which
+        // leaves one tile fewer in flight.
         __builtin_amdgcn_sched_barrier(0);
-        const bool next_unit = lc.s != cc.s || lc.u != cc.u;
-        compute(kc, vc, bc, next_unit, lc);
+    };
+    // compute the tile of cursor cc from slot sl, then move cc on (if a tile follows)
+    auto consume = [&](int sl, bool has_next) __attribute__((always_inline)) {
+        Cursor nc = cc;
+        bool next_unit = false;
+        if (has_next) {
+            advance(a, nc);
+            next_unit = nc.s != cc.s || nc.u != cc.u;
+        }
+        compute(kbuf[sl], vbufs[sl], bbuf[sl], next_unit, nc);
         if (next_unit) finish(cc);
-        cc = lc;
+        cc = nc;
     };
 
     load_q(cc);
-    load_kv(lc, kA, vA, bA);
-    int k = 0;
-    for (; k + 2 < n; k += 2) {
-        step(kA, vA, bA, kB, vB, bB);
-        step(kB, vB, bB, kA, vA, bA);
-    }
-    if (k + 1 < n) {
-        step(kA, vA, bA, kB, vB, bB);
-        compute(kB, vB, bB, false, cc);
+    load_kv(lc, kbuf[0], vbufs[0], bbuf[0]);
+    if (n >= 2 * R - 1) {
+        // Every step of the main loop loads one tile and computes one, so the number
+        // of loads in flight is the same on every path and the compiler waits for
+        // exactly the tile being computed.
+#pragma unroll
+        for (int r = 1; r < R - 1; ++r) produce(r);
+        const int loading = n - (R - 1);   // steps that also load a tile
+        int k = 0;
+        for (; k + R <= loading; k += R) {
+#pragma unroll
+            for (int j = 0; j < R; ++j) {
+                prio();
+                produce((j + R - 1) % R);
+                consume(j, true);
+            }
+        }
+        // fewer than R loading steps left, then R - 1 tiles to compute; k % R == 0
+#pragma unroll
+        for (int j = 0; j < 2 * R - 2; ++j) {
+            if (k + j < n) {
+                prio();
+                if (k + j < loading) produce((j + R - 1) % R);
+                consume(j % R, k + j + 1 < n);
+            }
+        }
     } else {
-        compute(kA, vA, bA, false, cc);
+        // short slice: two buffers
+#pragma unroll
+        for (int j = 0; j < 2 * R - 2; ++j) {
+            if (j < n) {
+                prio();
+                if (j + 1 < n) produce((j + 1) % 2);
+                consume(j % 2, j + 1 < n);
+            }
+        }
     }
     finish(cc);
     __builtin_amdgcn_s_setprio(0);
@@ -591,7 +628,7 @@ void attn_mfma_streamk(StreamArgs a) {
 // ---------------------------------------------------------------------------------
 template <int D, int DT, int OUT_DT, int BS>
 __global__ __launch_bounds__(kWaves * 64)
-__attribute__((amdgpu_waves_per_eu(valu_waves_per_simd<D, DT == DT_F32 ? 4 : 2>())))
+__attribute__((amdgpu_waves_per_eu(valu_waves_per_simd<D, DT == DT_F32 ? 4 : 2, true>())))
 void attn_valu_streamk(StreamArgs a) {
     using bits_t = typename std::conditional<DT == DT_F32, uint32_t, uint16_t>::type;
     constexpr int E = sizeof(bits_t);
