@@ -15,10 +15,10 @@ lognormal around 2048 (capped at 8192).  The host allocator's work for the step
 step is the same work.
 
 Prints one JSON line: decode KV GB/s over the whole step (algorithmic bytes / step
-time), seq-tokens/s, the partition kernel against the HBM roofline (HIP events on the
-launch stream), the kernel's measured HBM traffic when a committed counter summary
-under profiles/ matches the current kernel sources, and the CPU oracle timed on the
-host cores as a baseline.
+time, over K steps with nothing else queued), seq-tokens/s, the partition kernel
+against the HBM roofline (HIP events on the launch stream, over K more steps), the
+kernel's measured HBM traffic when a committed counter summary under profiles/ matches
+the current kernel sources, and the CPU oracle timed on the host cores as a baseline.
 """
 import argparse
 import glob
@@ -73,7 +73,8 @@ def copy_calibration(mib):
 
 # Sources that determine the attention kernels' code and launch shape; a counter summary
 # records their digest, and its traffic figure is only reported while they match.
-KERNEL_SOURCES = ("paged_kv_cache_15_amd/csrc/attention_common.h",
+KERNEL_SOURCES = ("paged_kv_cache_15_amd/csrc/common.h",
+                  "paged_kv_cache_15_amd/csrc/attention_common.h",
                   "paged_kv_cache_15_amd/csrc/attention_host.h",
                   "paged_kv_cache_15_amd/csrc/decode_attention.hip",
                   "paged_kv_cache_15_amd/csrc/decode_attention_streamk.hip")
@@ -313,20 +314,27 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    # The step rate comes from steps with nothing else on the stream (a recorded event
+    # costs the queue a few microseconds); a second pass with events around each launch
+    # gives the per-kernel durations.
     log(f"[bench] timing {args.steps} steps")
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms_per_step = elapsed * 1e3 / args.steps
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    log(f"[bench] per-kernel timing, {args.steps} more steps")
+    for i in range(args.steps):
         starts[i].record(stream)
         step(evs[i])
     torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
     part_ms = sum(evs[i][0].elapsed_time(evs[i][1]) for i in range(args.steps)) / args.steps
     red_ms = sum(evs[i][1].elapsed_time(evs[i][2]) for i in range(args.steps)) / args.steps
     rac_ms = sum(starts[i].elapsed_time(evs[i][0]) for i in range(args.steps)) / args.steps
-    ms_per_step = elapsed * 1e3 / args.steps
 
     kv_bytes, attn_bytes = attention_bytes(lens, nb_total, w, out.element_size())
     write_bytes = 2 * 2 * n_app * w.num_kv_heads * w.head_dim * w.elem_bytes + 4 * n_app
