@@ -55,6 +55,41 @@ def paged_decode(q, k_pool, v_pool, tables, context_lens, scale, dtype, block_si
     return out
 
 
+def paged_prefill(q, k_pool, v_pool, tables, context_lens, q_start, scale, dtype, block_size,
+                  seqs=None):
+    """Causal multi-query attention over the pool: prefill, and prefill in chunks.
+
+    deepsonar "PagedAttention de vLLM …" §2.5: a request only tracks how many of its
+    tokens are already computed, so a whole prompt, a chunk of a long prompt and the
+    rest of a prompt after a prefix-cache hit are the same operation; §2.6: that
+    attention too reads the blocks through the table.  Reading: the queries of
+    sequence s are rows q_start[s] .. q_start[s+1] - 1 of q, its last
+    n_s = q_start[s+1] - q_start[s] tokens (already written to the pool, whose
+    context_lens[s] tokens include them); query i sits at position
+    context_lens[s] - n_s + i and attends to keys 0 .. that position (causal).
+
+    q: float64 [total][Hq][d].  Returns float64 [total][Hq][d]; with `seqs` given,
+    only those sequences' rows are computed (the others are NaN).
+    """
+    q = np.asarray(q, dtype=np.float64)
+    out = np.full(q.shape, np.nan)
+    rows = range(len(context_lens)) if seqs is None else seqs
+    for b in rows:
+        L, r0, r1 = int(context_lens[b]), int(q_start[b]), int(q_start[b + 1])
+        n = r1 - r0
+        if n < 0 or n > L:
+            raise ValueError("a sequence needs 0 <= query count <= context length")
+        if n == 0:
+            continue
+        kb, vb = gather_sequence(k_pool, v_pool, tables[b], L, block_size)
+        k = storage_bits_to_f64(kb, dtype)
+        v = storage_bits_to_f64(vb, dtype)
+        for i in range(n):
+            p = L - n + i
+            out[r0 + i] = dense_decode(q[r0 + i], k[:p + 1], v[:p + 1], scale)
+    return out
+
+
 def partial_state(z, v):
     """Softmax state of one slice of tokens: (max score, sum of weights, weighted V)."""
     m = z.max()
