@@ -310,6 +310,37 @@ paged_kv_status paged_attention_reduce(const paged_kv_pool_desc* desc, void* out
                                        int32_t partition_tokens, const void* workspace,
                                        size_t workspace_bytes, void* stream);
 
+/* Causal multi-query attention over the pool: prefill, prefill in chunks, and the rest
+ * of a prompt after a prefix-cache hit ([DS] §2.5: a request only counts how many of its
+ * tokens are computed, so these are one operation; §2.6: it reads the blocks through
+ * the table too; [DL] continuous batching section: the compute-heavy phase).  The last
+ * n_s = q_start[s+1] - q_start[s] tokens of sequence s are queries; their K/V must
+ * already be in the pool (reshape_and_cache), counted in context_lens[s].  Query i of
+ * sequence s sits at position context_lens[s] - n_s + i and attends to keys 0 .. that
+ * position.
+ *   out           device [total][num_q_heads][head_dim], type out_dtype (desc->dtype or
+ *                 PAGED_KV_F32); row q_start[s] + i is query i of sequence s
+ *   q             device [total][num_q_heads][head_dim], type desc->dtype
+ *   q_start       device int32[num_seqs + 1], non-decreasing, q_start[0] = 0 (rows of
+ *                 out/q past q_start[num_seqs] are neither read nor written)
+ *   block_tables, max_blocks_per_seq, context_lens, scale: as for paged_attention_decode
+ *   max_q_len     host bound on every n_s (sizes the launch; 0 launches nothing)
+ *   max_context_len  host bound on every context_lens[s], >= max_q_len
+ * A sequence with n_s > context_lens[s] or context_lens[s] outside [1, max_context_len],
+ * or whose table holds an id outside [0, num_blocks) below its length, gets NaN rows; a
+ * sequence with n_s < 0 or n_s > max_q_len gets none written.  Requires an fp16/bf16
+ * pool with block_size 16 or 32 (UNSUPPORTED otherwise), head_dim 64, 128 or 256,
+ * num_q_heads % num_kv_heads == 0, at most 16 query heads per KV head and
+ * num_seqs * num_kv_heads <= 65535.  Needs no workspace.  Results do not depend on where
+ * blocks sit in the pool. */
+paged_kv_status paged_attention_prefill(const paged_kv_pool_desc* desc, void* out,
+                                        int32_t out_dtype, const void* q, const int32_t* q_start,
+                                        const void* k_pool, const void* v_pool,
+                                        const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                        const int32_t* context_lens, int32_t num_seqs,
+                                        int32_t num_q_heads, int32_t max_q_len,
+                                        int32_t max_context_len, float scale, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -9,7 +9,7 @@ from dataclasses import dataclass, field
 import numpy as np
 
 from .allocator import BlockAllocator
-from .attention import paged_decode
+from .attention import paged_decode, paged_prefill
 from .lowp import to_storage_bits, storage_bits_to_f64
 from .pool import new_pool, reshape_and_cache, copy_block
 
@@ -36,7 +36,8 @@ def padded_tables(alloc, seqs, max_blocks=None):
 
 
 def run(w, attend_rows=None, compute_attention=True):
-    """Replay workload `w`.  attend_rows: batch rows to compute per attend op (None = all).
+    """Replay workload `w`.  attend_rows: batch rows (sequences of a prefill op) to compute
+    per attention op (None = all).
     A workload built without values replays the allocator only (pools stay None)."""
     alloc = BlockAllocator(w.num_blocks, w.block_size, w.free_order)
     has_values = any(x is not None for x in w.kv)
@@ -80,6 +81,20 @@ def run(w, attend_rows=None, compute_attention=True):
                 q = storage_bits_to_f64(to_storage_bits(w.q[qidx], w.dtype), w.dtype)
                 res.outputs.append(paged_decode(q, k_pool, v_pool, tables, lens, w.scale,
                                                 w.dtype, w.block_size, seqs=attend_rows))
+            else:
+                res.outputs.append(None)
+        elif kind == "prefill":
+            # causal attention of each listed sequence's last counts[i] tokens
+            seqs, counts, qidx = op[1], op[2], op[3]
+            tables = padded_tables(alloc, seqs)
+            lens = np.asarray([alloc.context_len(s) for s in seqs], dtype=np.int32)
+            q_start = np.concatenate([[0], np.cumsum(counts)]).astype(np.int64)
+            res.tables.append(tables)
+            res.context_lens.append(lens)
+            if compute_attention and w.q[qidx] is not None:
+                q = storage_bits_to_f64(to_storage_bits(w.q[qidx], w.dtype), w.dtype)
+                res.outputs.append(paged_prefill(q, k_pool, v_pool, tables, lens, q_start, w.scale,
+                                                 w.dtype, w.block_size, seqs=attend_rows))
             else:
                 res.outputs.append(None)
         else:

@@ -88,6 +88,8 @@ _SIGNATURES = {
                                                  _i32, _i32, _i32, _f32, _i32, _vp, _sz, _vp]),
     "paged_attention_reduce": (ctypes.c_int, [_descp, _vp, _i32, _vp, _i32, _i32, _i32, _i32, _vp,
                                               _sz, _vp]),
+    "paged_attention_prefill": (ctypes.c_int, [_descp, _vp, _i32, _vp, _vp, _vp, _vp, _vp, _i32,
+                                               _vp, _i32, _i32, _i32, _i32, _f32, _vp]),
 }
 
 
@@ -372,6 +374,22 @@ def paged_attention_partition(desc, out, out_dtype, q, k_pool, v_pool, block_tab
                                                      block_tables, context_lens, num_q_heads,
                                                      max_context_len, scale, partition_tokens,
                                                      workspace, stream)))
+
+
+def paged_attention_prefill(desc, out, out_dtype, q, q_start, k_pool, v_pool, block_tables,
+                            context_lens, num_q_heads, max_q_len, max_context_len, scale,
+                            stream=None):
+    """q_start: int32 [B+1] device (query rows of sequence s: q_start[s] .. q_start[s+1]-1);
+    block_tables: int32 [B][max_blocks] device; context_lens: int32 [B] device."""
+    if isinstance(out_dtype, str):
+        out_dtype = DTYPE_CODES[out_dtype]
+    _check("paged_attention_prefill",
+           lib.paged_attention_prefill(ctypes.byref(desc), _ptr(out), int(out_dtype), _ptr(q),
+                                       _ptr(q_start), _ptr(k_pool), _ptr(v_pool),
+                                       _ptr(block_tables), int(block_tables.shape[1]),
+                                       _ptr(context_lens), int(context_lens.shape[0]),
+                                       int(num_q_heads), int(max_q_len), int(max_context_len),
+                                       float(scale), _stream(stream)))
 
 
 def paged_attention_reduce(desc, out, out_dtype, context_lens, num_q_heads, max_context_len,

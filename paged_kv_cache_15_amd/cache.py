@@ -122,3 +122,23 @@ class PagedKVCache:
         B.paged_attention_decode(self.desc, out, out_dtype, q, self.k_pool, self.v_pool, tables_d,
                                  lens_d, hq, max_ctx, scale, partition_tokens, ws, stream)
         return out, tables, lens
+
+    def attend_prefill(self, seqs, q_counts, q, scale, out_dtype=None, stream=None):
+        """Causal attention of each sequence's last q_counts[i] tokens (already appended and
+        written) over its whole context: q is [sum(q_counts)][Hq][d] on the device, rows
+        in sequence order."""
+        tables, lens = self.block_tables(seqs)
+        out_dtype = out_dtype or self.dtype
+        counts = np.asarray(q_counts, dtype=np.int32)
+        q_start = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+        max_ctx = int(lens.max()) if len(lens) else 1
+        max_q = int(counts.max()) if len(counts) else 0
+        hq, d = q.shape[1], q.shape[2]
+        out = torch.empty((int(q_start[-1]), hq, d), dtype=TORCH_DTYPES[out_dtype],
+                          device=self.device)
+        B.paged_attention_prefill(self.desc, out, out_dtype, q,
+                                  torch.from_numpy(q_start).to(self.device), self.k_pool,
+                                  self.v_pool, torch.from_numpy(tables).to(self.device),
+                                  torch.from_numpy(lens).to(self.device), hq, max_q, max_ctx,
+                                  scale, stream)
+        return out, tables, lens

@@ -1,0 +1,390 @@
+// Paged prefill / chunked-prefill attention for gfx950: causal multi-query attention
+// over the block pool.
+//
+// What is computed (deepsonar "PagedAttention de vLLM …" §2.5: a whole prompt, a chunk
+// of a long prompt and the rest of a prompt after a prefix-cache hit are one and the
+// same step, since a request only counts its computed tokens; §2.6: this attention
+// also reads the blocks through the table): the last n_s tokens of sequence s, already
+// written to the pool, are queries; query i sits at position ctx_s - n_s + i and
+// attends to keys 0 .. that position.  How (deeplearn.tn "PagedAttention : comment
+// optimiser la mémoire GPU …", continuous batching section: prefill is the
+// compute-heavy phase; PagedAttention vs. FlashAttention: tiles of K and V stream
+// through on-chip memory with an incremental softmax, nothing of size queries x keys
+// goes back to HBM).
+//
+// Work decomposition.  A workgroup of 4 waves takes one KV head g of one sequence and
+// a run of TQ query tokens; its rows are (token, query head of g's group) pairs,
+// token-major, 64*C rows in all (C = 256 / head_dim column blocks of 16 rows per
+// wave), so each K/V tile a wave loads serves 16*C query rows.  Every wave streams the
+// keys 0 .. (largest position among its rows) in 16-token tiles straight from the pool
+// into MFMA operands, with the decode kernels' orientation: S^T = K . Q^T
+// (v_mfma_f32_16x16x32, query rows on the N side) and O^T += V^T . P^T (the weights
+// come out of the score product already in the B-operand layout; 16-bit head plus
+// remainder, as in decode).  The causal mask is per lane (each lane owns one query row
+// of a block); the online softmax is base 2 with lazy rescaling.  The query tiles of
+// one (sequence, KV head) are dispatched one after the other, the last (most keys)
+// first, so the K/V they all read stays in L2.
+//
+// Block sizes 16 and 32 (a 32-token block is two 16-token sub-blocks in the pool).
+
+#include "attention_common.h"
+
+namespace {
+
+using namespace pkv_dev;
+
+struct PrefillArgs {
+    void* out;
+    const void* q;
+    const int32_t* q_start;     // [num_seqs + 1]
+    const void* k_pool;
+    const void* v_pool;
+    const int32_t* block_tables;
+    const int32_t* context_lens;
+    int32_t num_seqs;
+    int32_t max_blocks_per_seq;
+    int32_t num_q_heads;
+    int32_t num_kv_heads;
+    int32_t group;
+    int32_t num_blocks;
+    int32_t max_q_len;
+    int32_t max_context_len;
+    int32_t tokens_per_wg;      // TQ
+    int32_t q_tiles;            // ceil(max_q_len / TQ)
+    float scale_log2;
+};
+
+// C: 16-row column blocks per wave.  Twice as many would halve the K/V loads per query
+// row, but the compiler then needs more than the 512 registers of a wave and spills.
+template <int D>
+constexpr int prefill_blocks() { return 256 / D; }
+
+template <int D, int DT, int OUT_DT, int BS>
+__global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(1)))
+void attn_prefill_mfma(PrefillArgs a) {
+    constexpr int KI = D / 32;
+    constexpr int MT = D / 16;
+    constexpr int C = prefill_blocks<D>();
+    constexpr int RW = 16 * C;            // query rows per wave
+    constexpr int TILE = BS * D;          // elements of one (block, KV head) region
+    constexpr int TPB = BS / kTile;       // 16-token tiles (sub-blocks) per block
+    using kvec = typename std::conditional<DT == DT_BF16, bf16x8, f16x8>::type;
+
+    // x: query tile, last first; y: sequence * KV heads + KV head
+    const int qt = a.q_tiles - 1 - (int)blockIdx.x;
+    const int s = blockIdx.y / a.num_kv_heads;
+    const int g = blockIdx.y - s * a.num_kv_heads;
+    const int lane = threadIdx.x & 63;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int gq = lane & 15, quad = lane >> 4;
+    const int G = a.group;
+
+    const int r0 = a.q_start[s], r1 = a.q_start[s + 1];
+    const int n = r1 - r0;
+    if (n < 0 || n > a.max_q_len) return;          // unusable query range: rows unknown
+    const int t_begin = qt * a.tokens_per_wg;
+    if (t_begin >= n) return;
+    const int ctx = a.context_lens[s];
+    const int t_end = min(n, t_begin + a.tokens_per_wg);
+    // this wave's rows: w*RW .. w*RW + RW - 1 of the workgroup, row = token * G + head
+    const int row0 = w * RW;
+    const int valid_rows = (t_end - t_begin) * G;
+    if (row0 >= valid_rows) return;
+    const bool bad_len = ctx < 1 || ctx > a.max_context_len || n > ctx;
+
+    // per block b: this lane's row, its token, head and position
+    int tok[C], head[C], pos[C];
+    bool live[C];
+#pragma unroll
+    for (int b = 0; b < C; ++b) {
+        const int r = row0 + 16 * b + gq;
+        live[b] = r < valid_rows;
+        const int rr = live[b] ? r : valid_rows - 1;    // padded rows repeat the last one
+        tok[b] = t_begin + rr / G;
+        head[b] = g * G + rr % G;
+        pos[b] = ctx - n + tok[b];
+    }
+    if (bad_len) {
+#pragma unroll
+        for (int b = 0; b < C; ++b)
+            if (live[b])
+                for (int e = 0; e < D / 4; ++e)
+                    store_out<OUT_DT>(a.out, ((int64_t)(r0 + tok[b]) * a.num_q_heads + head[b]) * D +
+                                                 4 * quad + 16 * (e / 4) + e % 4, NAN);
+        return;
+    }
+    // keys this wave needs: up to the position of its last valid row
+    const int last_tok = t_begin + (min(row0 + RW, valid_rows) - 1) / G;
+    const int n_keys = ctx - n + last_tok + 1;
+    const int ntiles = (n_keys + kTile - 1) / kTile;
+
+    // query operands: lane holds q[row gq][32*kk + 8*quad .. +8] of each block
+    kvec qop[C][KI];
+#pragma unroll
+    for (int b = 0; b < C; ++b) {
+        const uint16_t* qh = static_cast<const uint16_t*>(a.q) +
+                             ((int64_t)(r0 + tok[b]) * a.num_q_heads + head[b]) * D + 8 * quad;
+#pragma unroll
+        for (int kk = 0; kk < KI; ++kk)
+            qop[b][kk] = __builtin_bit_cast(kvec, *reinterpret_cast<const i32x4*>(qh + 32 * kk));
+    }
+
+    const uint16_t* kbase = static_cast<const uint16_t*>(a.k_pool) + (int64_t)g * TILE;
+    const uint16_t* vbase = static_cast<const uint16_t*>(a.v_pool) + (int64_t)g * TILE;
+    const int64_t blk_stride = (int64_t)a.num_kv_heads * TILE;
+    const int voff = gq * 4 + quad;
+    const int32_t* trow = a.block_tables + (int64_t)s * a.max_blocks_per_seq;
+
+    f32x4 acc[C][MT];
+    float m[C], lsum[C];
+#pragma unroll
+    for (int b = 0; b < C; ++b) {
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) acc[b][mt] = (f32x4){0.f, 0.f, 0.f, 0.f};
+        m[b] = kNegInf;
+        lsum[b] = 0.f;
+    }
+    bool bad_block = false;
+
+    auto load = [&](int it, i32x4 (&kr)[KI], i32x2 (&vr)[MT]) __attribute__((always_inline)) {
+        int32_t bid = sload(trow, it / TPB);
+        if ((uint32_t)bid >= (uint32_t)a.num_blocks) {
+            bad_block = true;
+            bid = 0;
+        }
+        const int64_t sub = (int64_t)(it % TPB) * (kTile * D);
+        const i32x4* kt = reinterpret_cast<const i32x4*>(kbase + bid * blk_stride + sub) + lane;
+        const i32x2* vt = reinterpret_cast<const i32x2*>(vbase + bid * blk_stride + sub) + voff;
+        // plain (cached) loads: the other waves and query tiles of this sequence read the
+        // same tiles
+#pragma unroll
+        for (int kk = 0; kk < KI; ++kk) kr[kk] = kt[kk * 64];
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) vr[mt] = vt[mt * 64];
+    };
+
+    auto compute = [&](int it, i32x4 (&kr)[KI], i32x2 (&vr)[MT]) __attribute__((always_inline)) {
+        const int k0 = it * kTile + 4 * quad;          // this lane's 4 keys: k0 .. k0+3
+        const int valid = ctx - it * kTile;            // keys of this tile inside the context
+        if (valid < kTile) {
+            // slots past the context may hold anything (NaN included): clear them
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) {
+                uint32_t lo = (uint32_t)vr[mt][0], hi = (uint32_t)vr[mt][1];
+                if (4 * quad + 0 >= valid) lo &= 0xFFFF0000u;
+                if (4 * quad + 1 >= valid) lo &= 0x0000FFFFu;
+                if (4 * quad + 2 >= valid) hi &= 0xFFFF0000u;
+                if (4 * quad + 3 >= valid) hi &= 0x0000FFFFu;
+                vr[mt][0] = (int)lo;
+                vr[mt][1] = (int)hi;
+            }
+        }
+#pragma unroll
+        for (int b = 0; b < C; ++b) {
+            f32x4 sc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kk = 0; kk < KI; ++kk) {
+                if constexpr (DT == DT_BF16)
+                    sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kr[kk]),
+                                                                 qop[b][kk], sc, 0, 0, 0);
+                else
+                    sc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, kr[kk]),
+                                                                qop[b][kk], sc, 0, 0, 0);
+            }
+            float x[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) x[j] = (k0 + j <= pos[b]) ? sc[j] * a.scale_log2 : kNegInf;
+            const float xm = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+            if (__ballot(xm > m[b] + kRescaleSlack)) {
+                const float mnew = fmaxf(m[b], max_across_quads(xm));
+                const float alpha = exp2_fast(m[b] - mnew);
+                lsum[b] *= alpha;
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt) acc[b][mt] *= alpha;
+                m[b] = mnew;
+            }
+            s16x4 phi, plo;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const float pf = exp2_fast(x[j] - m[b]);
+                const uint16_t hi = f32_to_bits16<DT>(pf);
+                const uint16_t lo = f32_to_bits16<DT>(pf - bits_to_f32<DT>(hi));
+                phi[j] = (short)hi;
+                plo[j] = (short)lo;
+                lsum[b] += pf;
+            }
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) {
+                if constexpr (DT == DT_BF16) {
+                    const s16x4 va = __builtin_bit_cast(s16x4, vr[mt]);
+                    acc[b][mt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, phi, acc[b][mt], 0, 0, 0);
+                    acc[b][mt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, plo, acc[b][mt], 0, 0, 0);
+                } else {
+                    const f16x4 va = __builtin_bit_cast(f16x4, vr[mt]);
+                    acc[b][mt] = __builtin_amdgcn_mfma_f32_16x16x16f16(
+                        va, __builtin_bit_cast(f16x4, phi), acc[b][mt], 0, 0, 0);
+                    acc[b][mt] = __builtin_amdgcn_mfma_f32_16x16x16f16(
+                        va, __builtin_bit_cast(f16x4, plo), acc[b][mt], 0, 0, 0);
+                }
+            }
+        }
+    };
+
+    // two register sets: tile it+1 loads while tile it computes; every path issues the
+    // same loads, so the compiler waits for exactly the tile being computed
+    i32x4 kA[KI], kB[KI];
+    i32x2 vA[MT], vB[MT];
+    load(0, kA, vA);
+    int it = 0;
+    for (; it + 2 < ntiles; it += 2) {
+        load(it + 1, kB, vB);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(it, kA, vA);
+        load(it + 2, kA, vA);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(it + 1, kB, vB);
+    }
+    if (it + 1 < ntiles) {
+        load(it + 1, kB, vB);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(it, kA, vA);
+        compute(it + 1, kB, vB);
+    } else {
+        compute(it, kA, vA);
+    }
+
+    // normalise and write: lane holds row gq of block b, dims 16*mt + 4*quad .. +3
+#pragma unroll
+    for (int b = 0; b < C; ++b) {
+        const float lw = sum_across_quads(lsum[b]);
+        const float inv = 1.f / lw;
+        if (!live[b]) continue;
+        const int64_t ob = ((int64_t)(r0 + tok[b]) * a.num_q_heads + head[b]) * D;
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                store_out<OUT_DT>(a.out, ob + 16 * mt + 4 * quad + r,
+                                  bad_block ? NAN : acc[b][mt][r] * inv);
+    }
+}
+
+template <int D, int DT, int OUT, int BS>
+void launch_t(const PrefillArgs& a, dim3 grid, hipStream_t st) {
+    attn_prefill_mfma<D, DT, OUT, BS><<<grid, dim3(kWaves * 64), 0, st>>>(a);
+}
+
+template <int D, int DT, int BS>
+void launch_o(const PrefillArgs& a, int out_dtype, dim3 grid, hipStream_t st) {
+    if (out_dtype == PAGED_KV_F32) launch_t<D, DT, DT_F32, BS>(a, grid, st);
+    else launch_t<D, DT, DT, BS>(a, grid, st);
+}
+
+template <int D, int BS>
+void launch_dt(const PrefillArgs& a, int dtype, int out_dtype, dim3 grid, hipStream_t st) {
+    if (dtype == PAGED_KV_F16) launch_o<D, DT_F16, BS>(a, out_dtype, grid, st);
+    else launch_o<D, DT_BF16, BS>(a, out_dtype, grid, st);
+}
+
+template <int D>
+void launch_bs(const PrefillArgs& a, int bs, int dtype, int out_dtype, dim3 grid, hipStream_t st) {
+    if (bs == 32) launch_dt<D, 32>(a, dtype, out_dtype, grid, st);
+    else launch_dt<D, 16>(a, dtype, out_dtype, grid, st);
+}
+
+int tokens_per_workgroup(int head_dim, int group) { return 4 * 16 * (256 / head_dim) / group; }
+
+paged_kv_status launch_status(const char* what) {
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) {
+        pkv::set_error("%s launch failed: %s", what, hipGetErrorString(e));
+        return PAGED_KV_ERR_HIP;
+    }
+    return PAGED_KV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+paged_kv_status paged_attention_prefill(const paged_kv_pool_desc* desc, void* out,
+                                        int32_t out_dtype, const void* q, const int32_t* q_start,
+                                        const void* k_pool, const void* v_pool,
+                                        const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                        const int32_t* context_lens, int32_t num_seqs,
+                                        int32_t num_q_heads, int32_t max_q_len,
+                                        int32_t max_context_len, float scale, void* stream) {
+    pkv::clear_error();
+    if (!pkv::kernel_desc(desc, true)) return PAGED_KV_ERR_INVALID_ARG;
+    if (desc->dtype == PAGED_KV_F32 || desc->block_size == 1) {
+        pkv::set_error("prefill attention needs fp16/bf16 pools with block size 16 or 32");
+        return PAGED_KV_ERR_UNSUPPORTED;
+    }
+    if (num_seqs < 0 || num_q_heads < 1 || num_q_heads % desc->num_kv_heads) {
+        pkv::set_error("num_seqs %d < 0, or num_q_heads %d not a positive multiple of %d",
+                       num_seqs, num_q_heads, desc->num_kv_heads);
+        return PAGED_KV_ERR_INVALID_ARG;
+    }
+    const int group = num_q_heads / desc->num_kv_heads;
+    if (group > 16) {
+        pkv::set_error("at most 16 query heads per KV head (got %d)", group);
+        return PAGED_KV_ERR_UNSUPPORTED;
+    }
+    if (out_dtype != desc->dtype && out_dtype != PAGED_KV_F32) {
+        pkv::set_error("out_dtype must be the pool dtype or fp32");
+        return PAGED_KV_ERR_INVALID_ARG;
+    }
+    if (max_context_len < 1 || max_q_len < 0 || max_q_len > max_context_len) {
+        pkv::set_error("need 0 <= max_q_len (%d) <= max_context_len (%d), max_context_len >= 1",
+                       max_q_len, max_context_len);
+        return PAGED_KV_ERR_INVALID_ARG;
+    }
+    if ((int64_t)max_blocks_per_seq * desc->block_size < max_context_len) {
+        pkv::set_error("max_blocks_per_seq %d cannot hold max_context_len %d", max_blocks_per_seq,
+                       max_context_len);
+        return PAGED_KV_ERR_INVALID_ARG;
+    }
+    if (num_seqs == 0 || max_q_len == 0) return PAGED_KV_OK;
+    if (!out || !q || !q_start || !k_pool || !v_pool || !block_tables || !context_lens) {
+        pkv::set_error("null pointer argument");
+        return PAGED_KV_ERR_INVALID_ARG;
+    }
+    if ((reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(k_pool) |
+         reinterpret_cast<uintptr_t>(v_pool)) & 15) {
+        pkv::set_error("q and pools must be 16-byte aligned");
+        return PAGED_KV_ERR_INVALID_ARG;
+    }
+    PrefillArgs a;
+    a.out = out;
+    a.q = q;
+    a.q_start = q_start;
+    a.k_pool = k_pool;
+    a.v_pool = v_pool;
+    a.block_tables = block_tables;
+    a.context_lens = context_lens;
+    a.num_seqs = num_seqs;
+    a.max_blocks_per_seq = max_blocks_per_seq;
+    a.num_q_heads = num_q_heads;
+    a.num_kv_heads = desc->num_kv_heads;
+    a.group = group;
+    a.num_blocks = desc->num_blocks;
+    a.max_q_len = max_q_len;
+    a.max_context_len = max_context_len;
+    a.tokens_per_wg = tokens_per_workgroup(desc->head_dim, group);
+    a.q_tiles = (max_q_len + a.tokens_per_wg - 1) / a.tokens_per_wg;
+    a.scale_log2 = scale * kLog2e;
+    if ((int64_t)num_seqs * desc->num_kv_heads > 65535) {
+        pkv::set_error("at most 65535 (sequence, KV head) pairs per launch");
+        return PAGED_KV_ERR_UNSUPPORTED;
+    }
+    const dim3 grid((unsigned)a.q_tiles, (unsigned)(num_seqs * desc->num_kv_heads));
+    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    switch (desc->head_dim) {
+        case 64: launch_bs<64>(a, desc->block_size, desc->dtype, out_dtype, grid, st); break;
+        case 256: launch_bs<256>(a, desc->block_size, desc->dtype, out_dtype, grid, st); break;
+        default: launch_bs<128>(a, desc->block_size, desc->dtype, out_dtype, grid, st); break;
+    }
+    return launch_status("paged attention prefill kernel");
+}
+
+}  // extern "C"

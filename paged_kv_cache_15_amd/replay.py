@@ -54,6 +54,13 @@ def run_workload(w, device="cuda", out_dtype=None, partition_tokens=None, poison
             res.outputs.append(out)
             res.tables.append(tables)
             res.context_lens.append(lens)
+        elif kind == "prefill":
+            seqs, counts, qidx = op[1], op[2], op[3]
+            q = to_device(w.q[qidx], w.dtype, device)
+            out, tables, lens = cache.attend_prefill(seqs, counts, q, float(w.scale), out_dtype)
+            res.outputs.append(out)
+            res.tables.append(tables)
+            res.context_lens.append(lens)
         else:
             raise ValueError(f"unknown op {kind}")
     return res

@@ -321,3 +321,29 @@ def test_device_op_validation_without_gpu():
     waves = max(1, min(3072, -(-4 * 2 * 2 // 16)))   # 4 blocks x 2 seqs x 2 KV heads, >= 16 per wave
     assert wsk >= (waves + 2 * 2) * 4 * (128 + 2) * 4
     assert B.paged_attention_workspace_bytes(good, 2, 7, 64, 0) == 0     # 7 % 2 != 0
+
+
+def test_prefill_validation_without_gpu():
+    def pre(desc, **kw):
+        args = dict(out=_FakeTensor((10, 8, 128)), out_dtype="f32", q=_FakeTensor((10, 8, 128)),
+                    q_start=_FakeTensor((3,)), k_pool=_FakeTensor((1,)), v_pool=_FakeTensor((1,)),
+                    block_tables=_FakeTensor((2, 4)), context_lens=_FakeTensor((2,)),
+                    num_q_heads=8, max_q_len=10, max_context_len=64, scale=0.1, stream=0)
+        args.update(kw)
+        B.paged_attention_prefill(desc, **args)
+    for desc, status in [(B.make_desc(64, 16, 2, 128, "f32"), B.PAGED_KV_ERR_UNSUPPORTED),
+                         (B.make_desc(64, 1, 2, 128, "bf16"), B.PAGED_KV_ERR_UNSUPPORTED),
+                         (B.make_desc(64, 8, 2, 128, "bf16"), B.PAGED_KV_ERR_INVALID_ARG),
+                         (B.make_desc(64, 16, 2, 96, "bf16"), B.PAGED_KV_ERR_INVALID_ARG)]:
+        with pytest.raises(B.PagedKVError) as e:
+            pre(desc)
+        assert e.value.status == status
+    good = B.make_desc(64, 16, 2, 128, "bf16")
+    for kw in [dict(max_q_len=65), dict(max_context_len=65), dict(num_q_heads=7),
+               dict(out_dtype="f16"), dict(q=_FakeTensor((10, 8, 128), addr=4098))]:
+        with pytest.raises(B.PagedKVError):
+            pre(good, **kw)
+    with pytest.raises(B.PagedKVError) as e:
+        pre(B.make_desc(64, 16, 1, 128, "bf16"), num_q_heads=32)               # group 32
+    assert e.value.status == B.PAGED_KV_ERR_UNSUPPORTED
+    pre(good, max_q_len=0)                                                      # nothing to do

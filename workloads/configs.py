@@ -137,6 +137,13 @@ class _Builder:
                       if self.draw_values else None)
         self.ops.append(("attend", [int(s) for s in seqs], len(self.q) - 1))
 
+    def prefill(self, seqs, counts):
+        """Causal attention of each sequence's last counts[i] tokens (one query row each)."""
+        counts = [int(c) for c in counts]
+        self.q.append(_normal(self.ss.spawn(1)[0], (sum(counts), self.hq, self.d))
+                      if self.draw_values else None)
+        self.ops.append(("prefill", [int(s) for s in seqs], counts, len(self.q) - 1))
+
     def free(self, seq):
         self.ops.append(("free", int(seq)))
 
@@ -298,3 +305,65 @@ def make_custom(lengths, num_q_heads, num_kv_heads, head_dim, dtype, seed=0, num
     if free_order is not None:
         w.free_order = np.asarray(free_order, dtype=np.int32)
     return w
+
+
+PREFILL_NAMES = {
+    1: "prefill_gqa_b16_bf16",
+    2: "chunked_prefill_gqa_b32_bf16",
+}
+
+
+def make_prefill(prefix_lens, chunk_rounds, num_q_heads, num_kv_heads, head_dim, dtype,
+                 seed=0, block_size=16, name=None, draw_values=True):
+    """Sequences that already hold prefix_lens[i] tokens, then for each round of
+    chunk_rounds (a list of per-sequence token counts) an append of that many tokens and
+    a prefill op over them (the sequences with a count > 0)."""
+    ss = np.random.SeedSequence(2000 + seed).spawn(3)
+    rng_pool, rng_val = np.random.default_rng(ss[1]), ss[2]
+    b = _Builder(rng_val, num_kv_heads, num_q_heads, head_dim, draw_values)
+    seqs = [b.create() for _ in prefix_lens]
+    nz = [(s, int(n)) for s, n in zip(seqs, prefix_lens) if int(n) > 0]
+    if nz:
+        b.append([s for s, _ in nz], [n for _, n in nz])
+    total = [int(n) for n in prefix_lens]
+    for counts in chunk_rounds:
+        live = [(s, int(c)) for s, c in zip(seqs, counts) if int(c) > 0]
+        if not live:
+            continue
+        b.append([s for s, _ in live], [c for _, c in live])
+        b.prefill([s for s, _ in live], [c for _, c in live])
+        for i, c in enumerate(counts):
+            total[i] += int(c)
+    nb = max(1, _pool_size(sum(_blocks(t, block_size) for t in total)))
+    w = Workload(name=name or f"prefill_{seed}", num_q_heads=num_q_heads,
+                 num_kv_heads=num_kv_heads, head_dim=head_dim, dtype=dtype, num_blocks=nb,
+                 free_order=rng_pool.permutation(nb).astype(np.int32), ops=b.ops, kv=b.kv,
+                 q=b.q, scale=np.float32(1.0 / math.sqrt(head_dim)))
+    w.block_size = block_size
+    return w
+
+
+def make_prefill_config(k: int, small: bool = False, draw_values: bool = True,
+                        block_size: int = 16, head_dim: int = 128) -> Workload:
+    """Prefill workloads on the GQA 72B shape (64 query heads over 8 KV heads, bf16):
+    1: whole prompts, 16 sequences, lengths lognormal around 2048 (capped at 8192);
+    2: chunked prefill, 32 sequences holding lognormal contexts around 2048 that each
+       take a 512-token chunk.  small=True: 3 sequences around 300 tokens (chunk 96)."""
+    ss = np.random.SeedSequence(3000 + k + (100 if small else 0)).spawn(1)[0]
+    rng_len = np.random.default_rng(ss)
+    name = PREFILL_NAMES[k] + ("_small" if small else "")
+    if block_size != 16:
+        name += f"_bs{block_size}"
+    if head_dim != 128:
+        name += f"_d{head_dim}"
+    B, med, cap, chunk = (3, 300, 700, 96) if small else ((16, 2048, 8192, 512) if k == 1
+                                                           else (32, 2048, 8192, 512))
+    if k == 1:
+        lens = np.clip(np.rint(rng_len.lognormal(math.log(med), 0.6, size=B)), 16, cap).astype(int)
+        return make_prefill([0] * B, [list(lens)], 64, 8, head_dim, "bf16", seed=10 + k,
+                            block_size=block_size, name=name, draw_values=draw_values)
+    if k == 2:
+        ctx = np.clip(np.rint(rng_len.lognormal(math.log(med), 0.6, size=B)), 0, cap).astype(int)
+        return make_prefill(list(ctx), [[chunk] * B], 64, 8, head_dim, "bf16", seed=10 + k,
+                            block_size=block_size, name=name, draw_values=draw_values)
+    raise ValueError(f"no prefill workload {k}")
