@@ -49,6 +49,9 @@ def parse():
                     help="tokens per block of the pool (1, 16 or 32; workloads 2, 3 and 5)")
     ap.add_argument("--head-dim", type=int, default=None,
                     help="head size of the workload's heads (64, 128 or 256; workloads 2, 3, 5)")
+    ap.add_argument("--prefill", type=int, default=0, metavar="K",
+                    help="time paged prefill workload K (1: whole prompts, 2: chunked) instead "
+                         "of the decode step, and print its line")
     ap.add_argument("--partition-tokens", type=int, default=None,
                     help="0: stream-K schedule; > 0: fixed partitions (default: the workload's)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
@@ -233,6 +236,101 @@ def decode_graph_timing(layers=32, reps=20):
             "eager_us_per_step": round(res["eager"], 1), "graph_us_per_step": round(res["graph"], 1)}
 
 
+MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "f16": 2500.0}
+
+
+def prefill_flops(op, lens, w):
+    """Algorithmic flops of causal attention for a prefill op: each query at position p
+    meets p + 1 keys, 2*d flops for its score and 2*d for its share of the value sum,
+    per query head."""
+    counts = [int(c) for c in op[2]]
+    pairs = 0
+    for n, L in zip(counts, lens):
+        first = int(L) - n + 1          # keys seen by the first query of the chunk
+        pairs += n * first + n * (n - 1) // 2
+    return pairs * w.num_q_heads * 4 * w.head_dim
+
+
+def prefill_timing(k, steps, warmup, block_size=16, head_dim=128):
+    """Paged prefill on prefill workload k at full size: a step writes the chunk's K/V
+    (reshape_and_cache) and runs the causal attention over the pool; the attention
+    launch is timed with HIP events on its stream."""
+    import numpy as np
+    import torch
+    import workloads as W
+    from paged_kv_cache_15_amd import binding as B
+    from paged_kv_cache_15_amd.cache import PagedKVCache, TORCH_DTYPES
+    from paged_kv_cache_15_amd.replay import to_device
+
+    dev = torch.device("cuda:0")
+    w = W.make_prefill_config(k, block_size=block_size, head_dim=head_dim)
+    cache = PagedKVCache(w.num_blocks, w.num_kv_heads, w.head_dim, w.dtype, w.block_size,
+                         w.free_order, device=dev)
+    last = None
+    for op in w.ops:
+        if op[0] == "create":
+            cache.create()
+        elif op[0] == "append":
+            kv = w.kv[op[3]]
+            kd, vd = to_device(kv[0], w.dtype, dev), to_device(kv[1], w.dtype, dev)
+            slots, copies = B.paged_kv_append_batch(cache.pool, op[1], op[2])
+            slot_d = torch.from_numpy(slots).to(dev)
+            B.reshape_and_cache(cache.desc, kd, vd, cache.k_pool, cache.v_pool, slot_d)
+            last = (kd, vd, slot_d)
+        elif op[0] == "prefill":
+            pre = op
+    torch.cuda.synchronize()
+    new_k, new_v, slot_d = last
+    seqs, counts = pre[1], pre[2]
+    tables, lens = cache.block_tables(seqs)
+    q_start = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    q = to_device(w.q[pre[3]], w.dtype, dev)
+    out = torch.empty_like(q)
+    tables_d, lens_d = torch.from_numpy(tables).to(dev), torch.from_numpy(lens).to(dev)
+    q_start_d = torch.from_numpy(q_start).to(dev)
+    max_q, max_ctx = int(max(counts)), int(lens.max())
+    stream = torch.cuda.current_stream(dev)
+
+    def step(ev=None):
+        B.reshape_and_cache(cache.desc, new_k, new_v, cache.k_pool, cache.v_pool, slot_d,
+                            stream=stream)
+        if ev is not None:
+            ev[0].record(stream)
+        B.paged_attention_prefill(cache.desc, out, w.dtype, q, q_start_d, cache.k_pool,
+                                  cache.v_pool, tables_d, lens_d, w.num_q_heads, max_q, max_ctx,
+                                  float(w.scale), stream)
+        if ev is not None:
+            ev[1].record(stream)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    ms_step = (time.perf_counter() - t0) * 1e3 / steps
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+    for i in range(steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    ms_attn = sum(e[0].elapsed_time(e[1]) for e in evs) / steps
+    flops = prefill_flops(pre, lens, w)
+    peak = MFMA_PEAK_TFLOPS[w.dtype]
+    tf = flops / (ms_attn * 1e-3) / 1e12
+    cache.close()
+    return {
+        "workload": w.name, "sequences": len(seqs), "query_tokens": int(q_start[-1]),
+        "context_tokens": int(lens.sum()), "q_heads": w.num_q_heads, "kv_heads": w.num_kv_heads,
+        "head_dim": w.head_dim, "block_size": w.block_size, "dtype": w.dtype,
+        "ms_per_step": round(ms_step, 4), "attention_ms": round(ms_attn, 4),
+        "query_tokens_per_s": round(int(q_start[-1]) / (ms_step * 1e-3), 1),
+        "roofline": {"kernel": "paged_attention_prefill", "bound": "mfma",
+                     "achieved": round(tf, 2), "peak": peak, "unit": "TFLOP/s",
+                     "frac": round(tf / peak, 4), "algorithmic_flops_per_launch": flops},
+    }
+
+
 def main():
     args = parse()
     if args.copy_calibration:
@@ -243,6 +341,16 @@ def main():
               "(the path shards by sequence or KV head with no exchange, but this build "
               "measures a single MI355X)", file=sys.stderr)
         sys.exit(2)
+    if args.prefill:
+        res = prefill_timing(args.prefill, args.steps, args.warmup, args.block_size,
+                             args.head_dim or 128)
+        print(json.dumps({"metric": "paged prefill attention TFLOP/s, 1 MI355X",
+                          "value": res["roofline"]["achieved"], "unit": "TFLOP/s",
+                          "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+                          "ms_per_step": res["ms_per_step"], "higher_is_better": True,
+                          "dtype": res["dtype"], "data": "synthetic",
+                          "config": {"workload": res["workload"]}, **res}), flush=True)
+        return
     import numpy as np
     import torch
     import workloads as W
@@ -382,6 +490,7 @@ def main():
         del new_k, new_v
         res["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
     res["prefix_cache_host"] = prefix_cache_host()
+    res["prefill"] = prefill_timing(1, 10, 2)
     if not args.no_cpu_baseline:
         res["decode_graph"] = decode_graph_timing()
     print(json.dumps(res), flush=True)

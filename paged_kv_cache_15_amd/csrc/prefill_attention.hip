@@ -18,9 +18,9 @@
 // wave), so each K/V tile a wave loads serves 16*C query rows.  Every wave streams the
 // keys 0 .. (largest position among its rows) in 16-token tiles straight from the pool
 // into MFMA operands, with the decode kernels' orientation: S^T = K . Q^T
-// (v_mfma_f32_16x16x32, query rows on the N side) and O^T += V^T . P^T (the weights
-// come out of the score product already in the B-operand layout; 16-bit head plus
-// remainder, as in decode).  The causal mask is per lane (each lane owns one query row
+// (v_mfma_f32_16x16x32, query rows on the N side) and O^T += V^T . P^T over pairs of
+// tiles (v_mfma_f32_16x16x32 with K = 32 keys; the weights come out of the score
+// product already in the B-operand layout; 16-bit head plus remainder, as in decode).  The causal mask is per lane (each lane owns one query row
 // of a block); the online softmax is base 2 with lazy rescaling.  The query tiles of
 // one (sequence, KV head) are dispatched one after the other, the last (most keys)
 // first, so the K/V they all read stays in L2.
@@ -146,55 +146,79 @@ void attn_prefill_mfma(PrefillArgs a) {
     }
     bool bad_block = false;
 
-    auto load = [&](int it, i32x4 (&kr)[KI], i32x2 (&vr)[MT]) __attribute__((always_inline)) {
-        int32_t bid = sload(trow, it / TPB);
-        if ((uint32_t)bid >= (uint32_t)a.num_blocks) {
-            bad_block = true;
-            bid = 0;
+    // Keys go in pairs of 16-token tiles: one v_mfma_f32_16x16x32 takes 32 keys of the
+    // value product.  The order of keys inside a contraction is free, so lane group q
+    // takes keys 4q..4q+3 of the first tile followed by 4q..4q+3 of the second: that is
+    // what the lane already holds of both the weights (score-product layout) and V^T
+    // (two 8-byte loads), so nothing moves between lanes.
+    struct Pair {
+        i32x4 k[2][KI];
+        i32x2 v[2][MT];
+    };
+    // tiles 2j and 2j+1 (the second may lie past the wave's keys: then its V is zero
+    // and its scores are masked, since its keys are past every row's position)
+    auto load = [&](int j, Pair& pr) __attribute__((always_inline)) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int it = min(2 * j + h, ntiles - 1);
+            int32_t bid = sload(trow, it / TPB);
+            if ((uint32_t)bid >= (uint32_t)a.num_blocks) {
+                bad_block = true;
+                bid = 0;
+            }
+            const int64_t sub = (int64_t)(it % TPB) * (kTile * D);
+            const i32x4* kt = reinterpret_cast<const i32x4*>(kbase + bid * blk_stride + sub) + lane;
+            const i32x2* vt = reinterpret_cast<const i32x2*>(vbase + bid * blk_stride + sub) + voff;
+            // plain (cached) loads: the other waves and query tiles of this sequence read
+            // the same tiles
+#pragma unroll
+            for (int kk = 0; kk < KI; ++kk) pr.k[h][kk] = kt[kk * 64];
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) pr.v[h][mt] = vt[mt * 64];
         }
-        const int64_t sub = (int64_t)(it % TPB) * (kTile * D);
-        const i32x4* kt = reinterpret_cast<const i32x4*>(kbase + bid * blk_stride + sub) + lane;
-        const i32x2* vt = reinterpret_cast<const i32x2*>(vbase + bid * blk_stride + sub) + voff;
-        // plain (cached) loads: the other waves and query tiles of this sequence read the
-        // same tiles
-#pragma unroll
-        for (int kk = 0; kk < KI; ++kk) kr[kk] = kt[kk * 64];
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) vr[mt] = vt[mt * 64];
     };
 
-    auto compute = [&](int it, i32x4 (&kr)[KI], i32x2 (&vr)[MT]) __attribute__((always_inline)) {
-        const int k0 = it * kTile + 4 * quad;          // this lane's 4 keys: k0 .. k0+3
-        const int valid = ctx - it * kTile;            // keys of this tile inside the context
-        if (valid < kTile) {
-            // slots past the context may hold anything (NaN included): clear them
+    auto compute = [&](int j, Pair& pr) __attribute__((always_inline)) {
 #pragma unroll
-            for (int mt = 0; mt < MT; ++mt) {
-                uint32_t lo = (uint32_t)vr[mt][0], hi = (uint32_t)vr[mt][1];
-                if (4 * quad + 0 >= valid) lo &= 0xFFFF0000u;
-                if (4 * quad + 1 >= valid) lo &= 0x0000FFFFu;
-                if (4 * quad + 2 >= valid) hi &= 0xFFFF0000u;
-                if (4 * quad + 3 >= valid) hi &= 0x0000FFFFu;
-                vr[mt][0] = (int)lo;
-                vr[mt][1] = (int)hi;
+        for (int h = 0; h < 2; ++h) {
+            const int valid = 2 * j + h < ntiles ? ctx - (2 * j + h) * kTile : 0;
+            if (valid < kTile) {
+                // slots past the context may hold anything (NaN included): clear them
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt) {
+                    uint32_t lo = (uint32_t)pr.v[h][mt][0], hi = (uint32_t)pr.v[h][mt][1];
+                    if (4 * quad + 0 >= valid) lo &= 0xFFFF0000u;
+                    if (4 * quad + 1 >= valid) lo &= 0x0000FFFFu;
+                    if (4 * quad + 2 >= valid) hi &= 0xFFFF0000u;
+                    if (4 * quad + 3 >= valid) hi &= 0x0000FFFFu;
+                    pr.v[h][mt][0] = (int)lo;
+                    pr.v[h][mt][1] = (int)hi;
+                }
             }
         }
 #pragma unroll
         for (int b = 0; b < C; ++b) {
-            f32x4 sc = {0.f, 0.f, 0.f, 0.f};
+            float x[8];
 #pragma unroll
-            for (int kk = 0; kk < KI; ++kk) {
-                if constexpr (DT == DT_BF16)
-                    sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kr[kk]),
-                                                                 qop[b][kk], sc, 0, 0, 0);
-                else
-                    sc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, kr[kk]),
-                                                                qop[b][kk], sc, 0, 0, 0);
+            for (int h = 0; h < 2; ++h) {
+                f32x4 sc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int kk = 0; kk < KI; ++kk) {
+                    if constexpr (DT == DT_BF16)
+                        sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                            __builtin_bit_cast(bf16x8, pr.k[h][kk]), qop[b][kk], sc, 0, 0, 0);
+                    else
+                        sc = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                            __builtin_bit_cast(f16x8, pr.k[h][kk]), qop[b][kk], sc, 0, 0, 0);
+                }
+                const int k0 = (2 * j + h) * kTile + 4 * quad;   // this lane's 4 keys
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    x[4 * h + r] = (k0 + r <= pos[b]) ? sc[r] * a.scale_log2 : kNegInf;
             }
-            float x[4];
+            float xm = x[0];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) x[j] = (k0 + j <= pos[b]) ? sc[j] * a.scale_log2 : kNegInf;
-            const float xm = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+            for (int r = 1; r < 8; ++r) xm = fmaxf(xm, x[r]);
             if (__ballot(xm > m[b] + kRescaleSlack)) {
                 const float mnew = fmaxf(m[b], max_across_quads(xm));
                 const float alpha = exp2_fast(m[b] - mnew);
@@ -203,54 +227,60 @@ void attn_prefill_mfma(PrefillArgs a) {
                 for (int mt = 0; mt < MT; ++mt) acc[b][mt] *= alpha;
                 m[b] = mnew;
             }
-            s16x4 phi, plo;
+            // weights as a 16-bit head plus a 16-bit remainder (as in decode)
+            i32x4 phi, plo;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const float pf = exp2_fast(x[j] - m[b]);
-                const uint16_t hi = f32_to_bits16<DT>(pf);
-                const uint16_t lo = f32_to_bits16<DT>(pf - bits_to_f32<DT>(hi));
-                phi[j] = (short)hi;
-                plo[j] = (short)lo;
-                lsum[b] += pf;
+            for (int r = 0; r < 4; ++r) {
+                uint32_t hw[2], lw[2];
+#pragma unroll
+                for (int e = 0; e < 2; ++e) {
+                    const float pf = exp2_fast(x[2 * r + e] - m[b]);
+                    hw[e] = f32_to_bits16<DT>(pf);
+                    lw[e] = f32_to_bits16<DT>(pf - bits_to_f32<DT>(hw[e]));
+                    lsum[b] += pf;
+                }
+                phi[r] = (int)(hw[0] | hw[1] << 16);
+                plo[r] = (int)(lw[0] | lw[1] << 16);
             }
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt) {
+                const i32x4 va = {pr.v[0][mt][0], pr.v[0][mt][1], pr.v[1][mt][0], pr.v[1][mt][1]};
                 if constexpr (DT == DT_BF16) {
-                    const s16x4 va = __builtin_bit_cast(s16x4, vr[mt]);
-                    acc[b][mt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, phi, acc[b][mt], 0, 0, 0);
-                    acc[b][mt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, plo, acc[b][mt], 0, 0, 0);
+                    acc[b][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                        __builtin_bit_cast(bf16x8, va), __builtin_bit_cast(bf16x8, phi), acc[b][mt], 0, 0, 0);
+                    acc[b][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                        __builtin_bit_cast(bf16x8, va), __builtin_bit_cast(bf16x8, plo), acc[b][mt], 0, 0, 0);
                 } else {
-                    const f16x4 va = __builtin_bit_cast(f16x4, vr[mt]);
-                    acc[b][mt] = __builtin_amdgcn_mfma_f32_16x16x16f16(
-                        va, __builtin_bit_cast(f16x4, phi), acc[b][mt], 0, 0, 0);
-                    acc[b][mt] = __builtin_amdgcn_mfma_f32_16x16x16f16(
-                        va, __builtin_bit_cast(f16x4, plo), acc[b][mt], 0, 0, 0);
+                    acc[b][mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                        __builtin_bit_cast(f16x8, va), __builtin_bit_cast(f16x8, phi), acc[b][mt], 0, 0, 0);
+                    acc[b][mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                        __builtin_bit_cast(f16x8, va), __builtin_bit_cast(f16x8, plo), acc[b][mt], 0, 0, 0);
                 }
             }
         }
     };
 
-    // two register sets: tile it+1 loads while tile it computes; every path issues the
-    // same loads, so the compiler waits for exactly the tile being computed
-    i32x4 kA[KI], kB[KI];
-    i32x2 vA[MT], vB[MT];
-    load(0, kA, vA);
-    int it = 0;
-    for (; it + 2 < ntiles; it += 2) {
-        load(it + 1, kB, vB);
+    // two register sets: pair j+1 loads while pair j computes; every path issues the
+    // same loads, so the compiler waits for exactly the pair being computed
+    const int npairs = (ntiles + 1) / 2;
+    Pair pA, pB;
+    load(0, pA);
+    int j = 0;
+    for (; j + 2 < npairs; j += 2) {
+        load(j + 1, pB);
         __builtin_amdgcn_sched_barrier(0);
-        compute(it, kA, vA);
-        load(it + 2, kA, vA);
+        compute(j, pA);
+        load(j + 2, pA);
         __builtin_amdgcn_sched_barrier(0);
-        compute(it + 1, kB, vB);
+        compute(j + 1, pB);
     }
-    if (it + 1 < ntiles) {
-        load(it + 1, kB, vB);
+    if (j + 1 < npairs) {
+        load(j + 1, pB);
         __builtin_amdgcn_sched_barrier(0);
-        compute(it, kA, vA);
-        compute(it + 1, kB, vB);
+        compute(j, pA);
+        compute(j + 1, pB);
     } else {
-        compute(it, kA, vA);
+        compute(j, pA);
     }
 
     // normalise and write: lane holds row gq of block b, dims 16*mt + 4*quad .. +3
