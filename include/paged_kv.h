@@ -323,7 +323,8 @@ paged_kv_status paged_attention_reduce(const paged_kv_pool_desc* desc, void* out
  *   q             device [total][num_q_heads][head_dim], type desc->dtype
  *   q_start       device int32[num_seqs + 1], non-decreasing, q_start[0] = 0 (rows of
  *                 out/q past q_start[num_seqs] are neither read nor written)
- *   block_tables, max_blocks_per_seq, context_lens, scale: as for paged_attention_decode
+ *   block_tables, max_blocks_per_seq, context_lens: as for paged_attention_decode
+ *   scale         score scale, > 0 (INVALID_ARG otherwise)
  *   max_q_len     host bound on every n_s (sizes the launch; 0 launches nothing)
  *   max_context_len  host bound on every context_lens[s], >= max_q_len
  * A sequence with n_s > context_lens[s] or context_lens[s] outside [1, max_context_len],

@@ -20,8 +20,10 @@
 // into MFMA operands, with the decode kernels' orientation: S^T = K . Q^T
 // (v_mfma_f32_16x16x32, query rows on the N side) and O^T += V^T . P^T over pairs of
 // tiles (v_mfma_f32_16x16x32 with K = 32 keys; the weights come out of the score
-// product already in the B-operand layout; 16-bit head plus remainder, as in decode).  The causal mask is per lane (each lane owns one query row
-// of a block); the online softmax is base 2 with lazy rescaling.  The query tiles of
+// product already in the B-operand layout; 16-bit head plus remainder, as in decode).
+// The causal mask is per lane (each lane owns one query row of a block) and only
+// applied to tile pairs that reach past a row's position; the online softmax is base 2
+// with lazy rescaling, tested once per pair for all blocks.  The query tiles of
 // one (sequence, KV head) are dispatched one after the other, the last (most keys)
 // first, so the K/V they all read stays in L2.
 //
@@ -56,6 +58,8 @@ struct PrefillArgs {
 
 // C: 16-row column blocks per wave.  Twice as many would halve the K/V loads per query
 // row, but the compiler then needs more than the 512 registers of a wave and spills.
+// (Sharing each tile pair among the workgroup's four waves through LDS, with 3 or 4
+// blocks per wave, measured slower: 363-430 against 459-484 TFLOP/s.)
 template <int D>
 constexpr int prefill_blocks() { return 256 / D; }
 
@@ -117,6 +121,7 @@ void attn_prefill_mfma(PrefillArgs a) {
     const int last_tok = t_begin + (min(row0 + RW, valid_rows) - 1) / G;
     const int n_keys = ctx - n + last_tok + 1;
     const int ntiles = (n_keys + kTile - 1) / kTile;
+    const int pos_min = ctx - n + t_begin + row0 / G;   // this wave's first row
 
     // query operands: lane holds q[row gq][32*kk + 8*quad .. +8] of each block
     kvec qop[C][KI];
@@ -196,45 +201,68 @@ void attn_prefill_mfma(PrefillArgs a) {
                 }
             }
         }
+        // Scores of every block first (independent MFMA chains), then one rescale test
+        // for the pair, then weights and value products: one basic block, so the
+        // scheduler can overlap one block's softmax with another's MFMAs.
+        f32x4 sc[C][2];
 #pragma unroll
-        for (int b = 0; b < C; ++b) {
-            float x[8];
+        for (int h = 0; h < 2; ++h) {
 #pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                f32x4 sc = {0.f, 0.f, 0.f, 0.f};
+            for (int b = 0; b < C; ++b) {
+                f32x4 acc_s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int kk = 0; kk < KI; ++kk) {
                     if constexpr (DT == DT_BF16)
-                        sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                            __builtin_bit_cast(bf16x8, pr.k[h][kk]), qop[b][kk], sc, 0, 0, 0);
+                        acc_s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                            __builtin_bit_cast(bf16x8, pr.k[h][kk]), qop[b][kk], acc_s, 0, 0, 0);
                     else
-                        sc = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-                            __builtin_bit_cast(f16x8, pr.k[h][kk]), qop[b][kk], sc, 0, 0, 0);
+                        acc_s = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                            __builtin_bit_cast(f16x8, pr.k[h][kk]), qop[b][kk], acc_s, 0, 0, 0);
                 }
-                const int k0 = (2 * j + h) * kTile + 4 * quad;   // this lane's 4 keys
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    x[4 * h + r] = (k0 + r <= pos[b]) ? sc[r] * a.scale_log2 : kNegInf;
+                sc[b][h] = acc_s;
             }
-            float xm = x[0];
+        }
+        // causal mask, only where some key of the pair is past some row's position
+        // (scores stay unscaled: scale > 0 keeps their order)
+        if ((2 * j + 1) * kTile + kTile - 1 > pos_min) {
 #pragma unroll
-            for (int r = 1; r < 8; ++r) xm = fmaxf(xm, x[r]);
-            if (__ballot(xm > m[b] + kRescaleSlack)) {
-                const float mnew = fmaxf(m[b], max_across_quads(xm));
+            for (int b = 0; b < C; ++b)
+#pragma unroll
+                for (int h = 0; h < 2; ++h)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        if ((2 * j + h) * kTile + 4 * quad + r > pos[b]) sc[b][h][r] = kNegInf;
+        }
+        float xm[C];
+        bool grow = false;
+#pragma unroll
+        for (int b = 0; b < C; ++b) {
+            float t = fmaxf(fmaxf(sc[b][0][0], sc[b][0][1]), fmaxf(sc[b][0][2], sc[b][0][3]));
+            t = fmaxf(t, fmaxf(fmaxf(sc[b][1][0], sc[b][1][1]), fmaxf(sc[b][1][2], sc[b][1][3])));
+            xm[b] = t * a.scale_log2;
+            grow |= xm[b] > m[b] + kRescaleSlack;
+        }
+        if (__ballot(grow)) {
+#pragma unroll
+            for (int b = 0; b < C; ++b) {
+                const float mnew = fmaxf(m[b], max_across_quads(xm[b]));
                 const float alpha = exp2_fast(m[b] - mnew);
                 lsum[b] *= alpha;
 #pragma unroll
                 for (int mt = 0; mt < MT; ++mt) acc[b][mt] *= alpha;
                 m[b] = mnew;
             }
-            // weights as a 16-bit head plus a 16-bit remainder (as in decode)
+        }
+#pragma unroll
+        for (int b = 0; b < C; ++b) {
+            // weights 2^(scale*s - m) as a 16-bit head plus a 16-bit remainder (as in decode)
             i32x4 phi, plo;
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 uint32_t hw[2], lw[2];
 #pragma unroll
                 for (int e = 0; e < 2; ++e) {
-                    const float pf = exp2_fast(x[2 * r + e] - m[b]);
+                    const float pf = exp2_fast(fmaf(sc[b][r >> 1][2 * (r & 1) + e], a.scale_log2, -m[b]));
                     hw[e] = f32_to_bits16<DT>(pf);
                     lw[e] = f32_to_bits16<DT>(pf - bits_to_f32<DT>(hw[e]));
                     lsum[b] += pf;
@@ -362,6 +390,10 @@ paged_kv_status paged_attention_prefill(const paged_kv_pool_desc* desc, void* ou
     }
     if (out_dtype != desc->dtype && out_dtype != PAGED_KV_F32) {
         pkv::set_error("out_dtype must be the pool dtype or fp32");
+        return PAGED_KV_ERR_INVALID_ARG;
+    }
+    if (!(scale > 0.f)) {
+        pkv::set_error("prefill attention needs scale > 0 (got %g)", (double)scale);
         return PAGED_KV_ERR_INVALID_ARG;
     }
     if (max_context_len < 1 || max_q_len < 0 || max_q_len > max_context_len) {
