@@ -8,7 +8,8 @@
 //
 // Every (sequence, head unit, 16-token tile) of the batch is a tile; tiles are laid on
 // one line ordered by sequence, then unit, then block.  A fixed number W of waves each
-// take an equal contiguous slice of the line (to within one tile) and stream it with a
+// take a contiguous slice of the line (equal to within one tile, weighted by the XCD
+// the wave runs on: see weight_before) and stream it with a
 // two-deep load pipeline that never restarts at sequence or head boundaries.  When a
 // wave's slice covers a whole (sequence, unit) the wave writes the normalised output;
 // otherwise it writes the piece's (max, sum, weighted values), counts it in a per-unit
@@ -25,8 +26,8 @@
 // with 1 token per block a tile gathers 16 blocks (per-lane addresses, and V transposed
 // through LDS, since such a pool stores each token's values as one row).
 //
-// Results depend only on the logical token order and on W, never on where blocks sit
-// in the pool: placement and sharing leave them bit-identical.
+// Results depend only on the logical token order, W and the slice weights, never on
+// where blocks sit in the pool: placement and sharing leave them bit-identical.
 
 #include "attention_common.h"
 #include "attention_host.h"
@@ -57,6 +58,7 @@ struct StreamArgs {
     int32_t num_blocks;
     int32_t max_context_len;
     int32_t waves;           // W
+    int32_t weight_odd;      // slice weight of a wave of an odd workgroup (even: kWeightEven)
     float scale_log2;
 };
 
@@ -147,28 +149,62 @@ __device__ __forceinline__ int32_t tile_block(const StreamArgs& a, const Cursor&
     return bad ? 0 : bid;
 }
 
+// Slices may be weighted by the XCD their wave runs on.  Workgroup b is dispatched to
+// XCD b % 8, and on MI355X the odd XCDs stream the one-wave-per-SIMD launches (head_dim
+// 128 and up, 16- or 32-token blocks) about 10% slower than the even ones (measured
+// per-wave rates on the GQA workload: 0.77 against 0.855 tiles/us, the only systematic
+// spread left), so a wave of an odd workgroup gets w_odd / kWeightEven of an even
+// wave's share (w_odd = StreamArgs::weight_odd; equal weights elsewhere, where the
+// weighting measured slower).  Wave j belongs to workgroup j / kWaves; S(j), the weight
+// of waves 0 .. j-1, has a closed form, and so has its inverse, which the merge needs
+// to find the waves that hold a unit's pieces.
+constexpr int64_t kWeightEven = 64;
+
+struct SliceMap {
+    int64_t T;     // tiles on the line
+    int W;         // waves
+    int64_t wo;    // weight of an odd workgroup's wave
+    __device__ int64_t pair_weight() const { return kWaves * (kWeightEven + wo); }
+    __device__ int64_t weight_before(int64_t j) const {
+        const int64_t p = j / (2 * kWaves), r = j - p * 2 * kWaves;
+        return p * pair_weight() + (r < kWaves ? r * kWeightEven
+                                               : kWaves * kWeightEven + (r - kWaves) * wo);
+    }
+    // first tile of wave j's slice: floor(T S(j) / S(W))
+    __device__ int64_t start(int64_t j) const { return T * weight_before(j) / weight_before(W); }
+    // the wave whose slice holds tile t: the largest j with floor(T S(j) / S(W)) <= t,
+    // i.e. with S(j) <= M = floor(((t + 1) S(W) - 1) / T)
+    __device__ int wave_of(int64_t t) const {
+        const int64_t M = ((t + 1) * weight_before(W) - 1) / T;
+        const int64_t p = M / pair_weight(), rem = M - p * pair_weight();
+        const int64_t r = rem < kWaves * kWeightEven ? rem / kWeightEven
+                                                     : kWaves + (rem - kWaves * kWeightEven) / wo;
+        return (int)min(p * 2 * kWaves + r, (int64_t)W - 1);
+    }
+    // with few tiles per wave some slices are empty; those waves wrote no piece
+    __device__ bool empty(int j) const { return start(j + 1) == start(j); }
+    // no slice is empty when the lightest wave's share is at least one tile
+    __device__ bool dense() const { return T * min(wo, kWeightEven) >= weight_before(W); }
+};
+
+__device__ __forceinline__ SliceMap slice_map(const StreamArgs& a, int64_t T) {
+    return SliceMap{T, a.waves, (int64_t)a.weight_odd};
+}
+
 __device__ __forceinline__ void wave_slice(const StreamArgs& a, int64_t T, int j, int64_t& t0,
                                            int64_t& t1) {
-    t0 = (int64_t)j * T / a.waves;
-    t1 = (int64_t)(j + 1) * T / a.waves;
-}
-
-__device__ __forceinline__ int wave_of(int64_t t, int64_t T, int W) {
-    return (int)(((t + 1) * W - 1) / T);   // the wave whose slice holds tile t
-}
-
-// With fewer tiles than waves some slices are empty; those waves wrote no piece.
-__device__ __forceinline__ bool slice_empty(int j, int64_t T, int W) {
-    return (int64_t)(j + 1) * T / W == (int64_t)j * T / W;
+    const SliceMap sm = slice_map(a, T);
+    t0 = sm.start(j);
+    t1 = sm.start(j + 1);
 }
 
 // Number of pieces unit q was cut into (its tiles start at line position ta).
-__device__ __forceinline__ int unit_pieces(int64_t ta, int nt, int64_t T, int W, int& jf, int& jl) {
-    jf = wave_of(ta, T, W);
-    jl = wave_of(ta + nt - 1, T, W);
-    if (T >= W) return jl - jf + 1;
+__device__ __forceinline__ int unit_pieces(const SliceMap& sm, int64_t ta, int nt, int& jf, int& jl) {
+    jf = sm.wave_of(ta);
+    jl = sm.wave_of(ta + nt - 1);
+    if (sm.dense()) return jl - jf + 1;
     int cnt = 0;
-    for (int jj = jf; jj <= jl; ++jj) cnt += !slice_empty(jj, T, W);
+    for (int jj = jf; jj <= jl; ++jj) cnt += !sm.empty(jj);
     return cnt;
 }
 
@@ -214,7 +250,8 @@ __device__ void merge_unit(const StreamArgs& a, int q, int s, int u, int jf, int
                            int lane) {
     constexpr int EC = HC * D / 64;       // outputs per lane per head group
     const int G = a.heads_per_unit;
-    const int W = a.waves;
+    const SliceMap sm = slice_map(a, T);
+    const bool dense = sm.dense();
 #pragma unroll 1
     for (int g0 = 0; g0 < G; g0 += HC) {
         float Ml = kNegInf, Ll = 0.f, acc[EC];
@@ -241,8 +278,7 @@ __device__ void merge_unit(const StreamArgs& a, int q, int s, int u, int jf, int
 #pragma unroll
             for (int p = 0; p < PC; ++p) {
                 const int jj = k0 + p;
-                // with at least as many tiles as waves no slice is empty
-                if (jj > jl || (T < W && slice_empty(jj, T, W))) continue;
+                if (jj > jl || (!dense && sm.empty(jj))) continue;
                 bad |= __ballot(pm[p] != pm[p]) != 0;
                 const float mn = fmaxf(Ml, pm[p]);
                 const float sc = exp2_fast(Ml - mn), wt = exp2_fast(pm[p] - mn);
@@ -305,7 +341,7 @@ __device__ void publish_pieces(const StreamArgs& a, const int* s_pref, const Pen
         const int q = e ? q1 : q0, old = e ? old1 : old0;
         int jf, jl;
         const int64_t ta = (int64_t)a.units * uni(s_pref[s]) + (int64_t)u * nt;
-        if (old != unit_pieces(ta, nt, T, a.waves, jf, jl) - 1) continue;
+        if (old != unit_pieces(slice_map(a, T), ta, nt, jf, jl) - 1) continue;
         merge_unit<D, OUT_DT, HC, PC>(a, q, s, u, jf, jl, T, lane);
         if (lane == 0) __hip_atomic_store(a.counters + q, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
@@ -902,6 +938,11 @@ StreamArgs make_args(const pkv::StreamLaunch& L, const pkv::StreamPlan& P) {
     a.num_blocks = L.num_blocks;
     a.max_context_len = L.max_context_len;
     a.waves = P.waves;
+    // XCD-weighted slices where they measured faster (one wave per SIMD: head_dim 128
+    // and up; 16- or 32-token blocks): 0.744 against 0.735 of peak on the GQA workload,
+    // 0.793 against 0.781 on the MHA one; at head_dim 64 and block size 1 equal slices
+    // were faster (0.677 against 0.663, 0.571 against 0.557)
+    a.weight_odd = (L.head_dim >= 128 && L.block_size >= 16) ? 58 : (int32_t)kWeightEven;
     a.scale_log2 = L.scale * kLog2e;
     return a;
 }
