@@ -24,8 +24,8 @@
 // The causal mask is per lane (each lane owns one query row of a block) and only
 // applied to tile pairs that reach past a row's position; the online softmax is base 2
 // with lazy rescaling, tested once per pair for all blocks.  The query tiles of
-// one (sequence, KV head) are dispatched one after the other, the last (most keys)
-// first, so the K/V they all read stays in L2.
+// one (sequence, KV head) run on one XCD, one after the other, the last (most keys)
+// first, so the K/V they all read stays in that XCD's L2.
 //
 // Block sizes 16 and 32 (a 32-token block is two 16-token sub-blocks in the pool).
 
@@ -74,10 +74,16 @@ void attn_prefill_mfma(PrefillArgs a) {
     constexpr int TPB = BS / kTile;       // 16-token tiles (sub-blocks) per block
     using kvec = typename std::conditional<DT == DT_BF16, bf16x8, f16x8>::type;
 
-    // x: query tile, last first; y: sequence * KV heads + KV head
-    const int qt = a.q_tiles - 1 - (int)blockIdx.x;
-    const int s = blockIdx.y / a.num_kv_heads;
-    const int g = blockIdx.y - s * a.num_kv_heads;
+    // Workgroup b runs on XCD b % 8.  Pair y = sequence * KV heads + KV head is given to
+    // XCD y % 8 (so the K/V its query tiles all read stays in that XCD's L2, and with 8
+    // KV heads every XCD gets one head of every sequence); on each XCD the workgroups
+    // take its pairs in order, each pair's query tiles last first.
+    const int xcd = blockIdx.x % 8, idx = blockIdx.x / 8;
+    const int y = xcd + 8 * (idx / a.q_tiles);
+    if (y >= a.num_seqs * a.num_kv_heads) return;
+    const int qt = a.q_tiles - 1 - idx % a.q_tiles;
+    const int s = y / a.num_kv_heads;
+    const int g = y - s * a.num_kv_heads;
     const int lane = threadIdx.x & 63;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int gq = lane & 15, quad = lane >> 4;
@@ -435,11 +441,13 @@ paged_kv_status paged_attention_prefill(const paged_kv_pool_desc* desc, void* ou
     a.tokens_per_wg = tokens_per_workgroup(desc->head_dim, group);
     a.q_tiles = (max_q_len + a.tokens_per_wg - 1) / a.tokens_per_wg;
     a.scale_log2 = scale * kLog2e;
-    if ((int64_t)num_seqs * desc->num_kv_heads > 65535) {
-        pkv::set_error("at most 65535 (sequence, KV head) pairs per launch");
+    const int64_t pairs = (int64_t)num_seqs * desc->num_kv_heads;
+    const int64_t wgs = 8 * a.q_tiles * ((pairs + 7) / 8);
+    if (wgs > INT32_MAX) {
+        pkv::set_error("too many (sequence, KV head, query tile) workgroups for one launch");
         return PAGED_KV_ERR_UNSUPPORTED;
     }
-    const dim3 grid((unsigned)a.q_tiles, (unsigned)(num_seqs * desc->num_kv_heads));
+    const dim3 grid((unsigned)wgs);
     hipStream_t st = reinterpret_cast<hipStream_t>(stream);
     switch (desc->head_dim) {
         case 64: launch_bs<64>(a, desc->block_size, desc->dtype, out_dtype, grid, st); break;
