@@ -27,7 +27,9 @@
 // one (sequence, KV head) run on one XCD, one after the other, the last (most keys)
 // first, so the K/V they all read stays in that XCD's L2.
 //
-// Block sizes 16 and 32 (a 32-token block is two 16-token sub-blocks in the pool).
+// Block sizes 16 and 32 (a 32-token block is two 16-token sub-blocks in the pool), and 1
+// (each lane loads from its own token's block; V, token-major at that size, reaches the
+// value product through per-wave LDS rows, as in the decode kernels).
 
 #include "attention_common.h"
 
@@ -71,7 +73,10 @@ void attn_prefill_mfma(PrefillArgs a) {
     constexpr int C = prefill_blocks<D>();
     constexpr int RW = 16 * C;            // query rows per wave
     constexpr int TILE = BS * D;          // elements of one (block, KV head) region
-    constexpr int TPB = BS / kTile;       // 16-token tiles (sub-blocks) per block
+    constexpr int TPB = BS >= kTile ? BS / kTile : 1;   // 16-token tiles (sub-blocks) per block
+    constexpr int LDW = D + 8;            // block size 1: LDS row of one token's values
+    // block size 1: each wave transposes its tiles' token-major V through LDS rows
+    __shared__ uint16_t s_vt[BS == 1 ? kWaves * kTile * LDW : 1];
     using kvec = typename std::conditional<DT == DT_BF16, bf16x8, f16x8>::type;
 
     // Workgroup b runs on XCD b % 8.  Pair y = sequence * KV heads + KV head is given to
@@ -162,34 +167,69 @@ void attn_prefill_mfma(PrefillArgs a) {
     // takes keys 4q..4q+3 of the first tile followed by 4q..4q+3 of the second: that is
     // what the lane already holds of both the weights (score-product layout) and V^T
     // (two 8-byte loads), so nothing moves between lanes.
+    // V as loaded: V^T operands per 16 dims, or (block size 1) token rows like K
+    using vbuf = typename std::conditional<BS == 1, i32x4[KI], i32x2[MT]>::type;
     struct Pair {
         i32x4 k[2][KI];
-        i32x2 v[2][MT];
+        vbuf v[2];
     };
+    uint16_t* vrows = s_vt + w * kTile * LDW;
     // tiles 2j and 2j+1 (the second may lie past the wave's keys: then its V is zero
     // and its scores are masked, since its keys are past every row's position)
     auto load = [&](int j, Pair& pr) __attribute__((always_inline)) {
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
             const int it = min(2 * j + h, ntiles - 1);
-            int32_t bid = sload(trow, it / TPB);
-            if ((uint32_t)bid >= (uint32_t)a.num_blocks) {
-                bad_block = true;
-                bid = 0;
-            }
-            const int64_t sub = (int64_t)(it % TPB) * (kTile * D);
-            const i32x4* kt = reinterpret_cast<const i32x4*>(kbase + bid * blk_stride + sub) + lane;
-            const i32x2* vt = reinterpret_cast<const i32x2*>(vbase + bid * blk_stride + sub) + voff;
             // plain (cached) loads: the other waves and query tiles of this sequence read
             // the same tiles
+            if constexpr (BS == 1) {
+                // one block per token: lane l loads chunks 4*kk + l/16 of token l%16
+                bool bad;
+                const int32_t bid = lane_block_bs1(trow, it, ctx, a.num_blocks, lane, bad);
+                bad_block |= bad;
+                const i32x4* kt = reinterpret_cast<const i32x4*>(kbase + bid * blk_stride) + (lane >> 4);
+                const i32x4* vt = reinterpret_cast<const i32x4*>(vbase + bid * blk_stride) + (lane >> 4);
 #pragma unroll
-            for (int kk = 0; kk < KI; ++kk) pr.k[h][kk] = kt[kk * 64];
+                for (int kk = 0; kk < KI; ++kk) pr.k[h][kk] = kt[4 * kk];
 #pragma unroll
-            for (int mt = 0; mt < MT; ++mt) pr.v[h][mt] = vt[mt * 64];
+                for (int kk = 0; kk < KI; ++kk) pr.v[h][kk] = vt[4 * kk];
+            } else {
+                int32_t bid = sload(trow, it / TPB);
+                if ((uint32_t)bid >= (uint32_t)a.num_blocks) {
+                    bad_block = true;
+                    bid = 0;
+                }
+                const int64_t sub = (int64_t)(it % TPB) * (kTile * D);
+                const i32x4* kt = reinterpret_cast<const i32x4*>(kbase + bid * blk_stride + sub) + lane;
+                const i32x2* vt = reinterpret_cast<const i32x2*>(vbase + bid * blk_stride + sub) + voff;
+#pragma unroll
+                for (int kk = 0; kk < KI; ++kk) pr.k[h][kk] = kt[kk * 64];
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt) pr.v[h][mt] = vt[mt * 64];
+            }
         }
     };
 
     auto compute = [&](int j, Pair& pr) __attribute__((always_inline)) {
+        i32x2 vv[2][MT];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            if constexpr (BS == 1) {
+                // token rows -> V^T operand (4 tokens of one dim per lane) through LDS
+                lds_put_rows<uint16_t, KI>(vrows, LDW, lane, pr.v[h]);
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt) {
+                    uint32_t e[4];
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) e[r] = vrows[(4 * quad + r) * LDW + 16 * mt + gq];
+                    vv[h][mt][0] = (int)(e[0] | e[1] << 16);
+                    vv[h][mt][1] = (int)(e[2] | e[3] << 16);
+                }
+            } else {
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt) vv[h][mt] = pr.v[h][mt];
+            }
+        }
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
             const int valid = 2 * j + h < ntiles ? ctx - (2 * j + h) * kTile : 0;
@@ -197,13 +237,13 @@ void attn_prefill_mfma(PrefillArgs a) {
                 // slots past the context may hold anything (NaN included): clear them
 #pragma unroll
                 for (int mt = 0; mt < MT; ++mt) {
-                    uint32_t lo = (uint32_t)pr.v[h][mt][0], hi = (uint32_t)pr.v[h][mt][1];
+                    uint32_t lo = (uint32_t)vv[h][mt][0], hi = (uint32_t)vv[h][mt][1];
                     if (4 * quad + 0 >= valid) lo &= 0xFFFF0000u;
                     if (4 * quad + 1 >= valid) lo &= 0x0000FFFFu;
                     if (4 * quad + 2 >= valid) hi &= 0xFFFF0000u;
                     if (4 * quad + 3 >= valid) hi &= 0x0000FFFFu;
-                    pr.v[h][mt][0] = (int)lo;
-                    pr.v[h][mt][1] = (int)hi;
+                    vv[h][mt][0] = (int)lo;
+                    vv[h][mt][1] = (int)hi;
                 }
             }
         }
@@ -278,7 +318,7 @@ void attn_prefill_mfma(PrefillArgs a) {
             }
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt) {
-                const i32x4 va = {pr.v[0][mt][0], pr.v[0][mt][1], pr.v[1][mt][0], pr.v[1][mt][1]};
+                const i32x4 va = {vv[0][mt][0], vv[0][mt][1], vv[1][mt][0], vv[1][mt][1]};
                 if constexpr (DT == DT_BF16) {
                     acc[b][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
                         __builtin_bit_cast(bf16x8, va), __builtin_bit_cast(bf16x8, phi), acc[b][mt], 0, 0, 0);
@@ -353,6 +393,7 @@ void launch_dt(const PrefillArgs& a, int dtype, int out_dtype, dim3 grid, hipStr
 template <int D>
 void launch_bs(const PrefillArgs& a, int bs, int dtype, int out_dtype, dim3 grid, hipStream_t st) {
     if (bs == 32) launch_dt<D, 32>(a, dtype, out_dtype, grid, st);
+    else if (bs == 1) launch_dt<D, 1>(a, dtype, out_dtype, grid, st);
     else launch_dt<D, 16>(a, dtype, out_dtype, grid, st);
 }
 
@@ -380,8 +421,8 @@ paged_kv_status paged_attention_prefill(const paged_kv_pool_desc* desc, void* ou
                                         int32_t max_context_len, float scale, void* stream) {
     pkv::clear_error();
     if (!pkv::kernel_desc(desc, true)) return PAGED_KV_ERR_INVALID_ARG;
-    if (desc->dtype == PAGED_KV_F32 || desc->block_size == 1) {
-        pkv::set_error("prefill attention needs fp16/bf16 pools with block size 16 or 32");
+    if (desc->dtype == PAGED_KV_F32) {
+        pkv::set_error("prefill attention needs fp16/bf16 pools");
         return PAGED_KV_ERR_UNSUPPORTED;
     }
     if (num_seqs < 0 || num_q_heads < 1 || num_q_heads % desc->num_kv_heads) {

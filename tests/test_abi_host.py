@@ -332,7 +332,6 @@ def test_prefill_validation_without_gpu():
         args.update(kw)
         B.paged_attention_prefill(desc, **args)
     for desc, status in [(B.make_desc(64, 16, 2, 128, "f32"), B.PAGED_KV_ERR_UNSUPPORTED),
-                         (B.make_desc(64, 1, 2, 128, "bf16"), B.PAGED_KV_ERR_UNSUPPORTED),
                          (B.make_desc(64, 8, 2, 128, "bf16"), B.PAGED_KV_ERR_INVALID_ARG),
                          (B.make_desc(64, 16, 2, 96, "bf16"), B.PAGED_KV_ERR_INVALID_ARG)]:
         with pytest.raises(B.PagedKVError) as e:

@@ -1,10 +1,10 @@
 """Paged prefill / chunked-prefill attention (GPU) against the oracle.
 
 Causal multi-query attention over the pool: whole prompts, chunks on top of existing
-contexts, several chunk rounds per sequence, one-token chunks; both block sizes the
-kernel serves, head sizes 64/128/256, groups of 1 to 16 query heads (including groups
-that do not divide 16), fp16 and bf16, pool-typed and fp32 outputs.  Pools and tables
-bit-exact, attention within the input type's tolerance.
+contexts, several chunk rounds per sequence, one-token chunks; block sizes 1, 16 and
+32, head sizes 64/128/256, groups of 1 to 16 query heads (including groups that do not
+divide 16), fp16 and bf16, pool-typed and fp32 outputs.  Pools and tables bit-exact,
+attention within the input type's tolerance.
 """
 import numpy as np
 import pytest
@@ -31,7 +31,7 @@ def _run(w, out_dtype):
     return g
 
 
-@pytest.mark.parametrize("bs", [16, 32])
+@pytest.mark.parametrize("bs", [16, 32, 1])
 @pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "-".join(map(str, s)))
 def test_prefill_rounds_parity(shape, bs):
     dt, hq, hkv, d = shape
