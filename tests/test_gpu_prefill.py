@@ -116,3 +116,48 @@ def test_one_token_chunks_match_decode():
     torch.cuda.synchronize()
     assert float((a - b).abs().max()) <= 2e-3
     c.close()
+
+
+def test_invalid_inputs_give_nan_rows_or_none_without_reading():
+    """An out-of-range block id, a chunk longer than its context, a context past
+    max_context_len: NaN rows for that sequence; an unusable query range (negative
+    count): its rows are left alone; the other sequences are unaffected."""
+    from paged_kv_cache_15_amd import binding as B
+    from paged_kv_cache_15_amd.cache import TORCH_DTYPES
+    hq, hkv, d, dt = 16, 2, 128, "bf16"
+    w = W.make_prefill([0, 50, 0, 200, 30], [[40, 20, 64, 33, 10]], hq, hkv, d, dt, seed=77)
+    g = _run(w, "f32")
+    o = oreplay.run(w)
+    c = g.cache
+    tables, lens = g.tables[0].copy(), g.context_lens[0].copy()
+    counts = [40, 20, 64, 33, 10]
+    q_start = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    tables[1, 2] = c.desc.num_blocks + 3          # past the pool, below sequence 1's length
+    lens[2] = 30                                   # fewer tokens than its 64 queries
+    q_start_bad = q_start.copy()
+    q_start_bad[5] = q_start_bad[4] - 1            # sequence 4: negative query count
+    q = torch.from_numpy(w.q[0]).cuda().to(TORCH_DTYPES[dt])
+    out = torch.full((int(q_start[-1]), hq, d), 7.0, device="cuda")
+    B.paged_attention_prefill(c.desc, out, "f32", q, torch.from_numpy(q_start_bad).cuda(),
+                              c.k_pool, c.v_pool, torch.from_numpy(tables).cuda(),
+                              torch.from_numpy(lens).cuda(), hq, 64, int(lens.max()),
+                              float(w.scale))
+    torch.cuda.synchronize()
+    r = out.double().cpu().numpy()
+    rows = lambda s: slice(int(q_start[s]), int(q_start[s + 1]))
+    assert np.isnan(r[rows(1)]).all() and np.isnan(r[rows(2)]).all()
+    assert (r[rows(4)] == 7.0).all()
+    for s in (0, 3):
+        assert np.abs(r[rows(s)] - o.outputs[0][rows(s)]).max() <= TOL[dt], s
+    # a context longer than max_context_len: NaN rows for that sequence only
+    lens2 = g.context_lens[0].copy()
+    out.fill_(7.0)
+    B.paged_attention_prefill(c.desc, out, "f32", q, torch.from_numpy(q_start).cuda(),
+                              c.k_pool, c.v_pool, torch.from_numpy(g.tables[0]).cuda(),
+                              torch.from_numpy(lens2).cuda(), hq, 64, 200, float(w.scale))
+    torch.cuda.synchronize()
+    r = out.double().cpu().numpy()
+    assert np.isnan(r[rows(3)]).all()
+    for s in (0, 1, 2, 4):
+        assert np.abs(r[rows(s)] - o.outputs[0][rows(s)]).max() <= TOL[dt], s
+    c.close()
