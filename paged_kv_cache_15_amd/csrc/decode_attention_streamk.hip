@@ -7,10 +7,10 @@
 // softmax), scheduled differently:
 //
 // Every (sequence, head unit, 16-token tile) of the batch is a tile; tiles are laid on
-// one line ordered by sequence, then unit, then block.  A fixed number W of waves each
-// take a contiguous slice of the line (equal to within one tile, weighted by the XCD
-// the wave runs on: see weight_before) and stream it with a
-// two-deep load pipeline that never restarts at sequence or head boundaries.  When a
+// one line ordered by sequence, then unit, then position.  A fixed number W of waves
+// each take a contiguous slice of the line (equal to within one tile, or weighted by
+// the XCD the wave runs on: see SliceMap) and stream it with a two-deep load pipeline
+// that never restarts at sequence or head boundaries.  When a
 // wave's slice covers a whole (sequence, unit) the wave writes the normalised output;
 // otherwise it writes the piece's (max, sum, weighted values), counts it in a per-unit
 // counter, and the wave that completes the count merges the unit's pieces in slice
