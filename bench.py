@@ -83,11 +83,26 @@ KERNEL_SOURCES = ("paged_kv_cache_15_amd/csrc/common.h",
                   "paged_kv_cache_15_amd/csrc/decode_attention_streamk.hip")
 
 
-def kernel_source_digest():
+def code_text(src: str) -> str:
+    """A source's code without comments and blank space: what the compiler sees of it
+    (a comment edit does not change the kernel the counters were taken on)."""
+    import re
+    src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
+    lines = (re.sub(r"//.*", "", ln).strip() for ln in src.splitlines())
+    return "\n".join(" ".join(ln.split()) for ln in lines if ln)
+
+
+def kernel_source_digest(read=None):
+    """SHA-256 over the code text of the kernel sources (`read` maps a path to its text;
+    default: the files in this tree)."""
     h = hashlib.sha256()
     for rel in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
+        if read is None:
+            with open(os.path.join(ROOT, rel), encoding="utf-8") as f:
+                text = f.read()
+        else:
+            text = read(rel)
+        h.update(code_text(text).encode())
     return h.hexdigest()
 
 
