@@ -312,3 +312,23 @@ def test_prefix_cache_hit_gives_the_same_attention_bitwise(keep_first):
     assert np.abs(out_f64(out_hit)[0] - want).max() <= TOL[dt]
     c.close()
     r.close()
+
+
+@pytest.mark.parametrize("shape", [("bf16", 16, 2, 128), ("f16", 4, 4, 64)],
+                         ids=lambda s: "-".join(map(str, s)))
+def test_stream_k_batch_limit_and_fallback(shape):
+    """8192 sequences (the most the stream-K schedule takes: its per-sequence tile
+    prefix fills 32 KiB of LDS) and 8193 (falls back to 512-token partitions), short
+    ragged contexts: every row against the oracle."""
+    dt, hq, hkv, d = shape
+    rng = np.random.default_rng(8)
+    for n in (8192, 8193):
+        lens = rng.integers(1, 48, size=n)
+        w = W.make_custom(lens, hq, hkv, d, dt, seed=n % 97)
+        say(f"[edge] {n} sequences {shape}")
+        g = _run(w, "f32", 0)
+        o = oreplay.run(w)
+        assert_bookkeeping_equal(g, o)
+        err = assert_close(g.outputs[0], o.outputs[0], dt, "f32")
+        say(f"   max|err| {err:.3e}")
+        g.cache.close()
