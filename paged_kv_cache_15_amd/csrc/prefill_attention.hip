@@ -23,7 +23,11 @@
 // product already in the B-operand layout; 16-bit head plus remainder, as in decode).
 // The causal mask is per lane (each lane owns one query row of a block) and only
 // applied to tile pairs that reach past a row's position; the online softmax is base 2
-// with lazy rescaling, tested once per pair for all blocks.  The query tiles of
+// with lazy rescaling, tested once per pair for all blocks.  The pairs are software-
+// pipelined: the score products of pair j+1 are issued together with the weights and
+// value products of pair j, so the matrix cores and the vector ALU work side by side,
+// and the pairs that need neither the mask nor any clearing of slots past the context
+// run a branch-free step.  The query tiles of
 // one (sequence, KV head) run on one XCD, one after the other, the last (most keys)
 // first, so the K/V they all read stays in that XCD's L2.
 //
@@ -57,6 +61,33 @@ struct PrefillArgs {
     int32_t q_tiles;            // ceil(max_q_len / TQ)
     float scale_log2;
 };
+
+// Two weights as packed 16-bit heads (round to nearest even) and packed 16-bit
+// remainders w - head (also rounded): one packing conversion for each pair, the heads
+// widened back to float by bit operations (bf16) or a conversion (fp16).
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+template <int DT>
+__device__ __forceinline__ uint32_t pack2_16(float a, float b) {
+    if constexpr (DT == DT_BF16) return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){a, b}, bf16x2_t));
+    else return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){a, b}, f16x2_t));
+}
+template <int DT>
+__device__ __forceinline__ void split_pair(float w0, float w1, int& head, int& rest) {
+    const uint32_t h = pack2_16<DT>(w0, w1);
+    float r0, r1;
+    if constexpr (DT == DT_BF16) {
+        r0 = w0 - __uint_as_float(h << 16);
+        r1 = w1 - __uint_as_float(h & 0xFFFF0000u);
+    } else {
+        const f16x2_t hv = __builtin_bit_cast(f16x2_t, h);
+        r0 = w0 - (float)hv[0];
+        r1 = w1 - (float)hv[1];
+    }
+    head = (int)h;
+    rest = (int)pack2_16<DT>(r0, r1);
+}
 
 // C: 16-row column blocks per wave.  Twice as many would halve the K/V loads per query
 // row, but the compiler then needs more than the 512 registers of a wave and spills.
@@ -167,56 +198,146 @@ void attn_prefill_mfma(PrefillArgs a) {
     // takes keys 4q..4q+3 of the first tile followed by 4q..4q+3 of the second: that is
     // what the lane already holds of both the weights (score-product layout) and V^T
     // (two 8-byte loads), so nothing moves between lanes.
+    //
+    // Software pipeline: while the weights and value products of pair j are computed
+    // (vector ALU and the second half of the matrix work), the score products of pair
+    // j+1 are issued into the same basic block, so the two overlap; K of pair j+2 and V
+    // of pair j+1 load meanwhile.
     // V as loaded: V^T operands per 16 dims, or (block size 1) token rows like K
     using vbuf = typename std::conditional<BS == 1, i32x4[KI], i32x2[MT]>::type;
-    struct Pair {
+    struct KPair {
         i32x4 k[2][KI];
+    };
+    struct VPair {
         vbuf v[2];
     };
     uint16_t* vrows = s_vt + w * kTile * LDW;
-    // tiles 2j and 2j+1 (the second may lie past the wave's keys: then its V is zero
-    // and its scores are masked, since its keys are past every row's position)
-    auto load = [&](int j, Pair& pr) __attribute__((always_inline)) {
+    const int npairs = (ntiles + 1) / 2;
+
+    // block ids of pair j's tiles (the second may lie past the wave's keys: then it
+    // repeats the last tile, its V is zeroed and its scores masked, since its keys are
+    // past every row's position); block size 1: the lane's own token's block
+    auto pair_bids = [&](int j, int32_t (&bid)[2]) __attribute__((always_inline)) {
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
             const int it = min(2 * j + h, ntiles - 1);
-            // plain (cached) loads: the other waves and query tiles of this sequence read
-            // the same tiles
             if constexpr (BS == 1) {
-                // one block per token: lane l loads chunks 4*kk + l/16 of token l%16
                 bool bad;
-                const int32_t bid = lane_block_bs1(trow, it, ctx, a.num_blocks, lane, bad);
+                bid[h] = lane_block_bs1(trow, it, ctx, a.num_blocks, lane, bad);
                 bad_block |= bad;
-                const i32x4* kt = reinterpret_cast<const i32x4*>(kbase + bid * blk_stride) + (lane >> 4);
-                const i32x4* vt = reinterpret_cast<const i32x4*>(vbase + bid * blk_stride) + (lane >> 4);
-#pragma unroll
-                for (int kk = 0; kk < KI; ++kk) pr.k[h][kk] = kt[4 * kk];
-#pragma unroll
-                for (int kk = 0; kk < KI; ++kk) pr.v[h][kk] = vt[4 * kk];
             } else {
-                int32_t bid = sload(trow, it / TPB);
-                if ((uint32_t)bid >= (uint32_t)a.num_blocks) {
+                int32_t b = sload(trow, it / TPB);
+                if ((uint32_t)b >= (uint32_t)a.num_blocks) {
                     bad_block = true;
-                    bid = 0;
+                    b = 0;
                 }
+                bid[h] = b;
+            }
+        }
+    };
+    // plain (cached) loads: the other waves and query tiles of this sequence read the
+    // same tiles
+    auto load_k = [&](int j, const int32_t (&bid)[2], KPair& kp) __attribute__((always_inline)) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int it = min(2 * j + h, ntiles - 1);
+            if constexpr (BS == 1) {
+                const i32x4* kt = reinterpret_cast<const i32x4*>(kbase + bid[h] * blk_stride) + (lane >> 4);
+#pragma unroll
+                for (int kk = 0; kk < KI; ++kk) kp.k[h][kk] = kt[4 * kk];
+            } else {
                 const int64_t sub = (int64_t)(it % TPB) * (kTile * D);
-                const i32x4* kt = reinterpret_cast<const i32x4*>(kbase + bid * blk_stride + sub) + lane;
-                const i32x2* vt = reinterpret_cast<const i32x2*>(vbase + bid * blk_stride + sub) + voff;
+                const i32x4* kt = reinterpret_cast<const i32x4*>(kbase + bid[h] * blk_stride + sub) + lane;
 #pragma unroll
-                for (int kk = 0; kk < KI; ++kk) pr.k[h][kk] = kt[kk * 64];
+                for (int kk = 0; kk < KI; ++kk) kp.k[h][kk] = kt[kk * 64];
+            }
+        }
+    };
+    auto load_v = [&](int j, const int32_t (&bid)[2], VPair& vp) __attribute__((always_inline)) {
 #pragma unroll
-                for (int mt = 0; mt < MT; ++mt) pr.v[h][mt] = vt[mt * 64];
+        for (int h = 0; h < 2; ++h) {
+            const int it = min(2 * j + h, ntiles - 1);
+            if constexpr (BS == 1) {
+                const i32x4* vt = reinterpret_cast<const i32x4*>(vbase + bid[h] * blk_stride) + (lane >> 4);
+#pragma unroll
+                for (int kk = 0; kk < KI; ++kk) vp.v[h][kk] = vt[4 * kk];
+            } else {
+                const int64_t sub = (int64_t)(it % TPB) * (kTile * D);
+                const i32x2* vt = reinterpret_cast<const i32x2*>(vbase + bid[h] * blk_stride + sub) + voff;
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt) vp.v[h][mt] = vt[mt * 64];
             }
         }
     };
 
-    auto compute = [&](int j, Pair& pr) __attribute__((always_inline)) {
+    constexpr std::integral_constant<bool, false> kPlain{};
+    constexpr std::integral_constant<bool, true> kSpecial{};
+    // S^T = K . Q^T for both tiles and every block
+    auto scores = [&](const KPair& kp, f32x4 (&sc)[C][2]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+#pragma unroll
+            for (int b = 0; b < C; ++b) {
+                f32x4 acc_s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int kk = 0; kk < KI; ++kk) {
+                    if constexpr (DT == DT_BF16)
+                        acc_s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                            __builtin_bit_cast(bf16x8, kp.k[h][kk]), qop[b][kk], acc_s, 0, 0, 0);
+                    else
+                        acc_s = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                            __builtin_bit_cast(f16x8, kp.k[h][kk]), qop[b][kk], acc_s, 0, 0, 0);
+                }
+                sc[b][h] = acc_s;
+            }
+        }
+    };
+    // causal mask, only where some key of pair j is past some row's position (scores
+    // stay unscaled: scale > 0 keeps their order); then the pair's row maxima (scaled)
+    // and whether any of them passes the running maximum by more than the slack
+    float xm[C];
+    auto mask_and_max = [&](auto special, int j, f32x4 (&sc)[C][2]) __attribute__((always_inline)) {
+        if (decltype(special)::value && (2 * j + 1) * kTile + kTile - 1 > pos_min) {
+#pragma unroll
+            for (int b = 0; b < C; ++b)
+#pragma unroll
+                for (int h = 0; h < 2; ++h)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        if ((2 * j + h) * kTile + 4 * quad + r > pos[b]) sc[b][h][r] = kNegInf;
+        }
+        bool grow = false;
+#pragma unroll
+        for (int b = 0; b < C; ++b) {
+            // a chain of three-way maxima
+            float t = fmaxf(fmaxf(sc[b][0][0], sc[b][0][1]), sc[b][0][2]);
+            t = fmaxf(fmaxf(t, sc[b][0][3]), sc[b][1][0]);
+            t = fmaxf(fmaxf(t, sc[b][1][1]), sc[b][1][2]);
+            t = fmaxf(t, sc[b][1][3]);
+            xm[b] = t * a.scale_log2;
+            grow |= xm[b] > m[b] + kRescaleSlack;
+        }
+        return grow;
+    };
+    auto rescale = [&]() __attribute__((always_inline)) {
+#pragma unroll
+        for (int b = 0; b < C; ++b) {
+            const float mnew = fmaxf(m[b], max_across_quads(xm[b]));
+            const float alpha = exp2_fast(m[b] - mnew);
+            lsum[b] *= alpha;
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) acc[b][mt] *= alpha;
+            m[b] = mnew;
+        }
+    };
+    // weights of pair j and O^T += V^T . P^T
+    auto accumulate = [&](auto special, int j, const f32x4 (&sc)[C][2], const VPair& vp) __attribute__((always_inline)) {
         i32x2 vv[2][MT];
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
             if constexpr (BS == 1) {
                 // token rows -> V^T operand (4 tokens of one dim per lane) through LDS
-                lds_put_rows<uint16_t, KI>(vrows, LDW, lane, pr.v[h]);
+                lds_put_rows<uint16_t, KI>(vrows, LDW, lane, vp.v[h]);
 #pragma unroll
                 for (int mt = 0; mt < MT; ++mt) {
                     uint32_t e[4];
@@ -227,13 +348,13 @@ void attn_prefill_mfma(PrefillArgs a) {
                 }
             } else {
 #pragma unroll
-                for (int mt = 0; mt < MT; ++mt) vv[h][mt] = pr.v[h][mt];
+                for (int mt = 0; mt < MT; ++mt) vv[h][mt] = vp.v[h][mt];
             }
         }
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
             const int valid = 2 * j + h < ntiles ? ctx - (2 * j + h) * kTile : 0;
-            if (valid < kTile) {
+            if (decltype(special)::value && valid < kTile) {
                 // slots past the context may hold anything (NaN included): clear them
 #pragma unroll
                 for (int mt = 0; mt < MT; ++mt) {
@@ -247,74 +368,20 @@ void attn_prefill_mfma(PrefillArgs a) {
                 }
             }
         }
-        // Scores of every block first (independent MFMA chains), then one rescale test
-        // for the pair, then weights and value products: one basic block, so the
-        // scheduler can overlap one block's softmax with another's MFMAs.
-        f32x4 sc[C][2];
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-#pragma unroll
-            for (int b = 0; b < C; ++b) {
-                f32x4 acc_s = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int kk = 0; kk < KI; ++kk) {
-                    if constexpr (DT == DT_BF16)
-                        acc_s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                            __builtin_bit_cast(bf16x8, pr.k[h][kk]), qop[b][kk], acc_s, 0, 0, 0);
-                    else
-                        acc_s = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-                            __builtin_bit_cast(f16x8, pr.k[h][kk]), qop[b][kk], acc_s, 0, 0, 0);
-                }
-                sc[b][h] = acc_s;
-            }
-        }
-        // causal mask, only where some key of the pair is past some row's position
-        // (scores stay unscaled: scale > 0 keeps their order)
-        if ((2 * j + 1) * kTile + kTile - 1 > pos_min) {
-#pragma unroll
-            for (int b = 0; b < C; ++b)
-#pragma unroll
-                for (int h = 0; h < 2; ++h)
-#pragma unroll
-                    for (int r = 0; r < 4; ++r)
-                        if ((2 * j + h) * kTile + 4 * quad + r > pos[b]) sc[b][h][r] = kNegInf;
-        }
-        float xm[C];
-        bool grow = false;
-#pragma unroll
-        for (int b = 0; b < C; ++b) {
-            float t = fmaxf(fmaxf(sc[b][0][0], sc[b][0][1]), fmaxf(sc[b][0][2], sc[b][0][3]));
-            t = fmaxf(t, fmaxf(fmaxf(sc[b][1][0], sc[b][1][1]), fmaxf(sc[b][1][2], sc[b][1][3])));
-            xm[b] = t * a.scale_log2;
-            grow |= xm[b] > m[b] + kRescaleSlack;
-        }
-        if (__ballot(grow)) {
-#pragma unroll
-            for (int b = 0; b < C; ++b) {
-                const float mnew = fmaxf(m[b], max_across_quads(xm[b]));
-                const float alpha = exp2_fast(m[b] - mnew);
-                lsum[b] *= alpha;
-#pragma unroll
-                for (int mt = 0; mt < MT; ++mt) acc[b][mt] *= alpha;
-                m[b] = mnew;
-            }
-        }
 #pragma unroll
         for (int b = 0; b < C; ++b) {
             // weights 2^(scale*s - m) as a 16-bit head plus a 16-bit remainder (as in decode)
             i32x4 phi, plo;
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                uint32_t hw[2], lw[2];
-#pragma unroll
-                for (int e = 0; e < 2; ++e) {
-                    const float pf = exp2_fast(fmaf(sc[b][r >> 1][2 * (r & 1) + e], a.scale_log2, -m[b]));
-                    hw[e] = f32_to_bits16<DT>(pf);
-                    lw[e] = f32_to_bits16<DT>(pf - bits_to_f32<DT>(hw[e]));
-                    lsum[b] += pf;
-                }
-                phi[r] = (int)(hw[0] | hw[1] << 16);
-                plo[r] = (int)(lw[0] | lw[1] << 16);
+                const float p0 = exp2_fast(fmaf(sc[b][r >> 1][2 * (r & 1)], a.scale_log2, -m[b]));
+                const float p1 = exp2_fast(fmaf(sc[b][r >> 1][2 * (r & 1) + 1], a.scale_log2, -m[b]));
+                int hw, lw;
+                split_pair<DT>(p0, p1, hw, lw);
+                phi[r] = hw;
+                plo[r] = lw;
+                lsum[b] += p0;
+                lsum[b] += p1;
             }
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt) {
@@ -334,27 +401,66 @@ void attn_prefill_mfma(PrefillArgs a) {
         }
     };
 
-    // two register sets: pair j+1 loads while pair j computes; every path issues the
-    // same loads, so the compiler waits for exactly the pair being computed
-    const int npairs = (ntiles + 1) / 2;
-    Pair pA, pB;
-    load(0, pA);
+    // Buffers: K of pair j+1 and V of pair j are in use during step j; K of pair j+2 and
+    // V of pair j+1 load into the other two.  Every step issues the same loads (past the
+    // last pair they repeat it), so the compiler waits for exactly what a step uses.
+    // Block ids are looked up a step before the loads that use them.
+    KPair kA, kB;
+    VPair vA, vB;
+    int32_t bid_v[2], bid_k[2], bid_n[2];
+    f32x4 S[C][2];
+    pair_bids(0, bid_n);
+    load_k(0, bid_n, kA);
+    load_v(0, bid_n, vA);
+    pair_bids(min(1, npairs - 1), bid_v);
+    load_k(min(1, npairs - 1), bid_v, kB);
+    pair_bids(min(2, npairs - 1), bid_k);
+    scores(kA, S);
+    bool grow = mask_and_max(kSpecial, 0, S);
+
+    // step j: S holds pair j's scores, kn K of pair j+1, vc V of pair j (j + 1 < npairs)
+    auto step = [&](auto special, int j, const KPair& kn, KPair& kl, const VPair& vc, VPair& vl) __attribute__((always_inline)) {
+        if (__ballot(grow)) rescale();
+        load_v(j + 1, bid_v, vl);
+        load_k(min(j + 2, npairs - 1), bid_k, kl);
+        pair_bids(min(j + 3, npairs - 1), bid_n);
+        f32x4 sn[C][2];
+        scores(kn, sn);
+        accumulate(special, j, S, vc);
+        grow = mask_and_max(special, j + 1, sn);
+#pragma unroll
+        for (int b = 0; b < C; ++b) {
+            S[b][0] = sn[b][0];
+            S[b][1] = sn[b][1];
+        }
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            bid_v[h] = bid_k[h];
+            bid_k[h] = bid_n[h];
+        }
+    };
+    // Pairs before j_plain need neither the causal mask nor V zeroing (every key is at
+    // or before every row's position, and every slot is inside the context): their steps
+    // run without those branches, so each step is one basic block.
+    const int t_zero = min(ntiles, ctx / kTile);          // first tile with slots to clear
+    const int j_mask = (pos_min + 1) / (2 * kTile);        // first pair with a key past pos_min
+    const int j_plain = min(j_mask, t_zero / 2);
     int j = 0;
+    for (; j + 2 < npairs && j + 2 < j_plain; j += 2) {
+        step(kPlain, j, kB, kA, vA, vB);
+        step(kPlain, j + 1, kA, kB, vB, vA);
+    }
     for (; j + 2 < npairs; j += 2) {
-        load(j + 1, pB);
-        __builtin_amdgcn_sched_barrier(0);
-        compute(j, pA);
-        load(j + 2, pA);
-        __builtin_amdgcn_sched_barrier(0);
-        compute(j + 1, pB);
+        step(kSpecial, j, kB, kA, vA, vB);
+        step(kSpecial, j + 1, kA, kB, vB, vA);
     }
     if (j + 1 < npairs) {
-        load(j + 1, pB);
-        __builtin_amdgcn_sched_barrier(0);
-        compute(j, pA);
-        compute(j + 1, pB);
+        step(kSpecial, j, kB, kA, vA, vB);
+        if (__ballot(grow)) rescale();
+        accumulate(kSpecial, j + 1, S, vB);
     } else {
-        compute(j, pA);
+        if (__ballot(grow)) rescale();
+        accumulate(kSpecial, j, S, vA);
     }
 
     // normalise and write: lane holds row gq of block b, dims 16*mt + 4*quad .. +3
