@@ -331,8 +331,9 @@ paged_kv_status paged_attention_reduce(const paged_kv_pool_desc* desc, void* out
  * or whose table holds an id outside [0, num_blocks) below its length, gets NaN rows; a
  * sequence with n_s < 0 or n_s > max_q_len gets none written.  Requires an fp16/bf16
  * pool (UNSUPPORTED otherwise) with block_size 1, 16 or 32, head_dim 64, 128 or 256,
- * num_q_heads % num_kv_heads == 0 and at most 16 query heads per KV head.  Needs no
- * workspace.  Results do not depend on where blocks sit in the pool. */
+ * num_q_heads % num_kv_heads == 0 and at most 16 query heads per KV head; out, q and
+ * the pools must be 16-byte aligned (INVALID_ARG otherwise).  Needs no workspace.
+ * Results do not depend on where blocks sit in the pool. */
 paged_kv_status paged_attention_prefill(const paged_kv_pool_desc* desc, void* out,
                                         int32_t out_dtype, const void* q, const int32_t* q_start,
                                         const void* k_pool, const void* v_pool,

@@ -89,6 +89,18 @@ __device__ __forceinline__ void split_pair(float w0, float w1, int& head, int& r
     rest = (int)pack2_16<DT>(r0, r1);
 }
 
+// Four consecutive outputs (element i a multiple of 4, out 16-byte aligned) in one
+// store: 16 bytes of fp32 or 8 bytes of packed 16-bit values.
+template <int OUT_DT>
+__device__ __forceinline__ void store_out4(void* out, int64_t i, f32x4 v) {
+    if constexpr (OUT_DT == DT_F32) {
+        *reinterpret_cast<f32x4*>(static_cast<float*>(out) + i) = v;
+    } else {
+        const i32x2 p = {(int)pack2_16<OUT_DT>(v[0], v[1]), (int)pack2_16<OUT_DT>(v[2], v[3])};
+        *reinterpret_cast<i32x2*>(static_cast<uint16_t*>(out) + i) = p;
+    }
+}
+
 // C: 16-row column blocks per wave.  Twice as many would halve the K/V loads per query
 // row, but the compiler then needs more than the 512 registers of a wave and spills.
 // (Sharing each tile pair among the workgroup's four waves through LDS, with 3 or 4
@@ -125,12 +137,20 @@ void attn_prefill_mfma(PrefillArgs a) {
     const int gq = lane & 15, quad = lane >> 4;
     const int G = a.group;
 
-    const int r0 = a.q_start[s], r1 = a.q_start[s + 1];
+    // Everything that depends on the sequence alone is read at once (scalar loads, all in
+    // flight together): the query range, the context length and the block ids of the
+    // first four tiles (clamped to the table row; ids past the context are never used).
+    // The first K/V loads then wait for one memory round trip, not three.
+    const int32_t* trow = a.block_tables + (int64_t)s * a.max_blocks_per_seq;
+    const int r0 = sload(a.q_start, s), r1 = sload(a.q_start, s + 1);
+    const int ctx = sload(a.context_lens, s);
+    int32_t id0[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) id0[i] = BS == 1 ? 0 : sload(trow, min(i / TPB, a.max_blocks_per_seq - 1));
     const int n = r1 - r0;
     if (n < 0 || n > a.max_q_len) return;          // unusable query range: rows unknown
     const int t_begin = qt * a.tokens_per_wg;
     if (t_begin >= n) return;
-    const int ctx = a.context_lens[s];
     const int t_end = min(n, t_begin + a.tokens_per_wg);
     // this wave's rows: w*RW .. w*RW + RW - 1 of the workgroup, row = token * G + head
     const int row0 = w * RW;
@@ -180,7 +200,6 @@ void attn_prefill_mfma(PrefillArgs a) {
     const uint16_t* vbase = static_cast<const uint16_t*>(a.v_pool) + (int64_t)g * TILE;
     const int64_t blk_stride = (int64_t)a.num_kv_heads * TILE;
     const int voff = gq * 4 + quad;
-    const int32_t* trow = a.block_tables + (int64_t)s * a.max_blocks_per_seq;
 
     f32x4 acc[C][MT];
     float m[C], lsum[C];
@@ -217,6 +236,21 @@ void attn_prefill_mfma(PrefillArgs a) {
     // block ids of pair j's tiles (the second may lie past the wave's keys: then it
     // repeats the last tile, its V is zeroed and its scores masked, since its keys are
     // past every row's position); block size 1: the lane's own token's block
+    auto check_bid = [&](int32_t b) __attribute__((always_inline)) {
+        if ((uint32_t)b >= (uint32_t)a.num_blocks) {
+            bad_block = true;
+            b = 0;
+        }
+        return b;
+    };
+    // pairs 0 and 1 (tiles 0..3) from the ids read at the start
+    auto first_bids = [&](int j, int32_t (&bid)[2]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int it = min(2 * j + h, ntiles - 1);
+            bid[h] = check_bid(it == 0 ? id0[0] : it == 1 ? id0[1] : it == 2 ? id0[2] : id0[3]);
+        }
+    };
     auto pair_bids = [&](int j, int32_t (&bid)[2]) __attribute__((always_inline)) {
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
@@ -226,12 +260,7 @@ void attn_prefill_mfma(PrefillArgs a) {
                 bid[h] = lane_block_bs1(trow, it, ctx, a.num_blocks, lane, bad);
                 bad_block |= bad;
             } else {
-                int32_t b = sload(trow, it / TPB);
-                if ((uint32_t)b >= (uint32_t)a.num_blocks) {
-                    bad_block = true;
-                    b = 0;
-                }
-                bid[h] = b;
+                bid[h] = check_bid(sload(trow, it / TPB));
             }
         }
     };
@@ -409,10 +438,15 @@ void attn_prefill_mfma(PrefillArgs a) {
     VPair vA, vB;
     int32_t bid_v[2], bid_k[2], bid_n[2];
     f32x4 S[C][2];
-    pair_bids(0, bid_n);
+    if constexpr (BS == 1) {
+        pair_bids(0, bid_n);
+        pair_bids(min(1, npairs - 1), bid_v);
+    } else {
+        first_bids(0, bid_n);
+        first_bids(min(1, npairs - 1), bid_v);
+    }
     load_k(0, bid_n, kA);
     load_v(0, bid_n, vA);
-    pair_bids(min(1, npairs - 1), bid_v);
     load_k(min(1, npairs - 1), bid_v, kB);
     pair_bids(min(2, npairs - 1), bid_k);
     scores(kA, S);
@@ -471,11 +505,12 @@ void attn_prefill_mfma(PrefillArgs a) {
         if (!live[b]) continue;
         const int64_t ob = ((int64_t)(r0 + tok[b]) * a.num_q_heads + head[b]) * D;
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
+        for (int mt = 0; mt < MT; ++mt) {
+            f32x4 v;
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
-                store_out<OUT_DT>(a.out, ob + 16 * mt + 4 * quad + r,
-                                  bad_block ? NAN : acc[b][mt][r] * inv);
+            for (int r = 0; r < 4; ++r) v[r] = bad_block ? NAN : acc[b][mt][r] * inv;
+            store_out4<OUT_DT>(a.out, ob + 16 * mt + 4 * quad, v);
+        }
     }
 }
 
@@ -564,9 +599,9 @@ paged_kv_status paged_attention_prefill(const paged_kv_pool_desc* desc, void* ou
         pkv::set_error("null pointer argument");
         return PAGED_KV_ERR_INVALID_ARG;
     }
-    if ((reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(k_pool) |
-         reinterpret_cast<uintptr_t>(v_pool)) & 15) {
-        pkv::set_error("q and pools must be 16-byte aligned");
+    if ((reinterpret_cast<uintptr_t>(out) | reinterpret_cast<uintptr_t>(q) |
+         reinterpret_cast<uintptr_t>(k_pool) | reinterpret_cast<uintptr_t>(v_pool)) & 15) {
+        pkv::set_error("out, q and pools must be 16-byte aligned");
         return PAGED_KV_ERR_INVALID_ARG;
     }
     PrefillArgs a;

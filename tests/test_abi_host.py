@@ -340,6 +340,7 @@ def test_prefill_validation_without_gpu():
     good = B.make_desc(64, 16, 2, 128, "bf16")
     for kw in [dict(max_q_len=65), dict(max_context_len=65), dict(num_q_heads=7),
                dict(out_dtype="f16"), dict(q=_FakeTensor((10, 8, 128), addr=4098)),
+               dict(out=_FakeTensor((10, 8, 128), addr=4104)),                # misaligned out
                dict(scale=0.0), dict(scale=-0.1)]:
         with pytest.raises(B.PagedKVError):
             pre(good, **kw)
