@@ -53,8 +53,20 @@ def test_full_size_configs(k):
     """Full sizes, in the launch configuration the bench times (the workload's own
     partition setting: stream-K, or 512-token partitions for the long-context one):
     whole pools bit-exact, attention on sampled sequences."""
+    _full_size(k, 16, None)
+
+
+@pytest.mark.parametrize("bs,d", [(1, None), (32, None), (16, 64), (16, 256)],
+                         ids=["bs1", "bs32", "d64", "d256"])
+def test_full_size_block_and_head_sizes(bs, d):
+    """The GQA workload's lengths at the other block and head sizes the bench measures
+    (`--block-size`, `--head-dim`), at full size: pools bit-exact, sampled sequences."""
+    _full_size(3, bs, d)
+
+
+def _full_size(k, bs, d):
     from paged_kv_cache_15_amd.replay import run_workload
-    w = W.make_config(k)
+    w = W.make_config(k, block_size=bs, head_dim=d)
     say(f"[parity-full] config {k} {w.name}")
     g = run_workload(w, "cuda", out_dtype="f32")
     torch.cuda.synchronize()

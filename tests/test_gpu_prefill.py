@@ -62,14 +62,18 @@ def test_prefill_small_configs(k):
     g.cache.close()
 
 
-@pytest.mark.parametrize("k", [1, 2])
-def test_prefill_full_size_sampled(k):
-    """Full sizes as the bench runs them: every output finite, pools bit-exact, and the
-    oracle on sampled query rows (first, middle and last query of three sequences; a
-    query at position p is the oracle's prefill of a one-token chunk over p + 1 tokens)."""
+@pytest.mark.parametrize("k,bs,d", [(1, 16, 128), (2, 16, 128), (1, 32, 128), (1, 1, 128),
+                                    (1, 16, 64), (1, 16, 256)],
+                         ids=["whole", "chunked", "whole-bs32", "whole-bs1", "whole-d64",
+                              "whole-d256"])
+def test_prefill_full_size_sampled(k, bs, d):
+    """Full sizes as the bench runs them (also at the block and head sizes it measures):
+    every output finite, pools bit-exact, and the oracle on sampled query rows (first,
+    middle and last query of three sequences; a query at position p is the oracle's
+    prefill of a one-token chunk over p + 1 tokens)."""
     from oracle.attention import paged_prefill
     from oracle import lowp
-    w = W.make_prefill_config(k)
+    w = W.make_prefill_config(k, block_size=bs, head_dim=d)
     say(f"[prefill-full] {w.name}")
     g = _run(w, "f32")
     o = oreplay.run(w, compute_attention=False)
