@@ -229,7 +229,10 @@ def decode_graph_timing(layers=32, reps=20):
     keys = [to_device(rng.standard_normal((sum(lens), 8, 128)).astype(np.float32), "bf16", "cuda")] * layers
     kv.append(seqs, lens, keys, keys)
     mx = max(lens) + 1
-    st = DecodeStep(kv, len(lens), 64, (mx + 15) // 16, mx, 1 / np.sqrt(128.0), 0, "bf16")
+    from paged_kv_cache_15_amd import binding as B
+    pt = B.paged_attention_auto_partition_tokens(kv.desc, len(lens), 64, mx)
+    st = DecodeStep(kv, len(lens), 64, (mx + 15) // 16, mx, 1 / np.sqrt(128.0), B.PARTITION_AUTO,
+                    "bf16")
     nk = to_device(rng.standard_normal((layers, len(lens), 8, 128)).astype(np.float32), "bf16", "cuda")
     q = to_device(rng.standard_normal((layers, len(lens), 64, 128)).astype(np.float32), "bf16", "cuda")
     st.set_step(seqs, nk, nk, q)
@@ -247,7 +250,8 @@ def decode_graph_timing(layers=32, reps=20):
         torch.cuda.synchronize()
         res[name] = e0.elapsed_time(e1) * 1e3 / reps
     kv.close()
-    return {"layers": layers, "batch": len(lens), "launches_per_step": 2 * layers,
+    return {"layers": layers, "batch": len(lens), "partition_tokens": pt,
+            "launches_per_step": (2 if pt == 0 else 3) * layers,
             "eager_us_per_step": round(res["eager"], 1), "graph_us_per_step": round(res["graph"], 1)}
 
 

@@ -242,6 +242,22 @@ paged_kv_status reshape_and_cache(const paged_kv_pool_desc* desc, const void* ke
                                   void* k_pool, void* v_pool, const int32_t* slot_mapping,
                                   int32_t num_tokens, void* stream);
 
+/* partition_tokens value that lets the library pick the schedule for the batch shape
+ * (paged_attention_auto_partition_tokens). */
+#define PAGED_KV_PARTITION_AUTO (-1)
+
+/* The schedule PAGED_KV_PARTITION_AUTO picks, as a partition_tokens value: 0 (stream-K)
+ * when the batch has at least 65536 (sequence, head unit, 16-token tile) tiles on the
+ * bound max_context_len (64 per wave slot of the chip), else fixed partitions: 512
+ * tokens when that gives at least 256 (sequence, head unit, partition) workgroups, one
+ * per compute unit, else 256.  A head unit is a KV head for the MFMA kernels (fp16/bf16
+ * with 2 to 16 query heads per KV head) and a query head otherwise.  Small batches go
+ * to fixed partitions because stream-K then has few tiles per wave and merges many
+ * pieces per unit at the end of the launch.  Depends on the arguments only (no device
+ * state), so workspace sizing and the launches agree.  -1 if an argument is invalid. */
+int32_t paged_attention_auto_partition_tokens(const paged_kv_pool_desc* desc, int32_t num_seqs,
+                                              int32_t num_q_heads, int32_t max_context_len);
+
 /* Bytes of workspace paged_attention_decode needs for this batch shape and pool (0 when
  * nothing needs merging).  Same partition_tokens convention as paged_attention_decode.
  * 0 if an argument is invalid. */
@@ -269,7 +285,9 @@ size_t paged_attention_workspace_bytes(const paged_kv_pool_desc* desc, int32_t n
  *                 sequence's head unit cut by those splits are merged by log-sum-exp
  *                 (used for up to 8192 sequences; larger batches fall back to 512-token
  *                 partitions).  > 0: fixed split-K partitions of that many tokens
- *                 (multiple of 16), merged the same way.
+ *                 (multiple of 16), merged the same way.  PAGED_KV_PARTITION_AUTO (-1):
+ *                 the value paged_attention_auto_partition_tokens returns for the same
+ *                 arguments.  Other negative values: INVALID_ARG.
  *   workspace     device buffer of paged_attention_workspace_bytes(...) bytes (may be
  *                 NULL when that is 0).  Zero-fill it once before its first use (e.g.
  *                 hipMemsetAsync): the stream-K schedule keeps per-(sequence, head unit)

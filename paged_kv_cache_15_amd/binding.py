@@ -81,6 +81,7 @@ _SIGNATURES = {
     "paged_kv_prefix_stats": (ctypes.c_int, [_vp, _i64p, _i64p, _i64p]),
     "paged_kv_copy_blocks": (ctypes.c_int, [_descp, _vp, _vp, _vp, _i32, _vp]),
     "reshape_and_cache": (ctypes.c_int, [_descp, _vp, _vp, _i64, _i64, _vp, _vp, _vp, _i32, _vp]),
+    "paged_attention_auto_partition_tokens": (_i32, [_descp, _i32, _i32, _i32]),
     "paged_attention_workspace_bytes": (_sz, [_descp, _i32, _i32, _i32, _i32]),
     "paged_attention_decode": (ctypes.c_int, [_descp, _vp, _i32, _vp, _vp, _vp, _vp, _i32, _vp,
                                               _i32, _i32, _i32, _f32, _i32, _vp, _sz, _vp]),
@@ -335,6 +336,15 @@ def reshape_and_cache(desc, key, value, k_pool, v_pool, slot_mapping, num_tokens
            lib.reshape_and_cache(ctypes.byref(desc), _ptr(key), _ptr(value), int(key_stride),
                                  int(value_stride), _ptr(k_pool), _ptr(v_pool), _ptr(slot_mapping),
                                  int(num_tokens), _stream(stream)))
+
+
+PARTITION_AUTO = -1
+
+
+def paged_attention_auto_partition_tokens(desc, num_seqs, num_q_heads, max_context_len):
+    """The partition_tokens value PARTITION_AUTO resolves to (0 = stream-K), -1 if invalid."""
+    return int(lib.paged_attention_auto_partition_tokens(ctypes.byref(desc), num_seqs,
+                                                         num_q_heads, max_context_len))
 
 
 def paged_attention_workspace_bytes(desc, num_seqs, num_q_heads, max_context_len,

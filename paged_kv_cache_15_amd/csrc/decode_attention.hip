@@ -681,6 +681,22 @@ bool use_streamk(int32_t part_tokens, int32_t num_seqs) {
     return part_tokens == 0 && num_seqs <= pkv::kStreamMaxSeqs;
 }
 
+// The automatic schedule (PAGED_KV_PARTITION_AUTO).  Measured on MI355X with 32-layer
+// decode steps of 64 query / 8 KV heads, contexts 256..2048: stream-K took 25-30 us a
+// layer for 1-8 sequences and 47.5 for 32, fixed partitions 13.5-19.6 and 43.5 (256
+// tokens best up to 4 sequences, 512 from 8); on the 128-sequence GQA workload stream-K
+// is the faster one.
+constexpr int64_t kAutoStreamTiles = 65536;     // 64 tiles per wave slot of the chip
+constexpr int64_t kAutoMinWorkgroups = 256;     // one per compute unit
+
+int32_t auto_partition_tokens(const paged_kv_pool_desc* desc, int32_t num_seqs, int32_t hq,
+                              int32_t max_ctx) {
+    const bool mfma = desc->dtype != PAGED_KV_F32 && hq / desc->num_kv_heads >= 2;
+    const int64_t units = (int64_t)num_seqs * (mfma ? desc->num_kv_heads : hq);
+    if (units * ((max_ctx + kTile - 1) / kTile) >= kAutoStreamTiles) return 0;
+    return units * ((max_ctx + 511) / 512) >= kAutoMinWorkgroups ? 512 : 256;
+}
+
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 size_t workspace_for(int64_t num_seqs, int64_t hq, int64_t d, int64_t max_parts) {
@@ -714,6 +730,7 @@ paged_kv_status make_plan(Plan& pl, const paged_kv_pool_desc* desc, void* out, i
         return PAGED_KV_ERR_INVALID_ARG;
     }
     if (max_ctx < 1) { pkv::set_error("max_context_len must be >= 1"); return PAGED_KV_ERR_INVALID_ARG; }
+    if (part_tokens == PAGED_KV_PARTITION_AUTO) part_tokens = auto_partition_tokens(desc, num_seqs, hq, max_ctx);
     pl.streamk = use_streamk(part_tokens, num_seqs);
     if (part_tokens == 0) part_tokens = pkv::kDefaultPartitionTokens;
     if (part_tokens < 0 || part_tokens % kTile) {
@@ -853,12 +870,22 @@ paged_kv_status launch_status(const char* what) {
 
 extern "C" {
 
+int32_t paged_attention_auto_partition_tokens(const paged_kv_pool_desc* desc, int32_t num_seqs,
+                                              int32_t num_q_heads, int32_t max_context_len) {
+    if (!pkv::valid_desc(desc) || num_seqs < 0 || num_q_heads < 1 || max_context_len < 1 ||
+        num_q_heads % desc->num_kv_heads)
+        return -1;
+    return auto_partition_tokens(desc, num_seqs, num_q_heads, max_context_len);
+}
+
 size_t paged_attention_workspace_bytes(const paged_kv_pool_desc* desc, int32_t num_seqs,
                                        int32_t num_q_heads, int32_t max_context_len,
                                        int32_t partition_tokens) {
     if (!pkv::valid_desc(desc) || num_seqs < 0 || num_q_heads < 1 || max_context_len < 1 ||
-        partition_tokens < 0 || num_q_heads % desc->num_kv_heads)
+        partition_tokens < PAGED_KV_PARTITION_AUTO || num_q_heads % desc->num_kv_heads)
         return 0;
+    if (partition_tokens == PAGED_KV_PARTITION_AUTO)
+        partition_tokens = auto_partition_tokens(desc, num_seqs, num_q_heads, max_context_len);
     if (use_streamk(partition_tokens, num_seqs)) {
         bool ok = false;
         pkv::StreamPlan p = pkv::stream_plan(num_seqs, num_q_heads, desc->num_kv_heads, desc->dtype,

@@ -64,10 +64,11 @@ class LayeredKV:
 class DecodeStep:
     """One decode step (one new token per sequence) over all layers, eager or replayed
     from a HIP graph.  Shapes are fixed at construction: num_seqs rows, block tables
-    max_blocks wide, attention sized for max_context_len."""
+    max_blocks wide, attention sized for max_context_len.  partition_tokens as for
+    paged_attention_decode; by default the library picks the schedule for the shape."""
 
     def __init__(self, kv: LayeredKV, num_seqs, num_q_heads, max_blocks, max_context_len, scale,
-                 partition_tokens=0, out_dtype=None):
+                 partition_tokens=B.PARTITION_AUTO, out_dtype=None):
         self.kv = kv
         self.B, self.hq = num_seqs, num_q_heads
         self.max_blocks, self.max_ctx = max_blocks, max_context_len

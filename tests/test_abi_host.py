@@ -323,6 +323,36 @@ def test_device_op_validation_without_gpu():
     assert B.paged_attention_workspace_bytes(good, 2, 7, 64, 0) == 0     # 7 % 2 != 0
 
 
+def test_automatic_schedule_choice_without_gpu():
+    """PARTITION_AUTO: stream-K from 65536 tiles on the bound, else 512-token partitions
+    when they give at least 256 workgroups, else 256; workspace sizing resolves it the
+    same way; other negative values are rejected."""
+    auto = B.paged_attention_auto_partition_tokens
+    gqa = B.make_desc(64, 16, 8, 128, "bf16")          # MFMA kernels: unit = KV head
+    assert auto(gqa, 128, 64, 8192) == 0               # 128*8 units x 512 tiles
+    assert auto(gqa, 8, 64, 8192) == 512               # 64 units x 512 tiles = 32768
+    assert auto(gqa, 16, 64, 8192) == 0                # 128 x 512 = 65536
+    assert auto(gqa, 8, 64, 2049) == 512               # 64 units x 129 tiles; 64 x 5 >= 256
+    assert auto(gqa, 4, 64, 2049) == 256               # 32 x 5 = 160 workgroups: 256 tokens
+    assert auto(gqa, 1, 64, 2049) == 256
+    assert auto(gqa, 32, 64, 2049) == 512              # 256 x 129 = 33024 tiles
+    assert auto(gqa, 64, 64, 2048) == 0                # 512 x 128 = 65536 tiles
+    mha = B.make_desc(64, 16, 32, 128, "f16")          # group 1: VALU, unit = query head
+    assert auto(mha, 64, 32, 4096) == 0
+    assert auto(mha, 2, 32, 1024) == 256               # 64 units x 64 tiles; 64 x 2 < 256
+    f32 = B.make_desc(64, 16, 4, 64, "f32")            # fp32: VALU, unit = query head
+    assert auto(f32, 4, 16, 100) == 256
+    assert auto(gqa, 2, 7, 64) == -1                   # invalid: 7 % 8
+    for args in [(gqa, 8, 64, 2049), (gqa, 128, 64, 8192), (gqa, 1, 64, 300), (mha, 3, 32, 700)]:
+        pt = auto(*args)
+        assert B.paged_attention_workspace_bytes(*args, B.PARTITION_AUTO) == \
+            B.paged_attention_workspace_bytes(*args, pt)
+    assert B.paged_attention_workspace_bytes(gqa, 8, 64, 2049, -2) == 0
+    with pytest.raises(B.PagedKVError) as e:
+        _attn(B.make_desc(64, 16, 2, 128, "bf16"), partition_tokens=-2)
+    assert e.value.status == B.PAGED_KV_ERR_INVALID_ARG
+
+
 def test_prefill_validation_without_gpu():
     def pre(desc, **kw):
         args = dict(out=_FakeTensor((10, 8, 128)), out_dtype="f32", q=_FakeTensor((10, 8, 128)),

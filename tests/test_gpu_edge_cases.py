@@ -332,3 +332,40 @@ def test_stream_k_batch_limit_and_fallback(shape):
         err = assert_close(g.outputs[0], o.outputs[0], dt, "f32")
         say(f"   max|err| {err:.3e}")
         g.cache.close()
+
+
+@pytest.mark.parametrize("nseq,ctx_hi", [(1, 2000), (8, 2000), (40, 2000), (80, 2000)],
+                         ids=["1seq", "8seq", "40seq", "80seq"])
+def test_automatic_schedule_is_the_schedule_it_names(nseq, ctx_hi):
+    """PARTITION_AUTO gives bit for bit the result of the partition_tokens value it
+    resolves to (256/512-token partitions for small batches, stream-K for large ones),
+    and that result matches the oracle."""
+    from paged_kv_cache_15_amd import binding as B
+    from paged_kv_cache_15_amd.cache import PagedKVCache
+    from paged_kv_cache_15_amd.replay import to_device
+    from oracle.attention import dense_decode
+    rng = np.random.default_rng(nseq)
+    lens = rng.integers(1, ctx_hi + 1, nseq).tolist()
+    hq, hkv, d, dt = 64, 8, 128, "bf16"
+    c = PagedKVCache(sum((n + 15) // 16 for n in lens) + 8, hkv, d, dt, 16,
+                     rng.permutation(sum((n + 15) // 16 for n in lens) + 8).astype(np.int32))
+    seqs = [c.create() for _ in lens]
+    kv = rng.standard_normal((2, sum(lens), hkv, d)).astype(np.float32)
+    c.append(seqs, lens, to_device(kv[0], dt, "cuda"), to_device(kv[1], dt, "cuda"))
+    q = rng.standard_normal((nseq, hq, d)).astype(np.float32)
+    qd = to_device(q, dt, "cuda")
+    pt = B.paged_attention_auto_partition_tokens(c.desc, nseq, hq, max(lens))
+    say(f"[auto] {nseq} sequences up to {max(lens)} tokens -> partition_tokens {pt}")
+    a, _, _ = c.attend(seqs, qd, 0.088, "f32", partition_tokens=B.PARTITION_AUTO)
+    b, _, _ = c.attend(seqs, qd, 0.088, "f32", partition_tokens=pt)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+    # the oracle's dense decode on the same rounded inputs (gathered by position, not
+    # through the pool), for three sequences
+    qb = lowp.storage_bits_to_f64(lowp.to_storage_bits(q, dt), dt)
+    kb = lowp.storage_bits_to_f64(lowp.to_storage_bits(kv, dt), dt)
+    starts = np.concatenate([[0], np.cumsum(lens)])
+    for s in sorted({0, nseq - 1, int(np.argmax(lens))}):
+        ref = dense_decode(qb[s], kb[0, starts[s]:starts[s + 1]], kb[1, starts[s]:starts[s + 1]], 0.088)
+        assert np.abs(a[s].double().cpu().numpy() - ref).max() <= TOL[dt]
+    c.close()

@@ -16,7 +16,7 @@ def _bits(x, dt):
     return lowp.storage_bits_to_f64(lowp.to_storage_bits(x, dt), dt)
 
 
-@pytest.mark.parametrize("pt", [0, 512], ids=["streamk", "pt512"])
+@pytest.mark.parametrize("pt", [0, 512, -1], ids=["streamk", "pt512", "auto"])
 def test_decode_step_graph_matches_eager_bitwise(pt):
     from paged_kv_cache_15_amd.graph import LayeredKV, DecodeStep
     from paged_kv_cache_15_amd.replay import to_device
