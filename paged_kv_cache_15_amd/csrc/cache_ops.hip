@@ -35,14 +35,16 @@ __global__ __launch_bounds__(256) void reshape_and_cache_kernel(
     const int32_t t = (int32_t)(idx / per_token);
     const int32_t r = (int32_t)(idx - (int64_t)t * per_token);
     const int32_t h = r / chunks, c = r - h * chunks;
+    // the token's chunks do not depend on its slot: all three loads are in flight together
     const int32_t slot = slot_mapping[t];
+    const i32x4 kc = *reinterpret_cast<const i32x4*>(key + t * key_stride + (int64_t)h * head_dim + c * X);
+    const i32x4 vc = *reinterpret_cast<const i32x4*>(value + t * value_stride + (int64_t)h * head_dim + c * X);
+    // (an empty use keeps the compiler from sinking the two loads below the slot test)
+    asm volatile("" ::"v"(kc), "v"(vc));
     if (slot < 0 || (int64_t)slot >= num_slots) return;
     constexpr int TB = BS < 16 ? BS : 16;   // tokens per sub-block
     const int64_t blk = slot / BS;
     const int32_t sub = (slot % BS) / TB, off = slot % TB;
-
-    const i32x4 kc = *reinterpret_cast<const i32x4*>(key + t * key_stride + (int64_t)h * head_dim + c * X);
-    const i32x4 vc = *reinterpret_cast<const i32x4*>(value + t * value_stride + (int64_t)h * head_dim + c * X);
 
     const int64_t region = (blk * kv_heads + h) * (BS / TB) + sub;   // (block, head, sub-block)
     T* kdst = k_pool + ((region * chunks + c) * TB + off) * X;
