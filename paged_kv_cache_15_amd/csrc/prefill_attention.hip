@@ -14,7 +14,7 @@
 //
 // Work decomposition.  A workgroup of 4 waves takes one KV head g of one sequence and
 // a run of TQ query tokens; its rows are (token, query head of g's group) pairs,
-// token-major, 64*C rows in all (C = 256 / head_dim column blocks of 16 rows per
+// token-major, 64*C rows in all (C = prefill_blocks column blocks of 16 rows per
 // wave), so each K/V tile a wave loads serves 16*C query rows.  Every wave streams the
 // keys 0 .. (largest position among its rows) in 16-token tiles straight from the pool
 // into MFMA operands, with the decode kernels' orientation: S^T = K . Q^T
@@ -101,12 +101,14 @@ __device__ __forceinline__ void store_out4(void* out, int64_t i, f32x4 v) {
     }
 }
 
-// C: 16-row column blocks per wave.  Twice as many would halve the K/V loads per query
-// row, but the compiler then needs more than the 512 registers of a wave and spills.
-// (Sharing each tile pair among the workgroup's four waves through LDS, with 3 or 4
-// blocks per wave, measured slower: 363-430 against 459-484 TFLOP/s.)
+// C: 16-row column blocks per wave: every K/V load serves 16*C query rows, so more
+// blocks mean fewer loads per row (the load path bounds the kernel), up to the 512
+// registers of a wave.  Three at head_dim 128 fill them (one 16-byte reload from scratch
+// per tile pair remains) and beat two by 2-17% across the workloads; four at 64 and one
+// at 256.  (Sharing each tile pair among the workgroup's four waves through LDS, with 3
+// or 4 blocks per wave, measured slower: 363-430 against 459-484 TFLOP/s.)
 template <int D>
-constexpr int prefill_blocks() { return 256 / D; }
+constexpr int prefill_blocks() { return D == 128 ? 3 : 256 / D; }
 
 template <int D, int DT, int OUT_DT, int BS>
 __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(1)))
@@ -159,24 +161,34 @@ void attn_prefill_mfma(PrefillArgs a) {
     const bool bad_len = ctx < 1 || ctx > a.max_context_len || n > ctx;
 
     // per block b: this lane's row, its token, head and position
-    int tok[C], head[C], pos[C];
-    bool live[C];
+    // (recomputed where needed rather than held: at three blocks per wave every register
+    // counts)
+    auto row_info = [&](int b, bool& live, int& tok, int& head) __attribute__((always_inline)) {
+        const int r = row0 + 16 * b + gq;
+        live = r < valid_rows;
+        const int rr = live ? r : valid_rows - 1;       // padded rows repeat the last one
+        tok = t_begin + rr / G;
+        head = g * G + rr % G;
+    };
+    int pos[C];
 #pragma unroll
     for (int b = 0; b < C; ++b) {
-        const int r = row0 + 16 * b + gq;
-        live[b] = r < valid_rows;
-        const int rr = live[b] ? r : valid_rows - 1;    // padded rows repeat the last one
-        tok[b] = t_begin + rr / G;
-        head[b] = g * G + rr % G;
-        pos[b] = ctx - n + tok[b];
+        bool live;
+        int tok, head;
+        row_info(b, live, tok, head);
+        pos[b] = ctx - n + tok;
     }
     if (bad_len) {
 #pragma unroll
-        for (int b = 0; b < C; ++b)
-            if (live[b])
+        for (int b = 0; b < C; ++b) {
+            bool live;
+            int tok, head;
+            row_info(b, live, tok, head);
+            if (live)
                 for (int e = 0; e < D / 4; ++e)
-                    store_out<OUT_DT>(a.out, ((int64_t)(r0 + tok[b]) * a.num_q_heads + head[b]) * D +
+                    store_out<OUT_DT>(a.out, ((int64_t)(r0 + tok) * a.num_q_heads + head) * D +
                                                  4 * quad + 16 * (e / 4) + e % 4, NAN);
+        }
         return;
     }
     // keys this wave needs: up to the position of its last valid row
@@ -189,8 +201,11 @@ void attn_prefill_mfma(PrefillArgs a) {
     kvec qop[C][KI];
 #pragma unroll
     for (int b = 0; b < C; ++b) {
+        bool live;
+        int tok, head;
+        row_info(b, live, tok, head);
         const uint16_t* qh = static_cast<const uint16_t*>(a.q) +
-                             ((int64_t)(r0 + tok[b]) * a.num_q_heads + head[b]) * D + 8 * quad;
+                             ((int64_t)(r0 + tok) * a.num_q_heads + head) * D + 8 * quad;
 #pragma unroll
         for (int kk = 0; kk < KI; ++kk)
             qop[b][kk] = __builtin_bit_cast(kvec, *reinterpret_cast<const i32x4*>(qh + 32 * kk));
@@ -502,8 +517,11 @@ void attn_prefill_mfma(PrefillArgs a) {
     for (int b = 0; b < C; ++b) {
         const float lw = sum_across_quads(lsum[b]);
         const float inv = 1.f / lw;
-        if (!live[b]) continue;
-        const int64_t ob = ((int64_t)(r0 + tok[b]) * a.num_q_heads + head[b]) * D;
+        bool live;
+        int tok, head;
+        row_info(b, live, tok, head);
+        if (!live) continue;
+        const int64_t ob = ((int64_t)(r0 + tok) * a.num_q_heads + head) * D;
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
             f32x4 v;
@@ -538,7 +556,11 @@ void launch_bs(const PrefillArgs& a, int bs, int dtype, int out_dtype, dim3 grid
     else launch_dt<D, 16>(a, dtype, out_dtype, grid, st);
 }
 
-int tokens_per_workgroup(int head_dim, int group) { return 4 * 16 * (256 / head_dim) / group; }
+int tokens_per_workgroup(int head_dim, int group) {
+    const int blocks = head_dim == 64 ? prefill_blocks<64>() : head_dim == 256 ? prefill_blocks<256>()
+                                                                              : prefill_blocks<128>();
+    return 4 * 16 * blocks / group;
+}
 
 paged_kv_status launch_status(const char* what) {
     hipError_t e = hipGetLastError();
