@@ -27,9 +27,9 @@
 // pipelined: the score products of pair j+1 are issued together with the weights and
 // value products of pair j, so the matrix cores and the vector ALU work side by side,
 // and the pairs that need neither the mask nor any clearing of slots past the context
-// run a branch-free step.  The query tiles of
-// one (sequence, KV head) run on one XCD, one after the other, the last (most keys)
-// first, so the K/V they all read stays in that XCD's L2.
+// run a branch-free step.  The query tiles of one (sequence, KV head) run on one XCD,
+// one after the other, the last (most keys) first, so the K/V they all read stays in
+// that XCD's L2.
 //
 // Block sizes 16 and 32 (a 32-token block is two 16-token sub-blocks in the pool), and 1
 // (each lane loads from its own token's block; V, token-major at that size, reaches the
