@@ -357,8 +357,8 @@ def main():
         return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
-              "(the path shards by sequence or KV head with no exchange, but this build "
-              "measures a single MI355X)", file=sys.stderr)
+              "(the path shards by sequence or KV head with no exchange; what is measured "
+              "is one MI355X)", file=sys.stderr)
         sys.exit(2)
     if args.prefill:
         res = prefill_timing(args.prefill, args.steps, args.warmup, args.block_size,

@@ -55,7 +55,7 @@ typedef enum {
     PAGED_KV_OK = 0,
     PAGED_KV_ERR_INVALID_ARG = 1,     /* null pointer, bad size, unsupported shape value */
     PAGED_KV_ERR_OUT_OF_BLOCKS = 2,   /* the free queue cannot supply the blocks needed */
-    PAGED_KV_ERR_UNSUPPORTED = 3,     /* valid request this build has no kernel for */
+    PAGED_KV_ERR_UNSUPPORTED = 3,     /* valid request the library has no kernel for */
     PAGED_KV_ERR_HIP = 4,             /* a HIP runtime call failed */
     PAGED_KV_ERR_NO_SUCH_SEQ = 5,     /* unknown or released sequence id */
     PAGED_KV_ERR_BUFFER_TOO_SMALL = 6 /* caller buffer (copies list, workspace) too small */
