@@ -289,10 +289,14 @@ size_t paged_attention_workspace_bytes(const paged_kv_pool_desc* desc, int32_t n
  *                 the value paged_attention_auto_partition_tokens returns for the same
  *                 arguments.  Other negative values: INVALID_ARG.
  *   workspace     device buffer of paged_attention_workspace_bytes(...) bytes (may be
- *                 NULL when that is 0).  Zero-fill it once before its first use (e.g.
- *                 hipMemsetAsync): the stream-K schedule keeps per-(sequence, head unit)
- *                 merge counters in it, and every call leaves them at zero again.  The
- *                 rest is scratch.  Calls sharing one workspace must not overlap.
+ *                 NULL when that is 0).  Zero-fill it before its first use (e.g.
+ *                 hipMemsetAsync): the stream-K schedule keeps one merge counter per
+ *                 (sequence, head unit) at its start, and every call leaves them at
+ *                 zero again; the rest is scratch.  So a workspace can be reused without zero-filling again as
+ *                 long as no call has more counters (num_seqs x head units; a head unit
+ *                 is a KV head for fp16/bf16 with 2..16 query heads per KV head, else a
+ *                 query head) than a call made on it since the last zero-fill.  Calls
+ *                 sharing one workspace must not overlap.
  * A sequence whose context_len is outside [1, max_context_len], or whose table holds
  * an id outside [0, num_blocks) below its length, gets NaN outputs; nothing outside
  * the buffers is read.  Requires block_size 1, 16 or 32, head_dim 64, 128 or 256,

@@ -44,6 +44,24 @@ __device__ __forceinline__ uint16_t f32_to_bits16(float f) {
     else return __builtin_bit_cast(uint16_t, (_Float16)f);
 }
 
+// Partial results that another workgroup of the same launch merges may cross XCDs,
+// whose L2 caches are not kept coherent with each other inside a kernel.  They are
+// written and read with agent-scope relaxed atomics, which the compiler emits as
+// write-through stores and coherent loads (sc1); publishing them then only needs the
+// stores to have completed before a counter is bumped.  (An agent-scope release fence
+// would instead write back the XCD's whole L2, and such write-backs serialise across
+// the thousands of partial results of one launch.)
+__device__ __forceinline__ void put_coherent(float* p, float v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float get_coherent(const float* p) {
+    return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// Every vector memory operation this wave issued has completed (vmcnt counts stores
+// too on this architecture); the clobber keeps the compiler from moving memory
+// operations across it.
+__device__ __forceinline__ void wait_memory_done() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
 template <int OUT_DT>
 __device__ __forceinline__ void store_out(void* out, int64_t i, float v) {
     if constexpr (OUT_DT == DT_F32) static_cast<float*>(out)[i] = v;

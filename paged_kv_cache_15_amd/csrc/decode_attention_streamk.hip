@@ -209,19 +209,11 @@ __device__ __forceinline__ int unit_pieces(const SliceMap& sm, int64_t ta, int n
 }
 
 // Pieces cross XCDs, whose L2 caches are not kept coherent with each other inside a
-// kernel.  They are written and read with agent-scope relaxed atomics, which the
-// compiler emits as write-through stores and coherent loads (sc1), so publishing a
-// piece only needs its stores to have completed before the counter is bumped.  An
-// agent-scope release fence would instead write back the XCD's whole L2, and those
-// write-backs serialise across the thousands of pieces of one launch.
+// kernel: they are written and read with put_coherent / get_coherent (see
+// attention_common.h), so publishing a piece only needs its stores to have completed
+// before the counter is bumped.
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 constexpr int kPolicySc1 = 1 << 4;   // cache-policy operand bit of sc1 on gfx94x/gfx950
-__device__ __forceinline__ void put_coherent(float* p, float v) {
-    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ float get_coherent(const float* p) {
-    return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
 // 16-byte form of put_coherent for a wave-uniform region of `bytes` bytes at `base`
 // (a buffer store with the same sc1 policy); lanes whose offset falls outside the
 // region write nothing (the buffer's range check drops them).
@@ -232,10 +224,6 @@ __device__ __forceinline__ void put_coherent4(float* base, uint32_t bytes, uint3
     __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, v), r, off_bytes, 0,
                                            kPolicySc1);
 }
-// Every vector memory operation this wave issued has completed (vmcnt counts stores
-// too on this architecture); the clobber keeps the compiler from moving memory
-// operations across it.
-__device__ __forceinline__ void wait_memory_done() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 // Log-sum-exp merge of all pieces of unit q (written by waves jf..jl; empty slices wrote
 // none), in slice order, into the unit's G query-head output rows.  One wave, heads in
@@ -1008,9 +996,11 @@ StreamPlan stream_plan(int32_t num_seqs, int32_t hq, int32_t hkv, int32_t dtype,
                              (max_tiles + kStreamMinSlice - 1) / kStreamMinSlice));
     p.max_pieces = (int64_t)p.waves + (int64_t)num_seqs * p.units;
     const size_t rows = (size_t)p.max_pieces * p.heads_per_unit;
-    p.meta_off = 0;
-    p.cnt_off = align256((size_t)(num_seqs + 1) * sizeof(int32_t));
-    p.m_off = p.cnt_off + align256((size_t)num_seqs * p.units * sizeof(int32_t));
+    // the counters come first, so that a call with no more (sequence, unit) counters
+    // than an earlier one on the same workspace finds them at zero
+    p.cnt_off = 0;
+    p.meta_off = align256((size_t)num_seqs * p.units * sizeof(int32_t));
+    p.m_off = p.meta_off + align256((size_t)(num_seqs + 1) * sizeof(int32_t));
     p.l_off = p.m_off + align256(rows * sizeof(float));
     p.acc_off = p.l_off + align256(rows * sizeof(float));
     p.ws_bytes = p.acc_off + rows * head_dim * sizeof(float);
