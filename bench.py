@@ -53,7 +53,8 @@ def parse():
                     help="time paged prefill workload K (1: whole prompts, 2: chunked) instead "
                          "of the decode step, and print its line")
     ap.add_argument("--partition-tokens", type=int, default=None,
-                    help="0: stream-K schedule; > 0: fixed partitions (default: the workload's)")
+                    help="0: stream-K schedule; > 0: fixed partitions; -1: picked by batch shape "
+                         "(default: the workload's)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="bound on the oracle's timed CPU work")
     ap.add_argument("--no-cpu-baseline", action="store_true")
