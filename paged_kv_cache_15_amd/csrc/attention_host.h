@@ -28,7 +28,7 @@ struct StreamPlan {
     int32_t heads_per_unit;
     int32_t waves;         // W
     int64_t max_pieces;    // W + num_seqs * units: upper bound on partial results
-    size_t meta_off, cnt_off, m_off, l_off, acc_off, ws_bytes;
+    size_t cnt_off, m_off, l_off, acc_off, ws_bytes;
 };
 
 // Plan for a batch; `ok` false when the shape is outside what stream-K serves.

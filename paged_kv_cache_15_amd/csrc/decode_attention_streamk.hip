@@ -43,7 +43,6 @@ struct StreamArgs {
     const void* v_pool;
     const int32_t* block_tables;
     const int32_t* context_lens;
-    int32_t* meta;     // per-sequence tile prefix (written by workgroup 0)
     int32_t* counters; // per unit: pieces written so far; zero on entry, left zero
     float* ws_m;
     float* ws_l;
@@ -368,8 +367,6 @@ void attn_mfma_streamk(StreamArgs a) {
 
     extern __shared__ int s_pref[];
     const int tiles_per_unit = build_prefix(a, s_pref);
-    if (blockIdx.x == 0)
-        for (int i = threadIdx.x; i <= a.num_seqs; i += blockDim.x) a.meta[i] = s_pref[i];
     nan_invalid_sequences<D, OUT_DT>(a, s_pref);
     const int lane = threadIdx.x & 63;
     const int j = uni(blockIdx.x * kWaves + (threadIdx.x >> 6));
@@ -665,8 +662,6 @@ void attn_valu_streamk(StreamArgs a) {
 
     extern __shared__ int s_pref[];
     const int tiles_per_unit = build_prefix(a, s_pref);
-    if (blockIdx.x == 0)
-        for (int i = threadIdx.x; i <= a.num_seqs; i += blockDim.x) a.meta[i] = s_pref[i];
     nan_invalid_sequences<D, OUT_DT>(a, s_pref);
     const int lane = threadIdx.x & 63;
     const int j = uni(blockIdx.x * kWaves + (threadIdx.x >> 6));
@@ -911,7 +906,6 @@ StreamArgs make_args(const pkv::StreamLaunch& L, const pkv::StreamPlan& P) {
     a.v_pool = L.v_pool;
     a.block_tables = L.block_tables;
     a.context_lens = L.context_lens;
-    a.meta = reinterpret_cast<int32_t*>(ws + P.meta_off);
     a.counters = reinterpret_cast<int32_t*>(ws + P.cnt_off);
     a.ws_m = reinterpret_cast<float*>(ws + P.m_off);
     a.ws_l = reinterpret_cast<float*>(ws + P.l_off);
@@ -999,8 +993,7 @@ StreamPlan stream_plan(int32_t num_seqs, int32_t hq, int32_t hkv, int32_t dtype,
     // the counters come first, so that a call with no more (sequence, unit) counters
     // than an earlier one on the same workspace finds them at zero
     p.cnt_off = 0;
-    p.meta_off = align256((size_t)num_seqs * p.units * sizeof(int32_t));
-    p.m_off = p.meta_off + align256((size_t)(num_seqs + 1) * sizeof(int32_t));
+    p.m_off = align256((size_t)num_seqs * p.units * sizeof(int32_t));
     p.l_off = p.m_off + align256(rows * sizeof(float));
     p.acc_off = p.l_off + align256(rows * sizeof(float));
     p.ws_bytes = p.acc_off + rows * head_dim * sizeof(float);

@@ -316,7 +316,7 @@ def test_device_op_validation_without_gpu():
     assert B.paged_attention_workspace_bytes(good, 2, 8, 512, 512) == 0
     ws = B.paged_attention_workspace_bytes(good, 2, 8, 513, 512)
     assert ws >= 2 * 8 * 2 * (128 + 2) * 4
-    # stream-K (partition_tokens 0): meta + (waves + seqs*units) pieces of group x (d + 2)
+    # stream-K (partition_tokens 0): counters + (waves + seqs*units) pieces of group x (d + 2)
     wsk = B.paged_attention_workspace_bytes(good, 2, 8, 64, 0)
     waves = max(1, min(3072, -(-4 * 2 * 2 // 16)))   # 4 blocks x 2 seqs x 2 KV heads, >= 16 per wave
     assert wsk >= (waves + 2 * 2) * 4 * (128 + 2) * 4
