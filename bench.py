@@ -170,21 +170,26 @@ def cpu_baseline(w, seconds):
         "sample": f"fp64 NumPy oracle attention over {done} sequence decodes of the same step "
                   f"({done / len(lens):.2f} passes over its {len(lens)} sequences, "
                   f"{ctx_tokens} context tokens), {dt:.1f} s",
+        "prefix_cache": prefix_cache_oracle(),
     }
 
 
-def prefix_cache_host(seconds_cap=5.0):
-    """Host cost of prefix caching (deepsonar §2.4 hash chain) on the shared-prefix shape:
-    32 prompts of 2056 token ids, each requested 8 times; a request matches its prompt
-    against the cache, appends the uncached rest with token ids and is then released.
-    Library (C++ SHA-256 + allocator) and oracle (Python) do the same requests."""
+def _prefix_requests():
+    """The prefix-cache request stream: 32 prompts of 2056 token ids, each requested 8
+    times, and the pool size that holds them."""
     import numpy as np
-    from paged_kv_cache_15_amd import binding as B
-    from oracle import prefix_cache as opc
     rng = np.random.default_rng(4)
     prompts = [rng.integers(0, 50000, 2056).tolist() for _ in range(32)]
     order = [p for p in prompts for _ in range(8)]
-    nb, bs = 32 * 129 * 2, 16
+    return prompts, order, 32 * 129 * 2, 16
+
+
+def prefix_cache_host():
+    """Host cost of prefix caching (deepsonar §2.4 hash chain) on the shared-prefix shape:
+    a request matches its prompt against the cache, appends the uncached rest with token
+    ids and is then released (library: C++ SHA-256 + allocator)."""
+    from paged_kv_cache_15_amd import binding as B
+    prompts, order, nb, bs = _prefix_requests()
     desc = B.make_desc(nb, bs, 8, 128, "bf16", B.PAGED_KV_POOL_HOST_ONLY | B.PAGED_KV_POOL_PREFIX_CACHE)
     pool = B.paged_kv_pool_create(desc)
     hit_tokens = 0
@@ -196,6 +201,17 @@ def prefix_cache_host(seconds_cap=5.0):
         hit_tokens += n
     t_lib = time.perf_counter() - t0
     B.paged_kv_pool_destroy(pool)
+    hashed = sum((len(p) - 1) // bs for p in order) + sum(len(p) // bs for p in prompts)
+    return {"requests": len(order), "prompt_tokens": 2056, "hit_tokens": hit_tokens,
+            "library_us_per_request": round(t_lib / len(order) * 1e6, 2),
+            "library_block_hashes_per_s": round(hashed / t_lib, 1)}
+
+
+def prefix_cache_oracle(seconds_cap=5.0):
+    """The oracle's prefix-caching allocator (Python, hashlib) on the same request stream,
+    timed as part of the CPU baseline."""
+    from oracle import prefix_cache as opc
+    prompts, order, nb, bs = _prefix_requests()
     al = opc.PrefixCachingAllocator(nb, bs)
     t0, done = time.perf_counter(), 0
     for pr in order:
@@ -205,12 +221,7 @@ def prefix_cache_host(seconds_cap=5.0):
         done += 1
         if time.perf_counter() - t0 > seconds_cap:
             break
-    t_orc = time.perf_counter() - t0
-    hashed = sum((len(p) - 1) // bs for p in order) + sum(len(p) // bs for p in prompts)
-    return {"requests": len(order), "prompt_tokens": 2056, "hit_tokens": hit_tokens,
-            "library_us_per_request": round(t_lib / len(order) * 1e6, 2),
-            "library_block_hashes_per_s": round(hashed / t_lib, 1),
-            "oracle_us_per_request": round(t_orc / done * 1e6, 2), "oracle_requests": done}
+    return {"us_per_request": round((time.perf_counter() - t0) / done * 1e6, 2), "requests": done}
 
 
 def decode_graph_timing(layers=32, reps=20):
