@@ -246,7 +246,9 @@ paged_kv_status reshape_and_cache(const paged_kv_pool_desc* desc, const void* ke
  * (paged_attention_auto_partition_tokens). */
 #define PAGED_KV_PARTITION_AUTO (-1)
 
-/* The schedule PAGED_KV_PARTITION_AUTO picks, as a partition_tokens value: 0 (stream-K)
+/* A scheduling choice for paged_attention_decode below (what it computes is cited
+ * there; the schedule changes only the summation order within tolerance).
+ * The schedule PAGED_KV_PARTITION_AUTO picks, as a partition_tokens value: 0 (stream-K)
  * when the batch has at least 65536 (sequence, head unit, 16-token tile) tiles on the
  * bound max_context_len (64 per wave slot of the chip), else fixed partitions: 512
  * tokens when that gives at least 256 (sequence, head unit, partition) workgroups, one
