@@ -339,9 +339,11 @@ def test_stream_k_batch_limit_and_fallback(shape):
         g.cache.close()
 
 
-@pytest.mark.parametrize("nseq,ctx_hi", [(1, 2000), (8, 2000), (40, 2000), (80, 2000)],
-                         ids=["1seq", "8seq", "40seq", "80seq"])
-def test_automatic_schedule_is_the_schedule_it_names(nseq, ctx_hi):
+@pytest.mark.parametrize("nseq,ctx_hi,shape", [(1, 2000, ("bf16", 64, 8)), (8, 2000, ("bf16", 64, 8)),
+                                              (40, 2000, ("bf16", 64, 8)), (80, 2000, ("bf16", 64, 8)),
+                                              (8, 1500, ("f16", 16, 16)), (4, 900, ("f32", 8, 2))],
+                         ids=["1seq", "8seq", "40seq", "80seq", "mha-f16-8seq", "f32-4seq"])
+def test_automatic_schedule_is_the_schedule_it_names(nseq, ctx_hi, shape):
     """PARTITION_AUTO gives bit for bit the result of the partition_tokens value it
     resolves to (256/512-token partitions for small batches, stream-K for large ones),
     and that result matches the oracle."""
@@ -351,7 +353,8 @@ def test_automatic_schedule_is_the_schedule_it_names(nseq, ctx_hi):
     from oracle.attention import dense_decode
     rng = np.random.default_rng(nseq)
     lens = rng.integers(1, ctx_hi + 1, nseq).tolist()
-    hq, hkv, d, dt = 64, 8, 128, "bf16"
+    dt, hq, hkv = shape
+    d = 128
     c = PagedKVCache(sum((n + 15) // 16 for n in lens) + 8, hkv, d, dt, 16,
                      rng.permutation(sum((n + 15) // 16 for n in lens) + 8).astype(np.int32))
     seqs = [c.create() for _ in lens]
