@@ -104,11 +104,11 @@ __device__ __forceinline__ void store_out4(void* out, int64_t i, f32x4 v) {
 // C: 16-row column blocks per wave: every K/V load serves 16*C query rows, so more
 // blocks mean fewer loads per row (the load path bounds the kernel), up to the 512
 // registers of a wave.  Three at head_dim 128 fill them (one 16-byte reload from scratch
-// per tile pair remains) and beat two by 2-17% across the workloads; four at 64 and one
-// at 256.  (Sharing each tile pair among the workgroup's four waves through LDS, with 3
+// per tile pair remains) and beat two by 2-17% across the workloads; five at 64 (no
+// spill; four measured 0-9% slower, six spill and were slower) and one at 256.  (Sharing each tile pair among the workgroup's four waves through LDS, with 3
 // or 4 blocks per wave, measured slower: 363-430 against 459-484 TFLOP/s.)
 template <int D>
-constexpr int prefill_blocks() { return D == 128 ? 3 : 256 / D; }
+constexpr int prefill_blocks() { return D == 128 ? 3 : D == 64 ? 5 : 1; }
 
 template <int D, int DT, int OUT_DT, int BS>
 __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(1)))
