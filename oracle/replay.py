@@ -35,10 +35,16 @@ def padded_tables(alloc, seqs, max_blocks=None):
     return t
 
 
-def run(w, attend_rows=None, compute_attention=True):
+def run(w, attend_rows=None, compute_attention=True, last_rows="same"):
     """Replay workload `w`.  attend_rows: batch rows (sequences of a prefill op) to compute
-    per attention op (None = all).
+    per attention op (None = all); last_rows: the rows of the script's last attention op
+    instead ("same": attend_rows, None: all).
     A workload built without values replays the allocator only (pools stay None)."""
+    n_att = sum(1 for op in w.ops if op[0] in ("attend", "prefill"))
+    seen = 0
+
+    def rows_now():
+        return last_rows if (last_rows != "same" and seen == n_att) else attend_rows
     alloc = BlockAllocator(w.num_blocks, w.block_size, w.free_order)
     has_values = any(x is not None for x in w.kv)
     k_pool, v_pool = (new_pool(w.num_blocks, w.num_kv_heads, w.block_size, w.head_dim, w.dtype)
@@ -72,6 +78,7 @@ def run(w, attend_rows=None, compute_attention=True):
             res.slot_mappings.append(np.asarray(all_slots, dtype=np.int32))
             res.copies.append(np.asarray(all_copies, dtype=np.int32).reshape(-1, 2))
         elif kind == "attend":
+            seen += 1
             seqs, qidx = op[1], op[2]
             tables = padded_tables(alloc, seqs)
             lens = np.asarray([alloc.context_len(s) for s in seqs], dtype=np.int32)
@@ -80,11 +87,12 @@ def run(w, attend_rows=None, compute_attention=True):
             if compute_attention and w.q[qidx] is not None:
                 q = storage_bits_to_f64(to_storage_bits(w.q[qidx], w.dtype), w.dtype)
                 res.outputs.append(paged_decode(q, k_pool, v_pool, tables, lens, w.scale,
-                                                w.dtype, w.block_size, seqs=attend_rows))
+                                                w.dtype, w.block_size, seqs=rows_now()))
             else:
                 res.outputs.append(None)
         elif kind == "prefill":
             # causal attention of each listed sequence's last counts[i] tokens
+            seen += 1
             seqs, counts, qidx = op[1], op[2], op[3]
             tables = padded_tables(alloc, seqs)
             lens = np.asarray([alloc.context_len(s) for s in seqs], dtype=np.int32)
@@ -94,7 +102,7 @@ def run(w, attend_rows=None, compute_attention=True):
             if compute_attention and w.q[qidx] is not None:
                 q = storage_bits_to_f64(to_storage_bits(w.q[qidx], w.dtype), w.dtype)
                 res.outputs.append(paged_prefill(q, k_pool, v_pool, tables, lens, q_start, w.scale,
-                                                 w.dtype, w.block_size, seqs=attend_rows))
+                                                 w.dtype, w.block_size, seqs=rows_now()))
             else:
                 res.outputs.append(None)
         else:

@@ -328,6 +328,20 @@ def reshape_and_cache(desc, key, value, k_pool, v_pool, slot_mapping, num_tokens
     """key/value: [T][Hkv][d] tensors (token stride taken from the tensor unless given)."""
     if num_tokens is None:
         num_tokens = key.shape[0]
+    f = "reshape_and_cache"
+    for name, t in (("key", key), ("value", value)):
+        if _is_tensor(t):
+            _expect(f, t.dim() == 3 and tuple(t.shape[1:]) == (desc.num_kv_heads, desc.head_dim)
+                    and t.shape[0] >= num_tokens,
+                    f"{name} must be [>= {num_tokens}][{desc.num_kv_heads}][{desc.head_dim}] "
+                    f"(got {tuple(t.shape)})")
+            _expect(f, t.stride(2) == 1 and t.stride(1) == desc.head_dim,
+                    f"{name}: heads and dims must be contiguous")
+            _expect(f, t.element_size() == _ELEM_BYTES.get(desc.dtype),
+                    f"{name} element size does not match the pool")
+    if _is_tensor(slot_mapping):
+        _check_tensor(f, "slot_mapping", slot_mapping, int32=True)
+        _expect(f, slot_mapping.numel() >= num_tokens, "slot_mapping shorter than num_tokens")
     if key_stride is None:
         key_stride = key.stride(0)
     if value_stride is None:
@@ -353,10 +367,55 @@ def paged_attention_workspace_bytes(desc, num_seqs, num_q_heads, max_context_len
                                                    max_context_len, partition_tokens))
 
 
-def _attn_args(desc, out, out_dtype, q, k_pool, v_pool, block_tables, context_lens,
+_ELEM_BYTES = {PAGED_KV_F32: 4, PAGED_KV_F16: 2, PAGED_KV_BF16: 2}
+
+
+def _is_tensor(x):
+    return hasattr(x, "data_ptr") and hasattr(x, "is_contiguous")
+
+
+def _expect(func, cond, what):
+    if not cond:
+        raise ValueError(f"{func}: {what}")
+
+
+def _check_tensor(func, name, t, shape=None, elem_bytes=None, int32=False):
+    """Layout checks on a torch tensor argument (raw addresses are passed unchecked):
+    contiguous, int32 when asked, the element size of its storage type, and a shape."""
+    if not _is_tensor(t):
+        return
+    import torch
+    _expect(func, t.is_contiguous(), f"{name} must be contiguous")
+    if int32:
+        _expect(func, t.dtype == torch.int32, f"{name} must be int32 (got {t.dtype})")
+    if elem_bytes is not None:
+        _expect(func, t.element_size() == elem_bytes,
+                f"{name} has {t.element_size()}-byte elements, {elem_bytes} expected")
+    if shape is not None:
+        _expect(func, tuple(t.shape) == tuple(shape),
+                f"{name} has shape {tuple(t.shape)}, {tuple(shape)} expected")
+
+
+def _check_attn(func, desc, out, out_dtype, q, block_tables, context_lens, num_q_heads,
+                workspace):
+    _check_tensor(func, "context_lens", context_lens, int32=True)
+    _check_tensor(func, "block_tables", block_tables, int32=True)
+    nseq = int(context_lens.shape[0])
+    if _is_tensor(block_tables):
+        _expect(func, block_tables.dim() == 2 and block_tables.shape[0] == nseq,
+                f"block_tables must be [{nseq}][max_blocks] (got {tuple(block_tables.shape)})")
+    rows = (nseq, int(num_q_heads), int(desc.head_dim))
+    _check_tensor(func, "q", q, rows, _ELEM_BYTES.get(desc.dtype))
+    _check_tensor(func, "out", out, rows, _ELEM_BYTES.get(out_dtype))
+    if workspace is not None and _is_tensor(workspace):
+        _expect(func, workspace.is_contiguous(), "workspace must be contiguous")
+
+
+def _attn_args(func, desc, out, out_dtype, q, k_pool, v_pool, block_tables, context_lens,
                num_q_heads, max_context_len, scale, partition_tokens, workspace, stream):
     if isinstance(out_dtype, str):
         out_dtype = DTYPE_CODES[out_dtype]
+    _check_attn(func, desc, out, out_dtype, q, block_tables, context_lens, num_q_heads, workspace)
     ws_bytes = 0 if workspace is None else (workspace.numel() * workspace.element_size()
                                             if hasattr(workspace, "numel") else 0)
     return (ctypes.byref(desc), _ptr(out), int(out_dtype), _ptr(q), _ptr(k_pool), _ptr(v_pool),
@@ -370,7 +429,8 @@ def paged_attention_decode(desc, out, out_dtype, q, k_pool, v_pool, block_tables
                            workspace=None, stream=None):
     """block_tables: int32 [B][max_blocks] device tensor; context_lens: int32 [B] device."""
     _check("paged_attention_decode",
-           lib.paged_attention_decode(*_attn_args(desc, out, out_dtype, q, k_pool, v_pool,
+           lib.paged_attention_decode(*_attn_args("paged_attention_decode", desc, out, out_dtype,
+                                                  q, k_pool, v_pool,
                                                   block_tables, context_lens, num_q_heads,
                                                   max_context_len, scale, partition_tokens,
                                                   workspace, stream)))
@@ -380,7 +440,8 @@ def paged_attention_partition(desc, out, out_dtype, q, k_pool, v_pool, block_tab
                               num_q_heads, max_context_len, scale, partition_tokens=0,
                               workspace=None, stream=None):
     _check("paged_attention_partition",
-           lib.paged_attention_partition(*_attn_args(desc, out, out_dtype, q, k_pool, v_pool,
+           lib.paged_attention_partition(*_attn_args("paged_attention_partition", desc, out,
+                                                     out_dtype, q, k_pool, v_pool,
                                                      block_tables, context_lens, num_q_heads,
                                                      max_context_len, scale, partition_tokens,
                                                      workspace, stream)))
@@ -393,6 +454,15 @@ def paged_attention_prefill(desc, out, out_dtype, q, q_start, k_pool, v_pool, bl
     block_tables: int32 [B][max_blocks] device; context_lens: int32 [B] device."""
     if isinstance(out_dtype, str):
         out_dtype = DTYPE_CODES[out_dtype]
+    f = "paged_attention_prefill"
+    _check_tensor(f, "context_lens", context_lens, int32=True)
+    _check_tensor(f, "block_tables", block_tables, int32=True)
+    _check_tensor(f, "q_start", q_start, (int(context_lens.shape[0]) + 1,), int32=True)
+    if _is_tensor(q):
+        _expect(f, q.dim() == 3 and tuple(q.shape[1:]) == (int(num_q_heads), int(desc.head_dim)),
+                f"q must be [rows][{num_q_heads}][{desc.head_dim}] (got {tuple(q.shape)})")
+        _check_tensor(f, "q", q, elem_bytes=_ELEM_BYTES.get(desc.dtype))
+        _check_tensor(f, "out", out, tuple(q.shape), _ELEM_BYTES.get(out_dtype))
     _check("paged_attention_prefill",
            lib.paged_attention_prefill(ctypes.byref(desc), _ptr(out), int(out_dtype), _ptr(q),
                                        _ptr(q_start), _ptr(k_pool), _ptr(v_pool),
@@ -406,6 +476,10 @@ def paged_attention_reduce(desc, out, out_dtype, context_lens, num_q_heads, max_
                            partition_tokens=0, workspace=None, stream=None):
     if isinstance(out_dtype, str):
         out_dtype = DTYPE_CODES[out_dtype]
+    f = "paged_attention_reduce"
+    _check_tensor(f, "context_lens", context_lens, int32=True)
+    _check_tensor(f, "out", out, (int(context_lens.shape[0]), int(num_q_heads), int(desc.head_dim)),
+                  _ELEM_BYTES.get(out_dtype))
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check("paged_attention_reduce",
            lib.paged_attention_reduce(ctypes.byref(desc), _ptr(out), int(out_dtype),

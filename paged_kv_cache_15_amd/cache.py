@@ -106,15 +106,21 @@ class PagedKVCache:
                                 stream=stream)
         return slots, copies
 
-    def attend(self, seqs, q, scale, out_dtype=None, partition_tokens=0, stream=None):
-        """Decode attention of q ([len(seqs)][Hq][d] device tensor) over the sequences."""
+    def attend(self, seqs, q, scale, out_dtype=None, partition_tokens=0, stream=None,
+               out_fill=None):
+        """Decode attention of q ([len(seqs)][Hq][d] device tensor) over the sequences.
+        out_fill: a value to fill the output with before the call (tests fill NaN, so a
+        row the kernels never write cannot pass for a result)."""
         tables, lens = self.block_tables(seqs)
         out_dtype = out_dtype or self.dtype
         max_ctx = int(lens.max()) if len(lens) else 1
         tables_d = torch.from_numpy(tables).to(self.device)
         lens_d = torch.from_numpy(lens).to(self.device)
         hq, d = q.shape[1], q.shape[2]
-        out = torch.empty((len(seqs), hq, d), dtype=TORCH_DTYPES[out_dtype], device=self.device)
+        shape = (len(seqs), hq, d)
+        out = (torch.empty(shape, dtype=TORCH_DTYPES[out_dtype], device=self.device)
+               if out_fill is None else
+               torch.full(shape, out_fill, dtype=TORCH_DTYPES[out_dtype], device=self.device))
         nbytes = B.paged_attention_workspace_bytes(self.desc, len(seqs), hq, max_ctx,
                                                    partition_tokens)
         # zero-filled: the stream-K schedule keeps per-unit counters in the workspace
@@ -123,7 +129,8 @@ class PagedKVCache:
                                  lens_d, hq, max_ctx, scale, partition_tokens, ws, stream)
         return out, tables, lens
 
-    def attend_prefill(self, seqs, q_counts, q, scale, out_dtype=None, stream=None):
+    def attend_prefill(self, seqs, q_counts, q, scale, out_dtype=None, stream=None,
+                       out_fill=None):
         """Causal attention of each sequence's last q_counts[i] tokens (already appended and
         written) over its whole context: q is [sum(q_counts)][Hq][d] on the device, rows
         in sequence order."""
@@ -134,8 +141,10 @@ class PagedKVCache:
         max_ctx = int(lens.max()) if len(lens) else 1
         max_q = int(counts.max()) if len(counts) else 0
         hq, d = q.shape[1], q.shape[2]
-        out = torch.empty((int(q_start[-1]), hq, d), dtype=TORCH_DTYPES[out_dtype],
-                          device=self.device)
+        shape = (int(q_start[-1]), hq, d)
+        out = (torch.empty(shape, dtype=TORCH_DTYPES[out_dtype], device=self.device)
+               if out_fill is None else
+               torch.full(shape, out_fill, dtype=TORCH_DTYPES[out_dtype], device=self.device))
         B.paged_attention_prefill(self.desc, out, out_dtype, q,
                                   torch.from_numpy(q_start).to(self.device), self.k_pool,
                                   self.v_pool, torch.from_numpy(tables).to(self.device),

@@ -12,10 +12,11 @@ namespace pkv {
 
 // Stream-K decomposition: the (sequence, head unit, 16-token tile) tiles of the whole
 // batch form one line; `waves` waves each take an equal contiguous slice of it.
-// At most one wave per resident slot: 256 CUs x 4 SIMDs x the kernel's waves per SIMD
-// on MI355X (1024 from head_dim 128; at 64, 3072 for 16-bit values).
-inline int stream_max_waves(int head_dim, int elem_bytes, bool mfma) {
-    return 256 * 4 * kernel_waves_per_simd(head_dim, elem_bytes, mfma, true);
+// At most one wave per resident slot: compute units x 4 SIMDs x the kernel's waves per
+// SIMD (on MI355X's 256 compute units: 1024 from head_dim 128; at 64, 3072 for 16-bit
+// values).
+inline int stream_max_waves(int compute_units, int head_dim, int elem_bytes, bool mfma) {
+    return compute_units * 4 * kernel_waves_per_simd(head_dim, elem_bytes, mfma, true);
 }
 // The per-sequence tile prefix is built in LDS by every workgroup.
 constexpr int kStreamMaxSeqs = 8192;

@@ -45,4 +45,18 @@ constexpr int kernel_waves_per_simd(int d, int e, bool mfma, bool streamk) {
 }
 constexpr int kDefaultPartitionTokens = 512;
 
+// What the launch plans need to know about the device they launch on.
+struct DeviceShape {
+    int compute_units;   // hipDeviceAttributeMultiprocessorCount
+    int xcds;            // accelerator dies the compute units are spread over (workgroup b
+                         // runs on die b % xcds); compute_units / 32 on gfx950, else 1
+    bool mi355x_spx;     // gfx950 with all 256 compute units in one device: the shape the
+                         // stream-K XCD slice weights were measured on
+};
+// The current device's shape (cached per device).  With no usable device it returns
+// default_device_shape(), the MI355X in SPX mode, so that host-only sizing calls still
+// answer; no kernel can be launched then anyway.
+DeviceShape device_shape();
+DeviceShape default_device_shape();
+
 }  // namespace pkv

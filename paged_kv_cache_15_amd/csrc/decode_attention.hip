@@ -685,24 +685,36 @@ bool use_streamk(int32_t part_tokens, int32_t num_seqs) {
 // decode steps of 64 query / 8 KV heads, contexts 256..2048: stream-K took 25-30 us a
 // layer for 1-8 sequences and 47.5 for 32, fixed partitions 13.5-19.6 and 43.5 (256
 // tokens best up to 4 sequences, 512 from 8); on the 128-sequence GQA workload stream-K
-// is the faster one.
-constexpr int64_t kAutoStreamTiles = 65536;     // 64 tiles per wave slot of the chip
-constexpr int64_t kAutoMinWorkgroups = 256;     // one per compute unit
+// is the faster one.  Thresholds scale with the device's compute units: stream-K from 64
+// tiles per resident wave slot (4 SIMDs per compute unit), 512-token partitions from one
+// workgroup per compute unit.
+constexpr int64_t kAutoTilesPerSlot = 64;
 
 int32_t auto_partition_tokens(const paged_kv_pool_desc* desc, int32_t num_seqs, int32_t hq,
                               int32_t max_ctx) {
+    const int64_t cus = pkv::device_shape().compute_units;
     const bool mfma = desc->dtype != PAGED_KV_F32 && hq / desc->num_kv_heads >= 2;
     const int64_t units = (int64_t)num_seqs * (mfma ? desc->num_kv_heads : hq);
-    if (units * ((max_ctx + kTile - 1) / kTile) >= kAutoStreamTiles) return 0;
-    return units * ((max_ctx + 511) / 512) >= kAutoMinWorkgroups ? 512 : 256;
+    if (units * ((max_ctx + kTile - 1) / kTile) >= kAutoTilesPerSlot * 4 * cus) return 0;
+    return units * ((max_ctx + 511) / 512) >= cus ? 512 : 256;
 }
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
-size_t workspace_for(int64_t num_seqs, int64_t hq, int64_t d, int64_t max_parts) {
+// Bytes at the start of every workspace for the stream-K schedule's merge counters, one
+// int32 per (sequence, head unit).  Fixed-partition calls reserve the same prefix and
+// never touch it, so calls of either schedule leave the counters at zero.
+size_t counter_bytes(const paged_kv_pool_desc* desc, int64_t num_seqs, int64_t hq) {
+    const bool mfma = desc->dtype != PAGED_KV_F32 && hq / desc->num_kv_heads >= 2;
+    return align256((size_t)num_seqs * (mfma ? desc->num_kv_heads : hq) * sizeof(int32_t));
+}
+
+// Fixed partitions: counters | m, l: float[rows] | acc: float[rows][d], rows =
+// num_seqs * hq * max_parts.  Nothing when no sequence can need a second partition.
+size_t workspace_for(size_t cnt_bytes, int64_t num_seqs, int64_t hq, int64_t d, int64_t max_parts) {
     if (max_parts <= 1) return 0;
     const size_t rows = (size_t)num_seqs * hq * max_parts;
-    return 2 * align256(rows * sizeof(float)) + rows * d * sizeof(float);
+    return cnt_bytes + 2 * align256(rows * sizeof(float)) + rows * d * sizeof(float);
 }
 
 paged_kv_status make_plan(Plan& pl, const paged_kv_pool_desc* desc, void* out, int32_t out_dtype,
@@ -750,7 +762,8 @@ paged_kv_status make_plan(Plan& pl, const paged_kv_pool_desc* desc, void* out, i
                                  max_ctx, &ok);
         pl.ws_needed = pl.sp.ws_bytes;
     } else {
-        pl.ws_needed = workspace_for(num_seqs, hq, desc->head_dim, max_parts);
+        pl.ws_needed = workspace_for(counter_bytes(desc, num_seqs, hq), num_seqs, hq,
+                                     desc->head_dim, max_parts);
     }
     if (num_seqs > 0) {
         if (!out || !lens || (need_kv && (!q || !k_pool || !v_pool || !tables))) {
@@ -775,9 +788,11 @@ paged_kv_status make_plan(Plan& pl, const paged_kv_pool_desc* desc, void* out, i
     a.block_tables = tables;
     a.context_lens = lens;
     const size_t rows = (size_t)num_seqs * hq * max_parts;
-    a.ws_m = static_cast<float*>(ws);
-    a.ws_l = pl.ws_needed ? reinterpret_cast<float*>(static_cast<char*>(ws) + align256(rows * 4)) : nullptr;
-    a.ws_acc = pl.ws_needed ? reinterpret_cast<float*>(static_cast<char*>(ws) + 2 * align256(rows * 4)) : nullptr;
+    const size_t cnt = counter_bytes(desc, num_seqs, hq);
+    char* wsc = static_cast<char*>(ws);
+    a.ws_m = pl.ws_needed ? reinterpret_cast<float*>(wsc + cnt) : nullptr;
+    a.ws_l = pl.ws_needed ? reinterpret_cast<float*>(wsc + cnt + align256(rows * 4)) : nullptr;
+    a.ws_acc = pl.ws_needed ? reinterpret_cast<float*>(wsc + cnt + 2 * align256(rows * 4)) : nullptr;
     a.max_blocks_per_seq = max_blocks;
     a.num_q_heads = hq;
     a.num_kv_heads = desc->num_kv_heads;
@@ -894,7 +909,8 @@ size_t paged_attention_workspace_bytes(const paged_kv_pool_desc* desc, int32_t n
     }
     if (partition_tokens == 0) partition_tokens = pkv::kDefaultPartitionTokens;
     const int64_t max_parts = (max_context_len + (int64_t)partition_tokens - 1) / partition_tokens;
-    return workspace_for(num_seqs, num_q_heads, desc->head_dim, max_parts);
+    return workspace_for(counter_bytes(desc, num_seqs, num_q_heads), num_seqs, num_q_heads,
+                         desc->head_dim, max_parts);
 }
 
 paged_kv_status paged_attention_partition(const paged_kv_pool_desc* desc, void* out,

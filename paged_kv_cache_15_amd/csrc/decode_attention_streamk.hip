@@ -322,6 +322,17 @@ __device__ void publish_pieces(const StreamArgs& a, const int* s_pref, const Pen
     }
     old0 = __shfl(old0, 0);
     old1 = __shfl(old1, 0);
+    // Ordering of the merge's reads after the count, stated for gfx950: every piece was
+    // stored with the sc1 policy (written through to the device-coherent level, not kept
+    // dirty in the XCD's own L2), and its writer bumped the counter only after
+    // s_waitcnt vmcnt(0) had seen those stores acknowledged.  The counter is an
+    // agent-scope atomic, performed at that coherent level, so a bump that returns the
+    // final count comes after every other writer's pieces are there, and the merge reads
+    // them with sc1 loads, which do not hit stale lines in this XCD's L2.  What the
+    // hardware does not order for us is the compiler: this fence keeps it from moving
+    // the merge's loads above the counter's atomic (an agent-scope acquire fence would
+    // also invalidate the L2 here, which the sc1 loads already make unnecessary).
+    __atomic_signal_fence(__ATOMIC_ACQUIRE);
 #pragma unroll 1
     for (int e = 0; e < pd.n; ++e) {
         const int s = e ? pd.s1 : pd.s0, u = e ? pd.u1 : pd.u0, nt = e ? pd.nt1 : pd.nt0;
@@ -923,8 +934,11 @@ StreamArgs make_args(const pkv::StreamLaunch& L, const pkv::StreamPlan& P) {
     // XCD-weighted slices where they measured faster (one wave per SIMD: head_dim 128
     // and up; 16- or 32-token blocks): 0.744 against 0.735 of peak on the GQA workload,
     // 0.793 against 0.781 on the MHA one; at head_dim 64 and block size 1 equal slices
-    // were faster (0.677 against 0.663, 0.571 against 0.557)
-    a.weight_odd = (L.head_dim >= 128 && L.block_size >= 16) ? 58 : (int32_t)kWeightEven;
+    // were faster (0.677 against 0.663, 0.571 against 0.557).  The weights were measured
+    // on MI355X in SPX mode (256 compute units, workgroup b on die b % 8); any other
+    // device shape gets equal slices.
+    a.weight_odd = (L.head_dim >= 128 && L.block_size >= 16 && pkv::device_shape().mi355x_spx)
+                       ? 58 : (int32_t)kWeightEven;
     a.scale_log2 = L.scale * kLog2e;
     return a;
 }
@@ -986,7 +1000,8 @@ StreamPlan stream_plan(int32_t num_seqs, int32_t hq, int32_t hkv, int32_t dtype,
     // at least kStreamMinSlice tiles per wave (on the bound max_tiles): thinner slices cut
     // every unit into many pieces, and the merge's round trips grow with their number
     p.waves = (int32_t)std::max<int64_t>(
-        1, std::min<int64_t>(stream_max_waves(head_dim, elem_bytes(dtype), p.mfma),
+        1, std::min<int64_t>(stream_max_waves(device_shape().compute_units, head_dim,
+                                              elem_bytes(dtype), p.mfma),
                              (max_tiles + kStreamMinSlice - 1) / kStreamMinSlice));
     p.max_pieces = (int64_t)p.waves + (int64_t)num_seqs * p.units;
     const size_t rows = (size_t)p.max_pieces * p.heads_per_unit;

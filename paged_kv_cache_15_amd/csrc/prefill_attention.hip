@@ -59,6 +59,7 @@ struct PrefillArgs {
     int32_t max_context_len;
     int32_t tokens_per_wg;      // TQ
     int32_t q_tiles;            // ceil(max_q_len / TQ)
+    int32_t xcds;               // dies of the device: workgroup b runs on die b % xcds
     float scale_log2;
 };
 
@@ -124,12 +125,14 @@ void attn_prefill_mfma(PrefillArgs a) {
     __shared__ uint16_t s_vt[BS == 1 ? kWaves * kTile * LDW : 1];
     using kvec = typename std::conditional<DT == DT_BF16, bf16x8, f16x8>::type;
 
-    // Workgroup b runs on XCD b % 8.  Pair y = sequence * KV heads + KV head is given to
-    // XCD y % 8 (so the K/V its query tiles all read stays in that XCD's L2, and with 8
-    // KV heads every XCD gets one head of every sequence); on each XCD the workgroups
-    // take its pairs in order, each pair's query tiles last first.
-    const int xcd = blockIdx.x % 8, idx = blockIdx.x / 8;
-    const int y = xcd + 8 * (idx / a.q_tiles);
+    // Workgroup b runs on XCD b % X (X = a.xcds, 8 on MI355X).  Pair y = sequence * KV
+    // heads + KV head is given to XCD y % X (so the K/V its query tiles all read stays in
+    // that XCD's L2, and with 8 KV heads on 8 dies every XCD gets one head of every
+    // sequence); on each XCD the workgroups take its pairs in order, each pair's query
+    // tiles last first.  The mapping is a bijection onto (pair, query tile) for any X, so
+    // X only matters for speed.
+    const int xcd = blockIdx.x % a.xcds, idx = blockIdx.x / a.xcds;
+    const int y = xcd + a.xcds * (idx / a.q_tiles);
     if (y >= a.num_seqs * a.num_kv_heads) return;
     const int qt = a.q_tiles - 1 - idx % a.q_tiles;
     const int s = y / a.num_kv_heads;
@@ -645,8 +648,9 @@ paged_kv_status paged_attention_prefill(const paged_kv_pool_desc* desc, void* ou
     a.tokens_per_wg = tokens_per_workgroup(desc->head_dim, group);
     a.q_tiles = (max_q_len + a.tokens_per_wg - 1) / a.tokens_per_wg;
     a.scale_log2 = scale * kLog2e;
+    a.xcds = pkv::device_shape().xcds;
     const int64_t pairs = (int64_t)num_seqs * desc->num_kv_heads;
-    const int64_t wgs = 8 * a.q_tiles * ((pairs + 7) / 8);
+    const int64_t wgs = (int64_t)a.xcds * a.q_tiles * ((pairs + a.xcds - 1) / a.xcds);
     if (wgs > INT32_MAX) {
         pkv::set_error("too many (sequence, KV head, query tile) workgroups for one launch");
         return PAGED_KV_ERR_UNSUPPORTED;

@@ -26,7 +26,8 @@ def to_device(x, dtype, device):
     return torch.from_numpy(np.ascontiguousarray(x)).to(device).to(TORCH_DTYPES[dtype])
 
 
-def run_workload(w, device="cuda", out_dtype=None, partition_tokens=None, poison=True):
+def run_workload(w, device="cuda", out_dtype=None, partition_tokens=None, poison=True,
+                 out_fill=None):
     cache = PagedKVCache(w.num_blocks, w.num_kv_heads, w.head_dim, w.dtype, w.block_size,
                          w.free_order, device=device, poison=poison)
     res = GpuReplay(cache=cache)
@@ -50,14 +51,16 @@ def run_workload(w, device="cuda", out_dtype=None, partition_tokens=None, poison
         elif kind == "attend":
             seqs, qidx = op[1], op[2]
             q = to_device(w.q[qidx], w.dtype, device)
-            out, tables, lens = cache.attend(seqs, q, float(w.scale), out_dtype, pt)
+            out, tables, lens = cache.attend(seqs, q, float(w.scale), out_dtype, pt,
+                                             out_fill=out_fill)
             res.outputs.append(out)
             res.tables.append(tables)
             res.context_lens.append(lens)
         elif kind == "prefill":
             seqs, counts, qidx = op[1], op[2], op[3]
             q = to_device(w.q[qidx], w.dtype, device)
-            out, tables, lens = cache.attend_prefill(seqs, counts, q, float(w.scale), out_dtype)
+            out, tables, lens = cache.attend_prefill(seqs, counts, q, float(w.scale), out_dtype,
+                                                     out_fill=out_fill)
             res.outputs.append(out)
             res.tables.append(tables)
             res.context_lens.append(lens)

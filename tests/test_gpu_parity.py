@@ -18,7 +18,8 @@ pytestmark = pytest.mark.gpu
 
 def _run_both(w, out_dtype=None, attend_rows=None, partition_tokens=None):
     from paged_kv_cache_15_amd.replay import run_workload
-    g = run_workload(w, "cuda", out_dtype=out_dtype, partition_tokens=partition_tokens)
+    g = run_workload(w, "cuda", out_dtype=out_dtype, partition_tokens=partition_tokens,
+                     out_fill=float("nan"))
     torch.cuda.synchronize()
     o = oreplay.run(w, attend_rows=attend_rows)
     return g, o
@@ -52,8 +53,10 @@ def _sample_rows(lens, n, seed):
 def test_full_size_configs(k):
     """Full sizes, in the launch configuration the bench times (the workload's own
     partition setting: stream-K, or 512-token partitions for the long-context one):
-    whole pools bit-exact, attention on sampled sequences."""
-    _full_size(k, 16, None)
+    whole pools bit-exact; attention of every sequence of the (last) decode step against
+    the oracle, earlier steps on sampled sequences; outputs start as NaN, so a row the
+    kernels never write fails."""
+    _full_size(k, 16, None, every_row=True)
 
 
 @pytest.mark.parametrize("bs,d", [(1, None), (32, None), (16, 64), (16, 256)],
@@ -61,24 +64,25 @@ def test_full_size_configs(k):
 def test_full_size_block_and_head_sizes(bs, d):
     """The GQA workload's lengths at the other block and head sizes the bench measures
     (`--block-size`, `--head-dim`), at full size: pools bit-exact, sampled sequences."""
-    _full_size(3, bs, d)
+    _full_size(3, bs, d, every_row=False)
 
 
-def _full_size(k, bs, d):
+def _full_size(k, bs, d, every_row):
     from paged_kv_cache_15_amd.replay import run_workload
     w = W.make_config(k, block_size=bs, head_dim=d)
     say(f"[parity-full] config {k} {w.name}")
-    g = run_workload(w, "cuda", out_dtype="f32")
+    g = run_workload(w, "cuda", out_dtype="f32", out_fill=float("nan"))
     torch.cuda.synchronize()
     lens = g.context_lens[0]
-    rows = _sample_rows(lens, 6, k)
-    o = oreplay.run(w, attend_rows=rows)
+    rows = _sample_rows(lens, 6 if every_row else 24, k)
+    o = oreplay.run(w, attend_rows=rows, last_rows=None if every_row else "same")
     assert_bookkeeping_equal(g, o)
     assert_pools_equal(g.cache, o, w.dtype)
-    for go, oo in zip(g.outputs, o.outputs):
-        err = max_err(go, oo, rows)
-        say(f"   rows {rows} max|err| {err:.3e}")
+    n = len(g.outputs)
+    for i, (go, oo) in enumerate(zip(g.outputs, o.outputs)):
+        rr = list(range(go.shape[0])) if (every_row and i == n - 1) else rows
+        err = max_err(go, oo, rr)
+        say(f"   attend {i}: {len(rr)} rows, max|err| {err:.3e}")
         assert err <= TOL[w.dtype]
-        gf = go.float()
-        assert torch.isfinite(gf).all()
+        assert torch.isfinite(go.float()).all()
     g.cache.close()

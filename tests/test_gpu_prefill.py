@@ -62,20 +62,25 @@ def test_prefill_small_configs(k):
     g.cache.close()
 
 
-@pytest.mark.parametrize("k,bs,d", [(1, 16, 128), (2, 16, 128), (1, 32, 128), (1, 1, 128),
-                                    (1, 16, 64), (1, 16, 256)],
+@pytest.mark.parametrize("k,bs,d,every", [(1, 16, 128, True), (2, 16, 128, True),
+                                          (1, 32, 128, False), (1, 1, 128, False),
+                                          (1, 16, 64, False), (1, 16, 256, False)],
                          ids=["whole", "chunked", "whole-bs32", "whole-bs1", "whole-d64",
                               "whole-d256"])
-def test_prefill_full_size_sampled(k, bs, d):
+def test_prefill_full_size_sampled(k, bs, d, every):
     """Full sizes as the bench runs them (also at the block and head sizes it measures):
-    every output finite, pools bit-exact, and the oracle on sampled query rows (first,
-    middle and last query of three sequences; a query at position p is the oracle's
-    prefill of a one-token chunk over p + 1 tokens)."""
+    pools bit-exact; outputs start as NaN and must all come back finite; the oracle on
+    every query row of the shortest and the longest sequence (whole prompts and chunked
+    prefill, the launch the bench times; first, middle and last rows at the other sizes)
+    and on 64 random rows (a query at position p is the oracle's prefill of a one-token
+    chunk over p + 1 tokens)."""
     from oracle.attention import paged_prefill
     from oracle import lowp
     w = W.make_prefill_config(k, block_size=bs, head_dim=d)
     say(f"[prefill-full] {w.name}")
-    g = _run(w, "f32")
+    from paged_kv_cache_15_amd.replay import run_workload
+    g = run_workload(w, "cuda", out_dtype="f32", out_fill=float("nan"))
+    torch.cuda.synchronize()
     o = oreplay.run(w, compute_attention=False)
     assert_bookkeeping_equal(g, o)
     assert_pools_equal(g.cache, o, w.dtype)
@@ -84,19 +89,34 @@ def test_prefill_full_size_sampled(k, bs, d):
     starts = np.concatenate([[0], np.cumsum(counts)])
     got = g.outputs[-1]
     assert torch.isfinite(got).all()
+    got = got.double().cpu().numpy()
     q = lowp.storage_bits_to_f64(lowp.to_storage_bits(w.q[op[3]], w.dtype), w.dtype)
     tables, lens = o.tables[-1], o.context_lens[-1]
     worst = 0.0
-    for s in sorted({int(counts.argmin()), int(counts.argmax()), 5}):
+    ends = sorted({int(np.argmin(lens)), int(np.argmax(lens))})
+    for s in ends:
         n, L = int(counts[s]), int(lens[s])
-        for i in sorted({0, n // 2, n - 1}):
-            row = int(starts[s] + i)
-            want = paged_prefill(q[row:row + 1], o.k_pool, o.v_pool, tables[s:s + 1],
-                                 [L - n + i + 1], np.array([0, 1]), w.scale, w.dtype,
-                                 w.block_size)
-            err = float(np.abs(got[row].double().cpu().numpy() - want[0]).max())
-            worst = max(worst, err)
+        if every:
+            want = paged_prefill(q, o.k_pool, o.v_pool, tables, lens, starts, w.scale, w.dtype,
+                                 w.block_size, seqs=[s])
+            rows = slice(int(starts[s]), int(starts[s + 1]))
+            worst = max(worst, float(np.abs(got[rows] - want[rows]).max()))
+        else:
+            for i in sorted({0, n // 2, n - 1}):
+                row = int(starts[s] + i)
+                want = paged_prefill(q[row:row + 1], o.k_pool, o.v_pool, tables[s:s + 1],
+                                     [L - n + i + 1], np.array([0, 1]), w.scale, w.dtype,
+                                     w.block_size)
+                worst = max(worst, float(np.abs(got[row] - want[0]).max()))
         say(f"   sequence {s} (n {n}, context {L}) max|err| so far {worst:.3e}")
+    rng = np.random.default_rng(k * 100 + bs + d)
+    for row in rng.choice(int(starts[-1]), size=64, replace=False):
+        s = int(np.searchsorted(starts, row, side="right") - 1)
+        n, L, i = int(counts[s]), int(lens[s]), int(row - starts[s])
+        want = paged_prefill(q[row:row + 1], o.k_pool, o.v_pool, tables[s:s + 1],
+                             [L - n + i + 1], np.array([0, 1]), w.scale, w.dtype, w.block_size)
+        worst = max(worst, float(np.abs(got[row] - want[0]).max()))
+    say(f"   + 64 random rows: max|err| {worst:.3e}")
     assert worst <= TOL[w.dtype]
     g.cache.close()
 
