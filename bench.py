@@ -58,6 +58,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="bound on the oracle's timed CPU work")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="only the decode step (no prefill, graph-step and step-loop lines)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (3 times) and exit: the "
                          "known-size reference for scaling HBM byte counters")
@@ -131,6 +133,63 @@ def attention_bytes(lens, nblocks, w, out_elem):
     q = len(lens) * w.num_q_heads * w.head_dim * w.elem_bytes
     out = len(lens) * w.num_q_heads * w.head_dim * out_elem
     return kv, kv + q + out + 4 * int(nblocks) + 4 * len(lens)
+
+
+SCRUB_BYTES = 512 << 20     # written between timed launches: evicts L2 and the 256 MB MALL
+
+
+class Scrubber:
+    """A 512 MB buffer written (outside the timed region) before each timed launch, so
+    no launch finds the previous one's data in the L2s or the Infinity Cache."""
+
+    def __init__(self, dev):
+        import torch
+        self.buf = torch.empty(SCRUB_BYTES // 4, dtype=torch.int32, device=dev)
+        self.n = 0
+
+    def __call__(self):
+        self.n += 1
+        self.buf.fill_(self.n)
+
+
+def percentiles(xs):
+    import numpy as np
+    a = np.asarray(xs, dtype=np.float64)
+    return {"median": round(float(np.median(a)), 5), "p10": round(float(np.percentile(a, 10)), 5),
+            "p90": round(float(np.percentile(a, 90)), 5), "n": int(a.size)}
+
+
+def timed_launches(launch, stream, iters, scrub, before=None):
+    """HIP events on `stream` around `launch()` for `iters` launches; before each one
+    `scrub()` and then `before()` (untimed).  Returns the durations in ms."""
+    import torch
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(iters)]
+    for e0, e1 in evs:
+        scrub()
+        if before is not None:
+            before()
+        e0.record(stream)
+        launch()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    return [e0.elapsed_time(e1) for e0, e1 in evs]
+
+
+def read_bandwidth(dev, stream, iters=20, nbytes=2 << 30):
+    """The streaming-read probe over a 2 GiB buffer: the measured second denominator."""
+    import torch
+    from paged_kv_cache_15_amd import binding as B
+    buf = torch.ones(nbytes // 4, dtype=torch.int32, device=dev)
+    sink = torch.zeros(4, dtype=torch.int32, device=dev)
+    scrub = Scrubber(dev)
+    B.paged_kv_read_bandwidth_probe(buf, sink, stream=stream)
+    ms = timed_launches(lambda: B.paged_kv_read_bandwidth_probe(buf, sink, stream=stream), stream,
+                        iters, scrub)
+    st = percentiles(ms)
+    del buf, scrub
+    torch.cuda.empty_cache()
+    return {"bytes": nbytes, "launch_ms": st, "GB_per_s": round(nbytes / (st["median"] * 1e-3) / 1e9, 1)}
 
 
 def cpu_baseline(w, seconds):
@@ -265,6 +324,121 @@ def decode_graph_timing(layers=32, reps=20):
     return {"layers": layers, "batch": len(lens), "partition_tokens": pt,
             "launches_per_step": (2 if pt == 0 else 3) * layers,
             "eager_us_per_step": round(res["eager"], 1), "graph_us_per_step": round(res["graph"], 1)}
+
+
+def long_context_step_loop(dev, iters=50):
+    """The long-context workload's eight decode steps as a serving loop runs them (16
+    sequences of 16k-32k tokens, 64 q / 8 kv heads, d 128, bf16, 512-token partitions
+    merged by log-sum-exp).  Per step: the host allocator reserves one slot per sequence,
+    the slot mapping, block tables and lengths are copied to the device, then the cache
+    write and attention (partition + merge launches) run; the step ends with a device
+    synchronisation.  Each part is timed (host parts by the wall clock, device parts by
+    HIP events), and so is the whole step.  The new tokens' K/V and the queries are on the
+    device before the loop (a model produces them there).  After the loop, the attention
+    of the last step is timed on its own (median of `iters` scrubbed launches)."""
+    import numpy as np
+    import torch
+    import workloads as W
+    from paged_kv_cache_15_amd import binding as B
+    from paged_kv_cache_15_amd.cache import PagedKVCache, TORCH_DTYPES
+    from paged_kv_cache_15_amd.replay import to_device
+    w = W.make_config(5)
+    cache = PagedKVCache(w.num_blocks, w.num_kv_heads, w.head_dim, w.dtype, w.block_size,
+                         w.free_order, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    ops = [op for op in w.ops]
+    steps, pending = [], None
+    for op in ops:
+        if op[0] == "create":
+            cache.create()
+        elif op[0] == "append" and sum(op[2]) > len(op[1]):            # the prefill
+            k, v = w.kv[op[3]]
+            cache.append(op[1], op[2], to_device(k, w.dtype, dev), to_device(v, w.dtype, dev))
+        elif op[0] == "append":
+            k, v = w.kv[op[3]]
+            pending = (op[1], op[2], to_device(k, w.dtype, dev), to_device(v, w.dtype, dev))
+        elif op[0] == "attend":
+            steps.append(pending + (to_device(w.q[op[2]], w.dtype, dev),))
+    torch.cuda.synchronize()
+    seqs = steps[0][0]
+    hq, d, pt = w.num_q_heads, w.head_dim, w.partition_tokens
+    final_lens = [L for L in w.final_lengths().values()]
+    max_ctx = int(max(final_lens))
+    max_blocks = (max_ctx + w.block_size - 1) // w.block_size
+    nbytes = B.paged_attention_workspace_bytes(cache.desc, len(seqs), hq, max_ctx, pt)
+    ws = torch.zeros(max(nbytes, 16), dtype=torch.uint8, device=dev)
+    out = torch.empty((len(seqs), hq, d), dtype=TORCH_DTYPES[w.dtype], device=dev)
+
+    def attend(tables_d, lens_d):
+        B.paged_attention_partition(cache.desc, out, w.dtype, q, cache.k_pool, cache.v_pool,
+                                    tables_d, lens_d, hq, max_ctx, float(w.scale), pt, ws, stream)
+        B.paged_attention_reduce(cache.desc, out, w.dtype, lens_d, hq, max_ctx, pt, ws, stream)
+
+    # warm-up: attention over the prefilled state (read-only)
+    q = steps[0][4]
+    t, L = cache.block_tables(seqs, max_blocks)
+    attend(torch.from_numpy(t).to(dev), torch.from_numpy(L).to(dev))
+    torch.cuda.synchronize()
+    rows, total_bytes = [], 0
+    t_loop = time.perf_counter()
+    for sq, counts, kd, vd, q in steps:
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        t0 = time.perf_counter()
+        slots, copies = B.paged_kv_append_batch(cache.pool, sq, counts)
+        tables, lens = cache.block_tables(sq, max_blocks)
+        t1 = time.perf_counter()
+        slot_d = torch.from_numpy(slots).to(dev)
+        tables_d, lens_d = torch.from_numpy(tables).to(dev), torch.from_numpy(lens).to(dev)
+        pairs = torch.from_numpy(np.ascontiguousarray(copies)).to(dev) if len(copies) else None
+        t2 = time.perf_counter()
+        e[0].record(stream)
+        if pairs is not None:
+            B.paged_kv_copy_blocks(cache.desc, cache.k_pool, cache.v_pool, pairs, len(copies),
+                                   stream)
+        B.reshape_and_cache(cache.desc, kd, vd, cache.k_pool, cache.v_pool, slot_d, stream=stream)
+        e[1].record(stream)
+        attend(tables_d, lens_d)
+        e[2].record(stream)
+        torch.cuda.synchronize()
+        t3 = time.perf_counter()
+        kv, ab = attention_bytes(lens, int((tables >= 0).sum()), w, out.element_size())
+        total_bytes += ab
+        rows.append({"host_alloc_ms": round((t1 - t0) * 1e3, 4), "h2d_ms": round((t2 - t1) * 1e3, 4),
+                     "cache_write_ms": round(e[0].elapsed_time(e[1]), 4),
+                     "attention_ms": round(e[1].elapsed_time(e[2]), 4),
+                     "step_ms": round((t3 - t0) * 1e3, 4), "copies": int(len(copies))})
+    loop_s = time.perf_counter() - t_loop
+    # the last step's attention alone, scrubbed launches (the kernel's roofline figure)
+    scrub = Scrubber(dev)
+    part_ms = timed_launches(lambda: B.paged_attention_partition(
+        cache.desc, out, w.dtype, q, cache.k_pool, cache.v_pool, tables_d, lens_d, hq, max_ctx,
+        float(w.scale), pt, ws, stream), stream, iters, scrub)
+    red_ms = timed_launches(lambda: B.paged_attention_reduce(
+        cache.desc, out, w.dtype, lens_d, hq, max_ctx, pt, ws, stream), stream, iters, scrub,
+        before=lambda: B.paged_attention_partition(
+            cache.desc, out, w.dtype, q, cache.k_pool, cache.v_pool, tables_d, lens_d, hq,
+            max_ctx, float(w.scale), pt, ws, stream))
+    kv, ab = attention_bytes(lens, int((tables >= 0).sum()), w, out.element_size())
+    pst, rst = percentiles(part_ms), percentiles(red_ms)
+    del scrub
+    cache.close()
+    torch.cuda.empty_cache()
+    mean = {k: round(float(np.mean([r[k] for r in rows])), 4) for k in rows[0] if k != "copies"}
+    return {
+        "workload": w.name, "batch": len(seqs), "steps": len(rows), "partition_tokens": pt,
+        "per_step": rows, "mean": mean,
+        "loop_ms": round(loop_s * 1e3, 3),
+        "loop_seq_tokens_per_s": round(len(seqs) * len(rows) / loop_s, 1),
+        "loop_GB_per_s": round(total_bytes / loop_s / 1e9, 1),
+        "last_step_partition_ms": pst, "last_step_reduce_ms": rst,
+        "roofline": {"kernel": "paged_attention_partition (512-token partitions)", "bound": "hbm",
+                     "achieved": round(ab / (pst["median"] * 1e-3) / 1e9, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(ab / (pst["median"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                     "algorithmic_bytes_per_launch": ab,
+                     "frac_with_merge": round(ab / ((pst["median"] + rst["median"]) * 1e-3) / 1e9
+                                              / HBM_PEAK_GBS, 4)},
+    }
 
 
 MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "f16": 2500.0}
@@ -464,16 +638,36 @@ def main():
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     ms_per_step = elapsed * 1e3 / args.steps
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    log(f"[bench] per-kernel timing, {args.steps} more steps")
-    for i in range(args.steps):
-        starts[i].record(stream)
-        step(evs[i])
-    torch.cuda.synchronize()
-    part_ms = sum(evs[i][0].elapsed_time(evs[i][1]) for i in range(args.steps)) / args.steps
-    red_ms = sum(evs[i][1].elapsed_time(evs[i][2]) for i in range(args.steps)) / args.steps
-    rac_ms = sum(starts[i].elapsed_time(evs[i][0]) for i in range(args.steps)) / args.steps
+    # Per-kernel durations: at least 50 launches of each, HIP events on the launch stream
+    # around each one, a 512 MB scrub write before each (outside the events).
+    iters = max(50, args.steps)
+    scrub = Scrubber(dev)
+    log(f"[bench] per-kernel timing, {iters} launches each, scrubbed")
+    rac = timed_launches(lambda: B.reshape_and_cache(cache.desc, new_k, new_v, cache.k_pool,
+                                                     cache.v_pool, slot_d, stream=stream),
+                         stream, iters, scrub)
+
+    def partition():
+        B.paged_attention_partition(cache.desc, out, out_dtype, q, cache.k_pool, cache.v_pool,
+                                    tables_d, lens_d, w.num_q_heads, max_ctx, float(w.scale), pt,
+                                    ws, stream)
+
+    def reduce():
+        B.paged_attention_reduce(cache.desc, out, out_dtype, lens_d, w.num_q_heads, max_ctx, pt,
+                                 ws, stream)
+    part = timed_launches(partition, stream, iters, scrub)
+    streamk = pt == 0 or (pt == B.PARTITION_AUTO and B.paged_attention_auto_partition_tokens(
+        cache.desc, len(seqs), w.num_q_heads, max_ctx) == 0)
+    # under stream-K the merge happens inside the partition launch: nothing to time
+    red = None if streamk else timed_launches(reduce, stream, iters, scrub, before=partition)
+    part_st, rac_st = percentiles(part), percentiles(rac)
+    red_st = None if red is None else percentiles(red)
+    part_ms, rac_ms = part_st["median"], rac_st["median"]
+    red_ms = None if red_st is None else red_st["median"]
+    del scrub
+    torch.cuda.empty_cache()
+    log("[bench] streaming-read probe")
+    probe = read_bandwidth(dev, stream)
 
     kv_bytes, attn_bytes = attention_bytes(lens, nb_total, w, out.element_size())
     write_bytes = 2 * 2 * n_app * w.num_kv_heads * w.head_dim * w.elem_bytes + 4 * n_app
@@ -506,7 +700,12 @@ def main():
         "kv_bytes_per_step": kv_bytes,
         "step_bytes": step_bytes,
         "kernel_ms": {"reshape_and_cache": round(rac_ms, 5), "paged_attention_partition": round(part_ms, 5),
-                      "paged_attention_reduce": round(red_ms, 5)},
+                      "paged_attention_reduce": None if red_ms is None else round(red_ms, 5)},
+        "kernel_ms_stats": {"reshape_and_cache": rac_st, "paged_attention_partition": part_st,
+                            "paged_attention_reduce": red_st,
+                            "protocol": f"median of {iters} launches each, HIP events on the "
+                                        "launch stream, 512 MB scrub write before each launch "
+                                        "outside the events"},
         "host_alloc_ms_per_step": round(t_host * 1e3, 4),
         "roofline": {
             "kernel": "paged_attention_partition",
@@ -514,16 +713,28 @@ def main():
             "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
             "algorithmic_bytes_per_launch": attn_bytes,
             "traffic_source": traffic_src,
+            "launch_ms": part_st,
+            "measured_read_GB_per_s": probe["GB_per_s"],
+            "frac_of_measured_read": round(achieved / probe["GB_per_s"], 4),
         },
+        "read_probe": probe,
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
         del new_k, new_v
         res["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
     res["prefix_cache_host"] = prefix_cache_host()
-    res["prefill"] = prefill_timing(1, 10, 2)
-    if not args.no_cpu_baseline:
+    if not args.no_extras:
+        del out, q, tables_d, lens_d, ws
+        cache.close()
+        del cache
+        torch.cuda.empty_cache()
+        log("[bench] prefill")
+        res["prefill"] = prefill_timing(1, 10, 2)
+        log("[bench] decode graph")
         res["decode_graph"] = decode_graph_timing()
+        log("[bench] long-context step loop")
+        res["long_context_step_loop"] = long_context_step_loop(dev)
     print(json.dumps(res), flush=True)
 
 

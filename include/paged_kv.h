@@ -366,6 +366,17 @@ paged_kv_status paged_attention_prefill(const paged_kv_pool_desc* desc, void* ou
                                         int32_t num_q_heads, int32_t max_q_len,
                                         int32_t max_context_len, float scale, void* stream);
 
+/* ------------------------------------------------------------ measurement ---- */
+
+/* A plain streaming read of `bytes` bytes at `buf` (device, 16-byte aligned, a multiple
+ * of 16), with the access pattern of the attention kernels' K/V loads (16-byte
+ * nontemporal loads, 1 KiB contiguous per wave instruction, one wave per SIMD): the
+ * measured read bandwidth that the decode roofline is stated against beside the part's
+ * specified peak.  `sink` is a device int32 that is written only in a case no real
+ * buffer reaches (it keeps the loads alive).  Errors: INVALID_ARG. */
+paged_kv_status paged_kv_read_bandwidth_probe(const void* buf, size_t bytes, void* sink,
+                                              void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -90,6 +90,56 @@ def paged_prefill(q, k_pool, v_pool, tables, context_lens, q_start, scale, dtype
     return out
 
 
+def causal_rows(q, k, v, scale, first_pos):
+    """Causal attention of one sequence's consecutive query rows, all rows at once.
+
+    Query i sits at position first_pos + i and sees keys 0 .. first_pos + i (the same
+    reading as paged_prefill).  Per query head h (KV head h // (Hq / Hkv)): the score
+    matrix scale * Q K^T, the keys past each row's position removed, the softmax of each
+    row (exp(z - row max) / row sum) and its product with V: dense_decode of every row,
+    written as matrix products.  q: float64 [n][Hq][d]; k, v: float64 [>= first_pos + n]
+    [Hkv][d].  Returns float64 [n][Hq][d].
+    """
+    q = np.asarray(q, dtype=np.float64)
+    n, hq, d = q.shape
+    hkv = k.shape[1]
+    if hq % hkv:
+        raise ValueError("query heads must be a multiple of KV heads")
+    group = hq // hkv
+    L = int(first_pos) + n
+    hidden = np.arange(L)[None, :] > (int(first_pos) + np.arange(n))[:, None]
+    out = np.empty((n, hq, d), dtype=np.float64)
+    for h in range(hq):
+        g = h // group
+        z = q[:, h, :] @ k[:L, g, :].T          # (the steps below work in place: the
+        z *= float(scale)                      # matrices are large)
+        np.putmask(z, hidden, -np.inf)
+        z -= z.max(axis=1, keepdims=True)
+        np.exp(z, out=z)
+        out[:, h, :] = (z @ v[:L, g, :]) / z.sum(axis=1, keepdims=True)
+    return out
+
+
+def paged_prefill_rows(q, k_pool, v_pool, tables, context_lens, q_start, scale, dtype,
+                       block_size, seqs):
+    """paged_prefill for the listed sequences with each sequence's rows computed at once
+    by causal_rows (same reading, same result up to rounding order); the other rows are
+    NaN."""
+    q = np.asarray(q, dtype=np.float64)
+    out = np.full(q.shape, np.nan)
+    for b in seqs:
+        L, r0, r1 = int(context_lens[b]), int(q_start[b]), int(q_start[b + 1])
+        n = r1 - r0
+        if n < 0 or n > L:
+            raise ValueError("a sequence needs 0 <= query count <= context length")
+        if n == 0:
+            continue
+        kb, vb = gather_sequence(k_pool, v_pool, tables[b], L, block_size)
+        out[r0:r1] = causal_rows(q[r0:r1], storage_bits_to_f64(kb, dtype),
+                                 storage_bits_to_f64(vb, dtype), scale, L - n)
+    return out
+
+
 def partial_state(z, v):
     """Softmax state of one slice of tokens: (max score, sum of weights, weighted V)."""
     m = z.max()

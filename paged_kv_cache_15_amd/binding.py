@@ -89,6 +89,7 @@ _SIGNATURES = {
                                                  _i32, _i32, _i32, _f32, _i32, _vp, _sz, _vp]),
     "paged_attention_reduce": (ctypes.c_int, [_descp, _vp, _i32, _vp, _i32, _i32, _i32, _i32, _vp,
                                               _sz, _vp]),
+    "paged_kv_read_bandwidth_probe": (ctypes.c_int, [_vp, _sz, _vp, _vp]),
     "paged_attention_prefill": (ctypes.c_int, [_descp, _vp, _i32, _vp, _vp, _vp, _vp, _vp, _i32,
                                                _vp, _i32, _i32, _i32, _i32, _f32, _vp]),
 }
@@ -487,3 +488,12 @@ def paged_attention_reduce(desc, out, out_dtype, context_lens, num_q_heads, max_
                                       int(num_q_heads), int(max_context_len),
                                       int(partition_tokens), _ptr(workspace), ws_bytes,
                                       _stream(stream)))
+
+
+# ------------------------------------------------------------ measurement ----
+def paged_kv_read_bandwidth_probe(buf, sink, nbytes=None, stream=None):
+    """Streaming read of `buf` (a device tensor, or an address with nbytes given)."""
+    if nbytes is None:
+        nbytes = buf.numel() * buf.element_size()
+    _check("paged_kv_read_bandwidth_probe",
+           lib.paged_kv_read_bandwidth_probe(_ptr(buf), int(nbytes), _ptr(sink), _stream(stream)))

@@ -74,7 +74,7 @@ def test_prefill_full_size_sampled(k, bs, d, every):
     prefill, the launch the bench times; first, middle and last rows at the other sizes)
     and on 64 random rows (a query at position p is the oracle's prefill of a one-token
     chunk over p + 1 tokens)."""
-    from oracle.attention import paged_prefill
+    from oracle.attention import paged_prefill, paged_prefill_rows
     from oracle import lowp
     w = W.make_prefill_config(k, block_size=bs, head_dim=d)
     say(f"[prefill-full] {w.name}")
@@ -97,8 +97,8 @@ def test_prefill_full_size_sampled(k, bs, d, every):
     for s in ends:
         n, L = int(counts[s]), int(lens[s])
         if every:
-            want = paged_prefill(q, o.k_pool, o.v_pool, tables, lens, starts, w.scale, w.dtype,
-                                 w.block_size, seqs=[s])
+            want = paged_prefill_rows(q, o.k_pool, o.v_pool, tables, lens, starts, w.scale,
+                                      w.dtype, w.block_size, seqs=[s])
             rows = slice(int(starts[s]), int(starts[s + 1]))
             worst = max(worst, float(np.abs(got[rows] - want[rows]).max()))
         else:

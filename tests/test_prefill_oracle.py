@@ -150,3 +150,38 @@ def test_pins_catch_planted_prefill_mistakes(kind):
         except AssertionError:
             caught += 1
     assert caught >= 1, kind
+
+
+@pytest.mark.parametrize("dt,hq,hkv,d,bs", [("bf16", 8, 2, 64, 16), ("f16", 4, 4, 32, 1),
+                                           ("bf16", 6, 3, 16, 32)])
+def test_matrix_form_equals_row_by_row_and_sdpa(dt, hq, hkv, d, bs):
+    """The matrix form (causal_rows / paged_prefill_rows) against the row-by-row oracle
+    and against PyTorch's causal attention in float64, whole prompts and chunks."""
+    rng = np.random.default_rng(hq * 13 + d + bs)
+    lens = [1, 17, 40, 75]
+    kp, vp, tab, kv = _pool(rng, lens, hkv, d, dt, bs)
+    counts = [1, 9, 40, 30]                        # a whole prompt (40) and chunks
+    starts = np.concatenate([[0], np.cumsum(counts)])
+    q = _queries(rng, int(starts[-1]), hq, d, dt)
+    scale = 1 / np.sqrt(d)
+    a = ATT.paged_prefill(q, kp, vp, tab, lens, starts, scale, dt, bs)
+    b = ATT.paged_prefill_rows(q, kp, vp, tab, lens, starts, scale, dt, bs, seqs=range(len(lens)))
+    assert np.abs(a - b).max() <= 1e-12
+    for i, (L, n) in enumerate(zip(lens, counts)):
+        ref = _sdpa_causal(q[starts[i]:starts[i + 1]], kv[i][0], kv[i][1], scale)
+        assert np.abs(b[starts[i]:starts[i + 1]] - ref).max() <= 1e-12
+
+
+def test_matrix_form_catches_a_dropped_mask():
+    """Planted mistake: without removing the keys past each row's position the matrix
+    form no longer matches the row-by-row oracle."""
+    rng = np.random.default_rng(3)
+    k = rng.standard_normal((20, 2, 8))
+    v = rng.standard_normal((20, 2, 8))
+    q = rng.standard_normal((20, 4, 8))
+    good = ATT.causal_rows(q, k, v, 0.3, 0)
+    rows = np.stack([ATT.dense_decode(q[i], k[:i + 1], v[:i + 1], 0.3) for i in range(20)])
+    assert np.abs(good - rows).max() <= 1e-12
+    nomask = np.stack([ATT.dense_decode(q[i], k, v, 0.3) for i in range(20)])
+    assert np.abs(good - nomask).max() > 1e-3
+
