@@ -111,12 +111,14 @@ def causal_rows(q, k, v, scale, first_pos):
     out = np.empty((n, hq, d), dtype=np.float64)
     for h in range(hq):
         g = h // group
-        z = q[:, h, :] @ k[:L, g, :].T          # (the steps below work in place: the
-        z *= float(scale)                      # matrices are large)
+        kg = np.ascontiguousarray(k[:L, g, :])  # (contiguous operands keep the products on
+        vg = np.ascontiguousarray(v[:L, g, :])  # BLAS; the steps below work in place)
+        z = q[:, h, :] @ kg.T
+        z *= float(scale)
         np.putmask(z, hidden, -np.inf)
         z -= z.max(axis=1, keepdims=True)
         np.exp(z, out=z)
-        out[:, h, :] = (z @ v[:L, g, :]) / z.sum(axis=1, keepdims=True)
+        out[:, h, :] = (z @ vg) / z.sum(axis=1, keepdims=True)
     return out
 
 

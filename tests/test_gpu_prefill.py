@@ -90,21 +90,25 @@ def test_prefill_full_size_sampled(k, bs, d, every):
     got = g.outputs[-1]
     assert torch.isfinite(got).all()
     got = got.double().cpu().numpy()
-    q = lowp.storage_bits_to_f64(lowp.to_storage_bits(w.q[op[3]], w.dtype), w.dtype)
     tables, lens = o.tables[-1], o.context_lens[-1]
+    qraw = w.q[op[3]]
+
+    def qrows(r0, r1):   # the oracle's rounding of only the rows it needs
+        return lowp.storage_bits_to_f64(lowp.to_storage_bits(qraw[r0:r1], w.dtype), w.dtype)
     worst = 0.0
     ends = sorted({int(np.argmin(lens)), int(np.argmax(lens))})
     for s in ends:
         n, L = int(counts[s]), int(lens[s])
+        r0, r1 = int(starts[s]), int(starts[s + 1])
         if every:
-            want = paged_prefill_rows(q, o.k_pool, o.v_pool, tables, lens, starts, w.scale,
-                                      w.dtype, w.block_size, seqs=[s])
-            rows = slice(int(starts[s]), int(starts[s + 1]))
-            worst = max(worst, float(np.abs(got[rows] - want[rows]).max()))
+            want = paged_prefill_rows(qrows(r0, r1), o.k_pool, o.v_pool, tables[s:s + 1],
+                                      lens[s:s + 1], np.array([0, n]), w.scale, w.dtype,
+                                      w.block_size, seqs=[0])
+            worst = max(worst, float(np.abs(got[r0:r1] - want).max()))
         else:
             for i in sorted({0, n // 2, n - 1}):
-                row = int(starts[s] + i)
-                want = paged_prefill(q[row:row + 1], o.k_pool, o.v_pool, tables[s:s + 1],
+                row = r0 + i
+                want = paged_prefill(qrows(row, row + 1), o.k_pool, o.v_pool, tables[s:s + 1],
                                      [L - n + i + 1], np.array([0, 1]), w.scale, w.dtype,
                                      w.block_size)
                 worst = max(worst, float(np.abs(got[row] - want[0]).max()))
@@ -113,7 +117,7 @@ def test_prefill_full_size_sampled(k, bs, d, every):
     for row in rng.choice(int(starts[-1]), size=64, replace=False):
         s = int(np.searchsorted(starts, row, side="right") - 1)
         n, L, i = int(counts[s]), int(lens[s]), int(row - starts[s])
-        want = paged_prefill(q[row:row + 1], o.k_pool, o.v_pool, tables[s:s + 1],
+        want = paged_prefill(qrows(row, row + 1), o.k_pool, o.v_pool, tables[s:s + 1],
                              [L - n + i + 1], np.array([0, 1]), w.scale, w.dtype, w.block_size)
         worst = max(worst, float(np.abs(got[row] - want[0]).max()))
     say(f"   + 64 random rows: max|err| {worst:.3e}")
