@@ -313,6 +313,26 @@ paged_kv_status paged_attention_decode(const paged_kv_pool_desc* desc, void* out
                                        int32_t partition_tokens, void* workspace,
                                        size_t workspace_bytes, void* stream);
 
+/* paged_attention_decode for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.  Same
+ * arguments, results and errors as paged_attention_decode (bit-identical outputs for
+ * the same schedule), without the workspace: the partial results and merge counters
+ * live in a static device array of the library, 64 MiB per device, held by every
+ * device the library runs on until the process ends (1 MiB of it for counters, one
+ * int32 per (sequence, head unit); 63 MiB for partial results).  A call that would need
+ * more returns PAGED_KV_ERR_BUFFER_TOO_SMALL before launching anything.  It makes no
+ * allocation of its own: the array's address is looked up once per device (first call
+ * with that device current), its counters cleared there by a fill kernel on `stream`.
+ * All calls on one device share the array and every call leaves the counters at zero,
+ * so calls on one device must not overlap (two streams at once race on the array). */
+paged_kv_status paged_attention_decode_static(const paged_kv_pool_desc* desc, void* out,
+                                              int32_t out_dtype, const void* q, const void* k_pool,
+                                              const void* v_pool, const int32_t* block_tables,
+                                              int32_t max_blocks_per_seq,
+                                              const int32_t* context_lens, int32_t num_seqs,
+                                              int32_t num_q_heads, int32_t max_context_len,
+                                              float scale, int32_t partition_tokens, void* stream);
+
 /* The two halves of paged_attention_decode, exposed so each kernel can be timed on its
  * own.  With fixed partitions, paged_attention_partition writes `out` for sequences that
  * fit one partition and the per-partition (max, sum, weighted values) state of the

@@ -87,6 +87,8 @@ _SIGNATURES = {
                                               _i32, _i32, _i32, _f32, _i32, _vp, _sz, _vp]),
     "paged_attention_partition": (ctypes.c_int, [_descp, _vp, _i32, _vp, _vp, _vp, _vp, _i32, _vp,
                                                  _i32, _i32, _i32, _f32, _i32, _vp, _sz, _vp]),
+    "paged_attention_decode_static": (ctypes.c_int, [_descp, _vp, _i32, _vp, _vp, _vp, _vp, _i32,
+                                                     _vp, _i32, _i32, _i32, _f32, _i32, _vp]),
     "paged_attention_reduce": (ctypes.c_int, [_descp, _vp, _i32, _vp, _i32, _i32, _i32, _i32, _vp,
                                               _sz, _vp]),
     "paged_kv_read_bandwidth_probe": (ctypes.c_int, [_vp, _sz, _vp, _vp]),
@@ -435,6 +437,18 @@ def paged_attention_decode(desc, out, out_dtype, q, k_pool, v_pool, block_tables
                                                   block_tables, context_lens, num_q_heads,
                                                   max_context_len, scale, partition_tokens,
                                                   workspace, stream)))
+
+
+def paged_attention_decode_static(desc, out, out_dtype, q, k_pool, v_pool, block_tables,
+                                  context_lens, num_q_heads, max_context_len, scale,
+                                  partition_tokens=0, stream=None):
+    """paged_attention_decode without a workspace: the library's static scratch."""
+    args = _attn_args("paged_attention_decode_static", desc, out, out_dtype, q, k_pool, v_pool,
+                      block_tables, context_lens, num_q_heads, max_context_len, scale,
+                      partition_tokens, None, stream)
+    # the same arguments minus (workspace, workspace_bytes)
+    _check("paged_attention_decode_static",
+           lib.paged_attention_decode_static(*args[:14], args[16]))
 
 
 def paged_attention_partition(desc, out, out_dtype, q, k_pool, v_pool, block_tables, context_lens,

@@ -54,7 +54,10 @@ struct StreamLaunch {
     int32_t block_size;
     int32_t max_context_len;
     float scale;
-    void* workspace;
+    // workspace, split: the per-(sequence, head unit) merge counters (zero on entry, left
+    // zero) and the partial results (m, l, acc from StreamPlan::m_off on, rebased to 0)
+    int32_t* counters;
+    char* data;
 };
 
 // One launch: partition work and the merge of multi-piece units.

@@ -35,6 +35,8 @@
 // 16 blocks, each lane loading from its own token's block, and V (stored token-major at
 // that size) is turned into the V^T operand through LDS.
 
+#include <mutex>
+
 #include "attention_common.h"
 #include "attention_host.h"
 
@@ -663,6 +665,21 @@ __global__ __launch_bounds__(D * reduce_groups_max<D>()) void attn_reduce_kernel
 // host side
 // ---------------------------------------------------------------------------------
 
+// Scratch of paged_attention_decode_static, for callers that cannot allocate: a fixed
+// region of merge counters (zero between calls: zeroed once per device, and every call
+// leaves the counters it uses at zero) followed by room for partial results.  Each device
+// the library runs on holds its own copy until the process ends; calls on one device
+// share it, so calls that overlap there race.
+constexpr size_t kStaticScratchBytes = size_t(64) << 20;
+constexpr size_t kStaticCounterBytes = size_t(1) << 20;
+static __device__ __align__(256) char scratch[kStaticScratchBytes];
+
+__global__ void zero_words(int32_t* p, int64_t n) {
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+         i += (int64_t)gridDim.x * blockDim.x)
+        p[i] = 0;
+}
+
 struct Plan {
     PartitionArgs a;
     int dtype, out_dtype, head_dim, block_size;
@@ -717,12 +734,23 @@ size_t workspace_for(size_t cnt_bytes, int64_t num_seqs, int64_t hq, int64_t d, 
     return cnt_bytes + 2 * align256(rows * sizeof(float)) + rows * d * sizeof(float);
 }
 
+// Where a call's workspace lives: one caller buffer (counters first, then the partial
+// results), or the library's static scratch array (a fixed counter region, then the
+// partial results).
+struct WsSource {
+    char* buf;              // caller workspace, or NULL for the static scratch
+    size_t bytes;
+    char* static_base;      // this device's address of the static scratch array
+};
+
 paged_kv_status make_plan(Plan& pl, const paged_kv_pool_desc* desc, void* out, int32_t out_dtype,
                           const void* q, const void* k_pool, const void* v_pool,
                           const int32_t* tables, int32_t max_blocks, const int32_t* lens,
                           int32_t num_seqs, int32_t hq, int32_t max_ctx, float scale,
-                          int32_t part_tokens, void* ws, size_t ws_bytes, void* stream,
+                          int32_t part_tokens, const WsSource& src, void* stream,
                           bool need_kv) {
+    void* ws = src.buf;
+    const size_t ws_bytes = src.bytes;
     if (!pkv::kernel_desc(desc, true)) return PAGED_KV_ERR_INVALID_ARG;
     if (num_seqs < 0 || hq < 1) {
         pkv::set_error("num_seqs %d < 0 or num_q_heads %d < 1", num_seqs, hq);
@@ -770,7 +798,17 @@ paged_kv_status make_plan(Plan& pl, const paged_kv_pool_desc* desc, void* out, i
             pkv::set_error("null pointer argument");
             return PAGED_KV_ERR_INVALID_ARG;
         }
-        if (pl.ws_needed > 0 && (!ws || ws_bytes < pl.ws_needed)) {
+        if (src.static_base) {
+            const size_t cnt = counter_bytes(desc, num_seqs, hq);
+            if (pl.ws_needed > 0 &&
+                (cnt > kStaticCounterBytes || pl.ws_needed - cnt > kStaticScratchBytes - kStaticCounterBytes)) {
+                pkv::set_error("the static scratch holds %zu counter bytes and %zu bytes of partial "
+                               "results; this call needs %zu and %zu (use paged_attention_decode "
+                               "with a workspace)", kStaticCounterBytes,
+                               kStaticScratchBytes - kStaticCounterBytes, cnt, pl.ws_needed - cnt);
+                return PAGED_KV_ERR_BUFFER_TOO_SMALL;
+            }
+        } else if (pl.ws_needed > 0 && (!ws || ws_bytes < pl.ws_needed)) {
             pkv::set_error("workspace of %zu bytes needed (%zu given)", pl.ws_needed, ws_bytes);
             return PAGED_KV_ERR_BUFFER_TOO_SMALL;
         }
@@ -788,11 +826,21 @@ paged_kv_status make_plan(Plan& pl, const paged_kv_pool_desc* desc, void* out, i
     a.block_tables = tables;
     a.context_lens = lens;
     const size_t rows = (size_t)num_seqs * hq * max_parts;
-    const size_t cnt = counter_bytes(desc, num_seqs, hq);
-    char* wsc = static_cast<char*>(ws);
-    a.ws_m = pl.ws_needed ? reinterpret_cast<float*>(wsc + cnt) : nullptr;
-    a.ws_l = pl.ws_needed ? reinterpret_cast<float*>(wsc + cnt + align256(rows * 4)) : nullptr;
-    a.ws_acc = pl.ws_needed ? reinterpret_cast<float*>(wsc + cnt + 2 * align256(rows * 4)) : nullptr;
+    // counters, then the partial results (both schedules lay these out from `data` on)
+    int32_t* counters = nullptr;
+    char* data = nullptr;
+    if (pl.ws_needed) {
+        if (src.static_base) {
+            counters = reinterpret_cast<int32_t*>(src.static_base);
+            data = src.static_base + kStaticCounterBytes;
+        } else {
+            counters = reinterpret_cast<int32_t*>(ws);
+            data = static_cast<char*>(ws) + counter_bytes(desc, num_seqs, hq);
+        }
+    }
+    a.ws_m = pl.ws_needed ? reinterpret_cast<float*>(data) : nullptr;
+    a.ws_l = pl.ws_needed ? reinterpret_cast<float*>(data + align256(rows * 4)) : nullptr;
+    a.ws_acc = pl.ws_needed ? reinterpret_cast<float*>(data + 2 * align256(rows * 4)) : nullptr;
     a.max_blocks_per_seq = max_blocks;
     a.num_q_heads = hq;
     a.num_kv_heads = desc->num_kv_heads;
@@ -814,7 +862,8 @@ paged_kv_status make_plan(Plan& pl, const paged_kv_pool_desc* desc, void* out, i
     pl.stream = reinterpret_cast<hipStream_t>(stream);
     pl.sl = pkv::StreamLaunch{out, out_dtype, q, k_pool, v_pool, tables, max_blocks, lens,
                               num_seqs, hq, desc->num_kv_heads, desc->num_blocks, desc->dtype,
-                              desc->head_dim, desc->block_size, max_ctx, scale, ws};
+                              desc->head_dim, desc->block_size, max_ctx, scale, counters,
+                              data};
     return PAGED_KV_OK;
 }
 
@@ -881,6 +930,61 @@ paged_kv_status launch_status(const char* what) {
     return PAGED_KV_OK;
 }
 
+void launch_partition(const Plan& pl, void* stream) {
+    if (pl.streamk) pkv::launch_streamk_partition(pl.sl, pl.sp, stream);
+    else if (pl.head_dim == 64) launch_partition_b<64>(pl);
+    else if (pl.head_dim == 256) launch_partition_b<256>(pl);
+    else launch_partition_b<128>(pl);
+}
+
+// Fixed partitions only: the merge kernel (stream-K merges inside its one launch).
+void launch_reduce(const Plan& pl, int num_seqs) {
+    if (pl.streamk || pl.a.max_parts <= 1) return;
+    if (pl.head_dim == 64) launch_reduce_d<64>(pl, num_seqs);
+    else if (pl.head_dim == 256) launch_reduce_d<256>(pl, num_seqs);
+    else launch_reduce_d<128>(pl, num_seqs);
+}
+
+// This device's address of the static scratch array (host code may not use the array's
+// name itself: on the host it is only a stand-in for the symbol).  Looked up once per
+// device with that device current; `zeroed` tells whether its counters were cleared.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+char* g_scratch_addr[kMaxDevices];
+bool g_scratch_zeroed[kMaxDevices];
+
+paged_kv_status static_scratch(int& dev, char*& base) {
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+        (void)hipGetLastError();
+        pkv::set_error("no usable current HIP device for the static scratch");
+        return PAGED_KV_ERR_HIP;
+    }
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    if (!g_scratch_addr[dev]) {
+        void* p = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p) {
+            pkv::set_error("hipGetSymbolAddress of the static scratch failed: %s", hipGetErrorString(e));
+            return PAGED_KV_ERR_HIP;
+        }
+        g_scratch_addr[dev] = static_cast<char*>(p);
+    }
+    base = g_scratch_addr[dev];
+    return PAGED_KV_OK;
+}
+
+// Clears the counter region on `stream` the first time a call on this device launches
+// (a fill kernel, not a memset, so that it may also be recorded into a graph).
+paged_kv_status zero_static_counters(int dev, char* base, hipStream_t stream) {
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    if (g_scratch_zeroed[dev]) return PAGED_KV_OK;
+    zero_words<<<dim3(256), dim3(256), 0, stream>>>(reinterpret_cast<int32_t*>(base),
+                                                    (int64_t)(kStaticCounterBytes / sizeof(int32_t)));
+    const paged_kv_status st = launch_status("static scratch clear");
+    if (st == PAGED_KV_OK) g_scratch_zeroed[dev] = true;
+    return st;
+}
+
 }  // namespace
 
 extern "C" {
@@ -925,13 +1029,11 @@ paged_kv_status paged_attention_partition(const paged_kv_pool_desc* desc, void* 
     Plan pl;
     paged_kv_status st = make_plan(pl, desc, out, out_dtype, q, k_pool, v_pool, block_tables,
                                    max_blocks_per_seq, context_lens, num_seqs, num_q_heads,
-                                   max_context_len, scale, partition_tokens, workspace,
-                                   workspace_bytes, stream, true);
+                                   max_context_len, scale, partition_tokens,
+                                   WsSource{static_cast<char*>(workspace), workspace_bytes, nullptr},
+                                   stream, true);
     if (st != PAGED_KV_OK || num_seqs == 0) return st;
-    if (pl.streamk) pkv::launch_streamk_partition(pl.sl, pl.sp, stream);
-    else if (pl.head_dim == 64) launch_partition_b<64>(pl);
-    else if (pl.head_dim == 256) launch_partition_b<256>(pl);
-    else launch_partition_b<128>(pl);
+    launch_partition(pl, stream);
     return launch_status("paged attention partition kernel");
 }
 
@@ -943,16 +1045,14 @@ paged_kv_status paged_attention_reduce(const paged_kv_pool_desc* desc, void* out
     pkv::clear_error();
     Plan pl;
     const int32_t max_blocks = desc ? (max_context_len + desc->block_size - 1) / std::max(1, desc->block_size) : 0;
-    paged_kv_status st = make_plan(pl, desc, out, out_dtype, nullptr, nullptr, nullptr, nullptr,
-                                   max_blocks, context_lens, num_seqs, num_q_heads, max_context_len,
-                                   1.f, partition_tokens, const_cast<void*>(workspace),
-                                   workspace_bytes, stream, false);
+    paged_kv_status st = make_plan(
+        pl, desc, out, out_dtype, nullptr, nullptr, nullptr, nullptr, max_blocks, context_lens,
+        num_seqs, num_q_heads, max_context_len, 1.f, partition_tokens,
+        WsSource{static_cast<char*>(const_cast<void*>(workspace)), workspace_bytes, nullptr}, stream,
+        false);
     if (st != PAGED_KV_OK || num_seqs == 0) return st;
-    if (pl.streamk) return st;   // the stream-K launch merges in-kernel
-    if (pl.a.max_parts <= 1) return st;
-    if (pl.head_dim == 64) launch_reduce_d<64>(pl, num_seqs);
-    else if (pl.head_dim == 256) launch_reduce_d<256>(pl, num_seqs);
-    else launch_reduce_d<128>(pl, num_seqs);
+    if (pl.streamk || pl.a.max_parts <= 1) return st;   // nothing to merge in a second launch
+    launch_reduce(pl, num_seqs);
     return launch_status("paged attention reduce kernel");
 }
 
@@ -971,6 +1071,32 @@ paged_kv_status paged_attention_decode(const paged_kv_pool_desc* desc, void* out
     return paged_attention_reduce(desc, out, out_dtype, context_lens, num_seqs, num_q_heads,
                                   max_context_len, partition_tokens, workspace, workspace_bytes,
                                   stream);
+}
+
+paged_kv_status paged_attention_decode_static(const paged_kv_pool_desc* desc, void* out,
+                                              int32_t out_dtype, const void* q, const void* k_pool,
+                                              const void* v_pool, const int32_t* block_tables,
+                                              int32_t max_blocks_per_seq,
+                                              const int32_t* context_lens, int32_t num_seqs,
+                                              int32_t num_q_heads, int32_t max_context_len,
+                                              float scale, int32_t partition_tokens, void* stream) {
+    pkv::clear_error();
+    int dev = -1;
+    char* base = nullptr;
+    paged_kv_status st = static_scratch(dev, base);
+    if (st != PAGED_KV_OK) return st;
+    Plan pl;
+    st = make_plan(pl, desc, out, out_dtype, q, k_pool, v_pool, block_tables, max_blocks_per_seq,
+                   context_lens, num_seqs, num_q_heads, max_context_len, scale, partition_tokens,
+                   WsSource{nullptr, 0, base}, stream, true);
+    if (st != PAGED_KV_OK || num_seqs == 0) return st;
+    st = zero_static_counters(dev, base, pl.stream);
+    if (st != PAGED_KV_OK) return st;
+    launch_partition(pl, stream);
+    st = launch_status("paged attention partition kernel");
+    if (st != PAGED_KV_OK) return st;
+    launch_reduce(pl, num_seqs);
+    return launch_status("paged attention reduce kernel");
 }
 
 }  // extern "C"

@@ -910,17 +910,16 @@ void attn_valu_streamk(StreamArgs a) {
 // ---------------------------------------------------------------------------------
 StreamArgs make_args(const pkv::StreamLaunch& L, const pkv::StreamPlan& P) {
     StreamArgs a;
-    char* ws = static_cast<char*>(L.workspace);
     a.out = L.out;
     a.q = L.q;
     a.k_pool = L.k_pool;
     a.v_pool = L.v_pool;
     a.block_tables = L.block_tables;
     a.context_lens = L.context_lens;
-    a.counters = reinterpret_cast<int32_t*>(ws + P.cnt_off);
-    a.ws_m = reinterpret_cast<float*>(ws + P.m_off);
-    a.ws_l = reinterpret_cast<float*>(ws + P.l_off);
-    a.ws_acc = reinterpret_cast<float*>(ws + P.acc_off);
+    a.counters = L.counters;
+    a.ws_m = reinterpret_cast<float*>(L.data);
+    a.ws_l = reinterpret_cast<float*>(L.data + (P.l_off - P.m_off));
+    a.ws_acc = reinterpret_cast<float*>(L.data + (P.acc_off - P.m_off));
     a.num_seqs = L.num_seqs;
     a.max_blocks_per_seq = L.max_blocks_per_seq;
     a.num_q_heads = L.num_q_heads;
