@@ -60,6 +60,10 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true",
                     help="only the decode step (no prefill, graph-step and step-loop lines)")
+    ap.add_argument("--shared-prefix", action="store_true",
+                    help="only time the parallel-sampling workload (per-sample and shared-prefix "
+                         "decode) and print that line")
+    ap.add_argument("--shared-partition-tokens", type=int, default=0)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (3 times) and exit: the "
                          "known-size reference for scaling HBM byte counters")
@@ -441,6 +445,95 @@ def long_context_step_loop(dev, iters=50):
     }
 
 
+def shared_prefix_timing(dev, iters=50, partition_tokens=0, max_group=8):
+    """The parallel-sampling workload (32 prompts x 8 samples, 2056-token prompts forked,
+    tails of 64-512 tokens; 32 q / 8 kv heads, d 128, bf16): attention launched per
+    sample (the standard decode at the workload's 512-token partitions) and with each
+    prompt's shared blocks read once for its 8 samples (paged_attention_decode_shared_
+    prefix).  Median of `iters` scrubbed launches each.  Fractions of the HBM peak are
+    stated on the unique bytes: every distinct token's K/V once (a group's shared tokens
+    once, each sample's own tokens once), plus queries, outputs, tables and lengths."""
+    import numpy as np
+    import torch
+    import workloads as W
+    from paged_kv_cache_15_amd import binding as B
+    from paged_kv_cache_15_amd.cache import PagedKVCache, TORCH_DTYPES
+    from paged_kv_cache_15_amd.replay import to_device
+    w = W.make_config(4)
+    cache = PagedKVCache(w.num_blocks, w.num_kv_heads, w.head_dim, w.dtype, w.block_size,
+                         w.free_order, device=dev)
+    for op in w.ops:
+        if op[0] == "create":
+            cache.create()
+        elif op[0] == "fork":
+            cache.fork(op[1])
+        elif op[0] == "append":
+            k, v = w.kv[op[3]]
+            cache.append(op[1], op[2], to_device(k, w.dtype, dev), to_device(v, w.dtype, dev))
+        elif op[0] == "attend":
+            seqs, q = op[1], to_device(w.q[op[2]], w.dtype, dev)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    hq, d = w.num_q_heads, w.head_dim
+    tables, lens = cache.block_tables(seqs)
+    tables_d, lens_d = torch.from_numpy(tables).to(dev), torch.from_numpy(lens).to(dev)
+    max_ctx = int(lens.max())
+    out = torch.empty((len(seqs), hq, d), dtype=TORCH_DTYPES[w.dtype], device=dev)
+    gs, sh, max_shared = B.paged_kv_shared_prefix_groups(cache.pool, seqs, max_group, 16)
+    gs_d, sh_d = torch.from_numpy(gs).to(dev), torch.from_numpy(sh).to(dev)
+    nb_sh = B.paged_attention_shared_prefix_workspace_bytes(cache.desc, len(seqs), hq, max_ctx,
+                                                            len(sh), max_group, max_shared,
+                                                            partition_tokens)
+    ws_sh = torch.empty(nb_sh, dtype=torch.uint8, device=dev)
+    pt = w.partition_tokens
+    nb_std = B.paged_attention_workspace_bytes(cache.desc, len(seqs), hq, max_ctx, pt)
+    ws_std = torch.zeros(max(nb_std, 16), dtype=torch.uint8, device=dev)
+    scrub = Scrubber(dev)
+
+    def shared():
+        B.paged_attention_decode_shared_prefix(cache.desc, out, w.dtype, q, cache.k_pool,
+                                               cache.v_pool, tables_d, lens_d, hq, max_ctx,
+                                               float(w.scale), gs_d, sh_d, len(sh), max_group,
+                                               max_shared, partition_tokens, ws_sh, stream)
+
+    def standard():
+        B.paged_attention_decode(cache.desc, out, w.dtype, q, cache.k_pool, cache.v_pool,
+                                 tables_d, lens_d, hq, max_ctx, float(w.scale), pt, ws_std,
+                                 stream)
+    shared()
+    standard()
+    t_sh = percentiles(timed_launches(shared, stream, iters, scrub))
+    t_std = percentiles(timed_launches(standard, stream, iters, scrub))
+    grp = np.repeat(np.arange(len(sh)), np.diff(gs))
+    unique_tokens = int(sh.sum()) + int((lens - sh[grp]).sum())
+    per_tok = 2 * w.num_kv_heads * d * w.elem_bytes
+    extra = 2 * len(seqs) * hq * d * w.elem_bytes + 4 * int((tables >= 0).sum()) + 4 * len(seqs)
+    unique = unique_tokens * per_tok + extra
+    logical = int(lens.sum()) * per_tok + extra
+    distinct_blocks = len(np.unique(tables[tables >= 0]))
+    del scrub
+    cache.close()
+    torch.cuda.empty_cache()
+
+    def line(st):
+        ach = unique / (st["median"] * 1e-3) / 1e9
+        return {"launch_ms": st, "unique_GB_per_s": round(ach, 1),
+                "frac_of_peak_on_unique_bytes": round(ach / HBM_PEAK_GBS, 4),
+                "logical_GB_per_s": round(logical / (st["median"] * 1e-3) / 1e9, 1)}
+    return {"workload": w.name, "batch": len(seqs), "groups": len(sh), "max_group": max_group,
+            "shared_tokens_per_group": int(max_shared), "partition_tokens": partition_tokens,
+            "unique_bytes": unique, "logical_bytes": logical,
+            "distinct_blocks": distinct_blocks,
+            "distinct_block_bytes": distinct_blocks * w.block_size * per_tok,
+            "shared_prefix_decode": line(t_sh),
+            "per_sample_decode_pt512": line(t_std),
+            "roofline": {"kernel": "paged_attention_decode_shared_prefix (partition + merge)",
+                         "bound": "hbm", "unit": "GB/s", "peak": HBM_PEAK_GBS,
+                         "achieved": line(t_sh)["unique_GB_per_s"],
+                         "frac": line(t_sh)["frac_of_peak_on_unique_bytes"],
+                         "algorithmic_bytes_per_launch": unique}}
+
+
 MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "f16": 2500.0}
 
 
@@ -546,6 +639,16 @@ def main():
               "(the path shards by sequence or KV head with no exchange; what is measured "
               "is one MI355X)", file=sys.stderr)
         sys.exit(2)
+    if args.shared_prefix:
+        import torch
+        res = shared_prefix_timing(torch.device("cuda:0"), max(50, args.steps),
+                                   args.shared_partition_tokens)
+        print(json.dumps({"metric": "shared-prefix decode GB/s on unique bytes, 1 MI355X",
+                          "value": res["shared_prefix_decode"]["unique_GB_per_s"],
+                          "unit": "GB/s", "n_gpus": 1, "higher_is_better": True,
+                          "dtype": "bf16", "data": "synthetic",
+                          "config": {"workload": res["workload"]}, **res}), flush=True)
+        return
     if args.prefill:
         res = prefill_timing(args.prefill, args.steps, args.warmup, args.block_size,
                              args.head_dim or 128)
@@ -735,6 +838,8 @@ def main():
         res["decode_graph"] = decode_graph_timing()
         log("[bench] long-context step loop")
         res["long_context_step_loop"] = long_context_step_loop(dev)
+        log("[bench] shared-prefix decode")
+        res["shared_prefix"] = shared_prefix_timing(dev)
     print(json.dumps(res), flush=True)
 
 

@@ -354,6 +354,72 @@ paged_kv_status paged_attention_reduce(const paged_kv_pool_desc* desc, void* out
                                        int32_t partition_tokens, const void* workspace,
                                        size_t workspace_bytes, void* stream);
 
+/* --------------------------------------------------- shared-prefix decode ---- */
+
+/* Groups for paged_attention_decode_shared_prefix ([DS] §2.3: forked samples share the
+ * prompt's blocks; [DS] §2.4: prefix-cache hits share cached blocks).  Walks the batch
+ * in order and puts consecutive sequences in one group while all its members' tables
+ * start with the same blocks for at least max(1, min_shared_tokens) tokens (and the
+ * group has fewer than max_group members).  A group's shared length is its members'
+ * common leading blocks times block_size, capped at the shortest member's length; a
+ * group of one has shared length 0.
+ *   seq_ids            host int32[n]: the batch, in the order the attention call uses
+ *   group_start_out    host int32[n + 1]: members of group g are rows
+ *                      group_start_out[g] .. group_start_out[g + 1] - 1 of the batch
+ *   shared_tokens_out  host int32[n]: shared length of group g
+ *   num_groups_out, max_shared_out: number of groups, longest shared length
+ * Errors: INVALID_ARG (null pointers, n < 0, max_group < 1), NO_SUCH_SEQ. */
+paged_kv_status paged_kv_shared_prefix_groups(const paged_kv_pool* pool, const int32_t* seq_ids,
+                                              int32_t n, int32_t max_group,
+                                              int32_t min_shared_tokens, int32_t* group_start_out,
+                                              int32_t* shared_tokens_out, int32_t* num_groups_out,
+                                              int32_t* max_shared_out);
+
+/* Workspace bytes of paged_attention_decode_shared_prefix for this shape (0 if an
+ * argument is invalid). */
+size_t paged_attention_shared_prefix_workspace_bytes(const paged_kv_pool_desc* desc,
+                                                     int32_t num_seqs, int32_t num_q_heads,
+                                                     int32_t max_context_len, int32_t num_groups,
+                                                     int32_t max_group, int32_t max_shared_tokens,
+                                                     int32_t partition_tokens);
+
+/* Paged decode attention for a batch whose sequences share prompt prefixes ([DS] §2.3
+ * parallel sampling: the samples share the prompt's blocks by reference count; [DL]
+ * concrete benefits, flexible sharing of the KV cache): the same result as
+ * paged_attention_decode (within the attention tolerance; a different summation
+ * order), but the shared tokens of each group are read from the pool once for all its
+ * members.  The group's members times the query heads of a KV head form the columns of
+ * the matrix products over each shared tile (at most 64: max_group x query heads per KV
+ * head <= 64); each member's own tail is attended separately; a second launch merges,
+ * per sequence and query head, the shared-part partitions with the tail partitions by
+ * log-sum-exp.
+ *   group_start    device int32[num_groups + 1]: non-decreasing, group_start[0] = 0,
+ *                  group_start[num_groups] = num_seqs (as paged_kv_shared_prefix_groups
+ *                  returns it)
+ *   shared_tokens  device int32[num_groups]: tokens 0 .. shared_tokens[g] - 1 sit in the
+ *                  same blocks in every member's table, and every member's context
+ *                  holds at least that many tokens
+ *   max_group, max_shared_tokens  host bounds on members per group and on shared_tokens
+ *   partition_tokens  tokens per partition of the shared part and of each tail (a
+ *                  multiple of 16; 0: 512)
+ *   workspace      device buffer of paged_attention_shared_prefix_workspace_bytes(...)
+ *                  bytes (scratch; needs no zero-fill)
+ * Other arguments as for paged_attention_decode.  A sequence for which the group
+ * description does not hold (shared length above its length or above
+ * max_shared_tokens, a table that differs from its group's first one over the shared
+ * tokens, a group past the batch or larger than max_group) gets NaN outputs, as does one
+ * with an invalid length; nothing outside the buffers is read.  Requires an fp16/bf16 pool with block_size 16 or 32, head_dim 64,
+ * 128 or 256 and 2 to 16 query heads per KV head (UNSUPPORTED otherwise).  Results do
+ * not depend on where blocks sit in the pool. */
+paged_kv_status paged_attention_decode_shared_prefix(
+    const paged_kv_pool_desc* desc, void* out, int32_t out_dtype, const void* q,
+    const void* k_pool, const void* v_pool, const int32_t* block_tables,
+    int32_t max_blocks_per_seq, const int32_t* context_lens, int32_t num_seqs,
+    int32_t num_q_heads, int32_t max_context_len, float scale, const int32_t* group_start,
+    const int32_t* shared_tokens, int32_t num_groups, int32_t max_group,
+    int32_t max_shared_tokens, int32_t partition_tokens, void* workspace,
+    size_t workspace_bytes, void* stream);
+
 /* Causal multi-query attention over the pool: prefill, prefill in chunks, and the rest
  * of a prompt after a prefix-cache hit ([DS] §2.5: a request only counts how many of its
  * tokens are computed, so these are one operation; §2.6: it reads the blocks through
@@ -389,11 +455,12 @@ paged_kv_status paged_attention_prefill(const paged_kv_pool_desc* desc, void* ou
 /* ------------------------------------------------------------ measurement ---- */
 
 /* A plain streaming read of `bytes` bytes at `buf` (device, 16-byte aligned, a multiple
- * of 16), with the access pattern of the attention kernels' K/V loads (16-byte
- * nontemporal loads, 1 KiB contiguous per wave instruction, one wave per SIMD): the
- * measured read bandwidth that the decode roofline is stated against beside the part's
- * specified peak.  `sink` is a device int32 that is written only in a case no real
- * buffer reaches (it keeps the loads alive).  Errors: INVALID_ARG. */
+ * of 16), with the access pattern of the attention kernels' K/V loads: 16-byte
+ * nontemporal loads, 1 KiB contiguous per wave instruction, each wave streaming its own
+ * contiguous run, two waves per SIMD.  Its rate is the measured read bandwidth that the
+ * decode roofline is stated against beside the part's specified peak.  `sink` is a
+ * device int32 that is written only in a case no real buffer reaches (it keeps the loads
+ * alive).  Errors: INVALID_ARG. */
 paged_kv_status paged_kv_read_bandwidth_probe(const void* buf, size_t bytes, void* sink,
                                               void* stream);
 

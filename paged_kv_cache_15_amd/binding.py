@@ -92,6 +92,14 @@ _SIGNATURES = {
     "paged_attention_reduce": (ctypes.c_int, [_descp, _vp, _i32, _vp, _i32, _i32, _i32, _i32, _vp,
                                               _sz, _vp]),
     "paged_kv_read_bandwidth_probe": (ctypes.c_int, [_vp, _sz, _vp, _vp]),
+    "paged_kv_shared_prefix_groups": (ctypes.c_int, [_vp, _i32p, _i32, _i32, _i32, _i32p, _i32p,
+                                                     _i32p, _i32p]),
+    "paged_attention_shared_prefix_workspace_bytes": (_sz, [_descp, _i32, _i32, _i32, _i32, _i32,
+                                                            _i32, _i32]),
+    "paged_attention_decode_shared_prefix": (ctypes.c_int, [_descp, _vp, _i32, _vp, _vp, _vp, _vp,
+                                                            _i32, _vp, _i32, _i32, _i32, _f32, _vp,
+                                                            _vp, _i32, _i32, _i32, _i32, _vp, _sz,
+                                                            _vp]),
     "paged_attention_prefill": (ctypes.c_int, [_descp, _vp, _i32, _vp, _vp, _vp, _vp, _vp, _i32,
                                                _vp, _i32, _i32, _i32, _i32, _f32, _vp]),
 }
@@ -502,6 +510,45 @@ def paged_attention_reduce(desc, out, out_dtype, context_lens, num_q_heads, max_
                                       int(num_q_heads), int(max_context_len),
                                       int(partition_tokens), _ptr(workspace), ws_bytes,
                                       _stream(stream)))
+
+
+# --------------------------------------------------- shared-prefix decode ----
+def paged_kv_shared_prefix_groups(pool, seq_ids, max_group, min_shared_tokens=16):
+    """Returns (group_start int32[g+1], shared_tokens int32[g], max_shared)."""
+    ids, ids_p = _i32_array(seq_ids)
+    n = len(ids)
+    gs = np.zeros(n + 1, dtype=np.int32)
+    sh = np.zeros(max(n, 1), dtype=np.int32)
+    ng, ms = ctypes.c_int32(), ctypes.c_int32()
+    _check("paged_kv_shared_prefix_groups",
+           lib.paged_kv_shared_prefix_groups(pool, ids_p, n, int(max_group), int(min_shared_tokens),
+                                             gs.ctypes.data_as(_i32p), sh.ctypes.data_as(_i32p),
+                                             ctypes.byref(ng), ctypes.byref(ms)))
+    return gs[:ng.value + 1].copy(), sh[:ng.value].copy(), ms.value
+
+
+def paged_attention_shared_prefix_workspace_bytes(desc, num_seqs, num_q_heads, max_context_len,
+                                                  num_groups, max_group, max_shared_tokens,
+                                                  partition_tokens=0):
+    return int(lib.paged_attention_shared_prefix_workspace_bytes(
+        ctypes.byref(desc), int(num_seqs), int(num_q_heads), int(max_context_len),
+        int(num_groups), int(max_group), int(max_shared_tokens), int(partition_tokens)))
+
+
+def paged_attention_decode_shared_prefix(desc, out, out_dtype, q, k_pool, v_pool, block_tables,
+                                         context_lens, num_q_heads, max_context_len, scale,
+                                         group_start, shared_tokens, num_groups, max_group,
+                                         max_shared_tokens, partition_tokens=0, workspace=None,
+                                         stream=None):
+    """group_start int32 [G+1] and shared_tokens int32 [G]: device tensors."""
+    f = "paged_attention_decode_shared_prefix"
+    args = _attn_args(f, desc, out, out_dtype, q, k_pool, v_pool, block_tables, context_lens,
+                      num_q_heads, max_context_len, scale, partition_tokens, workspace, stream)
+    _check_tensor(f, "group_start", group_start, (int(num_groups) + 1,), int32=True)
+    _check_tensor(f, "shared_tokens", shared_tokens, (int(num_groups),), int32=True)
+    _check(f, lib.paged_attention_decode_shared_prefix(
+        *args[:13], _ptr(group_start), _ptr(shared_tokens), int(num_groups), int(max_group),
+        int(max_shared_tokens), int(partition_tokens), args[14], args[15], args[16]))
 
 
 # ------------------------------------------------------------ measurement ----

@@ -17,7 +17,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libpagedkv.so")
 SOURCES = ["allocator.cpp", "sha256.cpp", "device_info.cpp", "cache_ops.hip", "bandwidth_probe.hip", "decode_attention.hip",
-           "decode_attention_streamk.hip",
+           "decode_attention_streamk.hip", "decode_attention_shared.hip",
            "prefill_attention.hip"]
 ARCH = os.environ.get("PAGED_KV_ARCH", "gfx950")
 

@@ -129,6 +129,35 @@ class PagedKVCache:
                                  lens_d, hq, max_ctx, scale, partition_tokens, ws, stream)
         return out, tables, lens
 
+    def attend_shared(self, seqs, q, scale, out_dtype=None, max_group=8, min_shared_tokens=16,
+                      partition_tokens=0, stream=None, out_fill=None):
+        """Decode attention that reads each group's shared prompt blocks once ([DS] §2.3):
+        the host allocator forms the groups (consecutive sequences of the batch whose
+        tables start with the same blocks), then paged_attention_decode_shared_prefix.
+        Returns (out, group info)."""
+        tables, lens = self.block_tables(seqs)
+        hq, d = q.shape[1], q.shape[2]
+        max_group = max(1, min(int(max_group), 64 // (hq // self.desc.num_kv_heads)))
+        gs, sh, max_shared = B.paged_kv_shared_prefix_groups(self.pool, seqs, max_group,
+                                                             min_shared_tokens)
+        out_dtype = out_dtype or self.dtype
+        max_ctx = int(lens.max()) if len(lens) else 1
+        shape = (len(seqs), hq, d)
+        out = (torch.empty(shape, dtype=TORCH_DTYPES[out_dtype], device=self.device)
+               if out_fill is None else
+               torch.full(shape, out_fill, dtype=TORCH_DTYPES[out_dtype], device=self.device))
+        nbytes = B.paged_attention_shared_prefix_workspace_bytes(
+            self.desc, len(seqs), hq, max_ctx, len(sh), max_group, max_shared, partition_tokens)
+        ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=self.device)
+        B.paged_attention_decode_shared_prefix(
+            self.desc, out, out_dtype, q, self.k_pool, self.v_pool,
+            torch.from_numpy(tables).to(self.device), torch.from_numpy(lens).to(self.device), hq,
+            max_ctx, scale, torch.from_numpy(gs).to(self.device),
+            torch.from_numpy(sh).to(self.device), len(sh), max_group, max_shared,
+            partition_tokens, ws, stream)
+        return out, {"group_start": gs, "shared_tokens": sh, "num_groups": len(sh),
+                     "max_shared_tokens": max_shared, "max_group": max_group}
+
     def attend_prefill(self, seqs, q_counts, q, scale, out_dtype=None, stream=None,
                        out_fill=None):
         """Causal attention of each sequence's last q_counts[i] tokens (already appended and

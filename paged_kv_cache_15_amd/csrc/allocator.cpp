@@ -27,6 +27,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <array>
 #include <cstdarg>
 #include <cstring>
@@ -594,6 +595,55 @@ paged_kv_status paged_kv_stats(const paged_kv_pool* p, int64_t* num_free, int64_
     for (const Sequence& s : p->seqs)
         if (s.alive) w += (int64_t)p->desc.block_size * (int64_t)s.table.size() - s.length;
     *waste = w;
+    return PAGED_KV_OK;
+}
+
+paged_kv_status paged_kv_shared_prefix_groups(const paged_kv_pool* p, const int32_t* seq_ids,
+                                              int32_t n, int32_t max_group,
+                                              int32_t min_shared_tokens, int32_t* group_start_out,
+                                              int32_t* shared_tokens_out, int32_t* num_groups_out,
+                                              int32_t* max_shared_out) {
+    clear_error();
+    if (!p || n < 0 || max_group < 1 || (n > 0 && (!seq_ids || !group_start_out ||
+                                                    !shared_tokens_out)) ||
+        !num_groups_out || !max_shared_out) {
+        set_error("null pointer, n < 0 or max_group < 1");
+        return PAGED_KV_ERR_INVALID_ARG;
+    }
+    std::vector<const Sequence*> seqs(n);
+    for (int32_t i = 0; i < n; ++i) {
+        seqs[i] = find_seq(p, seq_ids[i]);
+        if (!seqs[i]) { set_error("no sequence %d", seq_ids[i]); return PAGED_KV_ERR_NO_SUCH_SEQ; }
+    }
+    const int64_t bs = p->desc.block_size;
+    const int64_t need = std::max<int64_t>(1, min_shared_tokens);
+    int32_t g = 0, max_shared = 0;
+    for (int32_t i = 0; i < n;) {
+        // grow the group while the tokens shared by all of its members stay >= need
+        const std::vector<int32_t>& first = seqs[i]->table;
+        int64_t common = (int64_t)first.size(), min_len = seqs[i]->length;
+        int32_t j = i + 1;
+        for (; j < n && j - i < max_group; ++j) {
+            const std::vector<int32_t>& t = seqs[j]->table;
+            int64_t c = 0;
+            const int64_t lim = std::min<int64_t>(common, (int64_t)t.size());
+            while (c < lim && t[c] == first[c]) ++c;
+            const int64_t len = std::min<int64_t>(min_len, seqs[j]->length);
+            if (std::min(c * bs, len) < need) break;
+            common = c;
+            min_len = len;
+        }
+        const int32_t shared = j - i > 1 ? (int32_t)std::min(common * bs, min_len) : 0;
+        group_start_out[g] = i;
+        shared_tokens_out[g] = shared;
+        max_shared = std::max(max_shared, shared);
+        ++g;
+        i = j;
+    }
+    if (n > 0) group_start_out[g] = n;
+    else if (group_start_out) group_start_out[0] = 0;
+    *num_groups_out = g;
+    *max_shared_out = max_shared;
     return PAGED_KV_OK;
 }
 

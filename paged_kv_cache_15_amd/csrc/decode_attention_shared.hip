@@ -1,0 +1,574 @@
+// Paged decode attention for batches whose sequences share a prompt prefix (gfx950).
+//
+// Parallel sampling (deepsonar "PagedAttention de vLLM …" §2.3: the samples of one
+// prompt share its blocks through reference counts and copy only the block they write;
+// deeplearn.tn "PagedAttention : comment optimiser la mémoire GPU …", concrete benefits
+// section: flexible sharing of the KV cache) leaves the prompt's K/V stored once while
+// every sample attends over it.  Attending sample by sample reads the shared blocks once
+// per sample.  Here the shared part is read once per group: its tiles are multiplied
+// against the queries of all the group's samples together (the group's samples times the
+// query heads of a KV head form the N side of the MFMA tiles, up to 64 slots), and each
+// sample's own tail is attended separately; a merge launch then combines, per sample and
+// query head, the prefix partitions with the tail partitions by log-sum-exp.  What is
+// computed is unchanged: softmax attention over the whole context of each sequence.
+//
+// Work items, one per wave (four per workgroup, no cross-wave merge):
+//   prefix item (group, KV head, partition p of the shared tokens): tokens
+//     [p PT, min((p + 1) PT, shared)), read through the table of the group's first
+//     member; the other members' table entries for those tokens are checked equal (a
+//     mismatch makes the group's results NaN);
+//   tail item (sequence, KV head, partition p of its own tokens): tokens
+//     [shared + p PT, min(shared + (p + 1) PT, ctx)).
+// Each item writes the raw (max, sum, weighted values) state of every query head it
+// serves into the workspace row (sequence, query head, partition index), where prefix
+// partitions come first and tail partitions follow; the merge folds them in order.
+// Only the logical token order decides the summation order, so placement in the pool
+// does not change the results.
+
+#include "attention_common.h"
+
+namespace {
+
+using namespace pkv_dev;
+
+struct SharedArgs {
+    void* out;
+    const void* q;
+    const void* k_pool;
+    const void* v_pool;
+    const int32_t* block_tables;
+    const int32_t* context_lens;
+    const int32_t* group_start;     // [num_groups + 1]
+    const int32_t* shared_tokens;   // [num_groups]
+    float* ws_m;
+    float* ws_l;
+    float* ws_acc;
+    int32_t num_seqs;
+    int32_t num_groups;
+    int32_t max_group;              // host bound on members per group
+    int32_t max_blocks_per_seq;
+    int32_t num_q_heads;
+    int32_t num_kv_heads;
+    int32_t group;                  // query heads per KV head (G)
+    int32_t num_blocks;
+    int32_t max_context_len;
+    int32_t partition_tokens;       // PT
+    int32_t max_shared;             // host bound on every shared_tokens[g]
+    int32_t block_size;
+    int32_t prefix_parts;           // partitions of the longest shared prefix (host bound)
+    int32_t tail_parts;             // partitions of the longest tail (host bound)
+    int32_t max_parts;              // workspace rows per (sequence, query head)
+    int64_t prefix_items;           // num_groups * Hkv * prefix_parts
+    int64_t items;                  // prefix_items + num_seqs * Hkv * tail_parts
+    float scale_log2;
+};
+
+__device__ __forceinline__ int uni(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+// Group of sequence s: the number of g in [1, num_groups) with group_start[g] <= s, which
+// for a non-decreasing group_start is the last group starting at or before s.  The lanes
+// of a wave compare 64 group starts per memory round trip (instead of a chain of
+// dependent scalar loads).  Every kernel that needs the group of a sequence uses this.
+__device__ __forceinline__ int group_of(const SharedArgs& a, int s) {
+    const int lane = threadIdx.x & 63;
+    int cnt = 0;
+    for (int g0 = 1; g0 < a.num_groups; g0 += 64) {
+        const int g = g0 + lane;
+        const bool le = g < a.num_groups && a.group_start[g] <= s;
+        cnt += __popcll(__ballot(le));
+    }
+    return cnt;
+}
+
+// One wave per item.  NB N-blocks of 16 query slots (slot n = member * G + head of the
+// KV head's group for a prefix item; n = head for a tail item, which uses N-block 0 only).
+template <int D, int DT, int BS, int NB>
+__global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(NB * D <= 256 ? 2 : 1)))
+void attn_mfma_shared(SharedArgs a) {
+    constexpr int KI = D / 32;
+    constexpr int MT = D / 16;
+    constexpr int TILE = BS * D;
+    constexpr int TPB = BS / kTile;
+    using kvec = typename std::conditional<DT == DT_BF16, bf16x8, f16x8>::type;
+    static_assert(BS >= kTile, "16- and 32-token blocks only");
+
+    const int lane = threadIdx.x & 63;
+    const int64_t item = (int64_t)blockIdx.x * kWaves + uni(threadIdx.x >> 6);
+    if (item >= a.items) return;
+    const int gq = lane & 15, quad = lane >> 4;
+    const int G = a.group;
+
+    // ---- decode the item ----
+    bool prefix;
+    int s0, members, h, p, start, end, part_index;
+    bool bad = false;
+    if (item < a.prefix_items) {
+        prefix = true;
+        const int per_group = a.num_kv_heads * a.prefix_parts;
+        const int g = (int)(item / per_group);
+        const int r = (int)(item - (int64_t)g * per_group);
+        h = r / a.prefix_parts;
+        p = r - h * a.prefix_parts;
+        s0 = sload(a.group_start, g);
+        members = sload(a.group_start, g + 1) - s0;
+        const int shared = sload(a.shared_tokens, g);
+        if (shared < 0 || shared > a.max_shared) return;   // the merge gives the group NaN
+        start = p * a.partition_tokens;
+        end = min(start + a.partition_tokens, shared);
+        // a malformed group range is never read through (the merge gives its rows NaN)
+        if (members < 1 || start >= end || s0 < 0 || s0 + members > a.num_seqs) return;
+        if (members > a.max_group) { bad = true; members = a.max_group; }
+        part_index = p;
+    } else {
+        // tail items partition-major: every sequence's first tail partition comes first,
+        // and the (mostly empty) later ones follow together at the end of the grid
+        prefix = false;
+        const int64_t t = item - a.prefix_items;
+        const int64_t per_part = (int64_t)a.num_seqs * a.num_kv_heads;
+        p = (int)(t / per_part);
+        const int r = (int)(t - (int64_t)p * per_part);
+        s0 = r / a.num_kv_heads;
+        h = r - s0 * a.num_kv_heads;
+        members = 1;
+        const int g = group_of(a, s0);
+        const int shared = sload(a.shared_tokens, g);
+        const int ctx = sload(a.context_lens, s0);
+        // invalid lengths are handled by the merge (NaN rows); nothing to read here
+        if (ctx < 1 || ctx > a.max_context_len || shared < 0 || shared > ctx ||
+            shared > a.max_shared) return;
+        start = shared + p * a.partition_tokens;
+        end = min(start + a.partition_tokens, ctx);
+        if (start >= end) return;
+        part_index = (shared + a.partition_tokens - 1) / a.partition_tokens + p;
+    }
+    const int slots = members * G;                 // query slots of this item
+    const int nb_used = (slots + 15) / 16;
+    const int32_t* trow = a.block_tables + (int64_t)s0 * a.max_blocks_per_seq;
+
+    // A prefix item reads the group's shared blocks through the first member's table; that
+    // every member's length covers them and its table lists the same blocks is checked by
+    // the merge, which gives the member NaN otherwise (checking here would hold up the
+    // first loads by a memory round trip per member).
+    (void)prefix;
+
+    // ---- queries: N-block nb, lane slot n = 16 nb + gq -> (member n / G, head n % G) ----
+    kvec qop[NB][KI];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+        const int n = min(16 * nb + gq, slots - 1);    // padded slots repeat the last one
+        const int m = n / G, j = n - m * G;
+        const uint16_t* qh = static_cast<const uint16_t*>(a.q) +
+                             ((int64_t)(s0 + m) * a.num_q_heads + h * G + j) * D + 8 * quad;
+#pragma unroll
+        for (int kk = 0; kk < KI; ++kk)
+            qop[nb][kk] = __builtin_bit_cast(kvec, *reinterpret_cast<const i32x4*>(qh + 32 * kk));
+    }
+
+    const uint16_t* kpool = static_cast<const uint16_t*>(a.k_pool) + (int64_t)h * TILE;
+    const uint16_t* vpool = static_cast<const uint16_t*>(a.v_pool) + (int64_t)h * TILE;
+    const int64_t blk_stride = (int64_t)a.num_kv_heads * TILE;
+    const int voff = gq * 4 + quad;
+
+    f32x4 acc[NB][MT];
+    float m_run[NB], lsum[NB];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) acc[nb][mt] = (f32x4){0.f, 0.f, 0.f, 0.f};
+        m_run[nb] = kNegInf;
+        lsum[nb] = 0.f;
+    }
+
+    const int t_begin = start / kTile, t_end = (end + kTile - 1) / kTile;
+    const int n = t_end - t_begin;
+
+    auto load = [&](int it, i32x4 (&kr)[KI], i32x2 (&vr)[MT]) __attribute__((always_inline)) {
+        int32_t bid = sload(trow, it / TPB);
+        if ((uint32_t)bid >= (uint32_t)a.num_blocks) {
+            bad = true;
+            bid = 0;
+        }
+        const int64_t base = (int64_t)bid * blk_stride + (it % TPB) * (kTile * D);
+        const i32x4* kt = reinterpret_cast<const i32x4*>(kpool + base) + lane;
+        const i32x2* vt = reinterpret_cast<const i32x2*>(vpool + base) + voff;
+#pragma unroll
+        for (int kk = 0; kk < KI; ++kk) kr[kk] = __builtin_nontemporal_load(kt + kk * 64);
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) vr[mt] = __builtin_nontemporal_load(vt + mt * 64);
+    };
+
+    auto compute = [&](int it, const i32x4 (&kr)[KI], i32x2 (&vr)[MT]) __attribute__((always_inline)) {
+        const int valid = min(kTile, end - it * kTile);   // tokens of the tile in range
+        const int first = max(0, start - it * kTile);     // (start is a tile boundary unless
+                                                          // a tail begins mid-tile)
+        const int tok0 = 4 * quad;
+        if (valid < kTile || first > 0) {
+            // slots outside [start, end) may hold anything (NaN included): clear them
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) {
+                uint32_t lo = (uint32_t)vr[mt][0], hi = (uint32_t)vr[mt][1];
+                if (tok0 + 0 >= valid || tok0 + 0 < first) lo &= 0xFFFF0000u;
+                if (tok0 + 1 >= valid || tok0 + 1 < first) lo &= 0x0000FFFFu;
+                if (tok0 + 2 >= valid || tok0 + 2 < first) hi &= 0xFFFF0000u;
+                if (tok0 + 3 >= valid || tok0 + 3 < first) hi &= 0x0000FFFFu;
+                vr[mt][0] = (int)lo;
+                vr[mt][1] = (int)hi;
+            }
+        }
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+            if (nb >= nb_used) break;
+            f32x4 sc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kk = 0; kk < KI; ++kk) {
+                if constexpr (DT == DT_BF16)
+                    sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kr[kk]),
+                                                                 qop[nb][kk], sc, 0, 0, 0);
+                else
+                    sc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, kr[kk]),
+                                                                qop[nb][kk], sc, 0, 0, 0);
+            }
+            float x[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                x[j] = (tok0 + j < valid && tok0 + j >= first) ? sc[j] * a.scale_log2 : kNegInf;
+            // lazy rescaling (the reference max moves only past a slack of 2^8)
+            const float xm = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+            if (__ballot(xm > m_run[nb] + kRescaleSlack)) {
+                const float mnew = fmaxf(m_run[nb], max_across_quads(xm));
+                const float alpha = exp2_fast(m_run[nb] - mnew);
+                lsum[nb] *= alpha;
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt) acc[nb][mt] *= alpha;
+                m_run[nb] = mnew;
+            }
+            // weights as a 16-bit head and a 16-bit remainder (as in the other decode
+            // kernels: one 16-bit rounding of p alone is too coarse for short contexts)
+            s16x4 phi, plo;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const float pf = exp2_fast(x[j] - m_run[nb]);
+                const uint16_t hi = f32_to_bits16<DT>(pf);
+                const uint16_t lo = f32_to_bits16<DT>(pf - bits_to_f32<DT>(hi));
+                phi[j] = (short)hi;
+                plo[j] = (short)lo;
+                lsum[nb] += pf;
+            }
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) {
+                if constexpr (DT == DT_BF16) {
+                    const s16x4 va = __builtin_bit_cast(s16x4, vr[mt]);
+                    acc[nb][mt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, phi, acc[nb][mt], 0, 0, 0);
+                    acc[nb][mt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, plo, acc[nb][mt], 0, 0, 0);
+                } else {
+                    const f16x4 va = __builtin_bit_cast(f16x4, vr[mt]);
+                    acc[nb][mt] = __builtin_amdgcn_mfma_f32_16x16x16f16(va, __builtin_bit_cast(f16x4, phi),
+                                                                       acc[nb][mt], 0, 0, 0);
+                    acc[nb][mt] = __builtin_amdgcn_mfma_f32_16x16x16f16(va, __builtin_bit_cast(f16x4, plo),
+                                                                       acc[nb][mt], 0, 0, 0);
+                }
+            }
+        }
+    };
+
+    // two-deep pipeline: every step loads one tile and computes the previous one
+    i32x4 kA[KI], kB[KI];
+    i32x2 vA[MT], vB[MT];
+    load(t_begin, kA, vA);
+    int i = 0;
+    for (; i + 2 < n; i += 2) {
+        load(t_begin + i + 1, kB, vB);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(t_begin + i, kA, vA);
+        load(t_begin + i + 2, kA, vA);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(t_begin + i + 1, kB, vB);
+    }
+    if (i + 1 < n) {
+        load(t_begin + i + 1, kB, vB);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(t_begin + i, kA, vA);
+        compute(t_begin + i + 1, kB, vB);
+    } else {
+        compute(t_begin + i, kA, vA);
+    }
+
+    // ---- write each served (sequence, query head)'s state for this partition ----
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+        if (nb >= nb_used) break;
+        const float lw = sum_across_quads(lsum[nb]);
+        const int nslot = 16 * nb + gq;
+        if (nslot >= slots) continue;
+        const int m = nslot / G, j = nslot - m * G;
+        const int64_t row = ((int64_t)(s0 + m) * a.num_q_heads + h * G + j) * a.max_parts + part_index;
+        float* dst = a.ws_acc + row * D;
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+            f32x4 v = acc[nb][mt];
+            if (bad) v = (f32x4){NAN, NAN, NAN, NAN};
+            *reinterpret_cast<f32x4*>(dst + 16 * mt + 4 * quad) = v;
+        }
+        if (quad == 0) {
+            a.ws_m[row] = bad ? NAN : m_run[nb];
+            a.ws_l[row] = bad ? NAN : lw;
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------------
+// Merge: per (query head, sequence), the ceil(shared / PT) prefix partitions and the
+// ceil((ctx - shared) / PT) tail partitions, in that order, by an online log-sum-exp
+//   M' = max(M, m_i), L' = L 2^(M - M') + l_i 2^(m_i - M'), acc likewise; out = acc / L.
+// One thread per head dim.
+// ---------------------------------------------------------------------------------
+template <int D, int OUT_DT>
+__global__ __launch_bounds__(D) void attn_shared_merge(SharedArgs a) {
+    constexpr int PC = 8;     // partitions folded per memory round trip
+    const int h = blockIdx.x, s = blockIdx.y, d = threadIdx.x;
+    const int64_t o = ((int64_t)s * a.num_q_heads + h) * D + d;
+    const int g = group_of(a, s);
+    const int ctx = sload(a.context_lens, s);
+    const int shared = sload(a.shared_tokens, g);
+    const int gs = sload(a.group_start, g), ge = sload(a.group_start, g + 1);
+    // a sequence outside its group's range (group_start not covering the batch in order)
+    // or past the group size the launch was planned for has no prefix state: NaN
+    const bool invalid = ctx < 1 || ctx > a.max_context_len || shared < 0 || shared > ctx ||
+                         shared > a.max_shared || gs < 0 || ge > a.num_seqs || s < gs ||
+                         s >= ge || s - gs >= a.max_group;
+    if (invalid) {
+        store_out<OUT_DT>(a.out, o, NAN);
+        return;
+    }
+    // The shared tokens were read through the group's first table: this sequence's table
+    // must list the same blocks for them.  Its entries are loaded together with the first
+    // partitions' states, and compared once both are in flight.
+    const int nblk = s == gs ? 0 : (shared + a.block_size - 1) / a.block_size;
+    const int32_t* mine = a.block_tables + (int64_t)s * a.max_blocks_per_seq;
+    const int32_t* first = a.block_tables + (int64_t)gs * a.max_blocks_per_seq;
+    int32_t t_mine = 0, t_first = 0;
+    if (d < nblk) {
+        t_mine = mine[d];
+        t_first = first[d];
+    }
+    const int np = (shared + a.partition_tokens - 1) / a.partition_tokens +
+                   (ctx - shared + a.partition_tokens - 1) / a.partition_tokens;
+    const int64_t row = ((int64_t)s * a.num_q_heads + h) * a.max_parts;
+    float M = kNegInf, l = 0.f, acc = 0.f;
+    bool bad = false, diff = false;
+    for (int i0 = 0; i0 < np; i0 += PC) {
+        float mv[PC], lv[PC], av[PC];
+#pragma unroll
+        for (int k = 0; k < PC; ++k) {   // slots past the end re-read the last partition
+            const int64_t r = row + min(i0 + k, np - 1);
+            mv[k] = a.ws_m[r];
+            lv[k] = a.ws_l[r];
+            av[k] = a.ws_acc[r * D + d];
+        }
+        if (i0 == 0) {
+            diff = t_mine != t_first;
+            for (int b = d + D; b < nblk; b += D) diff |= mine[b] != first[b];
+        }
+#pragma unroll
+        for (int k = 0; k < PC; ++k) {
+            if (i0 + k >= np) break;
+            bad |= mv[k] != mv[k];
+            const float mn = fmaxf(M, mv[k]);
+            const float sc = exp2_fast(M - mn), w = exp2_fast(mv[k] - mn);
+            l = l * sc + w * lv[k];
+            acc = acc * sc + w * av[k];
+            M = mn;
+        }
+    }
+    bad |= __syncthreads_or(diff);
+    store_out<OUT_DT>(a.out, o, bad ? NAN : acc / l);
+}
+
+// ---------------------------------------------------------------------------------
+// host side
+// ---------------------------------------------------------------------------------
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+struct SharedPlan {
+    SharedArgs a;
+    int nb;          // N-blocks: ceil(max_group * G / 16), 1, 2 or 4
+    size_t ws_bytes;
+};
+
+int n_blocks_for(int max_group, int group) {
+    const int slots = max_group * group;
+    return slots <= 16 ? 1 : slots <= 32 ? 2 : slots <= 64 ? 4 : 0;
+}
+
+size_t shared_workspace(int64_t num_seqs, int64_t hq, int64_t d, int64_t max_parts) {
+    const size_t rows = (size_t)num_seqs * hq * max_parts;
+    return 2 * align256(rows * sizeof(float)) + rows * d * sizeof(float);
+}
+
+template <int D, int DT, int BS>
+void launch_items(const SharedPlan& pl, dim3 grid, hipStream_t st) {
+    switch (pl.nb) {
+        case 1: attn_mfma_shared<D, DT, BS, 1><<<grid, dim3(kWaves * 64), 0, st>>>(pl.a); break;
+        case 2: attn_mfma_shared<D, DT, BS, 2><<<grid, dim3(kWaves * 64), 0, st>>>(pl.a); break;
+        default: attn_mfma_shared<D, DT, BS, 4><<<grid, dim3(kWaves * 64), 0, st>>>(pl.a); break;
+    }
+}
+
+template <int D>
+void launch_d(const SharedPlan& pl, int dtype, int out_dtype, int bs, hipStream_t st) {
+    const dim3 grid((unsigned)((pl.a.items + kWaves - 1) / kWaves));
+    if (dtype == PAGED_KV_F16) {
+        if (bs == 32) launch_items<D, DT_F16, 32>(pl, grid, st);
+        else launch_items<D, DT_F16, 16>(pl, grid, st);
+    } else {
+        if (bs == 32) launch_items<D, DT_BF16, 32>(pl, grid, st);
+        else launch_items<D, DT_BF16, 16>(pl, grid, st);
+    }
+    const dim3 mgrid((unsigned)pl.a.num_q_heads, (unsigned)pl.a.num_seqs);
+    if (out_dtype == PAGED_KV_F32) attn_shared_merge<D, DT_F32><<<mgrid, dim3(D), 0, st>>>(pl.a);
+    else if (out_dtype == PAGED_KV_F16) attn_shared_merge<D, DT_F16><<<mgrid, dim3(D), 0, st>>>(pl.a);
+    else attn_shared_merge<D, DT_BF16><<<mgrid, dim3(D), 0, st>>>(pl.a);
+}
+
+paged_kv_status plan_shared(SharedPlan& pl, const paged_kv_pool_desc* desc, int32_t num_seqs,
+                            int32_t hq, int32_t max_ctx, int32_t num_groups, int32_t max_group,
+                            int32_t max_shared, int32_t part_tokens) {
+    if (!pkv::kernel_desc(desc, true)) return PAGED_KV_ERR_INVALID_ARG;
+    if (num_seqs < 0 || hq < 1 || hq % desc->num_kv_heads) {
+        pkv::set_error("num_seqs %d < 0, or num_q_heads %d not a positive multiple of %d",
+                       num_seqs, hq, desc->num_kv_heads);
+        return PAGED_KV_ERR_INVALID_ARG;
+    }
+    const int group = hq / desc->num_kv_heads;
+    if (desc->dtype == PAGED_KV_F32 || group < 2 || desc->block_size < 16) {
+        pkv::set_error("shared-prefix decode needs an fp16/bf16 pool, >= 2 query heads per KV "
+                       "head and 16- or 32-token blocks");
+        return PAGED_KV_ERR_UNSUPPORTED;
+    }
+    if (max_ctx < 1 || num_groups < (num_seqs > 0 ? 1 : 0) || max_group < 1 || max_shared < 0 ||
+        max_shared > max_ctx) {
+        pkv::set_error("need max_context_len >= 1, num_groups >= 1, max_group >= 1 and "
+                       "0 <= max_shared_tokens <= max_context_len");
+        return PAGED_KV_ERR_INVALID_ARG;
+    }
+    pl.nb = n_blocks_for(max_group, group);
+    if (pl.nb == 0) {
+        pkv::set_error("max_group (%d) x query heads per KV head (%d) must be at most 64",
+                       max_group, group);
+        return PAGED_KV_ERR_UNSUPPORTED;
+    }
+    if (part_tokens == 0) part_tokens = pkv::kDefaultPartitionTokens;
+    if (part_tokens < 0 || part_tokens % kTile) {
+        pkv::set_error("partition_tokens %d must be 0 or a positive multiple of %d", part_tokens, kTile);
+        return PAGED_KV_ERR_INVALID_ARG;
+    }
+    SharedArgs& a = pl.a;
+    a = SharedArgs{};
+    a.num_seqs = num_seqs;
+    a.num_groups = num_groups;
+    a.max_group = max_group;
+    a.num_q_heads = hq;
+    a.num_kv_heads = desc->num_kv_heads;
+    a.group = group;
+    a.num_blocks = desc->num_blocks;
+    a.max_context_len = max_ctx;
+    a.partition_tokens = part_tokens;
+    a.max_shared = max_shared;
+    a.block_size = desc->block_size;
+    a.prefix_parts = (max_shared + part_tokens - 1) / part_tokens;
+    a.tail_parts = (max_ctx + part_tokens - 1) / part_tokens;
+    a.max_parts = a.prefix_parts + a.tail_parts;
+    a.prefix_items = (int64_t)num_groups * desc->num_kv_heads * a.prefix_parts;
+    a.items = a.prefix_items + (int64_t)num_seqs * desc->num_kv_heads * a.tail_parts;
+    if ((a.items + kWaves - 1) / kWaves > INT32_MAX || num_seqs > 65535) {
+        pkv::set_error("batch too large for one launch");
+        return PAGED_KV_ERR_UNSUPPORTED;
+    }
+    pl.ws_bytes = shared_workspace(num_seqs, hq, desc->head_dim, a.max_parts);
+    return PAGED_KV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t paged_attention_shared_prefix_workspace_bytes(const paged_kv_pool_desc* desc,
+                                                     int32_t num_seqs, int32_t num_q_heads,
+                                                     int32_t max_context_len, int32_t num_groups,
+                                                     int32_t max_group, int32_t max_shared_tokens,
+                                                     int32_t partition_tokens) {
+    SharedPlan pl;
+    if (plan_shared(pl, desc, num_seqs, num_q_heads, max_context_len, num_groups, max_group,
+                    max_shared_tokens, partition_tokens) != PAGED_KV_OK)
+        return 0;
+    return pl.ws_bytes;
+}
+
+paged_kv_status paged_attention_decode_shared_prefix(
+        const paged_kv_pool_desc* desc, void* out, int32_t out_dtype, const void* q,
+        const void* k_pool, const void* v_pool, const int32_t* block_tables,
+        int32_t max_blocks_per_seq, const int32_t* context_lens, int32_t num_seqs,
+        int32_t num_q_heads, int32_t max_context_len, float scale, const int32_t* group_start,
+        const int32_t* shared_tokens, int32_t num_groups, int32_t max_group,
+        int32_t max_shared_tokens, int32_t partition_tokens, void* workspace,
+        size_t workspace_bytes, void* stream) {
+    pkv::clear_error();
+    SharedPlan pl;
+    paged_kv_status st = plan_shared(pl, desc, num_seqs, num_q_heads, max_context_len, num_groups,
+                                     max_group, max_shared_tokens, partition_tokens);
+    if (st != PAGED_KV_OK) return st;
+    if (out_dtype != desc->dtype && out_dtype != PAGED_KV_F32) {
+        pkv::set_error("out_dtype must be the pool dtype or fp32");
+        return PAGED_KV_ERR_INVALID_ARG;
+    }
+    if ((int64_t)max_blocks_per_seq * desc->block_size < max_context_len) {
+        pkv::set_error("max_blocks_per_seq %d cannot hold max_context_len %d", max_blocks_per_seq,
+                       max_context_len);
+        return PAGED_KV_ERR_INVALID_ARG;
+    }
+    if (num_seqs == 0) return PAGED_KV_OK;
+    if (!out || !q || !k_pool || !v_pool || !block_tables || !context_lens || !group_start ||
+        !shared_tokens) {
+        pkv::set_error("null pointer argument");
+        return PAGED_KV_ERR_INVALID_ARG;
+    }
+    if (!workspace || workspace_bytes < pl.ws_bytes) {
+        pkv::set_error("workspace of %zu bytes needed (%zu given)", pl.ws_bytes, workspace_bytes);
+        return PAGED_KV_ERR_BUFFER_TOO_SMALL;
+    }
+    if ((reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(k_pool) |
+         reinterpret_cast<uintptr_t>(v_pool) | reinterpret_cast<uintptr_t>(workspace)) & 15) {
+        pkv::set_error("q, pools and workspace must be 16-byte aligned");
+        return PAGED_KV_ERR_INVALID_ARG;
+    }
+    SharedArgs& a = pl.a;
+    a.out = out;
+    a.q = q;
+    a.k_pool = k_pool;
+    a.v_pool = v_pool;
+    a.block_tables = block_tables;
+    a.context_lens = context_lens;
+    a.group_start = group_start;
+    a.shared_tokens = shared_tokens;
+    const size_t rows = (size_t)num_seqs * num_q_heads * a.max_parts;
+    char* ws = static_cast<char*>(workspace);
+    a.ws_m = reinterpret_cast<float*>(ws);
+    a.ws_l = reinterpret_cast<float*>(ws + align256(rows * 4));
+    a.ws_acc = reinterpret_cast<float*>(ws + 2 * align256(rows * 4));
+    a.max_blocks_per_seq = max_blocks_per_seq;
+    a.scale_log2 = scale * kLog2e;
+    hipStream_t sm = reinterpret_cast<hipStream_t>(stream);
+    switch (desc->head_dim) {
+        case 64: launch_d<64>(pl, desc->dtype, out_dtype, desc->block_size, sm); break;
+        case 256: launch_d<256>(pl, desc->dtype, out_dtype, desc->block_size, sm); break;
+        default: launch_d<128>(pl, desc->dtype, out_dtype, desc->block_size, sm); break;
+    }
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) {
+        pkv::set_error("shared-prefix attention launch failed: %s", hipGetErrorString(e));
+        return PAGED_KV_ERR_HIP;
+    }
+    return PAGED_KV_OK;
+}
+
+}  // extern "C"

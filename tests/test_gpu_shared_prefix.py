@@ -1,0 +1,187 @@
+"""Shared-prefix decode (GPU): the samples of a prompt read their shared blocks once.
+
+paged_attention_decode_shared_prefix computes the same attention as
+paged_attention_decode (deepsonar "PagedAttention de vLLM …" §2.3: forked samples share
+the prompt's blocks by reference count), reading each group's shared tokens once for
+all its members.  Checked against the oracle (every sequence), against the standard
+decode call, for placement invariance (bitwise), with groups the allocator forms from
+forks and prefix-cache hits, odd shared lengths, groups of one, every N-block width,
+block size 32, and malformed group descriptions (NaN rows, nothing read out of bounds).
+"""
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+from oracle import replay as oreplay
+from gpu_common import TOL, say, assert_pools_equal, assert_bookkeeping_equal, max_err, assert_close
+
+pytestmark = pytest.mark.gpu
+
+
+def _shared_attend(cache, w, seqs, q, out_dtype="f32", max_group=8, min_shared=16, pt=0):
+    out, info = cache.attend_shared(seqs, q, float(w.scale), out_dtype, max_group=max_group,
+                                    min_shared_tokens=min_shared, partition_tokens=pt,
+                                    out_fill=float("nan"))
+    torch.cuda.synchronize()
+    return out, info
+
+
+@pytest.mark.parametrize("small", [True, False], ids=["small", "full"])
+def test_config4_against_the_oracle(small):
+    from paged_kv_cache_15_amd.replay import run_workload, to_device
+    w = W.make_config(4, small=small)
+    say(f"[shared] {w.name}")
+    g = run_workload(w, "cuda", out_dtype="f32", out_fill=float("nan"))
+    seqs, qidx = w.attend_ops()[-1][1], w.attend_ops()[-1][2]
+    q = to_device(w.q[qidx], w.dtype, "cuda")
+    out, info = _shared_attend(g.cache, w, seqs, q)
+    n_prompts = 2 if small else 32
+    assert info["num_groups"] == n_prompts and info["max_shared_tokens"] == 2048
+    assert list(info["shared_tokens"]) == [2048] * n_prompts
+    o = oreplay.run(w)
+    assert_bookkeeping_equal(g, o)
+    assert_pools_equal(g.cache, o, w.dtype)
+    err = assert_close(out, o.outputs[0], w.dtype, "f32")
+    say(f"   vs oracle max|err| {err:.3e}; vs standard decode {float((out - g.outputs[0]).abs().max()):.3e}")
+    assert float((out - g.outputs[0]).abs().max()) <= 2 * TOL[w.dtype]
+    out16, _ = _shared_attend(g.cache, w, seqs, q, out_dtype="bf16")
+    assert_close(out16, o.outputs[0], w.dtype, "bf16")
+    g.cache.close()
+
+
+def test_placement_invariance_bitwise():
+    from paged_kv_cache_15_amd.replay import run_workload, to_device
+    w = W.make_config(4, small=True)
+    outs = []
+    for seed in (None, 7):
+        if seed is not None:
+            w.free_order = np.random.default_rng(seed).permutation(w.num_blocks).astype(np.int32)
+        g = run_workload(w, "cuda", out_dtype="f32")
+        seqs, qidx = w.attend_ops()[-1][1], w.attend_ops()[-1][2]
+        out, _ = _shared_attend(g.cache, w, seqs, to_device(w.q[qidx], w.dtype, "cuda"))
+        outs.append(out)
+        g.cache.close()
+    assert torch.equal(outs[0], outs[1])
+
+
+def _forked_batch(rng, hq, hkv, d, dt, bs, prompts, tails, fork_after=None):
+    """Prompts of the given lengths, each forked into len(tails[i]) samples that append
+    their own tails; returns the cache, the batch in group order and the host K/V."""
+    from paged_kv_cache_15_amd.cache import PagedKVCache
+    from paged_kv_cache_15_amd.replay import to_device
+    need = sum(-(-(p + max(t + [0])) // bs) * (len(t) + 1) for p, t in zip(prompts, tails)) + 16
+    c = PagedKVCache(need, hkv, d, dt, bs, rng.permutation(need).astype(np.int32))
+    batch = []
+    for p, ts in zip(prompts, tails):
+        s0 = c.create()
+        kv = rng.standard_normal((2, p, hkv, d)).astype(np.float32)
+        c.append([s0], [p], to_device(kv[0], dt, "cuda"), to_device(kv[1], dt, "cuda"))
+        group = [s0] + [c.fork(s0) for _ in ts[1:]]
+        for s, t in zip(group, ts):
+            if t:
+                kv = rng.standard_normal((2, t, hkv, d)).astype(np.float32)
+                c.append([s], [t], to_device(kv[0], dt, "cuda"), to_device(kv[1], dt, "cuda"))
+        batch += group
+    return c, batch
+
+
+def _oracle_of(c, seqs, q, scale, dt, bs):
+    from oracle.attention import paged_decode
+    from oracle import lowp
+    from gpu_common import pool_bits
+    tables, lens = c.block_tables(seqs)
+    qf = lowp.storage_bits_to_f64(lowp.to_storage_bits(q.float().cpu().numpy(), dt), dt)
+    return paged_decode(qf, pool_bits(c.k_pool, dt), pool_bits(c.v_pool, dt), tables, lens,
+                        np.float32(scale), dt, bs)
+
+
+@pytest.mark.parametrize("shape", [("bf16", 32, 8, 128, 16, 8), ("f16", 16, 8, 128, 16, 8),
+                                   ("bf16", 64, 8, 128, 16, 8), ("bf16", 32, 8, 128, 32, 8),
+                                   ("bf16", 16, 4, 64, 16, 16), ("f16", 16, 4, 256, 16, 4)],
+                         ids=lambda s: "-".join(map(str, s)))
+def test_groups_of_every_shape(shape):
+    """Group widths of 1, 2 and 4 N-blocks (2x8, 4x8, 8x8, 4x16 slots), block size 32,
+    head sizes 64 and 256; prompts with partial last blocks, samples without tails (the
+    shared length then ends inside a block), singletons, and a 512-token partition run."""
+    from paged_kv_cache_15_amd.replay import to_device
+    dt, hq, hkv, d, bs, mg = shape
+    rng = np.random.default_rng(hq + d + bs)
+    prompts = [1000, 37, 700, 513, 1]
+    tails = [[5, 0, 130, 17, 1, 600, 2, 40][:mg], [3, 9], [0, 0, 0], [64], [1, 7, 0, 300][:max(1, mg // 2)]]
+    c, batch = _forked_batch(rng, hq, hkv, d, dt, bs, prompts, tails)
+    q = to_device(rng.standard_normal((len(batch), hq, d)).astype(np.float32), dt, "cuda")
+    want = _oracle_of(c, batch, q, 0.09, dt, bs)
+    for pt in (0, 512, 64):
+        out, info = c.attend_shared(batch, q, 0.09, "f32", max_group=mg, min_shared_tokens=16,
+                                    partition_tokens=pt, out_fill=float("nan"))
+        torch.cuda.synchronize()
+        say(f"[shared] {shape} pt={pt} groups={info['num_groups']} shared={list(info['shared_tokens'])}")
+        assert_close(out, want, dt, "f32")
+    c.close()
+
+
+def test_prefix_cache_hits_group_too():
+    """Two requests that take the same cached prompt blocks over ([DS] §2.4) share them
+    in their tables: the helper groups them and the result matches the oracle."""
+    from paged_kv_cache_15_amd.cache import PagedKVCache
+    from paged_kv_cache_15_amd.replay import to_device
+    rng = np.random.default_rng(17)
+    hq, hkv, d, dt = 32, 8, 128, "bf16"
+    c = PagedKVCache(600, hkv, d, dt, 16, rng.permutation(600).astype(np.int32), prefix_cache=True)
+    prompt = rng.integers(0, 50000, 1200).tolist()
+    kv = rng.standard_normal((2, 1200, hkv, d)).astype(np.float32)
+    batch = []
+    for r in range(3):
+        s, n = c.create_prefix(prompt)
+        rest = prompt[n:] + rng.integers(0, 50000, 50 * (r + 1)).tolist()
+        extra = rng.standard_normal((2, len(rest) - (1200 - n), hkv, d)).astype(np.float32)
+        kk = np.concatenate([kv[0][n:], extra[0]]) if n < 1200 else extra[0]
+        vv = np.concatenate([kv[1][n:], extra[1]]) if n < 1200 else extra[1]
+        c.append_tokens([s], [rest], to_device(kk, dt, "cuda"), to_device(vv, dt, "cuda"))
+        batch.append(s)
+    q = to_device(rng.standard_normal((3, hq, d)).astype(np.float32), dt, "cuda")
+    out, info = c.attend_shared(batch, q, 0.088, "f32", max_group=8, min_shared_tokens=16,
+                                out_fill=float("nan"))
+    torch.cuda.synchronize()
+    assert info["num_groups"] == 1 and info["shared_tokens"][0] == 1184   # 74 full blocks
+    assert_close(out, _oracle_of(c, batch, q, 0.088, dt, 16), dt, "f32")
+    c.close()
+
+
+def test_malformed_groups_give_nan_without_faults():
+    from paged_kv_cache_15_amd import binding as B
+    from paged_kv_cache_15_amd.replay import to_device
+    rng = np.random.default_rng(23)
+    hq, hkv, d, dt = 32, 8, 128, "bf16"
+    c, batch = _forked_batch(rng, hq, hkv, d, dt, 16, [300, 200], [[4, 5, 6], [7, 8]])
+    q = to_device(rng.standard_normal((5, hq, d)).astype(np.float32), dt, "cuda")
+    tables, lens = c.block_tables(batch)
+    tab, bl = torch.from_numpy(tables).cuda(), torch.from_numpy(lens).cuda()
+    mx = int(lens.max())
+    good = _oracle_of(c, batch, q, 0.1, dt, 16)
+    cases = [
+        ([0, 3, 5], [288, 2000], [False] * 3 + [True] * 2),     # shared longer than the contexts
+        # members whose tables differ from the group's first (which reads its own blocks
+        # and stays right): NaN
+        ([0, 2, 5], [288, 192], [False, False, False, True, True]),
+        ([0, 4, 9], [288, 192], [False, False, False, True, True]),  # and a range past the batch
+        ([0, 3, 5], [-5, 192], [True] * 3 + [False] * 2),         # negative shared length
+    ]
+    for starts, shared, nan_rows in cases:
+        gs = torch.tensor(starts, dtype=torch.int32, device="cuda")
+        sh = torch.tensor(shared, dtype=torch.int32, device="cuda")
+        max_shared = max(0, min(max(shared), mx))
+        nbytes = B.paged_attention_shared_prefix_workspace_bytes(c.desc, 5, hq, mx, 2, 8, max_shared, 0)
+        ws = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
+        out = torch.full((5, hq, d), 3.0, dtype=torch.float32, device="cuda")
+        B.paged_attention_decode_shared_prefix(c.desc, out, "f32", q, c.k_pool, c.v_pool, tab, bl,
+                                               hq, mx, 0.1, gs, sh, 2, 8, max_shared, 0, ws)
+        torch.cuda.synchronize()
+        r = out.double().cpu().numpy()
+        for i, bad in enumerate(nan_rows):
+            if bad:
+                assert np.isnan(r[i]).all(), (starts, shared, i)
+            else:
+                assert np.abs(r[i] - good[i]).max() <= TOL[dt], (starts, shared, i)
+    c.close()

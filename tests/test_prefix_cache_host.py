@@ -136,3 +136,85 @@ def test_hit_takes_blocks_out_of_the_queue_and_eviction_follows_it():
     assert B.paged_kv_prefix_stats(p)[2] == 1
     assert B.paged_kv_seq_create_prefix(p, prompt)[1] == 0
     B.paged_kv_pool_destroy(p)
+
+
+def _groups_brute(tables, lens, bs, max_group, need):
+    """The grouping rule written out: consecutive sequences join while the tokens shared
+    by all members (common leading blocks x block size, capped at the shortest length)
+    stay >= max(1, need)."""
+    need = max(1, need)
+    starts, shared, i, n = [], [], 0, len(tables)
+    while i < n:
+        j, common, mlen = i + 1, len(tables[i]), lens[i]
+        while j < n and j - i < max_group:
+            c = 0
+            while c < min(common, len(tables[j])) and tables[j][c] == tables[i][c]:
+                c += 1
+            if min(c * bs, min(mlen, lens[j])) < need:
+                break
+            common, mlen = c, min(mlen, lens[j])
+            j += 1
+        starts.append(i)
+        shared.append(min(common * bs, mlen) if j - i > 1 else 0)
+        i = j
+    return starts + [n], shared
+
+
+def test_shared_prefix_groups_of_the_parallel_sampling_workload():
+    """32 prompts x 8 samples (2056-token prompts): 32 groups of 8 sharing 128 blocks."""
+    import workloads as W
+    w = W.make_config(4, draw_values=False)
+    p = _pool(w.num_blocks, w.block_size, w.free_order, prefix=False)
+    for op in w.ops:
+        if op[0] == "create":
+            B.paged_kv_seq_create(p)
+        elif op[0] == "fork":
+            B.paged_kv_seq_fork(p, op[1])
+        elif op[0] == "append":
+            B.paged_kv_append_batch(p, op[1], op[2])
+        elif op[0] == "attend":
+            seqs = op[1]
+    gs, sh, ms = B.paged_kv_shared_prefix_groups(p, seqs, 8, 16)
+    assert list(gs) == list(range(0, 257, 8)) and list(sh) == [2048] * 32 and ms == 2048
+    gs, sh, ms = B.paged_kv_shared_prefix_groups(p, seqs, 4, 16)       # groups cut at 4
+    assert list(gs) == list(range(0, 257, 4)) and list(sh) == [2048] * 64
+    gs, sh, ms = B.paged_kv_shared_prefix_groups(p, seqs, 8, 4096)     # more than is shared
+    assert list(gs) == list(range(257)) and ms == 0
+    B.paged_kv_pool_destroy(p)
+
+
+@pytest.mark.parametrize("bs", [1, 4, 16])
+def test_shared_prefix_groups_match_the_rule_on_random_forests(bs):
+    rng = random.Random(bs + 500)
+    for trial in range(20):
+        nb = 4000
+        p = _pool(nb, bs, None, prefix=False)
+        seqs = []
+        for _ in range(rng.randrange(1, 6)):
+            root = B.paged_kv_seq_create(p)
+            B.paged_kv_seq_append(p, root, rng.randrange(0, 8 * bs + 5))
+            fam = [root]
+            for _ in range(rng.randrange(0, 6)):
+                c = B.paged_kv_seq_fork(p, rng.choice(fam))
+                B.paged_kv_seq_append(p, c, rng.randrange(0, 3 * bs))
+                fam.append(c)
+            for s in fam:
+                if rng.random() < 0.5:
+                    B.paged_kv_seq_append(p, s, rng.randrange(0, 2 * bs))
+            seqs += fam
+        rng.shuffle(seqs) if rng.random() < 0.3 else None
+        seqs = [s for s in seqs if B.paged_kv_seq_info(p, s)[0] > 0] or [B.paged_kv_seq_create(p)]
+        tables, lens = B.paged_kv_block_tables(p, seqs, None)
+        rows = [[int(x) for x in t if x >= 0] for t in tables]
+        for mg in (1, 2, 8):
+            for need in (0, bs, 3 * bs):
+                gs, sh, ms = B.paged_kv_shared_prefix_groups(p, seqs, mg, need)
+                want_gs, want_sh = _groups_brute(rows, [int(x) for x in lens], bs, mg, need)
+                assert list(gs) == want_gs and list(sh) == want_sh, (trial, mg, need)
+                assert ms == max(want_sh)
+                for g in range(len(sh)):           # the description the kernel relies on
+                    members = range(gs[g], gs[g + 1])
+                    nblk = -(-int(sh[g]) // bs)
+                    assert all(rows[m][:nblk] == rows[gs[g]][:nblk] for m in members)
+                    assert all(lens[m] >= sh[g] for m in members)
+        B.paged_kv_pool_destroy(p)
