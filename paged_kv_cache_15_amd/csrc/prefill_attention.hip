@@ -35,6 +35,8 @@
 // (each lane loads from its own token's block; V, token-major at that size, reaches the
 // value product through per-wave LDS rows, as in the decode kernels).
 
+#include <algorithm>
+
 #include "attention_common.h"
 
 namespace {
@@ -90,6 +92,29 @@ __device__ __forceinline__ void split_pair(float w0, float w1, int& head, int& r
     rest = (int)pack2_16<DT>(r0, r1);
 }
 
+// The two weights a packed pair of 16-bit values stands for, as floats.
+template <int DT>
+__device__ __forceinline__ float2 unpack2_16(uint32_t h) {
+    if constexpr (DT == DT_BF16) {
+        return make_float2(__uint_as_float(h << 16), __uint_as_float(h & 0xFFFF0000u));
+    } else {
+        const f16x2_t hv = __builtin_bit_cast(f16x2_t, h);
+        return make_float2((float)hv[0], (float)hv[1]);
+    }
+}
+
+// Rows that see at least split_keys<DT>() keys take their weights as one 16-bit rounding
+// (summed into the row's denominator as rounded, so the softmax stays consistent); rows
+// with fewer keys keep the 16-bit head plus remainder.  One rounding moves the output by
+// sum_i w_i e_i (v_i - out), |e_i| <= u (unit roundoff: 2^-8 for bf16, 2^-11 for fp16):
+// two keys of spread-out values take bf16 past the 2e-3 bar, while with scores of unit
+// spread (the workloads' N(0, 1) queries and keys) the effective number of keys is
+// about 0.37 x the keys seen and the error's standard deviation about
+// (u / sqrt 3) / sqrt(effective keys): 1.2e-4 at 1024 bf16 keys (measured at 256 keys:
+// 1.7e-3 worst over 4k-token prompts, too close to the bar), 5.8e-5 at 64 fp16 keys.
+template <int DT>
+constexpr int split_keys() { return DT == DT_BF16 ? 1024 : 64; }
+
 // Four consecutive outputs (element i a multiple of 4, out 16-byte aligned) in one
 // store: 16 bytes of fp32 or 8 bytes of packed 16-bit values.
 template <int OUT_DT>
@@ -111,7 +136,7 @@ __device__ __forceinline__ void store_out4(void* out, int64_t i, f32x4 v) {
 template <int D>
 constexpr int prefill_blocks() { return D == 128 ? 3 : D == 64 ? 5 : 1; }
 
-template <int D, int DT, int OUT_DT, int BS>
+template <int D, int DT, int OUT_DT, int BS, bool SPLIT>
 __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(1)))
 void attn_prefill_mfma(PrefillArgs a) {
     constexpr int KI = D / 32;
@@ -162,6 +187,14 @@ void attn_prefill_mfma(PrefillArgs a) {
     const int valid_rows = (t_end - t_begin) * G;
     if (row0 >= valid_rows) return;
     const bool bad_len = ctx < 1 || ctx > a.max_context_len || n > ctx;
+    // Two launches share the work: SPLIT takes the workgroups whose first query sees fewer
+    // than split_keys keys, the other one the rest (and writes the NaN rows of invalid
+    // sequences).  The test is the same for every wave of a workgroup.
+    if constexpr (SPLIT) {
+        if (bad_len || ctx - n + t_begin + 1 >= split_keys<DT>()) return;
+    } else {
+        if (!bad_len && ctx - n + t_begin + 1 < split_keys<DT>()) return;
+    }
 
     // per block b: this lane's row, its token, head and position
     // (recomputed where needed rather than held: at three blocks per wave every register
@@ -423,12 +456,20 @@ void attn_prefill_mfma(PrefillArgs a) {
             for (int r = 0; r < 4; ++r) {
                 const float p0 = exp2_fast(fmaf(sc[b][r >> 1][2 * (r & 1)], a.scale_log2, -m[b]));
                 const float p1 = exp2_fast(fmaf(sc[b][r >> 1][2 * (r & 1) + 1], a.scale_log2, -m[b]));
-                int hw, lw;
-                split_pair<DT>(p0, p1, hw, lw);
-                phi[r] = hw;
-                plo[r] = lw;
-                lsum[b] += p0;
-                lsum[b] += p1;
+                if constexpr (SPLIT) {
+                    int hw, lw;
+                    split_pair<DT>(p0, p1, hw, lw);
+                    phi[r] = hw;
+                    plo[r] = lw;
+                    lsum[b] += p0;
+                    lsum[b] += p1;
+                } else {
+                    const uint32_t hw = pack2_16<DT>(p0, p1);
+                    const float2 pr = unpack2_16<DT>(hw);
+                    phi[r] = (int)hw;
+                    lsum[b] += pr.x;
+                    lsum[b] += pr.y;
+                }
             }
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt) {
@@ -436,13 +477,15 @@ void attn_prefill_mfma(PrefillArgs a) {
                 if constexpr (DT == DT_BF16) {
                     acc[b][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
                         __builtin_bit_cast(bf16x8, va), __builtin_bit_cast(bf16x8, phi), acc[b][mt], 0, 0, 0);
-                    acc[b][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                        __builtin_bit_cast(bf16x8, va), __builtin_bit_cast(bf16x8, plo), acc[b][mt], 0, 0, 0);
+                    if constexpr (SPLIT)
+                        acc[b][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                            __builtin_bit_cast(bf16x8, va), __builtin_bit_cast(bf16x8, plo), acc[b][mt], 0, 0, 0);
                 } else {
                     acc[b][mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
                         __builtin_bit_cast(f16x8, va), __builtin_bit_cast(f16x8, phi), acc[b][mt], 0, 0, 0);
-                    acc[b][mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-                        __builtin_bit_cast(f16x8, va), __builtin_bit_cast(f16x8, plo), acc[b][mt], 0, 0, 0);
+                    if constexpr (SPLIT)
+                        acc[b][mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                            __builtin_bit_cast(f16x8, va), __builtin_bit_cast(f16x8, plo), acc[b][mt], 0, 0, 0);
                 }
             }
         }
@@ -535,9 +578,16 @@ void attn_prefill_mfma(PrefillArgs a) {
     }
 }
 
+// Two launches: every query tile without the weight split, then (only the first tiles of
+// each sequence can hold queries that see fewer than split_keys keys) those tiles with it.
 template <int D, int DT, int OUT, int BS>
 void launch_t(const PrefillArgs& a, dim3 grid, hipStream_t st) {
-    attn_prefill_mfma<D, DT, OUT, BS><<<grid, dim3(kWaves * 64), 0, st>>>(a);
+    attn_prefill_mfma<D, DT, OUT, BS, false><<<grid, dim3(kWaves * 64), 0, st>>>(a);
+    PrefillArgs b = a;
+    b.q_tiles = std::min(a.q_tiles, (split_keys<DT>() - 1 + a.tokens_per_wg - 1) / a.tokens_per_wg);
+    const int64_t pairs = (int64_t)a.num_seqs * a.num_kv_heads;
+    const dim3 g2((unsigned)((int64_t)a.xcds * b.q_tiles * ((pairs + a.xcds - 1) / a.xcds)));
+    attn_prefill_mfma<D, DT, OUT, BS, true><<<g2, dim3(kWaves * 64), 0, st>>>(b);
 }
 
 template <int D, int DT, int BS>
