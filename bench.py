@@ -60,6 +60,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true",
                     help="only the decode step (no prefill, graph-step and step-loop lines)")
+    ap.add_argument("--decode-graph", action="store_true",
+                    help="only time the graph-captured 32-layer decode step of 8 sequences and "
+                         "print that line")
     ap.add_argument("--shared-prefix", action="store_true",
                     help="only time the parallel-sampling workload (per-sample and shared-prefix "
                          "decode) and print that line")
@@ -639,6 +642,14 @@ def main():
               "(the path shards by sequence or KV head with no exchange; what is measured "
               "is one MI355X)", file=sys.stderr)
         sys.exit(2)
+    if args.decode_graph:
+        res = decode_graph_timing()
+        print(json.dumps({"metric": "graph-captured decode step us, 1 MI355X",
+                          "value": res["graph_us_per_step"], "unit": "us",
+                          "higher_is_better": False, "n_gpus": 1, "dtype": "bf16",
+                          "data": "synthetic", "config": {"workload": "gqa_decode_graph_b8_l32"},
+                          **res}), flush=True)
+        return
     if args.shared_prefix:
         import torch
         res = shared_prefix_timing(torch.device("cuda:0"), max(50, args.steps),

@@ -477,3 +477,4 @@ def test_automatic_schedule_is_the_schedule_it_names(nseq, ctx_hi, shape):
         ref = dense_decode(qb[s], kb[0, starts[s]:starts[s + 1]], kb[1, starts[s]:starts[s + 1]], 0.088)
         assert np.abs(a[s].double().cpu().numpy() - ref).max() <= TOL[dt]
     c.close()
+
