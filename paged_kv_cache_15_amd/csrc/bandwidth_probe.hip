@@ -2,9 +2,8 @@
 // is also stated against (next to the 8 TB/s of the part's specification).
 //
 // The loads are those of the attention kernels' K/V stream: 16 bytes per lane, each
-// wave instruction reading 1 KiB contiguous, nontemporal, several instructions in
-// flight per wave, one wave per SIMD slot of the device and a grid-stride walk over the
-// buffer.  The XOR of everything read is stored only if it equals a value no probe
+// wave instruction reading 1 KiB contiguous, nontemporal, 16 instructions in flight per
+// wave, two waves per SIMD of the device, each wave streaming its own contiguous run.  The XOR of everything read is stored only if it equals a value no probe
 // buffer produces in practice, which keeps the loads without writing anything.
 
 #include <hip/hip_runtime.h>
@@ -15,21 +14,30 @@ namespace {
 
 typedef __attribute__((__vector_size__(4 * sizeof(int)))) int i32x4;
 
-constexpr int kUnroll = 8;   // 16-byte loads in flight per lane
+constexpr int kUnroll = 16;   // 1 KiB wave loads in flight per wave
 
+// Wave w of W reads the contiguous chunks [C w / W, C (w + 1) / W) of the C 1 KiB chunks
+// of the buffer (each wave streams its own run, as a decode wave streams its slice of
+// tiles); the last partial chunk, if any, is read by wave 0.
 __global__ __launch_bounds__(256) void stream_read_kernel(const i32x4* __restrict__ buf, int64_t n16,
                                                           int32_t* __restrict__ sink) {
-    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-    int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int lane = threadIdx.x & 63;
+    const int64_t waves = (int64_t)gridDim.x * 4;
+    const int64_t w = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int64_t chunks = n16 / 64;
+    const int64_t c1 = chunks * (w + 1) / waves;
+    int64_t c = chunks * w / waves;
     i32x4 acc = {0, 0, 0, 0};
-    for (; i + (kUnroll - 1) * stride < n16; i += kUnroll * stride) {
+    for (; c + kUnroll <= c1; c += kUnroll) {
         i32x4 v[kUnroll];
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u) v[u] = __builtin_nontemporal_load(buf + i + u * stride);
+        for (int u = 0; u < kUnroll; ++u) v[u] = __builtin_nontemporal_load(buf + (c + u) * 64 + lane);
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) acc ^= v[u];
     }
-    for (; i < n16; i += stride) acc ^= __builtin_nontemporal_load(buf + i);
+    for (; c < c1; ++c) acc ^= __builtin_nontemporal_load(buf + c * 64 + lane);
+    if (w == 0)
+        for (int64_t i = chunks * 64 + lane; i < n16; i += 64) acc ^= buf[i];
     const int x = acc[0] ^ acc[1] ^ acc[2] ^ acc[3];
     if (x == 0x5eed1e55) sink[0] = x;
 }
@@ -46,7 +54,8 @@ paged_kv_status paged_kv_read_bandwidth_probe(const void* buf, size_t bytes, voi
         pkv::set_error("need a 16-byte aligned buffer of a positive multiple of 16 bytes and a sink");
         return PAGED_KV_ERR_INVALID_ARG;
     }
-    const int blocks = pkv::device_shape().compute_units * 4;   // 4 waves per block: one per SIMD
+    // two waves per SIMD (a block's four waves land one on each SIMD of a compute unit)
+    const int blocks = pkv::device_shape().compute_units * 2;
     stream_read_kernel<<<dim3(blocks), dim3(256), 0, reinterpret_cast<hipStream_t>(stream)>>>(
         static_cast<const i32x4*>(buf), (int64_t)(bytes / 16), static_cast<int32_t*>(sink));
     const hipError_t e = hipGetLastError();
