@@ -578,16 +578,376 @@ void attn_prefill_mfma(PrefillArgs a) {
     }
 }
 
+// ---------------------------------------------------------------------------------------
+// Block sizes 16 and 32: K/V tiles staged through LDS and shared by the workgroup.
+//
+// The four waves of a workgroup hold different query rows of one (sequence, KV head)
+// and need the same keys, so each 32-key pair of tiles is fetched once per workgroup:
+// every wave copies a quarter of it from the pool straight into LDS (16-byte
+// global-to-LDS loads, no registers in between), the pair after it loads while the
+// current one is used, and one barrier per pair hands the buffers over.  With the K/V
+// buffers out of the registers a wave fits in half the register file: two waves per
+// SIMD, so one wave's exponentials and conversions run while the other's matrix
+// products do.  The row sums of the weights come out of the matrix cores as well (a
+// product with a block of ones), not from vector adds.
+//
+// Operand layout.  Every operand is one 16-byte LDS read, and the eight consecutive
+// lanes that LDS serves together touch eight different 16-byte bank groups:
+//  - V^T (value product, A operand): lane (dim row d, lane group q) takes the 16-byte
+//    chunk of 8 consecutive tokens, tile q/2, tokens 8(q%2)..+7, of its dim.  In LDS a
+//    16-dim block of a tile holds its 32 chunks (dim, half) at slot 2 dim + (half ^ bit 2
+//    of dim), so dims 0..7 of one half fall in eight different slots modulo 8.
+//  - The weights (B operand) must then hold those same 8 keys per lane group, so the
+//    score product S^T = K . Q^T is computed with permuted key rows: in product h (of
+//    two), row r stands for tile r/8, token 8((r/4)%2) + 4h + r%4.  Lane group q of the
+//    output then holds, over h = 0, 1, exactly tokens 8(q%2)..+7 of tile q/2.
+//  - K (score product, A operand): lane (row r, group q) reads the 16-byte chunk
+//    4kk + q of its row's token; in LDS a tile's chunk c of token t sits at slot
+//    16 c + (t ^ ((t & 8) >> 1)), which spreads the eight rows one LDS pass serves
+//    over eight slots modulo 8.
+// The copies apply these slot maps on the way in (each lane fetches the chunk that
+// belongs in its slot), so the pool layout is unchanged.
+template <int D>
+constexpr int lds_blocks() { return D == 64 ? 4 : D == 128 ? 3 : 2; }
+
+template <int D, int DT, int OUT_DT, int BS, bool SPLIT>
+__global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2)))
+void attn_prefill_lds(PrefillArgs a) {
+    constexpr int KI = D / 32;
+    constexpr int MT = D / 16;
+    constexpr int C = lds_blocks<D>();
+    constexpr int RW = 16 * C;            // query rows per wave
+    constexpr int TILE = BS * D;          // elements of one (block, KV head) region
+    constexpr int TPB = BS / kTile;       // 16-token tiles per block
+    constexpr int TE = kTile * D;         // elements of one 16-token tile
+    constexpr int PIECES = TE / 512;      // 1 KiB pieces per tile: each wave copies one of each
+    constexpr int STAGE = 4 * TE;         // K and V of a pair of tiles
+    __shared__ __attribute__((aligned(16))) uint16_t s_kv[2 * STAGE];
+    using kvec = typename std::conditional<DT == DT_BF16, bf16x8, f16x8>::type;
+
+    // same (pair, query tile) -> workgroup mapping as the register-streaming kernel
+    const int xcd = blockIdx.x % a.xcds, idx = blockIdx.x / a.xcds;
+    const int y = xcd + a.xcds * (idx / a.q_tiles);
+    if (y >= a.num_seqs * a.num_kv_heads) return;
+    const int qt = a.q_tiles - 1 - idx % a.q_tiles;
+    const int s = y / a.num_kv_heads;
+    const int g = y - s * a.num_kv_heads;
+    const int lane = threadIdx.x & 63;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int gq = lane & 15, quad = lane >> 4;
+    const int G = a.group;
+
+    const int32_t* trow = a.block_tables + (int64_t)s * a.max_blocks_per_seq;
+    const int r0 = sload(a.q_start, s), r1 = sload(a.q_start, s + 1);
+    const int ctx = sload(a.context_lens, s);
+    const int n = r1 - r0;
+    if (n < 0 || n > a.max_q_len) return;          // unusable query range: rows unknown
+    const int t_begin = qt * a.tokens_per_wg;
+    if (t_begin >= n) return;
+    const int t_end = min(n, t_begin + a.tokens_per_wg);
+    const int valid_rows = (t_end - t_begin) * G;
+    const bool bad_len = ctx < 1 || ctx > a.max_context_len || n > ctx;
+    // workgroup-uniform split test (see the register-streaming kernel)
+    if constexpr (SPLIT) {
+        if (bad_len || ctx - n + t_begin + 1 >= split_keys<DT>()) return;
+    } else {
+        if (!bad_len && ctx - n + t_begin + 1 < split_keys<DT>()) return;
+    }
+
+    // this wave's rows: w*RW .. w*RW + RW - 1 of the workgroup, row = token * G + head.  A
+    // wave without rows still copies its share of every tile and takes every barrier.
+    const int row0 = w * RW;
+    const bool has_rows = row0 < valid_rows;
+    auto row_info = [&](int b, bool& live, int& tok, int& head) __attribute__((always_inline)) {
+        const int r = row0 + 16 * b + gq;
+        live = r < valid_rows;
+        const int rr = live ? r : valid_rows - 1;       // padded rows repeat the last one
+        tok = t_begin + rr / G;
+        head = g * G + rr % G;
+    };
+    if (bad_len) {
+#pragma unroll
+        for (int b = 0; b < C; ++b) {
+            bool live;
+            int tok, head;
+            row_info(b, live, tok, head);
+            if (live)
+                for (int e = 0; e < D / 4; ++e)
+                    store_out<OUT_DT>(a.out, ((int64_t)(r0 + tok) * a.num_q_heads + head) * D +
+                                                 4 * quad + 16 * (e / 4) + e % 4, NAN);
+        }
+        return;
+    }
+    int pos[C];
+#pragma unroll
+    for (int b = 0; b < C; ++b) {
+        bool live;
+        int tok, head;
+        row_info(b, live, tok, head);
+        pos[b] = ctx - n + tok;
+    }
+    // keys of the workgroup (up to its last query's position) and of this wave
+    const int ntiles = (ctx - n + t_end + kTile - 1) / kTile;
+    const int npairs = (ntiles + 1) / 2;
+    const int last_tok = t_begin + (max(min(row0 + RW, valid_rows), 1) - 1) / G;
+    const int wave_pairs = has_rows ? (ctx - n + last_tok + 2 * kTile) / (2 * kTile) : 0;
+    const int pos_min = ctx - n + t_begin + row0 / G;   // this wave's first row
+
+    kvec qop[C][KI];
+#pragma unroll
+    for (int b = 0; b < C; ++b) {
+        bool live;
+        int tok, head;
+        row_info(b, live, tok, head);
+        const uint16_t* qh = static_cast<const uint16_t*>(a.q) +
+                             ((int64_t)(r0 + tok) * a.num_q_heads + head) * D + 8 * quad;
+#pragma unroll
+        for (int kk = 0; kk < KI; ++kk)
+            qop[b][kk] = __builtin_bit_cast(kvec, *reinterpret_cast<const i32x4*>(qh + 32 * kk));
+    }
+
+    const uint16_t* kbase = static_cast<const uint16_t*>(a.k_pool) + (int64_t)g * TILE;
+    const uint16_t* vbase = static_cast<const uint16_t*>(a.v_pool) + (int64_t)g * TILE;
+    const int64_t blk_stride = (int64_t)a.num_kv_heads * TILE;
+    bool bad_block = false;
+
+    // Block ids of pair j's tiles 2j, 2j+1 (past the workgroup's keys: the last tile
+    // again; its scores are masked and its V cleared), read a pair ahead of their use.
+    auto pair_ids = [&](int j, int64_t (&off)[2]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int it = min(2 * j + h, ntiles - 1);
+            int32_t b = sload(trow, it / TPB);
+            if ((uint32_t)b >= (uint32_t)a.num_blocks) {
+                bad_block = true;
+                b = 0;
+            }
+            off[h] = b * blk_stride + (it % TPB) * TE;   // the tile's elements in either pool
+        }
+    };
+    // Stage layout (elements): K tile 0, K tile 1 (TE each, chunks 4p..4p+3 in piece p),
+    // then V as MT 1 KiB blocks [tile 0 dims 16mt..16mt+15 | tile 1 same dims], in the
+    // slot orders above.  The copies are 1 KiB pieces, lane l filling slot l: K tile h
+    // piece p, or V block mt (lanes 0-31 from tile 0, 32-63 from tile 1); wave w takes
+    // pieces w, w + 4, ...
+    constexpr int KPIECES = 2 * PIECES;
+    constexpr int NPIECES = KPIECES + MT;
+    static_assert(KPIECES % kWaves == 0 && MT % kWaves == 0, "pieces per wave");
+    // the pool chunk that belongs in this lane's slot of a K piece / a V block
+    // (both slot maps are their own inverses)
+    const int k_src = ((lane >> 4) * 16 + ((lane & 15) ^ ((lane & 8) >> 1))) * 8;
+    const int v_dim = (lane & 31) >> 1;
+    const int v_src = v_dim * 16 + (((lane & 1) ^ (v_dim >> 2)) & 1) * 8;
+    auto issue = [&](int st, const int64_t (&off)[2]) __attribute__((always_inline)) {
+        const uint16_t* k0 = kbase + off[0] + k_src;
+        const uint16_t* k1 = kbase + off[1] + k_src;
+        const uint16_t* vsrc = vbase + ((lane >> 5) ? off[1] : off[0]) + v_src;
+        uint16_t* dst = s_kv + st * STAGE;
+#pragma unroll
+        for (int i = 0; i < NPIECES / kWaves; ++i) {
+            const int pc = w + kWaves * i;
+            if (i < KPIECES / kWaves) {
+                const int h = pc / PIECES, p = pc % PIECES;
+                __builtin_amdgcn_global_load_lds((h ? k1 : k0) + p * 512, dst + h * TE + p * 512, 16, 0, 0);
+            } else {
+                const int mt = pc - KPIECES;
+                __builtin_amdgcn_global_load_lds(vsrc + mt * 256, dst + 2 * TE + mt * 512, 16, 0, 0);
+            }
+        }
+    };
+
+    f32x4 acc[C][MT], accl[C];
+    float m[C];
+#pragma unroll
+    for (int b = 0; b < C; ++b) {
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) acc[b][mt] = (f32x4){0.f, 0.f, 0.f, 0.f};
+        accl[b] = (f32x4){0.f, 0.f, 0.f, 0.f};
+        m[b] = kNegInf;
+    }
+    // A-operand of ones: the product with the weights gives each row's weight sum
+    const int one2 = DT == DT_BF16 ? 0x3F803F80 : 0x3C003C00;
+    const i32x4 ones = {one2, one2, one2, one2};
+
+    auto mfma = [&](const i32x4& x, const i32x4& yv, f32x4 c) __attribute__((always_inline)) {
+        if constexpr (DT == DT_BF16)
+            return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, x),
+                                                          __builtin_bit_cast(bf16x8, yv), c, 0, 0, 0);
+        else
+            return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, x),
+                                                         __builtin_bit_cast(f16x8, yv), c, 0, 0, 0);
+    };
+
+    // per-lane LDS read offsets within a stage: K rows of score product h (tile gq/8,
+    // token 8((gq/4)%2) + 4h + gq%4, chunk 4kk + quad) and the V^T chunk
+    int k_rd[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int t = 8 * ((gq >> 2) & 1) + 4 * h + (gq & 3);
+        k_rd[h] = (gq >> 3) * TE + (quad * 16 + (t ^ ((t & 8) >> 1))) * 8;
+    }
+    const int v_rd = 2 * TE + (quad >> 1) * 256 + (2 * gq + (((quad & 1) ^ (gq >> 2)) & 1)) * 8;
+
+    // one pair of tiles from LDS stage `stg`
+    auto compute = [&](auto special, int j, const uint16_t* stg) __attribute__((always_inline)) {
+        f32x4 sc[C][2];
+#pragma unroll
+        for (int b = 0; b < C; ++b) sc[b][0] = sc[b][1] = (f32x4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+#pragma unroll
+            for (int kk = 0; kk < KI; ++kk) {
+                const i32x4 kop = *reinterpret_cast<const i32x4*>(stg + k_rd[h] + kk * 512);
+#pragma unroll
+                for (int b = 0; b < C; ++b)
+                    sc[b][h] = mfma(kop, __builtin_bit_cast(i32x4, qop[b][kk]), sc[b][h]);
+            }
+        }
+        if (decltype(special)::value && (2 * j + 1) * kTile + kTile - 1 > pos_min) {
+            // lane group q holds tile q/2, tokens 8(q%2) + 4h + r
+            const int kp0 = (2 * j + (quad >> 1)) * kTile + 8 * (quad & 1);
+#pragma unroll
+            for (int b = 0; b < C; ++b)
+#pragma unroll
+                for (int h = 0; h < 2; ++h)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        if (kp0 + 4 * h + r > pos[b]) sc[b][h][r] = kNegInf;
+        }
+        float xm[C];
+        bool grow = false;
+#pragma unroll
+        for (int b = 0; b < C; ++b) {
+            float t = fmaxf(fmaxf(sc[b][0][0], sc[b][0][1]), sc[b][0][2]);
+            t = fmaxf(fmaxf(t, sc[b][0][3]), sc[b][1][0]);
+            t = fmaxf(fmaxf(t, sc[b][1][1]), sc[b][1][2]);
+            t = fmaxf(t, sc[b][1][3]);
+            xm[b] = t * a.scale_log2;
+            grow |= xm[b] > m[b] + kRescaleSlack;
+        }
+        if (__ballot(grow)) {
+#pragma unroll
+            for (int b = 0; b < C; ++b) {
+                const float mnew = fmaxf(m[b], max_across_quads(xm[b]));
+                const float alpha = exp2_fast(m[b] - mnew);
+                accl[b] *= alpha;
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt) acc[b][mt] *= alpha;
+                m[b] = mnew;
+            }
+        }
+        i32x4 phi[C], plo[C];
+#pragma unroll
+        for (int b = 0; b < C; ++b) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const float p0 = exp2_fast(fmaf(sc[b][r >> 1][2 * (r & 1)], a.scale_log2, -m[b]));
+                const float p1 = exp2_fast(fmaf(sc[b][r >> 1][2 * (r & 1) + 1], a.scale_log2, -m[b]));
+                if constexpr (SPLIT) {
+                    int hw, lw;
+                    split_pair<DT>(p0, p1, hw, lw);
+                    phi[b][r] = hw;
+                    plo[b][r] = lw;
+                } else {
+                    phi[b][r] = (int)pack2_16<DT>(p0, p1);
+                }
+            }
+            accl[b] = mfma(ones, phi[b], accl[b]);
+            if constexpr (SPLIT) accl[b] = mfma(ones, plo[b], accl[b]);
+        }
+        // V^T operand: tile q/2, tokens 8(q%2)..+7 of dim 16 mt + gq (slots past the
+        // context may hold anything, NaN included: cleared)
+        const int vt = 2 * j + (quad >> 1);
+        const int vvalid = (vt < ntiles ? ctx - vt * kTile : 0) - 8 * (quad & 1);
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+            i32x4 va = *reinterpret_cast<const i32x4*>(stg + v_rd + mt * 512);
+            if (decltype(special)::value && vvalid < 8) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    uint32_t x = (uint32_t)va[e];
+                    if (2 * e >= vvalid) x &= 0xFFFF0000u;
+                    if (2 * e + 1 >= vvalid) x &= 0x0000FFFFu;
+                    va[e] = (int)x;
+                }
+            }
+#pragma unroll
+            for (int b = 0; b < C; ++b) {
+                acc[b][mt] = mfma(va, phi[b], acc[b][mt]);
+                if constexpr (SPLIT) acc[b][mt] = mfma(va, plo[b], acc[b][mt]);
+            }
+        }
+    };
+
+    constexpr std::integral_constant<bool, false> kPlain{};
+    constexpr std::integral_constant<bool, true> kSpecial{};
+    // pairs before j_plain need neither the causal mask nor V clearing for this wave
+    const int t_zero = min(ntiles, ctx / kTile);
+    const int j_mask = (pos_min + 1) / (2 * kTile);
+    const int j_plain = min(min(j_mask, t_zero / 2), wave_pairs);
+
+    // Pair j sits in stage j & 1.  At the barrier of step j every wave has finished pair
+    // j - 1 (so its stage may be overwritten by pair j + 1) and every copy of pair j has
+    // landed (each wave waits for its own copies before the barrier).
+    int64_t ids_next[2], ids_after[2];
+    pair_ids(0, ids_next);
+    issue(0, ids_next);
+    pair_ids(min(1, npairs - 1), ids_next);
+    int j = 0;
+    for (; j < j_plain; ++j) {
+        wait_memory_done();
+        __syncthreads();
+        if (j + 1 < npairs) issue((j + 1) & 1, ids_next);
+        pair_ids(min(j + 2, npairs - 1), ids_after);
+        compute(kPlain, j, s_kv + (j & 1) * STAGE);
+        ids_next[0] = ids_after[0];
+        ids_next[1] = ids_after[1];
+    }
+    for (; j < npairs; ++j) {
+        wait_memory_done();
+        __syncthreads();
+        if (j + 1 < npairs) issue((j + 1) & 1, ids_next);
+        pair_ids(min(j + 2, npairs - 1), ids_after);
+        if (j < wave_pairs) compute(kSpecial, j, s_kv + (j & 1) * STAGE);
+        ids_next[0] = ids_after[0];
+        ids_next[1] = ids_after[1];
+    }
+    if (!has_rows) return;
+
+    // normalise and write: lane holds row gq of block b, dims 16*mt + 4*quad .. +3
+#pragma unroll
+    for (int b = 0; b < C; ++b) {
+        const float inv = 1.f / accl[b][0];
+        bool live;
+        int tok, head;
+        row_info(b, live, tok, head);
+        if (!live) continue;
+        const int64_t ob = ((int64_t)(r0 + tok) * a.num_q_heads + head) * D;
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+            f32x4 v;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) v[r] = bad_block ? NAN : acc[b][mt][r] * inv;
+            store_out4<OUT_DT>(a.out, ob + 16 * mt + 4 * quad, v);
+        }
+    }
+}
+
 // Two launches: every query tile without the weight split, then (only the first tiles of
 // each sequence can hold queries that see fewer than split_keys keys) those tiles with it.
 template <int D, int DT, int OUT, int BS>
 void launch_t(const PrefillArgs& a, dim3 grid, hipStream_t st) {
-    attn_prefill_mfma<D, DT, OUT, BS, false><<<grid, dim3(kWaves * 64), 0, st>>>(a);
     PrefillArgs b = a;
     b.q_tiles = std::min(a.q_tiles, (split_keys<DT>() - 1 + a.tokens_per_wg - 1) / a.tokens_per_wg);
     const int64_t pairs = (int64_t)a.num_seqs * a.num_kv_heads;
     const dim3 g2((unsigned)((int64_t)a.xcds * b.q_tiles * ((pairs + a.xcds - 1) / a.xcds)));
-    attn_prefill_mfma<D, DT, OUT, BS, true><<<g2, dim3(kWaves * 64), 0, st>>>(b);
+    if constexpr (BS == 1) {
+        attn_prefill_mfma<D, DT, OUT, BS, false><<<grid, dim3(kWaves * 64), 0, st>>>(a);
+        attn_prefill_mfma<D, DT, OUT, BS, true><<<g2, dim3(kWaves * 64), 0, st>>>(b);
+    } else {
+        attn_prefill_lds<D, DT, OUT, BS, false><<<grid, dim3(kWaves * 64), 0, st>>>(a);
+        attn_prefill_lds<D, DT, OUT, BS, true><<<g2, dim3(kWaves * 64), 0, st>>>(b);
+    }
 }
 
 template <int D, int DT, int BS>
@@ -609,9 +969,14 @@ void launch_bs(const PrefillArgs& a, int bs, int dtype, int out_dtype, dim3 grid
     else launch_dt<D, 16>(a, dtype, out_dtype, grid, st);
 }
 
-int tokens_per_workgroup(int head_dim, int group) {
-    const int blocks = head_dim == 64 ? prefill_blocks<64>() : head_dim == 256 ? prefill_blocks<256>()
-                                                                              : prefill_blocks<128>();
+// query tokens per workgroup: its 4 waves' rows (16 per column block) over the group
+int tokens_per_workgroup(int head_dim, int group, int block_size) {
+    int blocks;
+    if (block_size == 1)
+        blocks = head_dim == 64 ? prefill_blocks<64>() : head_dim == 256 ? prefill_blocks<256>()
+                                                                        : prefill_blocks<128>();
+    else
+        blocks = head_dim == 64 ? lds_blocks<64>() : head_dim == 256 ? lds_blocks<256>() : lds_blocks<128>();
     return 4 * 16 * blocks / group;
 }
 
@@ -695,7 +1060,7 @@ paged_kv_status paged_attention_prefill(const paged_kv_pool_desc* desc, void* ou
     a.num_blocks = desc->num_blocks;
     a.max_q_len = max_q_len;
     a.max_context_len = max_context_len;
-    a.tokens_per_wg = tokens_per_workgroup(desc->head_dim, group);
+    a.tokens_per_wg = tokens_per_workgroup(desc->head_dim, group, desc->block_size);
     a.q_tiles = (max_q_len + a.tokens_per_wg - 1) / a.tokens_per_wg;
     a.scale_log2 = scale * kLog2e;
     a.xcds = pkv::device_shape().xcds;
