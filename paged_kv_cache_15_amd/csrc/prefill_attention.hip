@@ -14,26 +14,22 @@
 //
 // Work decomposition.  A workgroup of 4 waves takes one KV head g of one sequence and
 // a run of TQ query tokens; its rows are (token, query head of g's group) pairs,
-// token-major, 64*C rows in all (C = prefill_blocks column blocks of 16 rows per
-// wave), so each K/V tile a wave loads serves 16*C query rows.  Every wave streams the
-// keys 0 .. (largest position among its rows) in 16-token tiles straight from the pool
-// into MFMA operands, with the decode kernels' orientation: S^T = K . Q^T
-// (v_mfma_f32_16x16x32, query rows on the N side) and O^T += V^T . P^T over pairs of
-// tiles (v_mfma_f32_16x16x32 with K = 32 keys; the weights come out of the score
-// product already in the B-operand layout; 16-bit head plus remainder, as in decode).
-// The causal mask is per lane (each lane owns one query row of a block) and only
-// applied to tile pairs that reach past a row's position; the online softmax is base 2
-// with lazy rescaling, tested once per pair for all blocks.  The pairs are software-
-// pipelined: the score products of pair j+1 are issued together with the weights and
-// value products of pair j, so the matrix cores and the vector ALU work side by side,
-// and the pairs that need neither the mask nor any clearing of slots past the context
-// run a branch-free step.  The query tiles of one (sequence, KV head) run on one XCD,
-// one after the other, the last (most keys) first, so the K/V they all read stays in
-// that XCD's L2.
+// token-major, 64*C rows in all (C column blocks of 16 rows per wave).  The workgroup
+// walks the keys 0 .. (largest position among its rows) in pairs of 16-token tiles,
+// each pair copied once from the pool into LDS and used by all four waves, with the
+// decode kernels' orientation: S^T = K . Q^T (v_mfma_f32_16x16x32, query rows on the N
+// side) and O^T += V^T . P^T over the pair (v_mfma_f32_16x16x32 with K = 32 keys; the
+// weights come out of the score product already in the B-operand layout).  The causal
+// mask is per lane (each lane owns one query row of a block) and only applied to pairs
+// that reach past a row's position; the online softmax is base 2 with lazy rescaling,
+// tested once per pair for all blocks, and the pairs that need neither the mask nor any
+// clearing of slots past the context run a branch-free step.  The query tiles of one
+// (sequence, KV head) run on one XCD, the last (most keys) first, so the K/V they all
+// read stays in that XCD's L2.
 //
 // Block sizes 16 and 32 (a 32-token block is two 16-token sub-blocks in the pool), and 1
-// (each lane loads from its own token's block; V, token-major at that size, reaches the
-// value product through per-wave LDS rows, as in the decode kernels).
+// (every token in its own block: the copies gather per lane, and V, token-major at that
+// size, is transposed on its way into LDS).
 
 #include <algorithm>
 
@@ -92,17 +88,6 @@ __device__ __forceinline__ void split_pair(float w0, float w1, int& head, int& r
     rest = (int)pack2_16<DT>(r0, r1);
 }
 
-// The two weights a packed pair of 16-bit values stands for, as floats.
-template <int DT>
-__device__ __forceinline__ float2 unpack2_16(uint32_t h) {
-    if constexpr (DT == DT_BF16) {
-        return make_float2(__uint_as_float(h << 16), __uint_as_float(h & 0xFFFF0000u));
-    } else {
-        const f16x2_t hv = __builtin_bit_cast(f16x2_t, h);
-        return make_float2((float)hv[0], (float)hv[1]);
-    }
-}
-
 // Rows that see at least split_keys<DT>() keys take their weights as one 16-bit rounding
 // (summed into the row's denominator as rounded, so the softmax stays consistent); rows
 // with fewer keys keep the 16-bit head plus remainder.  One rounding moves the output by
@@ -127,459 +112,8 @@ __device__ __forceinline__ void store_out4(void* out, int64_t i, f32x4 v) {
     }
 }
 
-// C: 16-row column blocks per wave: every K/V load serves 16*C query rows, so more
-// blocks mean fewer loads per row (the load path bounds the kernel), up to the 512
-// registers of a wave.  Three at head_dim 128 fill them (one 16-byte reload from scratch
-// per tile pair remains) and beat two by 2-17% across the workloads; five at 64 (no
-// spill; four measured 0-9% slower, six spill and were slower) and one at 256.  (Sharing each tile pair among the workgroup's four waves through LDS, with 3
-// or 4 blocks per wave, measured slower: 363-430 against 459-484 TFLOP/s.)
-template <int D>
-constexpr int prefill_blocks() { return D == 128 ? 3 : D == 64 ? 5 : 1; }
-
-template <int D, int DT, int OUT_DT, int BS, bool SPLIT>
-__global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(1)))
-void attn_prefill_mfma(PrefillArgs a) {
-    constexpr int KI = D / 32;
-    constexpr int MT = D / 16;
-    constexpr int C = prefill_blocks<D>();
-    constexpr int RW = 16 * C;            // query rows per wave
-    constexpr int TILE = BS * D;          // elements of one (block, KV head) region
-    constexpr int TPB = BS >= kTile ? BS / kTile : 1;   // 16-token tiles (sub-blocks) per block
-    constexpr int LDW = D + 8;            // block size 1: LDS row of one token's values
-    // block size 1: each wave transposes its tiles' token-major V through LDS rows
-    __shared__ uint16_t s_vt[BS == 1 ? kWaves * kTile * LDW : 1];
-    using kvec = typename std::conditional<DT == DT_BF16, bf16x8, f16x8>::type;
-
-    // Workgroup b runs on XCD b % X (X = a.xcds, 8 on MI355X).  Pair y = sequence * KV
-    // heads + KV head is given to XCD y % X (so the K/V its query tiles all read stays in
-    // that XCD's L2, and with 8 KV heads on 8 dies every XCD gets one head of every
-    // sequence); on each XCD the workgroups take its pairs in order, each pair's query
-    // tiles last first.  The mapping is a bijection onto (pair, query tile) for any X, so
-    // X only matters for speed.
-    const int xcd = blockIdx.x % a.xcds, idx = blockIdx.x / a.xcds;
-    const int y = xcd + a.xcds * (idx / a.q_tiles);
-    if (y >= a.num_seqs * a.num_kv_heads) return;
-    const int qt = a.q_tiles - 1 - idx % a.q_tiles;
-    const int s = y / a.num_kv_heads;
-    const int g = y - s * a.num_kv_heads;
-    const int lane = threadIdx.x & 63;
-    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int gq = lane & 15, quad = lane >> 4;
-    const int G = a.group;
-
-    // Everything that depends on the sequence alone is read at once (scalar loads, all in
-    // flight together): the query range, the context length and the block ids of the
-    // first four tiles (clamped to the table row; ids past the context are never used).
-    // The first K/V loads then wait for one memory round trip, not three.
-    const int32_t* trow = a.block_tables + (int64_t)s * a.max_blocks_per_seq;
-    const int r0 = sload(a.q_start, s), r1 = sload(a.q_start, s + 1);
-    const int ctx = sload(a.context_lens, s);
-    int32_t id0[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) id0[i] = BS == 1 ? 0 : sload(trow, min(i / TPB, a.max_blocks_per_seq - 1));
-    const int n = r1 - r0;
-    if (n < 0 || n > a.max_q_len) return;          // unusable query range: rows unknown
-    const int t_begin = qt * a.tokens_per_wg;
-    if (t_begin >= n) return;
-    const int t_end = min(n, t_begin + a.tokens_per_wg);
-    // this wave's rows: w*RW .. w*RW + RW - 1 of the workgroup, row = token * G + head
-    const int row0 = w * RW;
-    const int valid_rows = (t_end - t_begin) * G;
-    if (row0 >= valid_rows) return;
-    const bool bad_len = ctx < 1 || ctx > a.max_context_len || n > ctx;
-    // Two launches share the work: SPLIT takes the workgroups whose first query sees fewer
-    // than split_keys keys, the other one the rest (and writes the NaN rows of invalid
-    // sequences).  The test is the same for every wave of a workgroup.
-    if constexpr (SPLIT) {
-        if (bad_len || ctx - n + t_begin + 1 >= split_keys<DT>()) return;
-    } else {
-        if (!bad_len && ctx - n + t_begin + 1 < split_keys<DT>()) return;
-    }
-
-    // per block b: this lane's row, its token, head and position
-    // (recomputed where needed rather than held: at three blocks per wave every register
-    // counts)
-    auto row_info = [&](int b, bool& live, int& tok, int& head) __attribute__((always_inline)) {
-        const int r = row0 + 16 * b + gq;
-        live = r < valid_rows;
-        const int rr = live ? r : valid_rows - 1;       // padded rows repeat the last one
-        tok = t_begin + rr / G;
-        head = g * G + rr % G;
-    };
-    int pos[C];
-#pragma unroll
-    for (int b = 0; b < C; ++b) {
-        bool live;
-        int tok, head;
-        row_info(b, live, tok, head);
-        pos[b] = ctx - n + tok;
-    }
-    if (bad_len) {
-#pragma unroll
-        for (int b = 0; b < C; ++b) {
-            bool live;
-            int tok, head;
-            row_info(b, live, tok, head);
-            if (live)
-                for (int e = 0; e < D / 4; ++e)
-                    store_out<OUT_DT>(a.out, ((int64_t)(r0 + tok) * a.num_q_heads + head) * D +
-                                                 4 * quad + 16 * (e / 4) + e % 4, NAN);
-        }
-        return;
-    }
-    // keys this wave needs: up to the position of its last valid row
-    const int last_tok = t_begin + (min(row0 + RW, valid_rows) - 1) / G;
-    const int n_keys = ctx - n + last_tok + 1;
-    const int ntiles = (n_keys + kTile - 1) / kTile;
-    const int pos_min = ctx - n + t_begin + row0 / G;   // this wave's first row
-
-    // query operands: lane holds q[row gq][32*kk + 8*quad .. +8] of each block
-    kvec qop[C][KI];
-#pragma unroll
-    for (int b = 0; b < C; ++b) {
-        bool live;
-        int tok, head;
-        row_info(b, live, tok, head);
-        const uint16_t* qh = static_cast<const uint16_t*>(a.q) +
-                             ((int64_t)(r0 + tok) * a.num_q_heads + head) * D + 8 * quad;
-#pragma unroll
-        for (int kk = 0; kk < KI; ++kk)
-            qop[b][kk] = __builtin_bit_cast(kvec, *reinterpret_cast<const i32x4*>(qh + 32 * kk));
-    }
-
-    const uint16_t* kbase = static_cast<const uint16_t*>(a.k_pool) + (int64_t)g * TILE;
-    const uint16_t* vbase = static_cast<const uint16_t*>(a.v_pool) + (int64_t)g * TILE;
-    const int64_t blk_stride = (int64_t)a.num_kv_heads * TILE;
-    const int voff = gq * 4 + quad;
-
-    f32x4 acc[C][MT];
-    float m[C], lsum[C];
-#pragma unroll
-    for (int b = 0; b < C; ++b) {
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) acc[b][mt] = (f32x4){0.f, 0.f, 0.f, 0.f};
-        m[b] = kNegInf;
-        lsum[b] = 0.f;
-    }
-    bool bad_block = false;
-
-    // Keys go in pairs of 16-token tiles: one v_mfma_f32_16x16x32 takes 32 keys of the
-    // value product.  The order of keys inside a contraction is free, so lane group q
-    // takes keys 4q..4q+3 of the first tile followed by 4q..4q+3 of the second: that is
-    // what the lane already holds of both the weights (score-product layout) and V^T
-    // (two 8-byte loads), so nothing moves between lanes.
-    //
-    // Software pipeline: while the weights and value products of pair j are computed
-    // (vector ALU and the second half of the matrix work), the score products of pair
-    // j+1 are issued into the same basic block, so the two overlap; K of pair j+2 and V
-    // of pair j+1 load meanwhile.
-    // V as loaded: V^T operands per 16 dims, or (block size 1) token rows like K
-    using vbuf = typename std::conditional<BS == 1, i32x4[KI], i32x2[MT]>::type;
-    struct KPair {
-        i32x4 k[2][KI];
-    };
-    struct VPair {
-        vbuf v[2];
-    };
-    uint16_t* vrows = s_vt + w * kTile * LDW;
-    const int npairs = (ntiles + 1) / 2;
-
-    // block ids of pair j's tiles (the second may lie past the wave's keys: then it
-    // repeats the last tile, its V is zeroed and its scores masked, since its keys are
-    // past every row's position); block size 1: the lane's own token's block
-    auto check_bid = [&](int32_t b) __attribute__((always_inline)) {
-        if ((uint32_t)b >= (uint32_t)a.num_blocks) {
-            bad_block = true;
-            b = 0;
-        }
-        return b;
-    };
-    // pairs 0 and 1 (tiles 0..3) from the ids read at the start
-    auto first_bids = [&](int j, int32_t (&bid)[2]) __attribute__((always_inline)) {
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            const int it = min(2 * j + h, ntiles - 1);
-            bid[h] = check_bid(it == 0 ? id0[0] : it == 1 ? id0[1] : it == 2 ? id0[2] : id0[3]);
-        }
-    };
-    auto pair_bids = [&](int j, int32_t (&bid)[2]) __attribute__((always_inline)) {
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            const int it = min(2 * j + h, ntiles - 1);
-            if constexpr (BS == 1) {
-                bool bad;
-                bid[h] = lane_block_bs1(trow, it, ctx, a.num_blocks, lane, bad);
-                bad_block |= bad;
-            } else {
-                bid[h] = check_bid(sload(trow, it / TPB));
-            }
-        }
-    };
-    // plain (cached) loads: the other waves and query tiles of this sequence read the
-    // same tiles
-    auto load_k = [&](int j, const int32_t (&bid)[2], KPair& kp) __attribute__((always_inline)) {
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            const int it = min(2 * j + h, ntiles - 1);
-            if constexpr (BS == 1) {
-                const i32x4* kt = reinterpret_cast<const i32x4*>(kbase + bid[h] * blk_stride) + (lane >> 4);
-#pragma unroll
-                for (int kk = 0; kk < KI; ++kk) kp.k[h][kk] = kt[4 * kk];
-            } else {
-                const int64_t sub = (int64_t)(it % TPB) * (kTile * D);
-                const i32x4* kt = reinterpret_cast<const i32x4*>(kbase + bid[h] * blk_stride + sub) + lane;
-#pragma unroll
-                for (int kk = 0; kk < KI; ++kk) kp.k[h][kk] = kt[kk * 64];
-            }
-        }
-    };
-    auto load_v = [&](int j, const int32_t (&bid)[2], VPair& vp) __attribute__((always_inline)) {
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            const int it = min(2 * j + h, ntiles - 1);
-            if constexpr (BS == 1) {
-                const i32x4* vt = reinterpret_cast<const i32x4*>(vbase + bid[h] * blk_stride) + (lane >> 4);
-#pragma unroll
-                for (int kk = 0; kk < KI; ++kk) vp.v[h][kk] = vt[4 * kk];
-            } else {
-                const int64_t sub = (int64_t)(it % TPB) * (kTile * D);
-                const i32x2* vt = reinterpret_cast<const i32x2*>(vbase + bid[h] * blk_stride + sub) + voff;
-#pragma unroll
-                for (int mt = 0; mt < MT; ++mt) vp.v[h][mt] = vt[mt * 64];
-            }
-        }
-    };
-
-    constexpr std::integral_constant<bool, false> kPlain{};
-    constexpr std::integral_constant<bool, true> kSpecial{};
-    // S^T = K . Q^T for both tiles and every block
-    auto scores = [&](const KPair& kp, f32x4 (&sc)[C][2]) __attribute__((always_inline)) {
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-#pragma unroll
-            for (int b = 0; b < C; ++b) {
-                f32x4 acc_s = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int kk = 0; kk < KI; ++kk) {
-                    if constexpr (DT == DT_BF16)
-                        acc_s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                            __builtin_bit_cast(bf16x8, kp.k[h][kk]), qop[b][kk], acc_s, 0, 0, 0);
-                    else
-                        acc_s = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-                            __builtin_bit_cast(f16x8, kp.k[h][kk]), qop[b][kk], acc_s, 0, 0, 0);
-                }
-                sc[b][h] = acc_s;
-            }
-        }
-    };
-    // causal mask, only where some key of pair j is past some row's position (scores
-    // stay unscaled: scale > 0 keeps their order); then the pair's row maxima (scaled)
-    // and whether any of them passes the running maximum by more than the slack
-    float xm[C];
-    auto mask_and_max = [&](auto special, int j, f32x4 (&sc)[C][2]) __attribute__((always_inline)) {
-        if (decltype(special)::value && (2 * j + 1) * kTile + kTile - 1 > pos_min) {
-#pragma unroll
-            for (int b = 0; b < C; ++b)
-#pragma unroll
-                for (int h = 0; h < 2; ++h)
-#pragma unroll
-                    for (int r = 0; r < 4; ++r)
-                        if ((2 * j + h) * kTile + 4 * quad + r > pos[b]) sc[b][h][r] = kNegInf;
-        }
-        bool grow = false;
-#pragma unroll
-        for (int b = 0; b < C; ++b) {
-            // a chain of three-way maxima
-            float t = fmaxf(fmaxf(sc[b][0][0], sc[b][0][1]), sc[b][0][2]);
-            t = fmaxf(fmaxf(t, sc[b][0][3]), sc[b][1][0]);
-            t = fmaxf(fmaxf(t, sc[b][1][1]), sc[b][1][2]);
-            t = fmaxf(t, sc[b][1][3]);
-            xm[b] = t * a.scale_log2;
-            grow |= xm[b] > m[b] + kRescaleSlack;
-        }
-        return grow;
-    };
-    auto rescale = [&]() __attribute__((always_inline)) {
-#pragma unroll
-        for (int b = 0; b < C; ++b) {
-            const float mnew = fmaxf(m[b], max_across_quads(xm[b]));
-            const float alpha = exp2_fast(m[b] - mnew);
-            lsum[b] *= alpha;
-#pragma unroll
-            for (int mt = 0; mt < MT; ++mt) acc[b][mt] *= alpha;
-            m[b] = mnew;
-        }
-    };
-    // weights of pair j and O^T += V^T . P^T
-    auto accumulate = [&](auto special, int j, const f32x4 (&sc)[C][2], const VPair& vp) __attribute__((always_inline)) {
-        i32x2 vv[2][MT];
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            if constexpr (BS == 1) {
-                // token rows -> V^T operand (4 tokens of one dim per lane) through LDS
-                lds_put_rows<uint16_t, KI>(vrows, LDW, lane, vp.v[h]);
-#pragma unroll
-                for (int mt = 0; mt < MT; ++mt) {
-                    uint32_t e[4];
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) e[r] = vrows[(4 * quad + r) * LDW + 16 * mt + gq];
-                    vv[h][mt][0] = (int)(e[0] | e[1] << 16);
-                    vv[h][mt][1] = (int)(e[2] | e[3] << 16);
-                }
-            } else {
-#pragma unroll
-                for (int mt = 0; mt < MT; ++mt) vv[h][mt] = vp.v[h][mt];
-            }
-        }
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            const int valid = 2 * j + h < ntiles ? ctx - (2 * j + h) * kTile : 0;
-            if (decltype(special)::value && valid < kTile) {
-                // slots past the context may hold anything (NaN included): clear them
-#pragma unroll
-                for (int mt = 0; mt < MT; ++mt) {
-                    uint32_t lo = (uint32_t)vv[h][mt][0], hi = (uint32_t)vv[h][mt][1];
-                    if (4 * quad + 0 >= valid) lo &= 0xFFFF0000u;
-                    if (4 * quad + 1 >= valid) lo &= 0x0000FFFFu;
-                    if (4 * quad + 2 >= valid) hi &= 0xFFFF0000u;
-                    if (4 * quad + 3 >= valid) hi &= 0x0000FFFFu;
-                    vv[h][mt][0] = (int)lo;
-                    vv[h][mt][1] = (int)hi;
-                }
-            }
-        }
-#pragma unroll
-        for (int b = 0; b < C; ++b) {
-            // weights 2^(scale*s - m) as a 16-bit head plus a 16-bit remainder (as in decode)
-            i32x4 phi, plo;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const float p0 = exp2_fast(fmaf(sc[b][r >> 1][2 * (r & 1)], a.scale_log2, -m[b]));
-                const float p1 = exp2_fast(fmaf(sc[b][r >> 1][2 * (r & 1) + 1], a.scale_log2, -m[b]));
-                if constexpr (SPLIT) {
-                    int hw, lw;
-                    split_pair<DT>(p0, p1, hw, lw);
-                    phi[r] = hw;
-                    plo[r] = lw;
-                    lsum[b] += p0;
-                    lsum[b] += p1;
-                } else {
-                    const uint32_t hw = pack2_16<DT>(p0, p1);
-                    const float2 pr = unpack2_16<DT>(hw);
-                    phi[r] = (int)hw;
-                    lsum[b] += pr.x;
-                    lsum[b] += pr.y;
-                }
-            }
-#pragma unroll
-            for (int mt = 0; mt < MT; ++mt) {
-                const i32x4 va = {vv[0][mt][0], vv[0][mt][1], vv[1][mt][0], vv[1][mt][1]};
-                if constexpr (DT == DT_BF16) {
-                    acc[b][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                        __builtin_bit_cast(bf16x8, va), __builtin_bit_cast(bf16x8, phi), acc[b][mt], 0, 0, 0);
-                    if constexpr (SPLIT)
-                        acc[b][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                            __builtin_bit_cast(bf16x8, va), __builtin_bit_cast(bf16x8, plo), acc[b][mt], 0, 0, 0);
-                } else {
-                    acc[b][mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-                        __builtin_bit_cast(f16x8, va), __builtin_bit_cast(f16x8, phi), acc[b][mt], 0, 0, 0);
-                    if constexpr (SPLIT)
-                        acc[b][mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-                            __builtin_bit_cast(f16x8, va), __builtin_bit_cast(f16x8, plo), acc[b][mt], 0, 0, 0);
-                }
-            }
-        }
-    };
-
-    // Buffers: K of pair j+1 and V of pair j are in use during step j; K of pair j+2 and
-    // V of pair j+1 load into the other two.  Every step issues the same loads (past the
-    // last pair they repeat it), so the compiler waits for exactly what a step uses.
-    // Block ids are looked up a step before the loads that use them.
-    KPair kA, kB;
-    VPair vA, vB;
-    int32_t bid_v[2], bid_k[2], bid_n[2];
-    f32x4 S[C][2];
-    if constexpr (BS == 1) {
-        pair_bids(0, bid_n);
-        pair_bids(min(1, npairs - 1), bid_v);
-    } else {
-        first_bids(0, bid_n);
-        first_bids(min(1, npairs - 1), bid_v);
-    }
-    load_k(0, bid_n, kA);
-    load_v(0, bid_n, vA);
-    load_k(min(1, npairs - 1), bid_v, kB);
-    pair_bids(min(2, npairs - 1), bid_k);
-    scores(kA, S);
-    bool grow = mask_and_max(kSpecial, 0, S);
-
-    // step j: S holds pair j's scores, kn K of pair j+1, vc V of pair j (j + 1 < npairs)
-    auto step = [&](auto special, int j, const KPair& kn, KPair& kl, const VPair& vc, VPair& vl) __attribute__((always_inline)) {
-        if (__ballot(grow)) rescale();
-        load_v(j + 1, bid_v, vl);
-        load_k(min(j + 2, npairs - 1), bid_k, kl);
-        pair_bids(min(j + 3, npairs - 1), bid_n);
-        f32x4 sn[C][2];
-        scores(kn, sn);
-        accumulate(special, j, S, vc);
-        grow = mask_and_max(special, j + 1, sn);
-#pragma unroll
-        for (int b = 0; b < C; ++b) {
-            S[b][0] = sn[b][0];
-            S[b][1] = sn[b][1];
-        }
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            bid_v[h] = bid_k[h];
-            bid_k[h] = bid_n[h];
-        }
-    };
-    // Pairs before j_plain need neither the causal mask nor V zeroing (every key is at
-    // or before every row's position, and every slot is inside the context): their steps
-    // run without those branches, so each step is one basic block.
-    const int t_zero = min(ntiles, ctx / kTile);          // first tile with slots to clear
-    const int j_mask = (pos_min + 1) / (2 * kTile);        // first pair with a key past pos_min
-    const int j_plain = min(j_mask, t_zero / 2);
-    int j = 0;
-    for (; j + 2 < npairs && j + 2 < j_plain; j += 2) {
-        step(kPlain, j, kB, kA, vA, vB);
-        step(kPlain, j + 1, kA, kB, vB, vA);
-    }
-    for (; j + 2 < npairs; j += 2) {
-        step(kSpecial, j, kB, kA, vA, vB);
-        step(kSpecial, j + 1, kA, kB, vB, vA);
-    }
-    if (j + 1 < npairs) {
-        step(kSpecial, j, kB, kA, vA, vB);
-        if (__ballot(grow)) rescale();
-        accumulate(kSpecial, j + 1, S, vB);
-    } else {
-        if (__ballot(grow)) rescale();
-        accumulate(kSpecial, j, S, vA);
-    }
-
-    // normalise and write: lane holds row gq of block b, dims 16*mt + 4*quad .. +3
-#pragma unroll
-    for (int b = 0; b < C; ++b) {
-        const float lw = sum_across_quads(lsum[b]);
-        const float inv = 1.f / lw;
-        bool live;
-        int tok, head;
-        row_info(b, live, tok, head);
-        if (!live) continue;
-        const int64_t ob = ((int64_t)(r0 + tok) * a.num_q_heads + head) * D;
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-            f32x4 v;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) v[r] = bad_block ? NAN : acc[b][mt][r] * inv;
-            store_out4<OUT_DT>(a.out, ob + 16 * mt + 4 * quad, v);
-        }
-    }
-}
-
 // ---------------------------------------------------------------------------------------
-// Block sizes 16 and 32: K/V tiles staged through LDS and shared by the workgroup.
+// K/V tiles staged through LDS and shared by the workgroup.
 //
 // The four waves of a workgroup hold different query rows of one (sequence, KV head)
 // and need the same keys, so each 32-key pair of tiles is fetched once per workgroup:
@@ -607,6 +141,13 @@ void attn_prefill_mfma(PrefillArgs a) {
 //    over eight slots modulo 8.
 // The copies apply these slot maps on the way in (each lane fetches the chunk that
 // belongs in its slot), so the pool layout is unchanged.
+//
+// Column blocks of 16 query rows per wave: as many as fit two waves per SIMD in the
+// registers (3 at head_dim 128: 0-3% faster than 2 at three waves per SIMD; 4 at 64;
+// 2 at 256, 1.8x faster than 1).  Measured on this design with v_mfma_f32_32x32x16
+// instead (one 32-query block per wave, two accumulator chains for the scores): 6-14%
+// slower, although that instruction alone reaches the full matrix rate and the 16x16x32
+// form about three quarters of it.
 template <int D>
 constexpr int lds_blocks() { return D == 64 ? 4 : D == 128 ? 3 : 2; }
 
@@ -618,14 +159,19 @@ void attn_prefill_lds(PrefillArgs a) {
     constexpr int C = lds_blocks<D>();
     constexpr int RW = 16 * C;            // query rows per wave
     constexpr int TILE = BS * D;          // elements of one (block, KV head) region
-    constexpr int TPB = BS / kTile;       // 16-token tiles per block
+    constexpr int TPB = BS >= kTile ? BS / kTile : 1;   // 16-token tiles per block
     constexpr int TE = kTile * D;         // elements of one 16-token tile
     constexpr int PIECES = TE / 512;      // 1 KiB pieces per tile: each wave copies one of each
     constexpr int STAGE = 4 * TE;         // K and V of a pair of tiles
     __shared__ __attribute__((aligned(16))) uint16_t s_kv[2 * STAGE];
     using kvec = typename std::conditional<DT == DT_BF16, bf16x8, f16x8>::type;
 
-    // same (pair, query tile) -> workgroup mapping as the register-streaming kernel
+    // Workgroup b runs on XCD b % X (X = a.xcds, 8 on MI355X).  Pair y = sequence * KV
+    // heads + KV head is given to XCD y % X (so the K/V its query tiles all read stays in
+    // that XCD's L2, and with 8 KV heads on 8 dies every XCD gets one head of every
+    // sequence); on each XCD the workgroups take its pairs in order, each pair's query
+    // tiles last first.  The mapping is a bijection onto (pair, query tile) for any X, so
+    // X only matters for speed.
     const int xcd = blockIdx.x % a.xcds, idx = blockIdx.x / a.xcds;
     const int y = xcd + a.xcds * (idx / a.q_tiles);
     if (y >= a.num_seqs * a.num_kv_heads) return;
@@ -647,7 +193,9 @@ void attn_prefill_lds(PrefillArgs a) {
     const int t_end = min(n, t_begin + a.tokens_per_wg);
     const int valid_rows = (t_end - t_begin) * G;
     const bool bad_len = ctx < 1 || ctx > a.max_context_len || n > ctx;
-    // workgroup-uniform split test (see the register-streaming kernel)
+    // Two launches share the work: SPLIT takes the workgroups whose first query sees fewer
+    // than split_keys keys, the other one the rest (and writes the NaN rows of invalid
+    // sequences).  The test is the same for every wave of a workgroup.
     if constexpr (SPLIT) {
         if (bad_len || ctx - n + t_begin + 1 >= split_keys<DT>()) return;
     } else {
@@ -711,19 +259,30 @@ void attn_prefill_lds(PrefillArgs a) {
     const int64_t blk_stride = (int64_t)a.num_kv_heads * TILE;
     bool bad_block = false;
 
-    // Block ids of pair j's tiles 2j, 2j+1 (past the workgroup's keys: the last tile
-    // again; its scores are masked and its V cleared), read a pair ahead of their use.
+    // Where pair j's tiles 2j, 2j+1 start in either pool (past the workgroup's keys: the
+    // last tile again; its scores are masked and its V cleared), read a pair ahead of
+    // their use.  Block sizes 16 and 32: one offset per tile, from scalar loads.  Block
+    // size 1: every token has its own block, and lane l gets the offsets of token
+    // kt1 = (l % 16) ^ ((l & 8) >> 1) of both tiles (vector loads of the table; tokens at
+    // or past ctx take the block of token ctx - 1), which is the token whose K chunks
+    // and V row the lane copies.
+    const int kt1 = (lane & 15) ^ ((lane & 8) >> 1);
     auto pair_ids = [&](int j, int64_t (&off)[2]) __attribute__((always_inline)) {
+        bool bad = false;
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
             const int it = min(2 * j + h, ntiles - 1);
-            int32_t b = sload(trow, it / TPB);
+            int32_t b;
+            if constexpr (BS == 1) b = trow[min(kTile * it + kt1, ctx - 1)];
+            else b = sload(trow, it / TPB);
             if ((uint32_t)b >= (uint32_t)a.num_blocks) {
-                bad_block = true;
+                bad = true;
                 b = 0;
             }
-            off[h] = b * blk_stride + (it % TPB) * TE;   // the tile's elements in either pool
+            off[h] = b * blk_stride + (BS == 1 ? 0 : (it % TPB) * TE);
         }
+        if constexpr (BS == 1) bad = __ballot(bad) != 0;
+        bad_block |= bad;
     };
     // Stage layout (elements): K tile 0, K tile 1 (TE each, chunks 4p..4p+3 in piece p),
     // then V as MT 1 KiB blocks [tile 0 dims 16mt..16mt+15 | tile 1 same dims], in the
@@ -734,24 +293,62 @@ void attn_prefill_lds(PrefillArgs a) {
     constexpr int NPIECES = KPIECES + MT;
     static_assert(KPIECES % kWaves == 0 && MT % kWaves == 0, "pieces per wave");
     // the pool chunk that belongs in this lane's slot of a K piece / a V block
-    // (both slot maps are their own inverses)
-    const int k_src = ((lane >> 4) * 16 + ((lane & 15) ^ ((lane & 8) >> 1))) * 8;
+    // (both slot maps are their own inverses); block size 1: chunk lane/16 of the
+    // lane's token kt1
+    const int k_src = BS == 1 ? (lane >> 4) * 8 : ((lane >> 4) * 16 + kt1) * 8;
     const int v_dim = (lane & 31) >> 1;
     const int v_src = v_dim * 16 + (((lane & 1) ^ (v_dim >> 2)) & 1) * 8;
+    // Block size 1 stores V token-major, so V^T chunks cannot be copied whole: lane l
+    // loads 16-byte chunks (8 dims) of token kt1 of tile l / 32 into registers and
+    // writes their 8 values to their slots after the pair's products.
+    constexpr int CPT = D / 8;                      // 16-byte chunks of a token's V row
+    constexpr int VPASS = BS == 1 ? CPT / 8 : 1;    // chunks per lane per pair
+    i32x4 vrow[VPASS];
     auto issue = [&](int st, const int64_t (&off)[2]) __attribute__((always_inline)) {
         const uint16_t* k0 = kbase + off[0] + k_src;
         const uint16_t* k1 = kbase + off[1] + k_src;
-        const uint16_t* vsrc = vbase + ((lane >> 5) ? off[1] : off[0]) + v_src;
         uint16_t* dst = s_kv + st * STAGE;
+        if constexpr (BS == 1) {
 #pragma unroll
-        for (int i = 0; i < NPIECES / kWaves; ++i) {
-            const int pc = w + kWaves * i;
-            if (i < KPIECES / kWaves) {
+            for (int i = 0; i < KPIECES / kWaves; ++i) {
+                const int pc = w + kWaves * i;
                 const int h = pc / PIECES, p = pc % PIECES;
-                __builtin_amdgcn_global_load_lds((h ? k1 : k0) + p * 512, dst + h * TE + p * 512, 16, 0, 0);
-            } else {
-                const int mt = pc - KPIECES;
-                __builtin_amdgcn_global_load_lds(vsrc + mt * 256, dst + 2 * TE + mt * 512, 16, 0, 0);
+                __builtin_amdgcn_global_load_lds((h ? k1 : k0) + p * 32, dst + h * TE + p * 512, 16, 0, 0);
+            }
+            const uint16_t* vr = vbase + ((lane >> 5) ? off[1] : off[0]) + ((lane >> 4) & 1) * 8;
+#pragma unroll
+            for (int k = 0; k < VPASS; ++k)
+                vrow[k] = *reinterpret_cast<const i32x4*>(vr + 16 * (k * kWaves + w));
+        } else {
+            const uint16_t* vsrc = vbase + ((lane >> 5) ? off[1] : off[0]) + v_src;
+#pragma unroll
+            for (int i = 0; i < NPIECES / kWaves; ++i) {
+                const int pc = w + kWaves * i;
+                if (i < KPIECES / kWaves) {
+                    const int h = pc / PIECES, p = pc % PIECES;
+                    __builtin_amdgcn_global_load_lds((h ? k1 : k0) + p * 512, dst + h * TE + p * 512, 16, 0, 0);
+                } else {
+                    const int mt = pc - KPIECES;
+                    __builtin_amdgcn_global_load_lds(vsrc + mt * 256, dst + 2 * TE + mt * 512, 16, 0, 0);
+                }
+            }
+        }
+    };
+    // block size 1: chunk c = 2 (k * 4 + w) + (l / 16) % 2 of the lane's V row (dims
+    // 8c .. 8c+7, all in block mt = c / 2) into slot 2 d + (half ^ bit 2 of d), element
+    // kt1 % 8, of tile l / 32 (d = dim % 16, half = kt1 / 8)
+    auto store_v = [&](int st) __attribute__((always_inline)) {
+        if constexpr (BS == 1) {
+            const int half = kt1 >> 3;
+            uint16_t* vb = s_kv + st * STAGE + 2 * TE + (lane >> 5) * 256 + ((lane >> 4) & 1) * 128 + (kt1 & 7);
+#pragma unroll
+            for (int k = 0; k < VPASS; ++k) {
+                uint16_t* vk = vb + (k * kWaves + w) * 512;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const uint32_t x = (uint32_t)vrow[k][e >> 1];
+                    vk[(2 * e + (half ^ (e >> 2))) * 8] = (uint16_t)(e & 1 ? x >> 16 : x);
+                }
             }
         }
     };
@@ -892,6 +489,7 @@ void attn_prefill_lds(PrefillArgs a) {
     int64_t ids_next[2], ids_after[2];
     pair_ids(0, ids_next);
     issue(0, ids_next);
+    store_v(0);
     pair_ids(min(1, npairs - 1), ids_next);
     int j = 0;
     for (; j < j_plain; ++j) {
@@ -900,6 +498,7 @@ void attn_prefill_lds(PrefillArgs a) {
         if (j + 1 < npairs) issue((j + 1) & 1, ids_next);
         pair_ids(min(j + 2, npairs - 1), ids_after);
         compute(kPlain, j, s_kv + (j & 1) * STAGE);
+        if (j + 1 < npairs) store_v((j + 1) & 1);
         ids_next[0] = ids_after[0];
         ids_next[1] = ids_after[1];
     }
@@ -909,6 +508,7 @@ void attn_prefill_lds(PrefillArgs a) {
         if (j + 1 < npairs) issue((j + 1) & 1, ids_next);
         pair_ids(min(j + 2, npairs - 1), ids_after);
         if (j < wave_pairs) compute(kSpecial, j, s_kv + (j & 1) * STAGE);
+        if (j + 1 < npairs) store_v((j + 1) & 1);
         ids_next[0] = ids_after[0];
         ids_next[1] = ids_after[1];
     }
@@ -941,13 +541,8 @@ void launch_t(const PrefillArgs& a, dim3 grid, hipStream_t st) {
     b.q_tiles = std::min(a.q_tiles, (split_keys<DT>() - 1 + a.tokens_per_wg - 1) / a.tokens_per_wg);
     const int64_t pairs = (int64_t)a.num_seqs * a.num_kv_heads;
     const dim3 g2((unsigned)((int64_t)a.xcds * b.q_tiles * ((pairs + a.xcds - 1) / a.xcds)));
-    if constexpr (BS == 1) {
-        attn_prefill_mfma<D, DT, OUT, BS, false><<<grid, dim3(kWaves * 64), 0, st>>>(a);
-        attn_prefill_mfma<D, DT, OUT, BS, true><<<g2, dim3(kWaves * 64), 0, st>>>(b);
-    } else {
-        attn_prefill_lds<D, DT, OUT, BS, false><<<grid, dim3(kWaves * 64), 0, st>>>(a);
-        attn_prefill_lds<D, DT, OUT, BS, true><<<g2, dim3(kWaves * 64), 0, st>>>(b);
-    }
+    attn_prefill_lds<D, DT, OUT, BS, false><<<grid, dim3(kWaves * 64), 0, st>>>(a);
+    attn_prefill_lds<D, DT, OUT, BS, true><<<g2, dim3(kWaves * 64), 0, st>>>(b);
 }
 
 template <int D, int DT, int BS>
@@ -970,13 +565,8 @@ void launch_bs(const PrefillArgs& a, int bs, int dtype, int out_dtype, dim3 grid
 }
 
 // query tokens per workgroup: its 4 waves' rows (16 per column block) over the group
-int tokens_per_workgroup(int head_dim, int group, int block_size) {
-    int blocks;
-    if (block_size == 1)
-        blocks = head_dim == 64 ? prefill_blocks<64>() : head_dim == 256 ? prefill_blocks<256>()
-                                                                        : prefill_blocks<128>();
-    else
-        blocks = head_dim == 64 ? lds_blocks<64>() : head_dim == 256 ? lds_blocks<256>() : lds_blocks<128>();
+int tokens_per_workgroup(int head_dim, int group) {
+    const int blocks = head_dim == 64 ? lds_blocks<64>() : head_dim == 256 ? lds_blocks<256>() : lds_blocks<128>();
     return 4 * 16 * blocks / group;
 }
 
@@ -1060,7 +650,7 @@ paged_kv_status paged_attention_prefill(const paged_kv_pool_desc* desc, void* ou
     a.num_blocks = desc->num_blocks;
     a.max_q_len = max_q_len;
     a.max_context_len = max_context_len;
-    a.tokens_per_wg = tokens_per_workgroup(desc->head_dim, group, desc->block_size);
+    a.tokens_per_wg = tokens_per_workgroup(desc->head_dim, group);
     a.q_tiles = (max_q_len + a.tokens_per_wg - 1) / a.tokens_per_wg;
     a.scale_log2 = scale * kLog2e;
     a.xcds = pkv::device_shape().xcds;
