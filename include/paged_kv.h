@@ -313,6 +313,39 @@ paged_kv_status paged_attention_decode(const paged_kv_pool_desc* desc, void* out
                                        int32_t partition_tokens, void* workspace,
                                        size_t workspace_bytes, void* stream);
 
+/* One decode step of a layer in a single launch where the schedule allows it: the cache
+ * write of reshape_and_cache for one new token per sequence, then paged_attention_decode
+ * over contexts that include that token.  deepsonar "PagedAttention de vLLM …" §2.2
+ * (each new token's K/V lands in its sequence's current block, then the attention reads
+ * the blocks through the table) and §2.6 (graph capture of the decode step: fewer
+ * launches per layer).
+ *   new_k, new_v  device [num_seqs][num_kv_heads][head_dim] of the pool dtype, rows
+ *                 contiguous, 16-byte aligned: the new token of sequence s.
+ *   slot_mapping  device int32 [num_seqs]: the pool slot of that token, which must be
+ *                 the slot of position context_lens[s] - 1 in the sequence's table
+ *                 (the allocator's append returns exactly that); -1 (or any slot
+ *                 outside the pool) writes nothing.
+ *   Every other argument as for paged_attention_decode, context_lens counting the new
+ *   token.  The caller owns all buffers.
+ * With fixed partitions and the matrix-core kernel (fp16/bf16, 2..16 query heads per KV
+ * head) this is one kernel: the workgroup whose partition holds position ctx - 1
+ * writes the token before reading, and the last workgroup of each (sequence, KV head)
+ * to finish merges the partitions in partition order (same arithmetic as the merge
+ * kernel; bit-identical to reshape_and_cache + paged_attention_decode when a sequence
+ * has at most 16 partitions).  Otherwise (stream-K, the vector-ALU kernel) it launches
+ * reshape_and_cache and then paged_attention_decode.  Errors as for
+ * paged_attention_decode, plus PAGED_KV_ERR_INVALID_ARG for null or misaligned
+ * new_k/new_v/slot_mapping; nothing is launched on an error. */
+paged_kv_status paged_attention_decode_append(const paged_kv_pool_desc* desc, void* out,
+                                              int32_t out_dtype, const void* q, const void* new_k,
+                                              const void* new_v, const int32_t* slot_mapping,
+                                              void* k_pool, void* v_pool,
+                                              const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                              const int32_t* context_lens, int32_t num_seqs,
+                                              int32_t num_q_heads, int32_t max_context_len,
+                                              float scale, int32_t partition_tokens, void* workspace,
+                                              size_t workspace_bytes, void* stream);
+
 /* paged_attention_decode for callers that cannot allocate device memory: code under
  * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.  Same
  * arguments, results and errors as paged_attention_decode (bit-identical outputs for

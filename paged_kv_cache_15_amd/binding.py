@@ -89,6 +89,9 @@ _SIGNATURES = {
                                                  _i32, _i32, _i32, _f32, _i32, _vp, _sz, _vp]),
     "paged_attention_decode_static": (ctypes.c_int, [_descp, _vp, _i32, _vp, _vp, _vp, _vp, _i32,
                                                      _vp, _i32, _i32, _i32, _f32, _i32, _vp]),
+    "paged_attention_decode_append": (ctypes.c_int, [_descp, _vp, _i32, _vp, _vp, _vp, _vp, _vp,
+                                                     _vp, _vp, _i32, _vp, _i32, _i32, _i32, _f32,
+                                                     _i32, _vp, _sz, _vp]),
     "paged_attention_reduce": (ctypes.c_int, [_descp, _vp, _i32, _vp, _i32, _i32, _i32, _i32, _vp,
                                               _sz, _vp]),
     "paged_kv_read_bandwidth_probe": (ctypes.c_int, [_vp, _sz, _vp, _vp]),
@@ -457,6 +460,32 @@ def paged_attention_decode_static(desc, out, out_dtype, q, k_pool, v_pool, block
     # the same arguments minus (workspace, workspace_bytes)
     _check("paged_attention_decode_static",
            lib.paged_attention_decode_static(*args[:14], args[16]))
+
+
+def paged_attention_decode_append(desc, out, out_dtype, q, new_k, new_v, slot_mapping, k_pool,
+                                  v_pool, block_tables, context_lens, num_q_heads,
+                                  max_context_len, scale, partition_tokens=0, workspace=None,
+                                  stream=None):
+    """One decode step of a layer: the cache write of the new token of every sequence
+    (new_k/new_v [B][Hkv][d] in the pool dtype, slot_mapping int32 [B]) and the
+    attention over contexts that include it."""
+    f = "paged_attention_decode_append"
+    args = _attn_args(f, desc, out, out_dtype, q, k_pool, v_pool, block_tables, context_lens,
+                      num_q_heads, max_context_len, scale, partition_tokens, workspace, stream)
+    n = int(context_lens.shape[0])
+    for name, t in (("new_k", new_k), ("new_v", new_v)):
+        if _is_tensor(t):
+            _check_tensor(f, name, t)
+            _expect(f, tuple(t.shape) == (n, desc.num_kv_heads, desc.head_dim),
+                    f"{name} must be [{n}][{desc.num_kv_heads}][{desc.head_dim}] (got {tuple(t.shape)})")
+            _expect(f, t.element_size() == _ELEM_BYTES.get(desc.dtype),
+                    f"{name} element size does not match the pool")
+    if _is_tensor(slot_mapping):
+        _check_tensor(f, "slot_mapping", slot_mapping, int32=True)
+        _expect(f, slot_mapping.numel() >= n, "slot_mapping shorter than the batch")
+    # (desc, out, out_dtype, q) + (new_k, new_v, slots) + (k_pool, v_pool, tables, ...)
+    _check(f, lib.paged_attention_decode_append(*args[:4], _ptr(new_k), _ptr(new_v),
+                                                _ptr(slot_mapping), *args[4:]))
 
 
 def paged_attention_partition(desc, out, out_dtype, q, k_pool, v_pool, block_tables, context_lens,

@@ -63,7 +63,28 @@ struct PartitionArgs {
     int32_t partition_tokens;
     int32_t max_parts;
     float scale_log2;  // scale * log2(e)
+    // Fused decode step (paged_attention_decode_append, MFMA kernel only): the new token
+    // of sequence s (rows new_k/new_v [num_seqs][num_kv_heads][head_dim]) is written to
+    // pool slot slots[s] by the workgroup that later reads it, and the workgroup that
+    // finishes a (sequence, KV head) last merges its partitions (counters: one int32 per
+    // (sequence, KV head), zero on entry and left zero).
+    const void* new_k;
+    const void* new_v;
+    const int32_t* slots;
+    int32_t* counters;
+    int64_t num_slots;
 };
+
+// One step of the partitions' log-sum-exp merge: state (M, l, acc) takes in a
+// partition's (m_i, l_i, acc_i).  Written with explicit fused multiply-adds so that
+// every kernel that merges (the merge kernel, the fused decode step) rounds alike.
+__device__ __forceinline__ void lse_fold(float& M, float& l, float& acc, float mi, float li, float ai) {
+    const float mn = fmaxf(M, mi);
+    const float sc = exp2_fast(M - mn), w = exp2_fast(mi - mn);
+    l = fmaf(w, li, l * sc);
+    acc = fmaf(w, ai, acc * sc);
+    M = mn;
+}
 
 // Final write of a workgroup's merged state for query head h (index into the group gq):
 // normalised output for a one-partition sequence, raw state for the merge otherwise.
@@ -99,9 +120,44 @@ __device__ __forceinline__ void write_partition_result(const PartitionArgs& a, i
 // and token quad l / 16, which is exactly the layout the score tile comes out in and
 // the layout the value product wants its B operand in, so P never leaves registers.
 // ---------------------------------------------------------------------------------
-template <int D, int DT, int OUT_DT, int BS>
-__global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(mfma_waves_per_simd<D, false>())))
+// Fused decode step: the new token's K/V row of (sequence s, KV head g) into its pool
+// slot, in the layout reshape_and_cache writes (threads 0 .. D/X - 1, one 16-byte chunk
+// each); a slot outside [0, num_slots) is skipped.
+template <int D, int BS>
+__device__ __forceinline__ void write_new_token(const PartitionArgs& a, int s, int g) {
+    constexpr int X = 8;                      // 16-bit elements per 16-byte chunk
+    constexpr int TB = BS < kTile ? BS : kTile;
+    const int c = threadIdx.x;
+    if (c >= D / X) return;
+    const int32_t slot = a.slots[s];
+    if (slot < 0 || (int64_t)slot >= a.num_slots) return;
+    const int64_t row = ((int64_t)s * a.num_kv_heads + g) * D + c * X;
+    const i32x4 kc = *reinterpret_cast<const i32x4*>(static_cast<const uint16_t*>(a.new_k) + row);
+    const i32x4 vc = *reinterpret_cast<const i32x4*>(static_cast<const uint16_t*>(a.new_v) + row);
+    const int64_t blk = slot / BS;
+    const int32_t sub = (slot % BS) / TB, off = slot % TB;
+    const int64_t region = (blk * a.num_kv_heads + g) * (BS / TB) + sub;
+    uint16_t* kdst = static_cast<uint16_t*>(const_cast<void*>(a.k_pool)) + ((region * (D / X) + c) * TB + off) * X;
+    *reinterpret_cast<i32x4*>(kdst) = kc;
+    uint16_t* vdst = static_cast<uint16_t*>(const_cast<void*>(a.v_pool)) + (region * D + (int64_t)c * X) * TB + off;
+    if constexpr (BS == 1) {
+        *reinterpret_cast<i32x4*>(vdst) = vc;
+    } else {
+#pragma unroll
+        for (int e = 0; e < X; ++e) vdst[e * TB] = (uint16_t)((uint32_t)vc[e / 2] >> (16 * (e % 2)));
+    }
+}
+
+// Waves per workgroup (the fused decode step measured slower with 8: the per-workgroup
+// fixed costs grow, and the tile chain does not shrink in proportion).
+template <bool FUSE, int D>
+constexpr int mfma_partition_waves() { return kWaves; }
+
+template <int D, int DT, int OUT_DT, int BS, bool FUSE>
+__global__ __launch_bounds__((mfma_partition_waves<FUSE, D>() * 64))
+__attribute__((amdgpu_waves_per_eu(mfma_waves_per_simd<D, false>())))
 void attn_mfma_kernel(PartitionArgs a) {
+    constexpr int NW = mfma_partition_waves<FUSE, D>();
     constexpr int KI = D / 32;   // QK MFMAs (and 16-byte K loads per lane) per tile
     constexpr int MT = D / 16;   // PV MFMA pairs (and 8-byte V loads per lane) per tile
     constexpr int TILE = BS * D;  // elements of one (block, KV head) region
@@ -109,7 +165,7 @@ void attn_mfma_kernel(PartitionArgs a) {
     constexpr int LDW = D + 8;    // block size 1: LDS row of one token's values
     using kvec = typename std::conditional<DT == DT_BF16, bf16x8, f16x8>::type;
     using vbuf = typename std::conditional<BS == 1, i32x4[KI], i32x2[MT]>::type;
-    __shared__ uint16_t s_vt[BS == 1 ? kWaves * kTile * LDW : 1];
+    __shared__ uint16_t s_vt[BS == 1 ? NW * kTile * LDW : 1];
 
     const int s = blockIdx.x / a.num_kv_heads, g = blockIdx.x - s * a.num_kv_heads;
     const int p = blockIdx.y;
@@ -119,6 +175,11 @@ void attn_mfma_kernel(PartitionArgs a) {
     const int ctx = a.context_lens[s];
     const bool bad_len = ctx < 1 || ctx > a.max_context_len;
     const int start = p * a.partition_tokens;
+    const int npart = bad_len ? 1 : (ctx + a.partition_tokens - 1) / a.partition_tokens;
+    if (FUSE && bad_len) {
+        // nothing reads this sequence's blocks: the write only has to happen
+        if (p == 0) write_new_token<D, BS>(a, s, g);
+    }
     if (bad_len) {
         if (p == 0) {
             for (int i = threadIdx.x; i < a.group * D; i += blockDim.x)
@@ -128,7 +189,6 @@ void attn_mfma_kernel(PartitionArgs a) {
     }
     if (start >= ctx) return;
     const int end = min(start + a.partition_tokens, ctx);
-    const int npart = (ctx + a.partition_tokens - 1) / a.partition_tokens;
     const int blk_begin = start / kTile, blk_end = (end + kTile - 1) / kTile;   // tiles
     const int32_t* trow = a.block_tables + (int64_t)s * a.max_blocks_per_seq;
 
@@ -279,13 +339,28 @@ void attn_mfma_kernel(PartitionArgs a) {
     // through the loop issues the same loads, so the compiler waits for exactly the
     // current block's loads and never drains the prefetch.
     const int nblk = blk_end - blk_begin;
-    const int n_w = nblk > w ? (nblk - w + kWaves - 1) / kWaves : 0;
+    const int n_w = nblk > w ? (nblk - w + NW - 1) / NW : 0;
+    // the first window's block ids are read before the fused write, so that both wait
+    // out the same memory round trips
+    int32_t id_first = 0;
+    if constexpr (BS != 1)
+        if (lane < min(64, n_w)) id_first = trow[(blk_begin + w + NW * lane) / TPB];
+    if constexpr (FUSE) {
+        // The new token (position ctx - 1) lies in the last partition: that workgroup
+        // writes it before any of its waves loads a tile, and its own loads then see it
+        // (the stores are complete, and L1 holds nothing of that block yet).
+        if (p == npart - 1) {
+            write_new_token<D, BS>(a, s, g);
+            wait_memory_done();
+            __syncthreads();
+        }
+    }
     for (int base = 0; base < n_w; base += 64) {
         const int cnt = min(64, n_w - base);
-        const int b0 = blk_begin + w + kWaves * base;
+        const int b0 = blk_begin + w + NW * base;
         if constexpr (BS != 1) {
-            id_v = 0;
-            if (lane < cnt) id_v = trow[(b0 + kWaves * lane) / TPB];
+            id_v = base == 0 ? id_first : 0;
+            if (base > 0 && lane < cnt) id_v = trow[(b0 + NW * lane) / TPB];
             const bool id_ok = (uint32_t)id_v < (uint32_t)a.num_blocks;
             if (__ballot(lane < cnt && !id_ok)) bad_block = true;
             id_v = id_ok ? id_v : 0;
@@ -293,23 +368,23 @@ void attn_mfma_kernel(PartitionArgs a) {
         load(0, b0, kA, vA);
         int i = 0;
         for (; i + 2 < cnt; i += 2) {
-            load(i + 1, b0 + kWaves * (i + 1), kB, vB);
-            compute(b0 + kWaves * i, kA, vA);
-            load(i + 2, b0 + kWaves * (i + 2), kA, vA);
-            compute(b0 + kWaves * (i + 1), kB, vB);
+            load(i + 1, b0 + NW * (i + 1), kB, vB);
+            compute(b0 + NW * i, kA, vA);
+            load(i + 2, b0 + NW * (i + 2), kA, vA);
+            compute(b0 + NW * (i + 1), kB, vB);
         }
         if (i + 1 < cnt) {
-            load(i + 1, b0 + kWaves * (i + 1), kB, vB);
-            compute(b0 + kWaves * i, kA, vA);
-            compute(b0 + kWaves * (i + 1), kB, vB);
+            load(i + 1, b0 + NW * (i + 1), kB, vB);
+            compute(b0 + NW * i, kA, vA);
+            compute(b0 + NW * (i + 1), kB, vB);
         } else {
-            compute(b0 + kWaves * i, kA, vA);
+            compute(b0 + NW * i, kA, vA);
         }
     }
 
     // ---- merge the four waves' states (fixed order) ----
-    __shared__ float sm_m[kWaves][16];
-    __shared__ float sm_l[kWaves][16];
+    __shared__ float sm_m[NW][16];
+    __shared__ float sm_l[NW][16];
     __shared__ float sm_acc[16][D + 4];
     const float lw = sum_across_quads(lsum);
     if (lane < 16) {
@@ -319,9 +394,9 @@ void attn_mfma_kernel(PartitionArgs a) {
     const bool any_bad = __syncthreads_or(bad_block);
     float mmax = kNegInf;
 #pragma unroll
-    for (int ww = 0; ww < kWaves; ++ww) mmax = fmaxf(mmax, sm_m[ww][gq]);
+    for (int ww = 0; ww < NW; ++ww) mmax = fmaxf(mmax, sm_m[ww][gq]);
     const float f = (m == kNegInf) ? 0.f : exp2_fast(m - mmax);
-    for (int ww = 0; ww < kWaves; ++ww) {
+    for (int ww = 0; ww < NW; ++ww) {
         if (ww == w && gq < a.group) {
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt) {
@@ -340,13 +415,90 @@ void attn_mfma_kernel(PartitionArgs a) {
         const int hg = i / D, d = i - hg * D;
         float mm = kNegInf;
 #pragma unroll
-        for (int ww = 0; ww < kWaves; ++ww) mm = fmaxf(mm, sm_m[ww][hg]);
+        for (int ww = 0; ww < NW; ++ww) mm = fmaxf(mm, sm_m[ww][hg]);
         float l = 0.f;
 #pragma unroll
-        for (int ww = 0; ww < kWaves; ++ww)
+        for (int ww = 0; ww < NW; ++ww)
             if (sm_m[ww][hg] != kNegInf) l += exp2_fast(sm_m[ww][hg] - mm) * sm_l[ww][hg];
-        write_partition_result<D, OUT_DT>(a, s, g * a.group + hg, p, npart, d, mm, l,
-                                          sm_acc[hg][d], any_bad);
+        if (FUSE && npart > 1) {
+            // partial state for the merge below, possibly read on another XCD: stored
+            // through to the device-coherent level
+            const int64_t row = ((int64_t)s * a.num_q_heads + g * a.group + hg) * a.max_parts + p;
+            put_coherent(a.ws_acc + row * D + d, any_bad ? NAN : sm_acc[hg][d]);
+            if (d == 0) {
+                put_coherent(a.ws_m + row, any_bad ? NAN : mm);
+                put_coherent(a.ws_l + row, any_bad ? NAN : l);
+            }
+        } else {
+            write_partition_result<D, OUT_DT>(a, s, g * a.group + hg, p, npart, d, mm, l,
+                                              sm_acc[hg][d], any_bad);
+        }
+    }
+    if constexpr (FUSE) {
+        if (npart > 1) {
+            // Count this partition in (s, g)'s counter once its state is stored; the
+            // workgroup that brings the count to npart merges all partitions in order
+            // (as the merge kernel does with one thread group) and resets the counter.
+            // Ordering as in the stream-K merge: sc1 stores complete before the
+            // agent-scope count, sc1 loads after it, and a compiler fence between.
+            __shared__ int s_old;
+            wait_memory_done();
+            __syncthreads();
+            if (threadIdx.x == 0)
+                s_old = __hip_atomic_fetch_add(a.counters + (int64_t)s * a.num_kv_heads + g, 1,
+                                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __syncthreads();
+            if (s_old != npart - 1) return;
+            __atomic_signal_fence(__ATOMIC_ACQUIRE);
+            // NO outputs per thread at a time, eight partitions per memory round trip
+            // (all their loads in flight together), folded in partition order.
+            constexpr int NO = 4;
+            for (int i0 = threadIdx.x; i0 < a.group * D; i0 += NO * blockDim.x) {
+                float M[NO], l[NO], acc[NO];
+                bool bad[NO];
+                int64_t row[NO];
+                int dd[NO];
+#pragma unroll
+                for (int o = 0; o < NO; ++o) {
+                    M[o] = kNegInf;
+                    l[o] = acc[o] = 0.f;
+                    bad[o] = false;
+                    const int i = min(i0 + o * (int)blockDim.x, a.group * D - 1);
+                    dd[o] = i % D;
+                    row[o] = ((int64_t)s * a.num_q_heads + g * a.group + i / D) * a.max_parts;
+                }
+                for (int p0 = 0; p0 < npart; p0 += 8) {
+                    float mv[NO][8], lv[NO][8], av[NO][8];
+#pragma unroll
+                    for (int o = 0; o < NO; ++o)
+#pragma unroll
+                        for (int k = 0; k < 8; ++k) {   // past the last partition: re-read it
+                            const int64_t r = row[o] + min(p0 + k, npart - 1);
+                            mv[o][k] = get_coherent(a.ws_m + r);
+                            lv[o][k] = get_coherent(a.ws_l + r);
+                            av[o][k] = get_coherent(a.ws_acc + r * D + dd[o]);
+                        }
+#pragma unroll
+                    for (int o = 0; o < NO; ++o)
+#pragma unroll
+                        for (int k = 0; k < 8; ++k) {
+                            if (p0 + k >= npart) break;
+                            bad[o] |= mv[o][k] != mv[o][k];
+                            lse_fold(M[o], l[o], acc[o], mv[o][k], lv[o][k], av[o][k]);
+                        }
+                }
+#pragma unroll
+                for (int o = 0; o < NO; ++o) {
+                    const int i = i0 + o * (int)blockDim.x;
+                    if (i < a.group * D)
+                        store_out<OUT_DT>(a.out, ((int64_t)s * a.num_q_heads + g * a.group + i / D) * D + i % D,
+                                          bad[o] ? NAN : acc[o] / l[o]);
+                }
+            }
+            if (threadIdx.x == 0)
+                __hip_atomic_store(a.counters + (int64_t)s * a.num_kv_heads + g, 0, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+        }
     }
 }
 
@@ -632,11 +784,7 @@ __global__ __launch_bounds__(D * reduce_groups_max<D>()) void attn_reduce_kernel
         for (int k = 0; k < 8; ++k) {
             if (i0 + k >= i_hi) break;
             bad |= mv[k] != mv[k];
-            const float mn = fmaxf(M, mv[k]);
-            const float sc = exp2_fast(M - mn), w = exp2_fast(mv[k] - mn);
-            l = l * sc + w * lv[k];
-            acc = acc * sc + w * av[k];
-            M = mn;
+            lse_fold(M, l, acc, mv[k], lv[k], av[k]);
         }
     }
     if (R > 1) {
@@ -649,13 +797,8 @@ __global__ __launch_bounds__(D * reduce_groups_max<D>()) void attn_reduce_kernel
         __syncthreads();
         if (g != 0) return;
         for (int gg = 1; gg < R; ++gg) {   // group 0 has partitions, so M is finite here
-            const float mg = s_ml[gg][0];
             bad |= s_bad[gg] != 0;
-            const float mn = fmaxf(M, mg);
-            const float sc = exp2_fast(M - mn), w = exp2_fast(mg - mn);   // empty group: w = 0
-            l = l * sc + w * s_ml[gg][1];
-            acc = acc * sc + w * s_acc[gg][d];
-            M = mn;
+            lse_fold(M, l, acc, s_ml[gg][0], s_ml[gg][1], s_acc[gg][d]);   // empty group: weight 0
         }
     }
     store_out<OUT_DT>(out, o, bad ? NAN : acc / l);
@@ -685,6 +828,7 @@ struct Plan {
     int dtype, out_dtype, head_dim, block_size;
     bool mfma;
     bool streamk;              // stream-K schedule (partition_tokens 0) or fixed partitions
+    bool fuse = false;         // fused decode step: cache write + attention + merge in one launch
     pkv::StreamPlan sp;
     pkv::StreamLaunch sl;
     dim3 grid;
@@ -850,6 +994,10 @@ paged_kv_status make_plan(Plan& pl, const paged_kv_pool_desc* desc, void* out, i
     a.partition_tokens = part_tokens;
     a.max_parts = max_parts;
     a.scale_log2 = scale * kLog2e;
+    a.new_k = a.new_v = nullptr;
+    a.slots = nullptr;
+    a.counters = counters;
+    a.num_slots = (int64_t)desc->num_blocks * desc->block_size;
     pl.dtype = desc->dtype;
     pl.out_dtype = out_dtype;
     pl.head_dim = desc->head_dim;
@@ -872,7 +1020,11 @@ void launch_partition_t(const Plan& pl) {
     if constexpr (DT == DT_F32) {
         attn_valu_kernel<D, DT, OUT, BS><<<pl.grid, dim3(kWaves * 64), 0, pl.stream>>>(pl.a);
     } else {
-        if (pl.mfma) attn_mfma_kernel<D, DT, OUT, BS><<<pl.grid, dim3(kWaves * 64), 0, pl.stream>>>(pl.a);
+        if (pl.mfma && pl.fuse)
+            attn_mfma_kernel<D, DT, OUT, BS, true><<<pl.grid, dim3(mfma_partition_waves<true, D>() * 64), 0,
+                                                     pl.stream>>>(pl.a);
+        else if (pl.mfma)
+            attn_mfma_kernel<D, DT, OUT, BS, false><<<pl.grid, dim3(kWaves * 64), 0, pl.stream>>>(pl.a);
         else attn_valu_kernel<D, DT, OUT, BS><<<pl.grid, dim3(kWaves * 64), 0, pl.stream>>>(pl.a);
     }
 }
@@ -1071,6 +1223,50 @@ paged_kv_status paged_attention_decode(const paged_kv_pool_desc* desc, void* out
     return paged_attention_reduce(desc, out, out_dtype, context_lens, num_seqs, num_q_heads,
                                   max_context_len, partition_tokens, workspace, workspace_bytes,
                                   stream);
+}
+
+paged_kv_status paged_attention_decode_append(const paged_kv_pool_desc* desc, void* out,
+                                              int32_t out_dtype, const void* q, const void* new_k,
+                                              const void* new_v, const int32_t* slot_mapping,
+                                              void* k_pool, void* v_pool,
+                                              const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                              const int32_t* context_lens, int32_t num_seqs,
+                                              int32_t num_q_heads, int32_t max_context_len,
+                                              float scale, int32_t partition_tokens, void* workspace,
+                                              size_t workspace_bytes, void* stream) {
+    pkv::clear_error();
+    Plan pl;
+    paged_kv_status st = make_plan(pl, desc, out, out_dtype, q, k_pool, v_pool, block_tables,
+                                   max_blocks_per_seq, context_lens, num_seqs, num_q_heads,
+                                   max_context_len, scale, partition_tokens,
+                                   WsSource{static_cast<char*>(workspace), workspace_bytes, nullptr},
+                                   stream, true);
+    if (st != PAGED_KV_OK || num_seqs == 0) return st;
+    if (!new_k || !new_v || !slot_mapping) {
+        pkv::set_error("null pointer argument");
+        return PAGED_KV_ERR_INVALID_ARG;
+    }
+    if ((reinterpret_cast<uintptr_t>(new_k) | reinterpret_cast<uintptr_t>(new_v)) & 15) {
+        pkv::set_error("new_k and new_v must be 16-byte aligned");
+        return PAGED_KV_ERR_INVALID_ARG;
+    }
+    if (pl.streamk || !pl.mfma) {
+        // schedules without a fused kernel: the cache write, then the attention
+        const int64_t row = (int64_t)desc->num_kv_heads * desc->head_dim;
+        st = reshape_and_cache(desc, new_k, new_v, row, row, k_pool, v_pool, slot_mapping, num_seqs, stream);
+        if (st != PAGED_KV_OK) return st;
+        launch_partition(pl, stream);
+        st = launch_status("paged attention partition kernel");
+        if (st != PAGED_KV_OK) return st;
+        launch_reduce(pl, num_seqs);
+        return launch_status("paged attention reduce kernel");
+    }
+    pl.fuse = true;
+    pl.a.new_k = new_k;
+    pl.a.new_v = new_v;
+    pl.a.slots = slot_mapping;
+    launch_partition(pl, stream);
+    return launch_status("fused paged decode step kernel");
 }
 
 paged_kv_status paged_attention_decode_static(const paged_kv_pool_desc* desc, void* out,

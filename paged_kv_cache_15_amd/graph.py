@@ -7,7 +7,9 @@ allocator: a block id names the same slot range in every layer's K/V buffers, so
 slot mapping and block tables of a step are computed once on the host (the allocator
 is host code and stays out of the graph) and copied into the graph's fixed device
 buffers before each replay.  The graph holds only kernel launches from libpagedkv.so
-(no memset or copy nodes): 2 x layers launches per replay.
+(no memset or copy nodes): per layer one fused launch (cache write, attention and
+merge: paged_attention_decode_append) where the schedule has one, else the cache write
+and the attention's launches.
 
 Copy-on-write copies, when an append makes any, are issued eagerly for every layer
 before the replay.
@@ -68,8 +70,9 @@ class DecodeStep:
     paged_attention_decode; by default the library picks the schedule for the shape."""
 
     def __init__(self, kv: LayeredKV, num_seqs, num_q_heads, max_blocks, max_context_len, scale,
-                 partition_tokens=B.PARTITION_AUTO, out_dtype=None):
+                 partition_tokens=B.PARTITION_AUTO, out_dtype=None, fused=True):
         self.kv = kv
+        self.fused = fused
         self.B, self.hq = num_seqs, num_q_heads
         self.max_blocks, self.max_ctx = max_blocks, max_context_len
         self.scale, self.pt = float(scale), partition_tokens
@@ -114,6 +117,12 @@ class DecodeStep:
         """All layers' kernels on the current stream."""
         kv = self.kv
         for l in range(kv.num_layers):
+            if self.fused:
+                B.paged_attention_decode_append(kv.desc, self.out[l], self.out_dtype, self.q[l],
+                                                self.new_k[l], self.new_v[l], self.slots, kv.k[l],
+                                                kv.v[l], self.tables, self.lens, self.hq,
+                                                self.max_ctx, self.scale, self.pt, self.ws)
+                continue
             B.reshape_and_cache(kv.desc, self.new_k[l], self.new_v[l], kv.k[l], kv.v[l], self.slots)
             B.paged_attention_decode(kv.desc, self.out[l], self.out_dtype, self.q[l], kv.k[l],
                                      kv.v[l], self.tables, self.lens, self.hq, self.max_ctx,

@@ -1,6 +1,7 @@
 """Graph-captured multi-layer decode step (GPU): every replay matches the eager step bit
-for bit, with the host's own work and synchronisations between replays, and one
-layer's attention matches the oracle."""
+for bit, with the host's own work and synchronisations between replays, the fused step
+(cache write, attention and merge in one launch) matches the separate launches bit for
+bit, and one layer's attention matches the oracle."""
 import numpy as np
 import pytest
 import torch
@@ -16,8 +17,11 @@ def _bits(x, dt):
     return lowp.storage_bits_to_f64(lowp.to_storage_bits(x, dt), dt)
 
 
-@pytest.mark.parametrize("pt", [0, 512, -1], ids=["streamk", "pt512", "auto"])
-def test_decode_step_graph_matches_eager_bitwise(pt):
+@pytest.mark.parametrize("pt,fused", [(0, True), (512, True), (-1, True), (512, False), (256, "mixed"),
+                                      (64, "mixed")],
+                         ids=["streamk", "pt512", "auto", "pt512-unfused", "pt256-fused-vs-unfused",
+                              "pt64-fused-vs-unfused"])
+def test_decode_step_graph_matches_eager_bitwise(pt, fused):
     from paged_kv_cache_15_amd.graph import LayeredKV, DecodeStep
     from paged_kv_cache_15_amd.replay import to_device
     L, hq, hkv, d, dt = 4, 32, 8, 128, "bf16"
@@ -34,8 +38,10 @@ def test_decode_step_graph_matches_eager_bitwise(pt):
         vals = [to_device(np.concatenate([r[1] for r in rows[l]]), dt, "cuda") for l in range(L)]
         kv.append(ss, lens0, keys, vals)
     max_ctx = max(lens0) + nsteps
-    steps = [DecodeStep(kv, len(lens0), hq, (max_ctx + 15) // 16, max_ctx, 1 / np.sqrt(d), pt, "f32")
-             for kv in kvs]
+    # "mixed": the graph of fused launches against eager separate launches
+    steps = [DecodeStep(kv, len(lens0), hq, (max_ctx + 15) // 16, max_ctx, 1 / np.sqrt(d), pt, "f32",
+                        fused=(fused if fused != "mixed" else i == 0))
+             for i, kv in enumerate(kvs)]
     history = [[list(r) for r in rows[l]] for l in range(L)]     # per layer, per seq: [k, v]
     for step in range(nsteps):
         nk = rng.standard_normal((L, len(lens0), hkv, d)).astype(np.float32)
@@ -52,7 +58,7 @@ def test_decode_step_graph_matches_eager_bitwise(pt):
             else:
                 st.launch()
         torch.cuda.synchronize()
-        say(f"[graph] step {step} partition_tokens={pt}")
+        say(f"[graph] step {step} partition_tokens={pt} fused={fused}")
         assert torch.equal(steps[0].out, steps[1].out), step
         for l in range(L):
             for s in range(len(lens0)):
