@@ -434,7 +434,9 @@ size_t paged_attention_shared_prefix_workspace_bytes(const paged_kv_pool_desc* d
  *                  holds at least that many tokens
  *   max_group, max_shared_tokens  host bounds on members per group and on shared_tokens
  *   partition_tokens  tokens per partition of the shared part and of each tail (a
- *                  multiple of 16; 0: 512)
+ *                  multiple of 16; 0: chosen from the shape, the largest of 4096 (or the
+ *                  longest context rounded up to 512), 2048, 1024 and 512 that leaves
+ *                  about four workgroups per compute unit)
  *   workspace      device buffer of paged_attention_shared_prefix_workspace_bytes(...)
  *                  bytes (scratch; needs no zero-fill)
  * Other arguments as for paged_attention_decode.  A sequence for which the group

@@ -12,13 +12,16 @@
 // query head, the prefix partitions with the tail partitions by log-sum-exp.  What is
 // computed is unchanged: softmax attention over the whole context of each sequence.
 //
-// Work items, one per wave (four per workgroup, no cross-wave merge):
+// Work items, one per workgroup (its four waves take the item's tiles in turn and merge
+// their states in LDS):
 //   prefix item (group, KV head, partition p of the shared tokens): tokens
 //     [p PT, min((p + 1) PT, shared)), read through the table of the group's first
 //     member; the other members' table entries for those tokens are checked equal (a
 //     mismatch makes the group's results NaN);
 //   tail item (sequence, KV head, partition p of its own tokens): tokens
-//     [shared + p PT, min(shared + (p + 1) PT, ctx)).
+//     [max(shared, j PT), min((j + 1) PT, ctx)) with j = floor(shared / PT) + p; the
+//     sequence's first tail item also writes what the merge needs to know of it (its
+//     number of partition states, or 0 where the group description does not hold).
 // Each item writes the raw (max, sum, weighted values) state of every query head it
 // serves into the workspace row (sequence, query head, partition index), where prefix
 // partitions come first and tail partitions follow; the merge folds them in order.
@@ -42,13 +45,13 @@ struct SharedArgs {
     const int32_t* context_lens;
     const int32_t* group_start;     // [num_groups + 1]
     const int32_t* shared_tokens;   // [num_groups]
+    i32x4* seq_desc;                // [num_seqs]: what the merge needs to know of each sequence
     float* ws_m;
     float* ws_l;
     float* ws_acc;
     int32_t num_seqs;
     int32_t num_groups;
     int32_t max_group;              // host bound on members per group
-    int32_t parts_per_item;         // consecutive tail partitions one tail item streams
     int32_t members_per_item;       // members one prefix item serves (16 NB / G)
     int32_t chunks;                 // prefix items per (group, KV head, partition)
     int32_t max_blocks_per_seq;
@@ -64,7 +67,7 @@ struct SharedArgs {
     int32_t tail_parts;             // partitions of the longest tail (host bound)
     int32_t max_parts;              // workspace rows per (sequence, query head)
     int64_t prefix_items;           // num_groups * Hkv * prefix_parts
-    int64_t items;                  // prefix_items + num_seqs * Hkv * ceil(tail_parts / k)
+    int64_t items;                  // prefix_items + num_seqs * Hkv * tail_parts
     float scale_log2;
 };
 
@@ -85,8 +88,9 @@ __device__ __forceinline__ int group_of(const SharedArgs& a, int s) {
     return cnt;
 }
 
-// One wave per item.  NB N-blocks of 16 query slots (slot n = member * G + head of the
-// KV head's group for a prefix item; n = head for a tail item, which uses N-block 0 only).
+// One workgroup per item; wave w takes the item's tiles w, w + 4, w + 8, ...  NB N-blocks
+// of 16 query slots (slot n = member * G + head of the KV head's group for a prefix item;
+// n = head for a tail item, which uses N-block 0 only).
 template <int D, int DT, int BS, int NB>
 __global__ __launch_bounds__(kWaves * 64)
 __attribute__((amdgpu_waves_per_eu(NB == 1 ? mfma_waves_per_simd<D, false>() : NB * D <= 256 ? 2 : 1)))
@@ -99,7 +103,10 @@ void attn_mfma_shared(SharedArgs a) {
     static_assert(BS >= kTile, "16- and 32-token blocks only");
 
     const int lane = threadIdx.x & 63;
-    const int64_t item = (int64_t)blockIdx.x * kWaves + uni(threadIdx.x >> 6);
+    const int w = uni(threadIdx.x >> 6);
+    const int64_t item = blockIdx.x;
+    // (every return before the merge below depends on the item alone: the whole
+    // workgroup takes it)
     if (item >= a.items) return;
     const int gq = lane & 15, quad = lane >> 4;
     const int G = a.group;
@@ -107,7 +114,6 @@ void attn_mfma_shared(SharedArgs a) {
     // ---- decode the item ----
     bool prefix;
     int s0, members, h, p, start, end, part_index;
-    int jb;         // absolute partition (token / PT) of the item's first tile
     bool bad = false;
     int lead = 0;   // batch row whose table the item reads through
     if (item < a.prefix_items) {
@@ -135,13 +141,11 @@ void attn_mfma_shared(SharedArgs a) {
         members = min(a.members_per_item, min(gsize, a.max_group) - c * a.members_per_item);
         if (members < 1) return;
         part_index = p;
-        jb = p;
     } else {
-        // Tail items chunk-major: every sequence's first chunk comes first, and the
-        // (mostly empty) later ones follow together at the end of the grid.  Tail
+        // Tail items partition-major: every sequence's first tail partition comes first,
+        // and the (mostly empty) later ones follow together at the end of the grid.  Tail
         // partitions sit at absolute multiples of PT ([max(shared, j PT), (j + 1) PT) for
-        // j >= shared / PT), so a tile never straddles two of them; chunk p streams
-        // parts_per_item of them back to back and writes each one's state.
+        // j >= shared / PT), so a tile never straddles two of them.
         prefix = false;
         const int64_t t = item - a.prefix_items;
         const int64_t per_part = (int64_t)a.num_seqs * a.num_kv_heads;
@@ -150,16 +154,33 @@ void attn_mfma_shared(SharedArgs a) {
         s0 = r / a.num_kv_heads;
         h = r - s0 * a.num_kv_heads;
         members = 1;
-        const int shared = sload(a.shared_tokens, group_of(a, s0));
+        const int g = group_of(a, s0);
+        const int shared = sload(a.shared_tokens, g);
         const int ctx = sload(a.context_lens, s0);
-        // invalid lengths are handled by the merge (NaN rows); nothing to read here
+        const int PT = a.partition_tokens;
+        if (h == 0 && p == 0) {
+            // The sequence's descriptor for the merge: its number of partition states,
+            // its group's first row and the blocks the shared tokens span (whose ids its
+            // table must repeat), or 0 states if the group description does not hold for
+            // it (the merge then writes NaN).
+            const int gs = sload(a.group_start, g), ge = sload(a.group_start, g + 1);
+            const bool valid = ctx >= 1 && ctx <= a.max_context_len && shared >= 0 &&
+                               shared <= ctx && shared <= a.max_shared && gs >= 0 &&
+                               ge <= a.num_seqs && s0 >= gs && s0 < ge && s0 - gs < a.max_group;
+            if (threadIdx.x == 0) {
+                const int np = (shared + PT - 1) / PT +
+                               (ctx > shared ? (ctx + PT - 1) / PT - shared / PT : 0);
+                a.seq_desc[s0] = valid ? (i32x4){np, gs, (shared + a.block_size - 1) / a.block_size, 0}
+                                       : (i32x4){0, 0, 0, 0};
+            }
+        }
+        // invalid lengths: nothing to read here (the merge gives the rows NaN)
         if (ctx < 1 || ctx > a.max_context_len || shared < 0 || shared > ctx ||
             shared > a.max_shared) return;
-        const int PT = a.partition_tokens;
         const int j0 = shared / PT;
-        jb = j0 + p * a.parts_per_item;
+        const int jb = j0 + p;   // absolute partition (token / PT)
         start = max(shared, jb * PT);
-        end = min((jb + a.parts_per_item) * PT, ctx);
+        end = min((jb + 1) * PT, ctx);
         if (start >= end) return;
         part_index = (shared + PT - 1) / PT + (jb - j0);
         lead = s0;
@@ -294,74 +315,87 @@ void attn_mfma_shared(SharedArgs a) {
         }
     };
 
-    // Write each served (sequence, query head)'s state for partition pidx and start the
-    // next partition from zero.
-    auto flush = [&](int pidx) __attribute__((always_inline)) {
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) {
-            if (nb >= nb_used) break;
-            const float lw = sum_across_quads(lsum[nb]);
-            const int nslot = 16 * nb + gq;
-            if (nslot < slots) {
-                const int m = nslot / G, j = nslot - m * G;
-                const int64_t row = ((int64_t)(s0 + m) * a.num_q_heads + h * G + j) * a.max_parts + pidx;
-                float* dst = a.ws_acc + row * D;
-#pragma unroll
-                for (int mt = 0; mt < MT; ++mt) {
-                    f32x4 v = acc[nb][mt];
-                    if (bad) v = (f32x4){NAN, NAN, NAN, NAN};
-                    *reinterpret_cast<f32x4*>(dst + 16 * mt + 4 * quad) = v;
-                }
-                if (quad == 0) {
-                    a.ws_m[row] = bad ? NAN : m_run[nb];
-                    a.ws_l[row] = bad ? NAN : lw;
-                }
-            }
-#pragma unroll
-            for (int mt = 0; mt < MT; ++mt) acc[nb][mt] = (f32x4){0.f, 0.f, 0.f, 0.f};
-            m_run[nb] = kNegInf;
-            lsum[nb] = 0.f;
-        }
-    };
-    // After tile `it`: its partition ends here when the next tile starts a new one (the
-    // partition boundaries are multiples of PT, a multiple of the tile).
-    const int tpp = a.partition_tokens / kTile;          // tiles per partition
-    int flush_at = min(t_end, (t_begin / tpp + 1) * tpp);  // tile index after the flush
-    int pidx = part_index;
-    (void)jb;
-    auto step_done = [&](int it) __attribute__((always_inline)) {
-        if (it + 1 == flush_at) {
-            flush(pidx);
-            ++pidx;
-            flush_at = min(t_end, flush_at + tpp);
-        }
-    };
-
-    // two-deep pipeline: every step loads one tile and computes the previous one
+    // Wave w's tiles: t_begin + w + 4 i.  Two register sets: the next tile's loads are in
+    // flight while the current one is computed.
+    const int n_w = n > w ? (n - w + kWaves - 1) / kWaves : 0;
     i32x4 kA[KI], kB[KI];
     i32x2 vA[MT], vB[MT];
-    load(t_begin, kA, vA);
+    const int t0 = t_begin + w;
+    if (n_w > 0) load(t0, kA, vA);
     int i = 0;
-    for (; i + 2 < n; i += 2) {
-        load(t_begin + i + 1, kB, vB);
+    for (; i + 2 < n_w; i += 2) {
+        load(t0 + kWaves * (i + 1), kB, vB);
         __builtin_amdgcn_sched_barrier(0);
-        compute(t_begin + i, kA, vA);
-        step_done(t_begin + i);
-        load(t_begin + i + 2, kA, vA);
+        compute(t0 + kWaves * i, kA, vA);
+        load(t0 + kWaves * (i + 2), kA, vA);
         __builtin_amdgcn_sched_barrier(0);
-        compute(t_begin + i + 1, kB, vB);
-        step_done(t_begin + i + 1);
+        compute(t0 + kWaves * (i + 1), kB, vB);
     }
-    if (i + 1 < n) {
-        load(t_begin + i + 1, kB, vB);
+    if (i + 1 < n_w) {
+        load(t0 + kWaves * (i + 1), kB, vB);
         __builtin_amdgcn_sched_barrier(0);
-        compute(t_begin + i, kA, vA);
-        step_done(t_begin + i);
-        compute(t_begin + i + 1, kB, vB);
-        step_done(t_begin + i + 1);
-    } else {
-        compute(t_begin + i, kA, vA);
-        step_done(t_begin + i);
+        compute(t0 + kWaves * i, kA, vA);
+        compute(t0 + kWaves * (i + 1), kB, vB);
+    } else if (i < n_w) {
+        compute(t0 + kWaves * i, kA, vA);
+    }
+
+    // ---- merge the four waves' states (fixed order), write the item's state ----
+    constexpr int NS = NB * 16;
+    __shared__ float sm_m[kWaves][NS];
+    __shared__ float sm_l[kWaves][NS];
+    __shared__ float sm_acc[NS][D + 4];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+        const float lw = sum_across_quads(lsum[nb]);
+        if (lane < 16) {
+            sm_m[w][16 * nb + lane] = m_run[nb];
+            sm_l[w][16 * nb + lane] = lw;
+        }
+    }
+    const bool any_bad = __syncthreads_or(bad);
+    float f[NB];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+        float mmax = kNegInf;
+#pragma unroll
+        for (int ww = 0; ww < kWaves; ++ww) mmax = fmaxf(mmax, sm_m[ww][16 * nb + gq]);
+        f[nb] = m_run[nb] == kNegInf ? 0.f : exp2_fast(m_run[nb] - mmax);
+    }
+    for (int ww = 0; ww < kWaves; ++ww) {
+        if (ww == w) {
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) {
+                if (nb >= nb_used) break;
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int d = 16 * mt + 4 * quad + r;
+                        const float v = acc[nb][mt][r] * f[nb];
+                        if (ww == 0) sm_acc[16 * nb + gq][d] = v;
+                        else sm_acc[16 * nb + gq][d] += v;
+                    }
+            }
+        }
+        __syncthreads();
+    }
+    for (int x = threadIdx.x; x < slots * D; x += kWaves * 64) {
+        const int sl = x / D, d = x - sl * D;
+        float mm = kNegInf;
+#pragma unroll
+        for (int ww = 0; ww < kWaves; ++ww) mm = fmaxf(mm, sm_m[ww][sl]);
+        float l = 0.f;
+#pragma unroll
+        for (int ww = 0; ww < kWaves; ++ww)
+            if (sm_m[ww][sl] != kNegInf) l += exp2_fast(sm_m[ww][sl] - mm) * sm_l[ww][sl];
+        const int m = sl / G, j = sl - m * G;
+        const int64_t row = ((int64_t)(s0 + m) * a.num_q_heads + h * G + j) * a.max_parts + part_index;
+        a.ws_acc[row * D + d] = any_bad ? NAN : sm_acc[sl][d];
+        if (d == 0) {
+            a.ws_m[row] = any_bad ? NAN : mm;
+            a.ws_l[row] = any_bad ? NAN : l;
+        }
     }
 }
 
@@ -374,35 +408,27 @@ void attn_mfma_shared(SharedArgs a) {
 // the KV head's query heads), all their partitions' loads in flight together.
 // ---------------------------------------------------------------------------------
 constexpr int kMergeOut = 2;
-constexpr int kMergeParts = 8;     // partitions folded per memory round trip
 
-template <int D, int OUT_DT>
+// KP: partitions folded per memory round trip (2 or 4 when no sequence has more, else 8;
+// past a sequence's last partition the slots re-read it).
+template <int D, int OUT_DT, int KP>
 __global__ __launch_bounds__(1024) void attn_shared_merge(SharedArgs a) {
     const int hk = blockIdx.x, s = blockIdx.y;
     const int G = a.group, n_out = G * D;
-    const int ctx = sload(a.context_lens, s);
-    const int g = group_of(a, s);
-    const int shared = sload(a.shared_tokens, g);
-    const int gs = sload(a.group_start, g), ge = sload(a.group_start, g + 1);
     const int64_t obase = ((int64_t)s * a.num_q_heads + hk * G) * D;
-    // a sequence outside its group's range (group_start not covering the batch in order)
-    // or past the group size the launch was planned for has no prefix state: NaN
-    const bool invalid = ctx < 1 || ctx > a.max_context_len || shared < 0 || shared > ctx ||
-                         shared > a.max_shared || gs < 0 || ge > a.num_seqs || s < gs ||
-                         s >= ge || s - gs >= a.max_group;
-    if (invalid) {
+    // written by the sequence's first tail item (np = 0: the group description does not
+    // hold for it, NaN)
+    const int32_t* dsc = reinterpret_cast<const int32_t*>(a.seq_desc + s);
+    const int np = sload(dsc, 0), gs = sload(dsc, 1), nblk = s == gs ? 0 : sload(dsc, 2);
+    if (np < 1) {
         for (int i = threadIdx.x; i < n_out; i += blockDim.x) store_out<OUT_DT>(a.out, obase + i, NAN);
         return;
     }
     // The shared tokens were read through the group's first table: this sequence's table
     // must list the same blocks for them.  Its entries are loaded together with the first
     // partitions' states, and compared once both are in flight.
-    const int nblk = s == gs ? 0 : (shared + a.block_size - 1) / a.block_size;
     const int32_t* mine = a.block_tables + (int64_t)s * a.max_blocks_per_seq;
     const int32_t* first = a.block_tables + (int64_t)gs * a.max_blocks_per_seq;
-    // prefix partitions, then the tail partitions at absolute multiples of PT
-    const int PT = a.partition_tokens;
-    const int np = (shared + PT - 1) / PT + (ctx > shared ? (ctx + PT - 1) / PT - shared / PT : 0);
     bool diff = false;
     for (int i0 = threadIdx.x * kMergeOut; i0 < n_out; i0 += blockDim.x * kMergeOut) {
         float M[kMergeOut], l[kMergeOut], acc[kMergeOut];
@@ -419,12 +445,12 @@ __global__ __launch_bounds__(1024) void attn_shared_merge(SharedArgs a) {
             acc[u] = 0.f;
             bad[u] = false;
         }
-        for (int p0 = 0; p0 < np; p0 += kMergeParts) {
-            float mv[kMergeOut][kMergeParts], lv[kMergeOut][kMergeParts], av[kMergeOut][kMergeParts];
+        for (int p0 = 0; p0 < np; p0 += KP) {
+            float mv[kMergeOut][KP], lv[kMergeOut][KP], av[kMergeOut][KP];
 #pragma unroll
             for (int u = 0; u < kMergeOut; ++u)
 #pragma unroll
-                for (int k = 0; k < kMergeParts; ++k) {   // slots past the end re-read the last
+                for (int k = 0; k < KP; ++k) {   // slots past the end re-read the last
                     const int64_t r = row[u] + min(p0 + k, np - 1);
                     mv[u][k] = a.ws_m[r];
                     lv[u][k] = a.ws_l[r];
@@ -435,7 +461,7 @@ __global__ __launch_bounds__(1024) void attn_shared_merge(SharedArgs a) {
 #pragma unroll
             for (int u = 0; u < kMergeOut; ++u)
 #pragma unroll
-                for (int k = 0; k < kMergeParts; ++k) {
+                for (int k = 0; k < KP; ++k) {
                     if (p0 + k >= np) break;
                     bad[u] |= mv[u][k] != mv[u][k];
                     const float mn = fmaxf(M[u], mv[u][k]);
@@ -476,9 +502,13 @@ int n_blocks_for(int max_group, int group) {
     return slots <= 16 ? 1 : slots <= 32 ? 2 : slots <= 64 ? 4 : 0;
 }
 
+// Workspace: sequence descriptors: int32[num_seqs][4] | m, l: float[rows] |
+// acc: float[rows][d], rows = num_seqs * hq * max_parts.  Scratch: every call writes what
+// it reads.
+size_t desc_region(int64_t num_seqs) { return align256((size_t)num_seqs * 4 * sizeof(int32_t)); }
 size_t shared_workspace(int64_t num_seqs, int64_t hq, int64_t d, int64_t max_parts) {
     const size_t rows = (size_t)num_seqs * hq * max_parts;
-    return 2 * align256(rows * sizeof(float)) + rows * d * sizeof(float);
+    return desc_region(num_seqs) + 2 * align256(rows * sizeof(float)) + rows * d * sizeof(float);
 }
 
 template <int D, int DT, int BS>
@@ -490,9 +520,16 @@ void launch_items(const SharedPlan& pl, dim3 grid, hipStream_t st) {
     }
 }
 
+template <int D, int KP>
+void launch_merge(const SharedPlan& pl, int out_dtype, dim3 grid, dim3 block, hipStream_t st) {
+    if (out_dtype == PAGED_KV_F32) attn_shared_merge<D, DT_F32, KP><<<grid, block, 0, st>>>(pl.a);
+    else if (out_dtype == PAGED_KV_F16) attn_shared_merge<D, DT_F16, KP><<<grid, block, 0, st>>>(pl.a);
+    else attn_shared_merge<D, DT_BF16, KP><<<grid, block, 0, st>>>(pl.a);
+}
+
 template <int D>
 void launch_d(const SharedPlan& pl, int dtype, int out_dtype, int bs, hipStream_t st) {
-    const dim3 grid((unsigned)((pl.a.items + kWaves - 1) / kWaves));
+    const dim3 grid((unsigned)pl.a.items);   // one workgroup per item
     if (dtype == PAGED_KV_F16) {
         if (bs == 32) launch_items<D, DT_F16, 32>(pl, grid, st);
         else launch_items<D, DT_F16, 16>(pl, grid, st);
@@ -503,9 +540,28 @@ void launch_d(const SharedPlan& pl, int dtype, int out_dtype, int bs, hipStream_
     const dim3 mgrid((unsigned)pl.a.num_kv_heads, (unsigned)pl.a.num_seqs);
     const int outs = pl.a.group * D;
     const dim3 mblock((unsigned)std::min(1024, ((outs + kMergeOut - 1) / kMergeOut + 63) / 64 * 64));
-    if (out_dtype == PAGED_KV_F32) attn_shared_merge<D, DT_F32><<<mgrid, mblock, 0, st>>>(pl.a);
-    else if (out_dtype == PAGED_KV_F16) attn_shared_merge<D, DT_F16><<<mgrid, mblock, 0, st>>>(pl.a);
-    else attn_shared_merge<D, DT_BF16><<<mgrid, mblock, 0, st>>>(pl.a);
+    if (pl.a.max_parts <= 2) launch_merge<D, 2>(pl, out_dtype, mgrid, mblock, st);
+    else if (pl.a.max_parts <= 4) launch_merge<D, 4>(pl, out_dtype, mgrid, mblock, st);
+    else launch_merge<D, 8>(pl, out_dtype, mgrid, mblock, st);
+}
+
+// Default partition size: the largest of 4096 tokens (or the longest context, rounded up
+// to 512), 2048, 1024, 512 at which the launch still has about four workgroups per compute
+// unit (prefix items, plus tail items counted at the tails' longest possible length).
+// Fewer, longer partitions mean fewer partial states to store and merge; on 32 prompts
+// x 8 samples (2,048 shared tokens, tails up to 520) the launch pair took 153 / 130 / 121
+// / 119 us at 512 / 1024 / 2048 / 4096 tokens.
+int32_t default_partition_tokens(int64_t num_seqs, int64_t hkv, int64_t num_groups,
+                                 int32_t max_shared, int32_t max_ctx) {
+    const int64_t want = 4 * (int64_t)pkv::device_shape().compute_units;
+    int32_t pt = std::min(4096, (max_ctx + 511) / 512 * 512);
+    while (pt > 512) {
+        const int64_t items = num_groups * hkv * ((max_shared + pt - 1) / pt) +
+                              num_seqs * hkv * ((max_ctx - max_shared + pt - 1) / pt);
+        if (items >= want) break;
+        pt = std::max(512, pt / 2 / kTile * kTile);
+    }
+    return std::max(pt, (int32_t)kTile);
 }
 
 paged_kv_status plan_shared(SharedPlan& pl, const paged_kv_pool_desc* desc, int32_t num_seqs,
@@ -538,7 +594,8 @@ paged_kv_status plan_shared(SharedPlan& pl, const paged_kv_pool_desc* desc, int3
     // One item serves the whole group (up to 4 N-blocks).  Serving 32 query slots as two
     // 16-slot items that read the same shared tiles (three waves per SIMD instead of two)
     // measured slower on the parallel-sampling workload: 148 against 136 us.
-    if (part_tokens == 0) part_tokens = pkv::kDefaultPartitionTokens;
+    if (part_tokens == 0)
+        part_tokens = default_partition_tokens(num_seqs, desc->num_kv_heads, num_groups, max_shared, max_ctx);
     if (part_tokens < 0 || part_tokens % kTile) {
         pkv::set_error("partition_tokens %d must be 0 or a positive multiple of %d", part_tokens, kTile);
         return PAGED_KV_ERR_INVALID_ARG;
@@ -559,12 +616,11 @@ paged_kv_status plan_shared(SharedPlan& pl, const paged_kv_pool_desc* desc, int3
     a.prefix_parts = (max_shared + part_tokens - 1) / part_tokens;
     a.tail_parts = (max_ctx + part_tokens - 1) / part_tokens;
     a.max_parts = a.prefix_parts + a.tail_parts;
-    a.parts_per_item = 1;
     a.members_per_item = std::max(1, 16 * pl.nb / group);
     a.chunks = (max_group + a.members_per_item - 1) / a.members_per_item;
     a.prefix_items = (int64_t)num_groups * desc->num_kv_heads * a.prefix_parts * a.chunks;
-    a.items = a.prefix_items + (int64_t)num_seqs * desc->num_kv_heads * a.tail_parts;   // k = 1
-    if ((a.items + kWaves - 1) / kWaves > INT32_MAX || num_seqs > 65535) {
+    a.items = a.prefix_items + (int64_t)num_seqs * desc->num_kv_heads * a.tail_parts;
+    if (a.items > INT32_MAX || num_seqs > 65535) {
         pkv::set_error("batch too large for one launch");
         return PAGED_KV_ERR_UNSUPPORTED;
     }
@@ -636,6 +692,8 @@ paged_kv_status paged_attention_decode_shared_prefix(
     a.shared_tokens = shared_tokens;
     const size_t rows = (size_t)num_seqs * num_q_heads * a.max_parts;
     char* ws = static_cast<char*>(workspace);
+    a.seq_desc = reinterpret_cast<i32x4*>(ws);
+    ws += desc_region(num_seqs);
     a.ws_m = reinterpret_cast<float*>(ws);
     a.ws_l = reinterpret_cast<float*>(ws + align256(rows * 4));
     a.ws_acc = reinterpret_cast<float*>(ws + 2 * align256(rows * 4));

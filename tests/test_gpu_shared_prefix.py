@@ -6,7 +6,8 @@ the prompt's blocks by reference count), reading each group's shared tokens once
 all its members.  Checked against the oracle (every sequence), against the standard
 decode call, for placement invariance (bitwise), with groups the allocator forms from
 forks and prefix-cache hits, odd shared lengths, groups of one, every N-block width,
-block size 32, and malformed group descriptions (NaN rows, nothing read out of bounds).
+block size 32, malformed group descriptions (NaN rows, nothing read out of bounds), and
+one workspace reused across calls (nothing a call reads is left over from another).
 """
 import numpy as np
 import pytest
@@ -184,4 +185,52 @@ def test_malformed_groups_give_nan_without_faults():
                 assert np.isnan(r[i]).all(), (starts, shared, i)
             else:
                 assert np.abs(r[i] - good[i]).max() <= TOL[dt], (starts, shared, i)
+    c.close()
+
+
+def test_workspace_reused_across_calls():
+    """The workspace is scratch: it starts filled with 0xFF bytes, and valid and malformed
+    calls alternate on it, with shrinking batches and two partition sizes; each result
+    matches the oracle (NaN rows where the group description does not hold), so nothing
+    a call reads is left over from an earlier one."""
+    from paged_kv_cache_15_amd import binding as B
+    from paged_kv_cache_15_amd.replay import to_device
+    rng = np.random.default_rng(29)
+    hq, hkv, d, dt = 32, 8, 128, "bf16"
+    c, batch = _forked_batch(rng, hq, hkv, d, dt, 16, [700, 300], [[40, 5, 300, 6], [7, 520]])
+    n = len(batch)
+    q = to_device(rng.standard_normal((n, hq, d)).astype(np.float32), dt, "cuda")
+    tables, lens = c.block_tables(batch)
+    tab, bl = torch.from_numpy(tables).cuda(), torch.from_numpy(lens).cuda()
+    mx = int(lens.max())
+    good = _oracle_of(c, batch, q, 0.1, dt, 16)
+    nbytes = max(B.paged_attention_shared_prefix_workspace_bytes(c.desc, n, hq, mx, 2, 8, mx, pt)
+                 for pt in (0, 64))
+    ws = torch.full((nbytes,), 255, dtype=torch.uint8, device="cuda")
+    cases = [  # (rows, group starts, shared lengths, partition tokens, NaN rows)
+        (n, [0, 4, 6], [688, 288], 0, []),
+        (n, [0, 4, 6], [688, 2000], 64, [4, 5]),        # shared above the second group's lengths
+        (n, [0, 4, 6], [688, 288], 64, []),
+        (n, [0, 3, 6], [688, 288], 0, [4, 5]),          # tables differ from the group's first
+        (4, [0, 4], [688], 0, []),                     # fewer rows, one group
+        (n, [0, 4, 9], [688, 288], 64, [4, 5]),         # a group range past the batch
+        (n, [0, 4, 6], [-3, 288], 0, [0, 1, 2, 3]),     # negative shared length
+        (n, [0, 4, 6], [688, 288], 0, []),
+    ]
+    for rows, starts, shared, pt, nan_rows in cases:
+        gs = torch.tensor(starts, dtype=torch.int32, device="cuda")
+        sh = torch.tensor(shared, dtype=torch.int32, device="cuda")
+        max_shared = max(0, min(max(shared), mx))
+        out = torch.full((rows, hq, d), 3.0, dtype=torch.float32, device="cuda")
+        B.paged_attention_decode_shared_prefix(c.desc, out, "f32", q[:rows], c.k_pool, c.v_pool,
+                                               tab[:rows], bl[:rows], hq, mx, 0.1, gs, sh,
+                                               len(shared), 8, max_shared, pt, ws)
+        torch.cuda.synchronize()
+        say(f"[shared] reuse rows={rows} starts={starts} shared={shared} pt={pt}")
+        r = out.double().cpu().numpy()
+        for i in range(rows):
+            if i in nan_rows:
+                assert np.isnan(r[i]).all(), (starts, shared, pt, i)
+            else:
+                assert np.abs(r[i] - good[i]).max() <= TOL[dt], (starts, shared, pt, i)
     c.close()
