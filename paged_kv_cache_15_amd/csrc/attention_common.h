@@ -135,4 +135,26 @@ __device__ __forceinline__ void lds_put_rows(T* rows, int ldw, int lane, const i
         *reinterpret_cast<i32x4*>(rows + (lane & 15) * ldw + (4 * i + (lane >> 4)) * X) = raw[i];
 }
 
+// Block size 1, whole-row loads.  A token's K (or V) row for one head is D contiguous
+// elements, D / 8 chunks of 16 bytes.  Load i of lane l reads chunk l % (D / 8) of the
+// tile's token (512 / D) i + l / (D / 8), so every load instruction reads whole rows (a
+// 256-byte row per 16 lanes at head_dim 128).  Loads in the score product's own operand
+// layout (16 tokens per instruction, 64 bytes of each) streamed at 0.56 of the HBM peak
+// on the GQA workload, whole rows at 0.71.  The rows then pass through the wave's LDS.
+// Block of the lane's token in load i, from idv = lane_block_bs1(...) (lane j < 16 holds
+// the block of the tile's token j).
+template <int D>
+__device__ __forceinline__ int32_t load_id_bs1(int32_t idv, int i, int lane) {
+    return __shfl(idv, (512 / D) * i + lane / (D / 8));
+}
+// Lane l's chunk of load i into the wave's LDS rows ([token][element], rows of ldw).
+template <int D, int NL>
+__device__ __forceinline__ void lds_put_whole_rows(uint16_t* rows, int ldw, int lane,
+                                                   const i32x4 (&raw)[NL]) {
+    constexpr int RPI = 512 / D, CPR = D / 8;
+#pragma unroll
+    for (int i = 0; i < NL; ++i)
+        *reinterpret_cast<i32x4*>(rows + (RPI * i + lane / CPR) * ldw + (lane % CPR) * 8) = raw[i];
+}
+
 }  // namespace pkv_dev

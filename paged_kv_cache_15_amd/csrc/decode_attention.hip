@@ -153,9 +153,11 @@ __device__ __forceinline__ void write_new_token(const PartitionArgs& a, int s, i
 template <bool FUSE, int D>
 constexpr int mfma_partition_waves() { return kWaves; }
 
+// (Block size 1 at head_dim 128 needs more than a third of the register file for its LDS
+// round trips: two waves per SIMD there.)
 template <int D, int DT, int OUT_DT, int BS, bool FUSE>
 __global__ __launch_bounds__((mfma_partition_waves<FUSE, D>() * 64))
-__attribute__((amdgpu_waves_per_eu(mfma_waves_per_simd<D, false>())))
+__attribute__((amdgpu_waves_per_eu(BS == 1 && D == 128 ? 2 : mfma_waves_per_simd<D, false>())))
 void attn_mfma_kernel(PartitionArgs a) {
     constexpr int NW = mfma_partition_waves<FUSE, D>();
     constexpr int KI = D / 32;   // QK MFMAs (and 16-byte K loads per lane) per tile
@@ -166,6 +168,7 @@ void attn_mfma_kernel(PartitionArgs a) {
     using kvec = typename std::conditional<DT == DT_BF16, bf16x8, f16x8>::type;
     using vbuf = typename std::conditional<BS == 1, i32x4[KI], i32x2[MT]>::type;
     __shared__ uint16_t s_vt[BS == 1 ? NW * kTile * LDW : 1];
+    __shared__ uint16_t s_kt[BS == 1 ? NW * kTile * LDW : 1];
 
     const int s = blockIdx.x / a.num_kv_heads, g = blockIdx.x - s * a.num_kv_heads;
     const int p = blockIdx.y;
@@ -210,6 +213,7 @@ void attn_mfma_kernel(PartitionArgs a) {
     const int64_t blk_stride = (int64_t)a.num_kv_heads * TILE;
     const int voff = gq * 4 + quad;   // 8-byte unit of row gq, tokens 4*quad.. of a V^T tile
     uint16_t* vrows = s_vt + w * kTile * LDW;
+    uint16_t* krows = s_kt + w * kTile * LDW;
 
     f32x4 acc[MT];
 #pragma unroll
@@ -221,20 +225,22 @@ void attn_mfma_kernel(PartitionArgs a) {
     vbuf vA, vB;
     int id_v = 0;    // block size >= 16: lane i holds the block of the wave's i-th tile
 
-    // K tile: load kk of lane l is 16-byte chunk 4*kk + l/16 of token l%16 (block size
-    // 16: bytes [1024*kk + 16*l, +16), each load instruction reads 1 KiB contiguous).
-    // V^T tile: load mt of lane l is row 16*mt + l%16, tokens 4*(l/16)..+3.
+    // K tile (block size >= 16): load kk of lane l is 16-byte chunk 4*kk + l/16 of token
+    // l%16 (block size 16: bytes [1024*kk + 16*l, +16), each load instruction reads 1 KiB
+    // contiguous).  V^T tile: load mt of lane l is row 16*mt + l%16, tokens 4*(l/16)..+3.
+    // Block size 1: whole rows, load i of lane l is chunk l % (D / 8) of token
+    // (512 / D) i + l / (D / 8), for K and V alike.
     auto load = [&](int idx, int b, i32x4 (&kr)[KI], vbuf& vr) __attribute__((always_inline)) {
         if constexpr (BS == 1) {
             bool bad;
-            const int32_t bid = lane_block_bs1(trow, b, ctx, a.num_blocks, lane, bad);
+            const int32_t idv = lane_block_bs1(trow, b, ctx, a.num_blocks, lane, bad);
             bad_block |= bad;
-            const i32x4* kt = reinterpret_cast<const i32x4*>(kbase + bid * blk_stride) + (lane >> 4);
-            const i32x4* vt = reinterpret_cast<const i32x4*>(vbase + bid * blk_stride) + (lane >> 4);
 #pragma unroll
-            for (int kk = 0; kk < KI; ++kk) kr[kk] = __builtin_nontemporal_load(kt + 4 * kk);
-#pragma unroll
-            for (int kk = 0; kk < KI; ++kk) vr[kk] = __builtin_nontemporal_load(vt + 4 * kk);
+            for (int i = 0; i < KI; ++i) {
+                const int64_t off = load_id_bs1<D>(idv, i, lane) * blk_stride;
+                kr[i] = __builtin_nontemporal_load(reinterpret_cast<const i32x4*>(kbase + off) + lane % (D / 8));
+                vr[i] = __builtin_nontemporal_load(reinterpret_cast<const i32x4*>(vbase + off) + lane % (D / 8));
+            }
         } else {
             const int32_t bid = __builtin_amdgcn_readlane(id_v, idx);
             const int64_t sub = (b & (TPB - 1)) * (kTile * D);   // 16-token sub-block
@@ -250,7 +256,12 @@ void attn_mfma_kernel(PartitionArgs a) {
     auto compute = [&](int b, i32x4 (&kr)[KI], vbuf& vin) __attribute__((always_inline)) {
         i32x2 vr[MT];
         if constexpr (BS == 1) {
-            lds_put_rows<uint16_t, KI>(vrows, LDW, lane, vin);
+            // K back in the score product's operand layout, V transposed
+            lds_put_whole_rows<D, KI>(krows, LDW, lane, kr);
+            lds_put_whole_rows<D, KI>(vrows, LDW, lane, vin);
+#pragma unroll
+            for (int kk = 0; kk < KI; ++kk)
+                kr[kk] = *reinterpret_cast<const i32x4*>(krows + (lane & 15) * LDW + 32 * kk + 8 * (lane >> 4));
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt) {
                 uint32_t e[4];

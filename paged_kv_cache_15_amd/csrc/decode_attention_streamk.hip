@@ -375,6 +375,7 @@ void attn_mfma_streamk(StreamArgs a) {
     // V registers as loaded: a V^T operand per 16 dims, or (block size 1) token rows
     using vbuf = typename std::conditional<BS == 1, i32x4[KI], i32x2[MT]>::type;
     __shared__ uint16_t s_vt[BS == 1 ? kWaves * kTile * LDW : 1];
+    __shared__ uint16_t s_kt[BS == 1 ? kWaves * kTile * LDW : 1];
 
     extern __shared__ int s_pref[];
     const int tiles_per_unit = build_prefix(a, s_pref);
@@ -394,13 +395,14 @@ void attn_mfma_streamk(StreamArgs a) {
     // load right where it is issued, draining the K/V prefetch.)
     const int gqc = min(gq, G - 1);
     const int64_t blk_stride = (int64_t)a.num_kv_heads * TILE;
-    // K: load kk of lane l is chunk 4*kk + l/16 of token l%16 of the tile (1 KiB
-    // contiguous per load instruction); V^T: load mt of lane l is dim 16*mt + l%16,
-    // tokens 4*(l/16)..+3 (512 bytes contiguous)
+    // Block size >= 16: K load kk of lane l is chunk 4*kk + l/16 of token l%16 of the tile
+    // (1 KiB contiguous per load instruction); V^T load mt of lane l is dim 16*mt + l%16,
+    // tokens 4*(l/16)..+3 (512 bytes contiguous).  Block size 1: whole rows (below).
     const int voff = gq * 4 + quad;
     const uint16_t* kpool = static_cast<const uint16_t*>(a.k_pool);
     const uint16_t* vpool = static_cast<const uint16_t*>(a.v_pool);
     uint16_t* vrows = s_vt + (threadIdx.x >> 6) * kTile * LDW;
+    uint16_t* krows = s_kt + (threadIdx.x >> 6) * kTile * LDW;
 
     Cursor lc = locate(a, s_pref, t0);   // tile being loaded (one ahead)
     Cursor cc = lc;                       // tile being computed
@@ -415,15 +417,15 @@ void attn_mfma_streamk(StreamArgs a) {
     };
     auto load_kv = [&](const Cursor& c, i32x4 (&kr)[KI], vbuf& vr, bool& bad) __attribute__((always_inline)) {
         if constexpr (BS == 1) {
-            const int32_t bid = lane_block_bs1(a.block_tables + (int64_t)c.s * a.max_blocks_per_seq,
+            // whole rows: load i of lane l is chunk l % (D / 8) of token (512 / D) i + l / (D / 8)
+            const int32_t idv = lane_block_bs1(a.block_tables + (int64_t)c.s * a.max_blocks_per_seq,
                                                c.it, c.ctx, a.num_blocks, lane, bad);
-            const int64_t base = bid * blk_stride + (int64_t)c.u * D;
-            const i32x4* kt = reinterpret_cast<const i32x4*>(kpool + base) + (lane >> 4);
-            const i32x4* vt = reinterpret_cast<const i32x4*>(vpool + base) + (lane >> 4);
 #pragma unroll
-            for (int kk = 0; kk < KI; ++kk) kr[kk] = __builtin_nontemporal_load(kt + 4 * kk);
-#pragma unroll
-            for (int kk = 0; kk < KI; ++kk) vr[kk] = __builtin_nontemporal_load(vt + 4 * kk);
+            for (int i = 0; i < KI; ++i) {
+                const int64_t base = load_id_bs1<D>(idv, i, lane) * blk_stride + (int64_t)c.u * D;
+                kr[i] = __builtin_nontemporal_load(reinterpret_cast<const i32x4*>(kpool + base) + lane % (D / 8));
+                vr[i] = __builtin_nontemporal_load(reinterpret_cast<const i32x4*>(vpool + base) + lane % (D / 8));
+            }
         } else {
             const int32_t bid = tile_block<BS>(a, c, bad);
             const int64_t base = (int64_t)c.u * TILE + bid * blk_stride + (c.it & (TPB - 1)) * (kTile * D);
@@ -490,7 +492,13 @@ void attn_mfma_streamk(StreamArgs a) {
                        const Cursor& nc) __attribute__((always_inline)) {
         i32x2 vr[MT];
         if constexpr (BS == 1) {
-            lds_put_rows<uint16_t, KI>(vrows, LDW, lane, vin);
+            // K back in the score product's operand layout (token l % 16, dims 32 kk +
+            // 8 (l / 16) ..), V transposed (4 tokens of one dim per lane)
+            lds_put_whole_rows<D, KI>(krows, LDW, lane, kr);
+            lds_put_whole_rows<D, KI>(vrows, LDW, lane, vin);
+#pragma unroll
+            for (int kk = 0; kk < KI; ++kk)
+                kr[kk] = *reinterpret_cast<const i32x4*>(krows + (lane & 15) * LDW + 32 * kk + 8 * (lane >> 4));
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt) {
                 uint32_t e[4];
