@@ -230,11 +230,21 @@ void attn_mfma_kernel(PartitionArgs a) {
     // contiguous).  V^T tile: load mt of lane l is row 16*mt + l%16, tokens 4*(l/16)..+3.
     // Block size 1: whole rows, load i of lane l is chunk l % (D / 8) of token
     // (512 / D) i + l / (D / 8), for K and V alike.
+    // Block size 1: lane l's id is that of token l % 16 of the tile (tokens at or past ctx
+    // take token ctx - 1's), read with a vector load one tile ahead, before the current
+    // tile's rows, so that waiting for the ids never waits for those rows.
+    int32_t id_next = 0;
+    auto fetch_ids = [&](int b) __attribute__((always_inline)) {
+        return trow[min(kTile * b + (lane & 15), ctx - 1)];
+    };
     auto load = [&](int idx, int b, i32x4 (&kr)[KI], vbuf& vr) __attribute__((always_inline)) {
         if constexpr (BS == 1) {
-            bool bad;
-            const int32_t idv = lane_block_bs1(trow, b, ctx, a.num_blocks, lane, bad);
-            bad_block |= bad;
+            const int32_t raw = id_next;                       // tile b's ids
+            id_next = fetch_ids(min(b + NW, blk_end - 1));     // the wave's next tile
+            __builtin_amdgcn_sched_barrier(0);
+            const bool oob = (uint32_t)raw >= (uint32_t)a.num_blocks;
+            if (__ballot(oob)) bad_block = true;
+            const int32_t idv = oob ? 0 : raw;
 #pragma unroll
             for (int i = 0; i < KI; ++i) {
                 const int64_t off = load_id_bs1<D>(idv, i, lane) * blk_stride;
@@ -366,6 +376,8 @@ void attn_mfma_kernel(PartitionArgs a) {
             __syncthreads();
         }
     }
+    if constexpr (BS == 1)
+        if (n_w > 0) id_next = fetch_ids(blk_begin + w);
     for (int base = 0; base < n_w; base += 64) {
         const int cnt = min(64, n_w - base);
         const int b0 = blk_begin + w + NW * base;

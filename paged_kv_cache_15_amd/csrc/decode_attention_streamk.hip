@@ -415,11 +415,33 @@ void attn_mfma_streamk(StreamArgs a) {
         for (int kk = 0; kk < KI; ++kk)
             qop[kk] = __builtin_bit_cast(kvec, *reinterpret_cast<const i32x4*>(qh + 32 * kk));
     };
-    auto load_kv = [&](const Cursor& c, i32x4 (&kr)[KI], vbuf& vr, bool& bad) __attribute__((always_inline)) {
+    // Block size 1: lane l's id is that of token l % 16 of the tile (tokens at or past ctx
+    // take token ctx - 1's), read with a vector load one step before the tile's rows are
+    // loaded: `ic` is the cursor of the tile whose ids are in flight, `ahead` its index in
+    // the slice (at the slice's end the last tile's ids are read again, so every step
+    // issues the same loads).  Issued ahead of the previous tile's rows, the ids are waited
+    // for without waiting for those rows.
+    Cursor ic = lc;
+    int ahead = 0;
+    int32_t id_next = 0;
+    auto fetch_ids = [&](const Cursor& c) __attribute__((always_inline)) {
+        return a.block_tables[(int64_t)c.s * a.max_blocks_per_seq +
+                              min(kTile * c.it + (lane & 15), c.ctx - 1)];
+    };
+    auto next_ids = [&]() __attribute__((always_inline)) {
+        if (ahead + 1 < n) {
+            advance(a, ic);
+            ++ahead;
+        }
+        id_next = fetch_ids(ic);
+    };
+    auto load_kv = [&](const Cursor& c, int32_t raw, i32x4 (&kr)[KI], vbuf& vr, bool& bad) __attribute__((always_inline)) {
         if constexpr (BS == 1) {
-            // whole rows: load i of lane l is chunk l % (D / 8) of token (512 / D) i + l / (D / 8)
-            const int32_t idv = lane_block_bs1(a.block_tables + (int64_t)c.s * a.max_blocks_per_seq,
-                                               c.it, c.ctx, a.num_blocks, lane, bad);
+            // whole rows: load i of lane l is chunk l % (D / 8) of token (512 / D) i + l / (D / 8);
+            // an id outside [0, num_blocks) reads block 0 and flags the unit
+            const bool oob = (uint32_t)raw >= (uint32_t)a.num_blocks;
+            bad = __ballot(oob) != 0;
+            const int32_t idv = oob ? 0 : raw;
 #pragma unroll
             for (int i = 0; i < KI; ++i) {
                 const int64_t base = load_id_bs1<D>(idv, i, lane) * blk_stride + (int64_t)c.u * D;
@@ -599,7 +621,14 @@ void attn_mfma_streamk(StreamArgs a) {
     // load the tile after the last one loaded into slot sl
     auto produce = [&](int sl) __attribute__((always_inline)) {
         advance(a, lc);
-        load_kv(lc, kbuf[sl], vbufs[sl], bbuf[sl]);
+        if constexpr (BS == 1) {
+            const int32_t raw = id_next;   // lc's ids (ic is lc here)
+            next_ids();
+            __builtin_amdgcn_sched_barrier(0);
+            load_kv(lc, raw, kbuf[sl], vbufs[sl], bbuf[sl]);
+        } else {
+            load_kv(lc, 0, kbuf[sl], vbufs[sl], bbuf[sl]);
+        }
         // Keep these loads ahead of everything that waits on the tile about to be
         // computed: left alone, the scheduler hoists the first score product (and with
         // it a wait on that tile's loads) into the block-id lookup's latency, which
@@ -620,7 +649,13 @@ void attn_mfma_streamk(StreamArgs a) {
     };
 
     load_q(cc);
-    load_kv(lc, kbuf[0], vbufs[0], bbuf[0]);
+    if constexpr (BS == 1) {
+        const int32_t raw = fetch_ids(lc);
+        next_ids();
+        load_kv(lc, raw, kbuf[0], vbufs[0], bbuf[0]);
+    } else {
+        load_kv(lc, 0, kbuf[0], vbufs[0], bbuf[0]);
+    }
     if (n >= 2 * R - 1) {
         // Every step of the main loop loads one tile and computes one, so the number
         // of loads in flight is the same on every path and the compiler waits for
