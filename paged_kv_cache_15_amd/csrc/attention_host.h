@@ -58,6 +58,17 @@ struct StreamLaunch {
     // zero) and the partial results (m, l, acc from StreamPlan::m_off on, rebased to 0)
     int32_t* counters;
     char* data;
+    // Partition states (pm_tiles > 0, MFMA kernel only): instead of merging, each wave
+    // stores the state of every 512-token (pm_tiles-tile) partition piece it computed
+    // into rows (sequence, query head, 2 p + k) of pm_m / pm_l / pm_acc (max_parts =
+    // pm_max_parts): k = 0 for the piece holding the partition's first tile, k = 1 for
+    // the rest of a partition that a slice boundary cut (m = -inf when there is none);
+    // the fixed-partition merge kernel then folds them.
+    int32_t pm_tiles = 0;
+    int32_t pm_max_parts = 0;
+    float* pm_m = nullptr;
+    float* pm_l = nullptr;
+    float* pm_acc = nullptr;
 };
 
 // One launch: partition work and the merge of multi-piece units.

@@ -766,7 +766,10 @@ constexpr int kReduceMaxGroups = 8;
 template <int D>
 constexpr int reduce_groups_max() { return 1024 / D < kReduceMaxGroups ? 1024 / D : kReduceMaxGroups; }
 
-template <int D, int OUT_DT>
+// PAIRS: the partition states of the stream-K schedule (pkv::StreamLaunch::pm_tiles): two
+// rows per partition, the second a cut-off rest (skipped when its m is -inf, which no
+// computed piece has), and every sequence has rows (one-partition ones included).
+template <int D, int OUT_DT, bool PAIRS>
 __global__ __launch_bounds__(D * reduce_groups_max<D>()) void attn_reduce_kernel(
         void* out, const int32_t* context_lens, int32_t num_q_heads, int32_t max_context_len,
         int32_t partition_tokens, int32_t max_parts, const float* ws_m, const float* ws_l,
@@ -787,9 +790,10 @@ __global__ __launch_bounds__(D * reduce_groups_max<D>()) void attn_reduce_kernel
         if (g == 0) store_out<OUT_DT>(out, o, NAN);
         return;
     }
-    const int np = (ctx + partition_tokens - 1) / partition_tokens;
-    if (np == 1) return;   // written by the partition kernel
-    const int64_t row = ((int64_t)s * num_q_heads + h) * max_parts;
+    const int parts = (ctx + partition_tokens - 1) / partition_tokens;
+    if (!PAIRS && parts == 1) return;   // written by the partition kernel
+    const int np = PAIRS ? 2 * parts : parts;   // rows to fold
+    const int64_t row = ((int64_t)s * num_q_heads + h) * (PAIRS ? 2 * max_parts : max_parts);
     const int per = (np + R - 1) / R;
     const int i_lo = min(np, g * per), i_hi = min(np, i_lo + per);
     float M = kNegInf, l = 0.f, acc = 0.f;
@@ -806,6 +810,7 @@ __global__ __launch_bounds__(D * reduce_groups_max<D>()) void attn_reduce_kernel
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
             if (i0 + k >= i_hi) break;
+            if (PAIRS && mv[k] == kNegInf) continue;
             bad |= mv[k] != mv[k];
             lse_fold(M, l, acc, mv[k], lv[k], av[k]);
         }
@@ -852,6 +857,7 @@ struct Plan {
     bool mfma;
     bool streamk;              // stream-K schedule (partition_tokens 0) or fixed partitions
     bool fuse = false;         // fused decode step: cache write + attention + merge in one launch
+    bool pm = false;           // fixed partitions' states from the stream-K schedule (use_pm)
     pkv::StreamPlan sp;
     pkv::StreamLaunch sl;
     dim3 grid;
@@ -894,11 +900,29 @@ size_t counter_bytes(const paged_kv_pool_desc* desc, int64_t num_seqs, int64_t h
 }
 
 // Fixed partitions: counters | m, l: float[rows] | acc: float[rows][d], rows =
-// num_seqs * hq * max_parts.  Nothing when no sequence can need a second partition.
-size_t workspace_for(size_t cnt_bytes, int64_t num_seqs, int64_t hq, int64_t d, int64_t max_parts) {
+// num_seqs * hq * max_parts (twice that for partition states from the stream-K schedule,
+// use_pm).  Nothing when no sequence can need a second partition.
+size_t workspace_for(size_t cnt_bytes, int64_t num_seqs, int64_t hq, int64_t d, int64_t max_parts,
+                     bool pm = false) {
     if (max_parts <= 1) return 0;
-    const size_t rows = (size_t)num_seqs * hq * max_parts;
+    const size_t rows = (size_t)num_seqs * hq * max_parts * (pm ? 2 : 1);
     return cnt_bytes + 2 * align256(rows * sizeof(float)) + rows * d * sizeof(float);
+}
+
+// Fixed partitions of long contexts in large batches: the partitions' states come from
+// the stream-K schedule (each wave streams a contiguous run of tiles and stores one state
+// per partition piece, pkv::StreamLaunch::pm_tiles) rather than from one workgroup per
+// partition, and the merge kernel folds them as usual.  From 8 partitions per sequence
+// and 16 (sequence, KV head, partition) items per compute unit, MFMA kernels at 16- and
+// 32-token blocks, up to 2048 sequences (the kernel's LDS holds a per-sequence prefix
+// beside the pieces).
+bool use_pm(const paged_kv_pool_desc* desc, int64_t num_seqs, int32_t hq, int64_t max_parts) {
+    const int group = hq / desc->num_kv_heads;
+    const bool mfma = desc->dtype != PAGED_KV_F32 && group >= 2 && group <= 16;
+    // (the kernel addresses the states with 32-bit byte offsets)
+    const bool fits = num_seqs * hq * 2 * max_parts * desc->head_dim * 4 < (int64_t(1) << 31);
+    return mfma && fits && desc->block_size >= 16 && num_seqs >= 1 && num_seqs <= 2048 && max_parts >= 8 &&
+           num_seqs * desc->num_kv_heads * max_parts >= 16 * (int64_t)pkv::device_shape().compute_units;
 }
 
 // Where a call's workspace lives: one caller buffer (counters first, then the partial
@@ -957,8 +981,15 @@ paged_kv_status make_plan(Plan& pl, const paged_kv_pool_desc* desc, void* out, i
                                  max_ctx, &ok);
         pl.ws_needed = pl.sp.ws_bytes;
     } else {
+        pl.pm = use_pm(desc, num_seqs, hq, max_parts);
+        if (pl.pm) {
+            bool ok = false;
+            pl.sp = pkv::stream_plan(num_seqs, hq, desc->num_kv_heads, desc->dtype, desc->head_dim,
+                                     max_ctx, &ok);
+            pl.pm = ok;
+        }
         pl.ws_needed = workspace_for(counter_bytes(desc, num_seqs, hq), num_seqs, hq,
-                                     desc->head_dim, max_parts);
+                                     desc->head_dim, max_parts, pl.pm);
     }
     if (num_seqs > 0) {
         if (!out || !lens || (need_kv && (!q || !k_pool || !v_pool || !tables))) {
@@ -992,7 +1023,7 @@ paged_kv_status make_plan(Plan& pl, const paged_kv_pool_desc* desc, void* out, i
     a.v_pool = v_pool;
     a.block_tables = tables;
     a.context_lens = lens;
-    const size_t rows = (size_t)num_seqs * hq * max_parts;
+    const size_t rows = (size_t)num_seqs * hq * max_parts * (pl.pm ? 2 : 1);
     // counters, then the partial results (both schedules lay these out from `data` on)
     int32_t* counters = nullptr;
     char* data = nullptr;
@@ -1035,6 +1066,13 @@ paged_kv_status make_plan(Plan& pl, const paged_kv_pool_desc* desc, void* out, i
                               num_seqs, hq, desc->num_kv_heads, desc->num_blocks, desc->dtype,
                               desc->head_dim, desc->block_size, max_ctx, scale, counters,
                               data};
+    if (pl.pm) {
+        pl.sl.pm_tiles = part_tokens / kTile;
+        pl.sl.pm_max_parts = max_parts;
+        pl.sl.pm_m = a.ws_m;
+        pl.sl.pm_l = a.ws_l;
+        pl.sl.pm_acc = a.ws_acc;
+    }
     return PAGED_KV_OK;
 }
 
@@ -1079,12 +1117,20 @@ void launch_partition_b(const Plan& pl) {
 template <int D, int OUT>
 void launch_reduce_t(const Plan& pl, int num_seqs) {
     // about 16 partitions per thread group, at most reduce_groups_max<D>() groups
-    const int groups = std::max(1, std::min(reduce_groups_max<D>(), (pl.a.max_parts + 15) / 16));
-    attn_reduce_kernel<D, OUT><<<dim3((unsigned)pl.a.num_q_heads, (unsigned)num_seqs),
-                                 dim3(D * groups), 0,
-                                 pl.stream>>>(pl.a.out, pl.a.context_lens, pl.a.num_q_heads,
-                                              pl.a.max_context_len, pl.a.partition_tokens,
-                                              pl.a.max_parts, pl.a.ws_m, pl.a.ws_l, pl.a.ws_acc);
+    const int rows = pl.pm ? 2 * pl.a.max_parts : pl.a.max_parts;
+    const int groups = std::max(1, std::min(reduce_groups_max<D>(), (rows + 15) / 16));
+    if (pl.pm)
+        attn_reduce_kernel<D, OUT, true><<<dim3((unsigned)pl.a.num_q_heads, (unsigned)num_seqs),
+                                           dim3(D * groups), 0,
+                                           pl.stream>>>(pl.a.out, pl.a.context_lens, pl.a.num_q_heads,
+                                                        pl.a.max_context_len, pl.a.partition_tokens,
+                                                        pl.a.max_parts, pl.a.ws_m, pl.a.ws_l, pl.a.ws_acc);
+    else
+        attn_reduce_kernel<D, OUT, false><<<dim3((unsigned)pl.a.num_q_heads, (unsigned)num_seqs),
+                                            dim3(D * groups), 0,
+                                            pl.stream>>>(pl.a.out, pl.a.context_lens, pl.a.num_q_heads,
+                                                         pl.a.max_context_len, pl.a.partition_tokens,
+                                                         pl.a.max_parts, pl.a.ws_m, pl.a.ws_l, pl.a.ws_acc);
 }
 
 template <int D>
@@ -1106,7 +1152,7 @@ paged_kv_status launch_status(const char* what) {
 }
 
 void launch_partition(const Plan& pl, void* stream) {
-    if (pl.streamk) pkv::launch_streamk_partition(pl.sl, pl.sp, stream);
+    if (pl.streamk || pl.pm) pkv::launch_streamk_partition(pl.sl, pl.sp, stream);
     else if (pl.head_dim == 64) launch_partition_b<64>(pl);
     else if (pl.head_dim == 256) launch_partition_b<256>(pl);
     else launch_partition_b<128>(pl);
@@ -1188,8 +1234,15 @@ size_t paged_attention_workspace_bytes(const paged_kv_pool_desc* desc, int32_t n
     }
     if (partition_tokens == 0) partition_tokens = pkv::kDefaultPartitionTokens;
     const int64_t max_parts = (max_context_len + (int64_t)partition_tokens - 1) / partition_tokens;
+    bool pm = use_pm(desc, num_seqs, num_q_heads, max_parts);
+    if (pm) {
+        bool ok = false;
+        pkv::stream_plan(num_seqs, num_q_heads, desc->num_kv_heads, desc->dtype, desc->head_dim,
+                         max_context_len, &ok);
+        pm = ok;
+    }
     return workspace_for(counter_bytes(desc, num_seqs, num_q_heads), num_seqs, num_q_heads,
-                         desc->head_dim, max_parts);
+                         desc->head_dim, max_parts, pm);
 }
 
 paged_kv_status paged_attention_partition(const paged_kv_pool_desc* desc, void* out,
@@ -1273,7 +1326,7 @@ paged_kv_status paged_attention_decode_append(const paged_kv_pool_desc* desc, vo
         pkv::set_error("new_k and new_v must be 16-byte aligned");
         return PAGED_KV_ERR_INVALID_ARG;
     }
-    if (pl.streamk || !pl.mfma) {
+    if (pl.streamk || pl.pm || !pl.mfma) {
         // schedules without a fused kernel: the cache write, then the attention
         const int64_t row = (int64_t)desc->num_kv_heads * desc->head_dim;
         st = reshape_and_cache(desc, new_k, new_v, row, row, k_pool, v_pool, slot_mapping, num_seqs, stream);

@@ -59,6 +59,12 @@ struct StreamArgs {
     int32_t waves;           // W
     int32_t weight_odd;      // slice weight of a wave of an odd workgroup (even: kWeightEven)
     float scale_log2;
+    // partition states (attn_mfma_streamk<..., true>): see pkv::StreamLaunch
+    int32_t pm_tiles;
+    int32_t pm_max_parts;
+    float* pm_m;
+    float* pm_l;
+    float* pm_acc;
 };
 
 __device__ __forceinline__ int tiles_of(int ctx, int max_ctx) {
@@ -363,7 +369,15 @@ __device__ void nan_invalid_sequences(const StreamArgs& a, const int* s_pref) {
 // is the fixed-partition MFMA kernel's: S^T = K.Q^T with 16x16x32 MFMAs, lazy-rescaled
 // base-2 softmax, O^T += V^T.P^T with P split into 16-bit head + remainder.
 // ---------------------------------------------------------------------------------
-template <int D, int DT, int OUT_DT, int BS>
+// Floats of LDS per wave that hold finished partition pieces (PM): 30 KiB (block size 1,
+// whose tiles also pass through LDS: 8 KiB).
+template <int BS>
+constexpr int kPmWaveFloats() { return BS == 1 ? 2048 : 7680; }
+
+// PM: partition states instead of outputs (pkv::StreamLaunch::pm_tiles).  Slices are then
+// at least two partitions long (fewer waves take part when the batch is small), so a
+// partition is cut at most once: into the piece that holds its first tile and the rest.
+template <int D, int DT, int OUT_DT, int BS, bool PM>
 __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(mfma_waves_per_simd<D, true>())))
 void attn_mfma_streamk(StreamArgs a) {
     constexpr int KI = D / 32;
@@ -376,6 +390,7 @@ void attn_mfma_streamk(StreamArgs a) {
     using vbuf = typename std::conditional<BS == 1, i32x4[KI], i32x2[MT]>::type;
     __shared__ uint16_t s_vt[BS == 1 ? kWaves * kTile * LDW : 1];
     __shared__ uint16_t s_kt[BS == 1 ? kWaves * kTile * LDW : 1];
+    __shared__ __attribute__((aligned(16))) float s_pm[PM ? kWaves * kPmWaveFloats<BS>() : 4];
 
     extern __shared__ int s_pref[];
     const int tiles_per_unit = build_prefix(a, s_pref);
@@ -385,7 +400,15 @@ void attn_mfma_streamk(StreamArgs a) {
     if (j >= a.waves) return;
     const int64_t T = (int64_t)a.units * tiles_per_unit;
     int64_t t0, t1;
-    wave_slice(a, T, j, t0, t1);
+    if constexpr (PM) {
+        const int W = (int)max<int64_t>(1, min<int64_t>(a.waves, T / (2 * a.pm_tiles)));
+        if (j >= W) return;
+        const SliceMap sm{T, W, (int64_t)a.weight_odd};
+        t0 = sm.start(j);
+        t1 = sm.start(j + 1);
+    } else {
+        wave_slice(a, T, j, t0, t1);
+    }
     if (t0 >= t1) return;
     const int n = (int)(t1 - t0);
     const int gq = lane & 15, quad = lane >> 4;
@@ -465,8 +488,83 @@ void attn_mfma_streamk(StreamArgs a) {
     for (int mt = 0; mt < MT; ++mt) acc[mt] = (f32x4){0.f, 0.f, 0.f, 0.f};
     float m = kNegInf, lsum = 0.f;
     bool unit_bad = false;
-    bool first_here = cc.it == 0;
+    bool first_here = PM ? cc.it % a.pm_tiles == 0 : cc.it == 0;
     Pending pend;
+
+    // PM: finished pieces wait in the wave's LDS region (G x D values, then G maxima, G
+    // sums, the first row and a flags word) and go to memory together at the end of the
+    // slice, so that no store sits between a tile's loads and the wait for them (stores
+    // every partition measured 0.62 of peak against 0.77 without).  A slice with more
+    // pieces than the region holds stores the rest directly.
+    const int pm_piece = (G * (D + 2) + 2 + 3) & ~3;         // floats per piece (16-byte aligned)
+    const int pm_cap = PM ? kPmWaveFloats<BS>() / pm_piece : 0;
+    float* pm_lds = s_pm + (threadIdx.x >> 6) * kPmWaveFloats<BS>();
+    int pm_count = 0;
+    const int64_t pm_stride = 2 * (int64_t)a.pm_max_parts;  // rows between query heads
+    auto capture = [&](const Cursor& c) __attribute__((always_inline)) {
+        const float lw = sum_across_quads(lsum);
+        const int p = c.it / a.pm_tiles;
+        const bool has_end = (c.it + 1) % a.pm_tiles == 0 || c.it == c.nt - 1;
+        // row of query head 0 of the unit; head h adds h * pm_stride
+        const int64_t row0 = ((int64_t)c.s * a.num_q_heads + c.u * G) * pm_stride + 2 * p;
+        const int kk = first_here ? 0 : 1;
+        const bool mark = first_here && has_end;            // not cut: the second row is empty
+        if (pm_count < pm_cap) {
+            float* pc = pm_lds + pm_count * pm_piece;
+            if (gq < G) {
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt)
+                    *reinterpret_cast<f32x4*>(pc + gq * D + 16 * mt + 4 * quad) =
+                        unit_bad ? (f32x4){NAN, NAN, NAN, NAN} : acc[mt];
+                if (quad == 0) {
+                    pc[G * D + gq] = unit_bad ? NAN : m;
+                    pc[G * D + G + gq] = unit_bad ? NAN : lw;
+                }
+            }
+            if (lane == 0) {
+                reinterpret_cast<int*>(pc)[G * (D + 2)] = (int)(row0 + kk);   // (fits: checked on the host)
+                reinterpret_cast<int*>(pc)[G * (D + 2) + 1] = mark ? 1 : 0;
+            }
+            ++pm_count;
+        } else if (gq < G) {
+            const int64_t row = row0 + gq * pm_stride + kk;
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+                *reinterpret_cast<f32x4*>(a.pm_acc + row * D + 16 * mt + 4 * quad) =
+                    unit_bad ? (f32x4){NAN, NAN, NAN, NAN} : acc[mt];
+            if (quad == 0) {
+                a.pm_m[row] = unit_bad ? NAN : m;
+                a.pm_l[row] = unit_bad ? NAN : lw;
+                if (mark) a.pm_m[row + 1] = kNegInf;
+            }
+        }
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) acc[mt] = (f32x4){0.f, 0.f, 0.f, 0.f};
+        m = kNegInf;
+        lsum = 0.f;
+        unit_bad = false;
+        first_here = true;
+    };
+    // the pieces held in LDS to memory: per piece, the G x D values 4 to a lane, then the
+    // maxima and sums (lane h < G), and the empty second rows of partitions not cut
+    auto store_pieces = [&]() __attribute__((always_inline)) {
+        for (int k = 0; k < pm_count; ++k) {
+            const float* pc = pm_lds + k * pm_piece;
+            const int64_t row_h0 = uni(reinterpret_cast<const int*>(pc)[G * (D + 2)]);
+            const int mark = uni(reinterpret_cast<const int*>(pc)[G * (D + 2) + 1]);
+            for (int i = 4 * lane; i < G * D; i += 256) {
+                const int h = i / D, d = i - h * D;
+                *reinterpret_cast<f32x4*>(a.pm_acc + (row_h0 + h * pm_stride) * D + d) =
+                    *reinterpret_cast<const f32x4*>(pc + i);
+            }
+            if (lane < G) {
+                const int64_t row = row_h0 + lane * pm_stride;
+                a.pm_m[row] = pc[G * D + lane];
+                a.pm_l[row] = pc[G * D + G + lane];
+                if (mark) a.pm_m[row + 1] = kNegInf;
+            }
+        }
+    };
 
     // Write the finished (or slice-cut) unit of cursor c, then reset the state.
     auto finish = [&](const Cursor& c) __attribute__((always_inline)) {
@@ -638,13 +736,17 @@ void attn_mfma_streamk(StreamArgs a) {
     // compute the tile of cursor cc from slot sl, then move cc on (if a tile follows)
     auto consume = [&](int sl, bool has_next) __attribute__((always_inline)) {
         Cursor nc = cc;
-        bool next_unit = false;
+        bool next_unit = false, flush = false;
         if (has_next) {
             advance(a, nc);
             next_unit = nc.s != cc.s || nc.u != cc.u;
+            flush = next_unit || (PM && nc.it % a.pm_tiles == 0);
         }
         compute(kbuf[sl], vbufs[sl], bbuf[sl], next_unit, nc);
-        if (next_unit) finish(cc);
+        if (flush) {
+            if constexpr (PM) capture(cc);
+            else finish(cc);
+        }
         cc = nc;
     };
 
@@ -692,9 +794,14 @@ void attn_mfma_streamk(StreamArgs a) {
             }
         }
     }
-    finish(cc);
+    if constexpr (PM) {
+        capture(cc);
+        store_pieces();
+    } else {
+        finish(cc);
+    }
     __builtin_amdgcn_s_setprio(0);
-    publish_pieces<D, OUT_DT, 8, (D == 64 ? 8 : 4)>(a, s_pref, pend, T, lane);
+    if constexpr (!PM) publish_pieces<D, OUT_DT, 8, (D == 64 ? 8 : 4)>(a, s_pref, pend, T, lane);
 }
 
 // ---------------------------------------------------------------------------------
@@ -982,6 +1089,11 @@ StreamArgs make_args(const pkv::StreamLaunch& L, const pkv::StreamPlan& P) {
     a.weight_odd = (L.head_dim >= 128 && L.block_size >= 16 && pkv::device_shape().mi355x_spx)
                        ? 58 : (int32_t)kWeightEven;
     a.scale_log2 = L.scale * kLog2e;
+    a.pm_tiles = L.pm_tiles;
+    a.pm_max_parts = L.pm_max_parts;
+    a.pm_m = L.pm_m;
+    a.pm_l = L.pm_l;
+    a.pm_acc = L.pm_acc;
     return a;
 }
 
@@ -992,7 +1104,8 @@ void launch_part_t(const StreamArgs& a, bool mfma, hipStream_t st) {
     if constexpr (DT == DT_F32) {
         attn_valu_streamk<D, DT, OUT, BS><<<grid, dim3(kWaves * 64), lds, st>>>(a);
     } else {
-        if (mfma) attn_mfma_streamk<D, DT, OUT, BS><<<grid, dim3(kWaves * 64), lds, st>>>(a);
+        if (mfma && a.pm_tiles > 0) attn_mfma_streamk<D, DT, OUT, BS, true><<<grid, dim3(kWaves * 64), lds, st>>>(a);
+        else if (mfma) attn_mfma_streamk<D, DT, OUT, BS, false><<<grid, dim3(kWaves * 64), lds, st>>>(a);
         else attn_valu_streamk<D, DT, OUT, BS><<<grid, dim3(kWaves * 64), lds, st>>>(a);
     }
 }
