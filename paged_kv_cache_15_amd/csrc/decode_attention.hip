@@ -167,8 +167,14 @@ void attn_mfma_kernel(PartitionArgs a) {
     constexpr int LDW = D + 8;    // block size 1: LDS row of one token's values
     using kvec = typename std::conditional<DT == DT_BF16, bf16x8, f16x8>::type;
     using vbuf = typename std::conditional<BS == 1, i32x4[KI], i32x2[MT]>::type;
-    __shared__ uint16_t s_vt[BS == 1 ? NW * kTile * LDW : 1];
-    __shared__ uint16_t s_kt[BS == 1 ? NW * kTile * LDW : 1];
+    // Block size 1: each wave's K and V rows during the tile loop, then (all waves past
+    // it) the wave merge's values; other block sizes keep the merge values apart.
+    __shared__ __attribute__((aligned(16))) uint16_t s_rows[BS == 1 ? 2 * NW * kTile * LDW : 1];
+    __shared__ __attribute__((aligned(16))) float s_merge[BS == 1 ? 4 : NW * 16 * (D + 4)];
+    static_assert(BS != 1 || 2 * NW * kTile * LDW * 2 >= NW * 16 * (D + 4) * 4, "merge fits the rows");
+    uint16_t* const s_vt = s_rows;
+    uint16_t* const s_kt = s_rows + NW * kTile * LDW;
+    float* const sm_acc = BS == 1 ? reinterpret_cast<float*>(s_rows) : s_merge;
 
     const int s = blockIdx.x / a.num_kv_heads, g = blockIdx.x - s * a.num_kv_heads;
     const int p = blockIdx.y;
@@ -406,55 +412,78 @@ void attn_mfma_kernel(PartitionArgs a) {
     }
 
     // ---- merge the four waves' states (fixed order) ----
+    // Each wave puts its row maxima, sums and raw values in LDS; after one barrier wave w
+    // folds value blocks w*MB .. w*MB + MB - 1 of every row over the waves in order (the
+    // first scaled, the rest by fused multiply-adds), so that the four waves share the
+    // fold and no wave waits on another's read-modify-write.
+    constexpr int MB = MT / NW;
+    static_assert(MT % NW == 0, "value blocks split evenly over the waves");
     __shared__ float sm_m[NW][16];
     __shared__ float sm_l[NW][16];
-    __shared__ float sm_acc[16][D + 4];
     const float lw = sum_across_quads(lsum);
     if (lane < 16) {
         sm_m[w][lane] = m;
         sm_l[w][lane] = lw;
     }
+    float* const my_rows = sm_acc + (w * 16 + gq) * (D + 4) + 4 * quad;
+    if constexpr (BS == 1) __syncthreads();   // every wave is past its K/V rows
+    if (gq < a.group) {
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) *reinterpret_cast<f32x4*>(my_rows + 16 * mt) = acc[mt];
+    }
     const bool any_bad = __syncthreads_or(bad_block);
-    float mmax = kNegInf;
+    // row gq over the waves: the common maximum, each wave's scale, the summed weights
+    float mw[NW], lwv[NW], fw[NW];
 #pragma unroll
-    for (int ww = 0; ww < NW; ++ww) mmax = fmaxf(mmax, sm_m[ww][gq]);
-    const float f = (m == kNegInf) ? 0.f : exp2_fast(m - mmax);
     for (int ww = 0; ww < NW; ++ww) {
-        if (ww == w && gq < a.group) {
+        mw[ww] = sm_m[ww][gq];
+        lwv[ww] = sm_l[ww][gq];
+    }
+    float mm = kNegInf;
 #pragma unroll
-            for (int mt = 0; mt < MT; ++mt) {
+    for (int ww = 0; ww < NW; ++ww) mm = fmaxf(mm, mw[ww]);
+    float l = 0.f;
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int d = 16 * mt + 4 * quad + r;
-                    const float v = acc[mt][r] * f;
-                    if (ww == 0) sm_acc[gq][d] = v;
-                    else sm_acc[gq][d] += v;
-                }
+    for (int ww = 0; ww < NW; ++ww) {
+        fw[ww] = mw[ww] == kNegInf ? 0.f : exp2_fast(mw[ww] - mm);
+        if (mw[ww] != kNegInf) l = fmaf(fw[ww], lwv[ww], l);
+    }
+    if (gq < a.group) {
+        const int h = g * a.group + gq;
+        const int64_t row = ((int64_t)s * a.num_q_heads + h) * a.max_parts + p;
+#pragma unroll
+        for (int j = 0; j < MB; ++j) {
+            const int d0 = 16 * (w * MB + j) + 4 * quad;
+            f32x4 v;
+#pragma unroll
+            for (int ww = 0; ww < NW; ++ww) {
+                const f32x4 x = *reinterpret_cast<const f32x4*>(sm_acc + (ww * 16 + gq) * (D + 4) + d0);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) v[r] = ww == 0 ? x[r] * fw[0] : fmaf(fw[ww], x[r], v[r]);
+            }
+            if (npart == 1) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    store_out<OUT_DT>(a.out, ((int64_t)s * a.num_q_heads + h) * D + d0 + r,
+                                      any_bad ? NAN : v[r] / l);
+            } else if (FUSE) {
+                // partial state for the merge below, possibly read on another XCD: stored
+                // through to the device-coherent level
+#pragma unroll
+                for (int r = 0; r < 4; ++r) put_coherent(a.ws_acc + row * D + d0 + r, any_bad ? NAN : v[r]);
+            } else {
+                if (any_bad) v = (f32x4){NAN, NAN, NAN, NAN};
+                *reinterpret_cast<f32x4*>(a.ws_acc + row * D + d0) = v;
             }
         }
-        __syncthreads();
-    }
-    for (int i = threadIdx.x; i < a.group * D; i += blockDim.x) {
-        const int hg = i / D, d = i - hg * D;
-        float mm = kNegInf;
-#pragma unroll
-        for (int ww = 0; ww < NW; ++ww) mm = fmaxf(mm, sm_m[ww][hg]);
-        float l = 0.f;
-#pragma unroll
-        for (int ww = 0; ww < NW; ++ww)
-            if (sm_m[ww][hg] != kNegInf) l += exp2_fast(sm_m[ww][hg] - mm) * sm_l[ww][hg];
-        if (FUSE && npart > 1) {
-            // partial state for the merge below, possibly read on another XCD: stored
-            // through to the device-coherent level
-            const int64_t row = ((int64_t)s * a.num_q_heads + g * a.group + hg) * a.max_parts + p;
-            put_coherent(a.ws_acc + row * D + d, any_bad ? NAN : sm_acc[hg][d]);
-            if (d == 0) {
+        if (npart > 1 && w == 0 && quad == 0) {
+            if (FUSE) {
                 put_coherent(a.ws_m + row, any_bad ? NAN : mm);
                 put_coherent(a.ws_l + row, any_bad ? NAN : l);
+            } else {
+                a.ws_m[row] = any_bad ? NAN : mm;
+                a.ws_l[row] = any_bad ? NAN : l;
             }
-        } else {
-            write_partition_result<D, OUT_DT>(a, s, g * a.group + hg, p, npart, d, mm, l,
-                                              sm_acc[hg][d], any_bad);
         }
     }
     if constexpr (FUSE) {
@@ -473,8 +502,9 @@ void attn_mfma_kernel(PartitionArgs a) {
             __syncthreads();
             if (s_old != npart - 1) return;
             __atomic_signal_fence(__ATOMIC_ACQUIRE);
-            // NO outputs per thread at a time, eight partitions per memory round trip
-            // (all their loads in flight together), folded in partition order.
+            // NO outputs per thread at a time, KB partitions per memory round trip (all
+            // their loads in flight together; four when there are no more, else eight),
+            // folded in partition order.
             constexpr int NO = 4;
             for (int i0 = threadIdx.x; i0 < a.group * D; i0 += NO * blockDim.x) {
                 float M[NO], l[NO], acc[NO];
@@ -490,26 +520,31 @@ void attn_mfma_kernel(PartitionArgs a) {
                     dd[o] = i % D;
                     row[o] = ((int64_t)s * a.num_q_heads + g * a.group + i / D) * a.max_parts;
                 }
-                for (int p0 = 0; p0 < npart; p0 += 8) {
-                    float mv[NO][8], lv[NO][8], av[NO][8];
+                auto fold = [&](auto kb) __attribute__((always_inline)) {
+                    constexpr int KB = decltype(kb)::value;
+                    for (int p0 = 0; p0 < npart; p0 += KB) {
+                        float mv[NO][KB], lv[NO][KB], av[NO][KB];
 #pragma unroll
-                    for (int o = 0; o < NO; ++o)
+                        for (int o = 0; o < NO; ++o)
 #pragma unroll
-                        for (int k = 0; k < 8; ++k) {   // past the last partition: re-read it
-                            const int64_t r = row[o] + min(p0 + k, npart - 1);
-                            mv[o][k] = get_coherent(a.ws_m + r);
-                            lv[o][k] = get_coherent(a.ws_l + r);
-                            av[o][k] = get_coherent(a.ws_acc + r * D + dd[o]);
-                        }
+                            for (int k = 0; k < KB; ++k) {   // past the last partition: re-read it
+                                const int64_t r = row[o] + min(p0 + k, npart - 1);
+                                mv[o][k] = get_coherent(a.ws_m + r);
+                                lv[o][k] = get_coherent(a.ws_l + r);
+                                av[o][k] = get_coherent(a.ws_acc + r * D + dd[o]);
+                            }
 #pragma unroll
-                    for (int o = 0; o < NO; ++o)
+                        for (int o = 0; o < NO; ++o)
 #pragma unroll
-                        for (int k = 0; k < 8; ++k) {
-                            if (p0 + k >= npart) break;
-                            bad[o] |= mv[o][k] != mv[o][k];
-                            lse_fold(M[o], l[o], acc[o], mv[o][k], lv[o][k], av[o][k]);
-                        }
-                }
+                            for (int k = 0; k < KB; ++k) {
+                                if (p0 + k >= npart) break;
+                                bad[o] |= mv[o][k] != mv[o][k];
+                                lse_fold(M[o], l[o], acc[o], mv[o][k], lv[o][k], av[o][k]);
+                            }
+                    }
+                };
+                if (npart <= 4) fold(std::integral_constant<int, 4>{});
+                else fold(std::integral_constant<int, 8>{});
 #pragma unroll
                 for (int o = 0; o < NO; ++o) {
                     const int i = i0 + o * (int)blockDim.x;
