@@ -148,8 +148,9 @@ __device__ __forceinline__ void write_new_token(const PartitionArgs& a, int s, i
     }
 }
 
-// Waves per workgroup (the fused decode step measured slower with 8: the per-workgroup
-// fixed costs grow, and the tile chain does not shrink in proportion).
+// Waves per workgroup.  Eight measured slower for the small-batch fused decode step:
+// its tile loop already moves the launch's K/V at the HBM rate (shorter per-wave chains
+// of tiles save nothing there), while the per-workgroup start and merge costs grow.
 template <bool FUSE, int D>
 constexpr int mfma_partition_waves() { return kWaves; }
 
