@@ -97,9 +97,10 @@ constexpr int valu_waves_per_simd() { return pkv::kernel_waves_per_simd(D, E, fa
 
 // Tiles in flight per wave in the stream-K MFMA kernel (ring of load buffers).  Two:
 // rings of 3 and 4 measured no faster at one wave per SIMD (the tiles in flight per CU
-// are not what limits the stream).
+// are not what limits the stream).  Three at head_dim 64 (4 KiB tiles, two waves per
+// SIMD).
 template <int D>
-constexpr int stream_depth() { return 2; }
+constexpr int stream_depth() { return D == 64 ? 3 : 2; }
 
 // Block size 1: every token of a tile sits in its own block.  Lane l gets the block of
 // token 16*it + (l & 15) of the table row (ids read through the scalar cache; tokens at
